@@ -1,0 +1,200 @@
+"""Pins of the placement / LRU-ring simulator: hand-worked traces (golden
+file), an independent list-based LRU model on random traces, calibration
+against a full sort, quota arithmetic, and the uniform-placement cold-hit rate
+under unbiased routing."""
+import os
+from collections import OrderedDict
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _run_golden(path):
+    sim = None
+    checked = 0
+    for raw in open(path):
+        line = raw.split("#", 1)[0].strip()
+        if not line:
+            continue
+        tok = line.split()
+        op, args = tok[0], [int(t) for t in tok[1:] if t.lstrip("-").isdigit()]
+        if op == "trace":
+            L, E, P, R = args
+            sim = oracle.Sim(L, E, P, R, slot_bytes=100)
+            sim.place_uniform()
+            name = tok[1]
+        elif op == "access":
+            sim.decode_layer(args[0], np.array([args[1]]))
+        elif op == "calibrate":
+            sim.calibrate(reset_counts=True)
+        elif op == "expect_stats":
+            st = sim.stats()
+            got = [st[k] for k in ("accesses", "pinned_hits", "cold_hits", "ring_hits", "fills",
+                                   "evictions")]
+            assert got == args, (name, got, args)
+            assert st["h2d_bytes"] == 100 * st["fills"]
+            checked += 1
+        elif op == "expect_event":
+            ev = sim.events()
+            seq, layer, expert, slot, victim = args
+            e = ev[seq - 1]
+            assert (int(e["seq"]), int(e["layer"]), int(e["expert"]), int(e["slot"]),
+                    int(e["victim"])) == (seq, layer, expert, slot, victim), (name, e)
+            checked += 1
+        elif op == "expect_slot_of":
+            slot_of = sim.placement()[0]
+            assert list(slot_of[args[0]]) == args[1:], (name, slot_of)
+            checked += 1
+        elif op == "expect_ring":
+            owner = sim.placement()[1]
+            assert list(owner) == args, (name, owner)
+            checked += 1
+        elif op == "end":
+            sim = None
+    return checked
+
+
+def test_golden_traces(golden_dir):
+    assert _run_golden(os.path.join(golden_dir, "placement_traces.txt")) == 19
+
+
+def test_quota_sums_to_budget():
+    for L, P in [(40, 6144), (40, 3072), (40, 10240), (40, 0), (3, 7), (40, 39)]:
+        q = [oracle.quota(L, P, l) for l in range(L)]
+        assert sum(q) == P and max(q) - min(q) <= 1
+        assert q == sorted(q, reverse=True)
+
+
+class ListLRU:
+    """Independent model: an ordered dict of ring residents, least recent
+    first; free ring slots handed out lowest first."""
+
+    def __init__(self, L, E, P, R):
+        self.L, self.E, self.P, self.R = L, E, P, R
+        self.pinned = {}
+        nxt = 0
+        for l in range(L):
+            q = P // L + (1 if l < P % L else 0)
+            for e in range(q):
+                self.pinned[(l, e)] = nxt
+                nxt += 1
+        self.ring = OrderedDict()  # key -> ring slot index
+        self.stats = dict(accesses=0, pinned_hits=0, cold_hits=0, ring_hits=0, fills=0,
+                          evictions=0)
+        self.events = []
+
+    def access(self, l, e):
+        s = self.stats
+        s["accesses"] += 1
+        if (l, e) in self.pinned:
+            s["pinned_hits"] += 1
+            return
+        s["cold_hits"] += 1
+        key = l * self.E + e
+        if key in self.ring:
+            s["ring_hits"] += 1
+            self.ring.move_to_end(key)
+            return
+        s["fills"] += 1
+        if len(self.ring) < self.R:
+            used = set(self.ring.values())
+            slot = min(set(range(self.R)) - used)
+            victim = -1
+        else:
+            victim, slot = self.ring.popitem(last=False)
+            s["evictions"] += 1
+        self.ring[key] = slot
+        self.events.append((len(self.events) + 1, l, e, self.P + slot, victim))
+
+
+@pytest.mark.parametrize("L,E,P,R,K", [(4, 16, 24, 4, 2), (3, 32, 40, 8, 8), (2, 8, 0, 8, 4),
+                                       (40, 256, 6144, 32, 8)])
+def test_simulator_matches_list_lru_on_random_traces(L, E, P, R, K):
+    rng = np.random.default_rng(L * 1000 + E + P + R)
+    n_tokens = 200_000 // (L * K) + 1
+    sim = oracle.Sim(L, E, P, R, slot_bytes=1)
+    sim.place_uniform()
+    ref = ListLRU(L, E, P, R)
+    # Zipf-ish routing so that ring hits, fills and evictions all occur
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    for t in range(n_tokens):
+        idx = np.stack([rng.choice(E, size=K, replace=False, p=p) for _ in range(L)]).astype(np.int32)
+        sim.decode_token(idx)
+        for l in range(L):
+            for e in idx[l]:
+                ref.access(l, int(e))
+    st = sim.stats()
+    for k, v in ref.stats.items():
+        assert st[k] == v, (k, st[k], v)
+    ev = sim.events()
+    got = [(int(e["seq"]), int(e["layer"]), int(e["expert"]), int(e["slot"]), int(e["victim"]))
+           for e in ev]
+    assert got == ref.events
+    assert st["fills"] > 0 and (P == 0 or st["pinned_hits"] > 0)
+    if R < E * L - P:
+        assert st["evictions"] > 0 and st["ring_hits"] > 0
+
+
+def test_calibration_matches_full_sort_and_keeps_slots():
+    rng = np.random.default_rng(12)
+    L, E, P, R = 5, 32, 70, 6
+    sim = oracle.Sim(L, E, P, R, slot_bytes=1)
+    sim.place_uniform()
+    for rnd in range(3):
+        before = sim.placement()[0].copy()
+        for _ in range(300):
+            sim.decode_token(np.stack([rng.choice(E, 3, replace=False, p=None) for _ in range(L)])
+                             .astype(np.int32))
+        counts = sim.placement()[3].copy()
+        sim.calibrate(reset_counts=True)
+        slot_of, owner, stamp, counts_after = sim.placement()
+        assert not counts_after.any()
+        pinned_slots = slot_of[slot_of >= 0]
+        assert sorted(pinned_slots.tolist()) == list(range(P))
+        for l in range(L):
+            q = oracle.quota(L, P, l)
+            top = np.lexsort((np.arange(E), -counts[l]))[:q]
+            assert set(np.flatnonzero(slot_of[l] >= 0)) == set(top.tolist())
+            kept = (before[l] >= 0) & (slot_of[l] >= 0)
+            assert np.array_equal(before[l][kept], slot_of[l][kept])
+        new = (before < 0) & (slot_of >= 0)
+        freed = np.sort(before[(before >= 0) & (slot_of < 0)])
+        assert np.array_equal(slot_of[new], freed)  # (layer, expert) order gets ascending slots
+        for r in range(R):  # no ring entry of a pinned expert survives
+            if owner[r] >= 0:
+                assert slot_of.ravel()[owner[r]] < 0
+
+
+def test_prefill_accesses_distinct_experts_ascending():
+    sim = oracle.Sim(1, 8, 2, 3, slot_bytes=1)
+    sim.place_uniform()  # pins 0, 1
+    idx = np.array([[5, 1], [3, 5], [7, 3], [0, 6]], dtype=np.int32)
+    sim.prefill_layer(0, idx)
+    st = sim.stats()
+    assert st["accesses"] == 6  # distinct {0,1,3,5,6,7}
+    assert st["pinned_hits"] == 2 and st["fills"] == 4 and st["evictions"] == 1
+    ev = sim.events()
+    assert [int(e["expert"]) for e in ev] == [3, 5, 6, 7]
+    assert int(ev[3]["victim"]) == 3  # 7 evicts the least recent, 3
+    counts = sim.placement()[3]
+    assert counts[0].tolist() == [1, 1, 0, 2, 0, 2, 1, 1]
+
+
+def test_uniform_placement_cold_rate_under_unbiased_routing():
+    """Unbiased routing with a uniform 60% pinned set: cold-hit rate = 1 - 0.6
+    up to sampling error."""
+    rng = np.random.default_rng(13)
+    L, E, K = 4, 256, 8
+    P = int(0.6 * L * E)
+    sim = oracle.Sim(L, E, P, 32, slot_bytes=1)
+    sim.place_uniform()
+    for _ in range(2000):
+        sim.decode_token(np.stack([rng.choice(E, K, replace=False) for _ in range(L)])
+                         .astype(np.int32))
+    st = sim.stats()
+    rate = st["cold_hits"] / st["accesses"]
+    q = sum(oracle.quota(L, P, l) for l in range(L)) / (L * E)
+    assert abs(rate - (1 - q)) < 0.01
