@@ -1,0 +1,224 @@
+/*
+ * moe_spark — resident expert caching for MoE decode on one MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; "device" pointers are HIP device
+ * memory (e.g. a torch tensor's data_ptr on ROCm), "host" pointers are
+ * ordinary CPU memory.  Streams are hipStream_t passed as void*.
+ *
+ * What the library implements, and where it is described:
+ *  "Luce Spark runs 35B MoE models on 16GB GPU without speed loss"
+ *  (theneuralfeed.com):
+ *   - opening paragraph: each token is routed to about 8 of 256 experts, so
+ *     only a fraction of the experts needs to sit in GPU memory;
+ *   - paragraph "The key components":
+ *     (1) calibrated placement — per-expert routing counts are accumulated
+ *         and the most-used set is pinned in GPU memory;
+ *     (2) a bounded asynchronous cache — a fixed ring of spare GPU slots; on
+ *         a cold expert the weights are copied asynchronously from pinned host
+ *         memory into a spare slot, evicting the least recently used entry,
+ *         which costs throughput but does not stall;
+ *     (3) the whole token runs as one graph instead of one graph per layer;
+ *     and full residency is bit-identical to all-GPU execution (here: outputs
+ *     are bit-identical at every residency).
+ *  "Luce Spark: Shattering the VRAM Ceiling for 35B MoEs on 16GB GPUs Without
+ *  the Offload Tax" (baguaai.com), "Event Core" and "Actionable Advice": hot
+ *  experts live in GPU memory, the long tail in system RAM, and the link
+ *  between them becomes the bottleneck.
+ *
+ * Ownership: the context owns the HBM slot arena ((P + R) expert slots), the
+ * pinned host arena (every expert, copied in by moe_spark_set_expert), all
+ * device tables, the token graphs and the fill-agent thread.  The caller owns
+ * activation buffers and the streams it passes in.
+ *
+ * Errors: every call returns a moe_spark_status; moe_spark_last_error()
+ * describes the last failure.  Calls that launch work are asynchronous on the
+ * compute stream; device-side faults of the method (a fill that never
+ * arrives) surface at moe_spark_synchronize().
+ */
+#ifndef MOE_SPARK_H
+#define MOE_SPARK_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_SPARK_OK = 0,
+    MOE_SPARK_E_INVALID = 1, /* bad argument or shape */
+    MOE_SPARK_E_NOMEM = 2,   /* an arena could not be allocated */
+    MOE_SPARK_E_HIP = 3,     /* a HIP call failed, or a device-side error */
+    MOE_SPARK_E_STATE = 4    /* call out of order (e.g. forward before all weights set) */
+} moe_spark_status;
+
+/* Expert weight formats (router weights are always fp32). */
+typedef enum {
+    MOE_SPARK_W_F32 = 0,  /* fp32, row-major [out][in] */
+    MOE_SPARK_W_Q4_0 = 1  /* GGUF Q4_0: per row, blocks of 32 along `in`, 18 bytes each:
+                             fp16 scale s (little endian), 16 bytes of codes; weight j in
+                             the low nibble of byte j, weight j+16 in the high nibble;
+                             value (q - 8) * s */
+} moe_spark_wfmt;
+
+/* Flags of moe_spark_layer_forward. */
+#define MOE_SPARK_PRE_RMSNORM 1u /* u = x / sqrt(mean(x^2) + eps) before router and experts */
+#define MOE_SPARK_RESIDUAL 2u    /* y = x + MoE(u) instead of y = MoE(u) */
+
+typedef struct {
+    int32_t n_layers;     /* L */
+    int32_t d_model;      /* d: multiple of 256, <= 8192 */
+    int32_t n_experts;    /* E: <= 1024 */
+    int32_t top_k;        /* K: 1 <= K <= min(E, 16) */
+    int32_t d_ff;         /* f: multiple of 128, <= 4096 */
+    int32_t wfmt;         /* moe_spark_wfmt */
+    float rms_eps;        /* RMSNorm epsilon (1e-6) */
+    int32_t n_bias_rows;  /* router-bias rows per layer (0 = no bias) */
+    int64_t resident_cap; /* P: pinned slots, global over layers, 0 <= P <= L*E */
+    int32_t ring_slots;   /* R: spare ring slots; R >= K unless P == L*E; R <= 1024 */
+    int32_t max_tokens;   /* largest n_tokens of moe_spark_prefill (0: no prefill) */
+    int64_t event_cap;    /* capacity of the fill-event log (0: default 1<<20) */
+} moe_spark_config;
+
+typedef struct {
+    int64_t accesses;      /* expert accesses (decode: per token, layer, rank;
+                              prefill: per layer, distinct expert) */
+    int64_t pinned_hits;   /* accesses served by a pinned slot */
+    int64_t cold_hits;     /* accesses to a non-pinned expert (= ring_hits + fills) */
+    int64_t ring_hits;     /* cold hits already in the ring */
+    int64_t fills;         /* cold hits copied host -> ring slot */
+    int64_t evictions;     /* fills that evicted a ring entry */
+    int64_t h2d_bytes;     /* fills * slot bytes */
+    int64_t fill_ns_sum;   /* host-observed latency of fills: request seen -> data ready */
+    int64_t fill_ns_max;
+    int64_t calib_uploads; /* experts copied into pinned slots by calibration */
+    int64_t tokens;        /* tokens run by the decode graph */
+} moe_spark_stats;
+
+typedef struct {
+    int64_t seq;     /* 1-based fill number */
+    int32_t layer, expert;
+    int32_t slot;    /* global slot id: pinned 0..P-1, ring P..P+R-1 */
+    int32_t kind;    /* MOE_SPARK_EV_FILL */
+    int32_t victim;  /* evicted layer*E+expert, or -1 (slot was empty) */
+    int32_t pad;
+} moe_spark_event;
+
+#define MOE_SPARK_EV_FILL 2
+
+typedef struct moe_spark_ctx moe_spark_ctx;
+
+/* Create a context: allocates the HBM slot arena ((P+R) slots), the pinned
+ * host arena (L*E slots) and all tables, and starts the fill agent.
+ * compute_stream / copy_stream: hipStream_t, or NULL to let the context make
+ * its own.  Errors: E_INVALID (bad config), E_NOMEM (arena), E_HIP. */
+moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_stream,
+                                  void* copy_stream, moe_spark_ctx** out);
+
+/* Stop the fill agent, free everything.  NULL is allowed. */
+void moe_spark_destroy(moe_spark_ctx* ctx);
+
+/* Text of the last error on this context (never NULL; "" when none). */
+const char* moe_spark_last_error(const moe_spark_ctx* ctx);
+
+/* Bytes of one expert slot (gate + up + down) in the configured format. */
+int64_t moe_spark_slot_bytes(const moe_spark_ctx* ctx);
+
+/* Router of one layer, host memory: w [E][d] fp32; bias [n_bias_rows][E]
+ * fp32 (added to the logits before top-k and softmax), or NULL when
+ * n_bias_rows == 0.  Copied; synchronous. */
+moe_spark_status moe_spark_set_router(moe_spark_ctx* ctx, int32_t layer, const float* w,
+                                      const float* bias);
+
+/* One expert, host memory: gate, up [f][d]; down [d][f]; in the configured
+ * format (row-major fp32, or GGUF Q4_0 blocks along the input dimension).
+ * Repacked into the pinned host arena; the caller may free its buffers.
+ * If the expert sits in a pinned slot its slot is refreshed. */
+moe_spark_status moe_spark_set_expert(moe_spark_ctx* ctx, int32_t layer, int32_t expert,
+                                      const void* gate, const void* up, const void* down);
+
+/* n experts with flat ids first .. first+n-1 (id = layer*E + expert) from one
+ * host buffer, each expert gate | up | down back to back (same formats as
+ * moe_spark_set_expert).  Repacks on host threads. */
+moe_spark_status moe_spark_set_experts(moe_spark_ctx* ctx, int64_t first, int64_t n,
+                                       const void* blob);
+
+/* Initial placement: layer l pins experts 0..q_l-1, q_l = floor(P/L) + [l < P mod L];
+ * pinned slots 0..P-1 in (layer, expert) order; the ring is emptied.
+ * Uploads the pinned experts; synchronous.  E_STATE before all weights are set. */
+moe_spark_status moe_spark_place_uniform(moe_spark_ctx* ctx);
+
+/* Calibrated placement: each layer pins its q_l most-counted experts (count
+ * descending, expert ascending).  Experts that stay keep their slot; freed
+ * slots (ascending) go to newly pinned experts in (layer, expert) order; a
+ * newly pinned expert's ring entry is emptied.  reset_counts != 0 zeroes the
+ * counts afterwards.  Synchronises both streams (call between tokens). */
+moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts);
+
+/* One MoE layer for n_tokens tokens, each run as a separate batch-1 decode
+ * step in order (route, then experts, then combine).  Device pointers:
+ * x [T][d] fp32 input, y [T][d] fp32 output (y may equal x),
+ * bias_row [T] int32 row of the router bias per token (NULL: row 0),
+ * topk_out [T][K] int32 and gates_out [T][K] fp32 (either may be NULL).
+ * flags: MOE_SPARK_PRE_RMSNORM | MOE_SPARK_RESIDUAL.  Counts, placement and
+ * stats are updated exactly as in a decode step of that layer. */
+moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, const float* x,
+                                         float* y, int32_t n_tokens, const int32_t* bias_row,
+                                         uint32_t flags, int32_t* topk_out, float* gates_out);
+
+/* Decode n_tokens independent tokens through all L layers, one graph launch
+ * per token: x_{l+1} = x_l + MoE_l(RMSNorm(x_l)).  x [T][d] fp32 device,
+ * updated in place; bias_row [T] int32 device or NULL.  The graph for a given
+ * (x, bias_row) pair is built once and replayed. */
+moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens,
+                                  const int32_t* bias_row);
+
+/* moe_spark_decode with n_tokens = 1. */
+moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int32_t* bias_row);
+
+/* Batched prefill of n_tokens (<= max_tokens) through all L layers: per layer
+ * RMSNorm, router, top-k, grouping by expert, and a grouped expert GEMM in
+ * bf16 on the matrix cores with fp32 accumulation; the layer's distinct
+ * experts are accessed once each in ascending id, non-pinned ones streamed
+ * through the ring in chunks of at most R.  x [T][d] fp32 device, in place;
+ * bias_row [T] int32 device or NULL.  Synchronises once per layer. */
+moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_tokens,
+                                   const int32_t* bias_row);
+
+/* Trace buffers (device, or NULL to stop tracing) filled by decode,
+ * token_forward and prefill: x_layers [cap][L][d] fp32 (input of each layer),
+ * topk [cap][L][K] int32, gates [cap][L][K] fp32; token index counts from 0
+ * at this call; tokens past cap are not traced.  layer_forward traces into
+ * the same buffers at [token][layer]. */
+moe_spark_status moe_spark_set_trace(moe_spark_ctx* ctx, float* x_layers, int32_t* topk,
+                                     float* gates, int64_t cap_tokens);
+
+moe_spark_status moe_spark_get_stats(moe_spark_ctx* ctx, moe_spark_stats* out);
+moe_spark_status moe_spark_reset_stats(moe_spark_ctx* ctx);
+
+/* Host outputs (each may be NULL): slot_of [L][E] (pinned slot or -1),
+ * ring_owner [R] (layer*E+expert or -1), ring_stamp [R] (LRU clock),
+ * counts [L][E]. */
+moe_spark_status moe_spark_get_placement(moe_spark_ctx* ctx, int32_t* slot_of,
+                                         int32_t* ring_owner, int64_t* ring_stamp,
+                                         int64_t* counts);
+
+/* Copy up to cap fill events (oldest first) to host memory; *n_total gets
+ * the number logged (events past event_cap are counted, not stored). */
+moe_spark_status moe_spark_get_events(moe_spark_ctx* ctx, moe_spark_event* out, int64_t cap,
+                                      int64_t* n_total);
+
+/* Wait for all work of the context; report device-side errors. */
+moe_spark_status moe_spark_synchronize(moe_spark_ctx* ctx);
+
+/* Time the expert kernels in isolation: replays the gate/up and down kernels
+ * of every layer with the last decoded token's selections, round-robin over
+ * layers, `iters` passes, bracketed by HIP events on the compute stream.
+ * Outputs microseconds per launch.  Writes only context scratch buffers. */
+moe_spark_status moe_spark_time_expert_kernels(moe_spark_ctx* ctx, int32_t iters,
+                                               float* us_gateup, float* us_down,
+                                               float* us_route);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,134 @@
+// Internal definitions shared by the host runtime and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_spark.h"
+
+namespace moe {
+
+constexpr int kMaxK = 16;        // largest top-k
+constexpr int kMaxE = 1024;      // largest expert count
+constexpr int kMaxR = 1024;      // largest ring
+constexpr int kQ4MaxK = 8;       // Q4_0 down kernel covers up to 8 experts per pass
+constexpr uint32_t kFifoCap = 4096;
+
+// Q4_0 target shape of the repacked GEMV kernels.
+constexpr int kQD = 2048;        // d
+constexpr int kQF = 512;         // f
+constexpr int kQNBD = kQD / 32;  // 64 blocks along d (one per lane)
+constexpr int kQNBF = kQF / 32;  // 16 blocks along f
+// Gate/up: a work-group owns 16 rows of gate and the same 16 rows of up.
+constexpr int kGURows = 16;
+constexpr int64_t kGUChunk = 4 * 8 * 64 * 16 + 4 * 64 * 16;        // 36,864 B
+constexpr int64_t kGURegion = (kQF / kGURows) * kGUChunk;          // 1,179,648 B
+constexpr int64_t kDownCodes = (int64_t)kQD * kQNBF * 16;          // 524,288 B
+constexpr int64_t kDownScales = (int64_t)kQD * kQNBF * 2;          // 65,536 B
+constexpr int64_t kQ4SlotBytes = kGURegion + kDownCodes + kDownScales;  // 1,769,472 B
+constexpr int kDownRowsPerWG = 8;
+
+// Device statistics counters (int64 each).
+enum DevStat { DS_ACC = 0, DS_PIN, DS_COLD, DS_RING, DS_FILL, DS_EVICT, DS_H2D, DS_TOKENS, DS_N };
+
+// Error bits.
+enum DevError { ERR_FILL_TIMEOUT = 1, ERR_FIFO_OVERRUN = 2, ERR_BAD_SLOT = 4 };
+
+// One fill request, written by the route kernel into host-mapped memory.
+struct FifoEntry {
+    uint64_t seq;   // written last; 0 = empty
+    int32_t key;    // layer*E + expert (index into the host arena)
+    int32_t ring;   // ring slot index 0..R-1
+};
+
+// Routing decision of one layer for the current token.
+struct LayerSel {
+    int32_t idx[kMaxK];
+    int32_t slot[kMaxK];
+    float gate[kMaxK];
+    uint64_t wait[kMaxK];  // fill sequence number to wait for (0: data already resident)
+    float inv_rms;
+    int32_t pad[3];
+};
+
+// Token index: base + *ptr (ptr may be null).
+struct TokRef {
+    const int32_t* ptr;
+    int32_t base;
+};
+
+struct PolicyTables {
+    int32_t* slot_of;      // [L*E]
+    int32_t* ring_owner;   // [R]
+    uint64_t* ring_stamp;  // [R]
+    uint64_t* ring_seq;    // [R] fill number of the current content
+    uint64_t* clock;       // LRU clock
+    uint64_t* fill_seq;    // fills issued
+    int64_t* counts;       // [L*E]
+    int64_t* stats;        // [DS_N]
+    moe_spark_event* events;
+    int64_t* n_events;
+    int64_t event_cap;
+    FifoEntry* fifo;       // host-mapped, device address
+    int32_t* error;
+    int64_t P;
+    int32_t R;
+    int32_t E;
+    int64_t slot_bytes;
+};
+
+struct RouteArgs {
+    const float* x_base;   // [T][d]
+    TokRef tok;            // selects x and bias row
+    TokRef trace_tok;      // selects the trace row
+    int32_t d, E, K, layer, L, norm;
+    float eps;
+    const float* wr;       // [E][d]
+    const float* bias;     // [rows][E] or null
+    const int32_t* bias_row;  // [T] or null
+    int32_t n_bias_rows;
+    float* logits;         // scratch [E]
+    uint32_t* done;        // last-block counter
+    LayerSel* sel;
+    float* u;              // [d] normalised input
+    float* ut;             // Q4_0 path: [8][64] float4, ut[j*64+b] = u[32b+4j .. +3]
+    PolicyTables pt;
+    float* tr_x;           // [cap][L][d] or null
+    int32_t* tr_topk;      // [cap][L][K] or null
+    float* tr_gates;
+    int64_t tr_cap;
+    int32_t* topk_out;     // [T][K] or null (indexed by tok)
+    float* gates_out;
+    int32_t q4;            // write ut
+};
+
+struct ExpertArgs {
+    const uint8_t* slots;  // slot arena
+    int64_t slot_bytes;
+    const LayerSel* sel;
+    const uint64_t* ready; // host-mapped [R] ready flags (device address)
+    int64_t P;
+    int64_t n_slots;       // P + R: slot ids outside [0, n_slots) are refused
+    int32_t R;
+    int32_t d, f, K;
+    const float* u;        // [d]
+    const float* ut;       // transposed u (Q4_0)
+    float* h;              // [K][f]; Q4_0: transposed per expert, see kernels
+    // down only
+    const float* x_base;   // residual input [T][d]
+    float* y_base;         // output [T][d]
+    TokRef tok;
+    int32_t residual;
+    int32_t advance;       // last layer of a decode token: bump the cursors
+    int32_t* cursors;      // [2]: x cursor, trace cursor
+    uint32_t* done;        // last-block counter (advance only)
+    int64_t* stats;
+    int32_t* error;
+    uint64_t spin_limit_ticks;  // fill wait limit, in wall-clock ticks (100 MHz)
+};
+
+// Launchers (kernels.hip).
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_gateup(const ExpertArgs& a, int wfmt, hipStream_t s);
+hipError_t launch_down(const ExpertArgs& a, int wfmt, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,651 @@
+// gfx950 kernels of the resident-expert-caching MoE decode path.
+//
+// Per layer and token (decode, batch 1):
+//   route   RMSNorm, router GEMV (+ Zipf bias), top-k, renormalised softmax,
+//           per-expert counts, slot lookup and the LRU spare-ring policy
+//           ("Luce Spark runs 35B MoE models on 16GB GPU without speed loss",
+//           opening paragraph for top-k routing; paragraph "The key
+//           components" for counts, pinned set and the LRU ring).
+//   gateup  h_k = silu(Wg_k u) * (Wu_k u) for the K chosen experts.
+//   down    x += sum_k g_k Wd_k h_k, summed in rank order.
+// The expert kernels read weights from whichever slot the route kernel chose;
+// the arithmetic never depends on the slot, so results are bit-identical at
+// every residency (same paragraph: full residency is bit-identical to
+// all-GPU execution).
+//
+// Q4_0 GEMVs stream one 16-byte block of 32 codes per lane per row, keep the
+// activation block in registers and factor the (q - 8) offset out of the
+// inner loop with per-block activation sums:
+//   sum_i s (q_i - 8) u_i = s (sum_i q_i u_i - 8 U_b),  U_b = sum of the block's u.
+// Every reduction has a fixed tree; there are no floating-point atomics.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xffffu));
+}
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+
+__device__ __forceinline__ int tok_value(const TokRef& t) { return t.base + (t.ptr ? *t.ptr : 0); }
+
+// Dot product of one Q4_0 block's 32 codes (16 bytes, GGUF nibble order:
+// weight j in the low nibble of byte j, weight j+16 in the high nibble) with
+// the block's activations u[0..31] held as 8 f32x4 (uu[j] = u[4j..4j+3]).
+__device__ __forceinline__ float q4_dot(const u32x4 c, const f32x4* uu) {
+    const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t lo = wd[m] & 0x0F0F0F0Fu;
+        const uint32_t hi = (wd[m] >> 4) & 0x0F0F0F0Fu;
+        const f32x4 ul = uu[m], uh = uu[4 + m];
+        acc += (float)(lo & 0xffu) * ul.x;
+        acc += (float)((lo >> 8) & 0xffu) * ul.y;
+        acc += (float)((lo >> 16) & 0xffu) * ul.z;
+        acc += (float)(lo >> 24) * ul.w;
+        acc += (float)(hi & 0xffu) * uh.x;
+        acc += (float)((hi >> 8) & 0xffu) * uh.y;
+        acc += (float)((hi >> 16) & 0xffu) * uh.z;
+        acc += (float)(hi >> 24) * uh.w;
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float block_sum(const f32x4* uu) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += (uu[j].x + uu[j].y) + (uu[j].z + uu[j].w);
+    return s;
+}
+
+// Wait until ring slot `ring` holds fill number `seq` (written by the host
+// fill agent after its copy completed).  Bounded: after `limit` wall-clock
+// ticks the error flag is raised and the work-group proceeds, so a lost fill
+// can never hang the GPU.  Every wave then acquires at system scope so that no
+// stale line of the slot's previous content is read.
+__device__ void wait_fill(const ExpertArgs& a, int ring, uint64_t seq) {
+    if (threadIdx.x == 0) {
+        const uint64_t* flag = a.ready + ring;
+        const uint64_t t0 = wall_clock64();
+        while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < seq) {
+            __builtin_amdgcn_s_sleep(4);
+            // once one fill has timed out, nobody waits again (no cascade of waits)
+            if (wall_clock64() - t0 > a.spin_limit_ticks ||
+                (__hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ERR_FILL_TIMEOUT)) {
+                atomicOr(a.error, (int)ERR_FILL_TIMEOUT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+}
+
+// ---------------------------------------------------------------- route
+
+// Grid: E/4 work-groups of 4 waves; wave w of group g computes logit 4g+w.
+// The last group to finish (device-scope counter) runs top-k, the gates and
+// the placement policy in its first wave.
+template <int NV>  // f32x4 per lane: d / 256
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tok = tok_value(a.tok);
+    const int d = a.d, E = a.E, K = a.K;
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(a.x_base + (int64_t)tok * d);
+
+    f32x4 xv[NV];
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        xv[j] = x4[j * 64 + lane];
+        ss += (xv[j].x * xv[j].x + xv[j].y * xv[j].y) + (xv[j].z * xv[j].z + xv[j].w * xv[j].w);
+    }
+    ss = wave_sum(ss);
+    const float inv = a.norm ? 1.0f / sqrtf(ss / (float)d + a.eps) : 1.0f;
+    f32x4 uv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        uv[j] = xv[j] * inv;
+
+    const int e = blockIdx.x * 4 + w;
+    if (e < E) {
+        const f32x4* wr4 = reinterpret_cast<const f32x4*>(a.wr + (int64_t)e * d);
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const f32x4 wv = wr4[j * 64 + lane];
+            acc += (wv.x * uv[j].x + wv.y * uv[j].y) + (wv.z * uv[j].z + wv.w * uv[j].w);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) {
+            float b = 0.0f;
+            if (a.bias) {
+                int row = a.bias_row ? a.bias_row[tok] : 0;
+                row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
+                b = a.bias[(int64_t)row * E + e];
+            }
+            a.logits[e] = acc + b;
+        }
+    }
+    if (blockIdx.x == 0 && w == 0) {
+        f32x4* u4 = reinterpret_cast<f32x4*>(a.u);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int c = j * 64 + lane;  // f32x4 index: floats 4c .. 4c+3, block c/8
+            u4[c] = uv[j];
+            if (a.q4) reinterpret_cast<f32x4*>(a.ut)[(c & 7) * (d / 32) + (c >> 3)] = uv[j];
+        }
+        const int ttok = tok_value(a.trace_tok);
+        if (a.tr_x && ttok < a.tr_cap) {
+            f32x4* t4 = reinterpret_cast<f32x4*>(a.tr_x + ((int64_t)ttok * a.L + a.layer) * d);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) t4[j * 64 + lane] = xv[j];
+        }
+    }
+
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const unsigned prev = atomicAdd(a.done, 1u);
+        s_last = (prev == gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (w != 0) return;
+    if (lane == 0) atomicExch(a.done, 0u);
+
+    // ---- top-k over (logit desc, index asc), K rounds of wave argmax
+    float lv[kMaxE / 64];
+    const int per = (E + 63) / 64;
+#pragma unroll
+    for (int i = 0; i < kMaxE / 64; ++i) {
+        const int ee = i * 64 + lane;
+        lv[i] = (i < per && ee < E) ? __builtin_nontemporal_load(a.logits + ee) : -INFINITY;
+    }
+    uint32_t taken = 0;
+    int sel_e[kMaxK];
+    float sel_l[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (k >= K) continue;
+        float bv = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kMaxE / 64; ++i) {
+            const int ee = i * 64 + lane;
+            if (i < per && ee < E && !(taken >> i & 1u)) {
+                if (lv[i] > bv || (lv[i] == bv && ee < be)) { bv = lv[i]; be = ee; }
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, 64);
+            const int oe = __shfl_xor(be, m, 64);
+            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        sel_e[k] = be;
+        sel_l[k] = bv;
+    }
+    // ---- gates: softmax over the chosen logits, shifted by the first
+    float gk[kMaxK];
+    float z = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (k >= K) continue;
+        gk[k] = expf(sel_l[k] - sel_l[0]);
+        z += gk[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (k >= K) continue;
+        gk[k] = gk[k] / z;
+    }
+
+    // ---- placement policy, in rank order (single wave)
+    PolicyTables& pt = const_cast<PolicyTables&>(a.pt);
+    const int32_t kbase = a.layer * E;
+    int my_slot = -1;
+    uint64_t my_wait = 0;
+    int any_cold = 0;
+    int pin_slot[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (k >= K) continue;
+        pin_slot[k] = pt.slot_of[kbase + sel_e[k]];
+        any_cold |= pin_slot[k] < 0;
+    }
+    if (lane < K) {
+        int myk = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k)
+            if (k == lane) myk = sel_e[k];
+        pt.counts[kbase + myk] += 1;
+    }
+    int64_t n_pin = 0, n_cold = 0, n_ring = 0, n_fill = 0, n_evict = 0;
+    if (!any_cold) {
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+            if (k >= K) continue;
+            if (lane == k) my_slot = pin_slot[k];
+        }
+        n_pin = K;
+    } else {
+        __shared__ int32_t r_owner[kMaxR];
+        __shared__ uint64_t r_stamp[kMaxR];
+        __shared__ uint64_t r_seq[kMaxR];
+        const int R = pt.R;
+        for (int r = lane; r < R; r += 64) {
+            r_owner[r] = pt.ring_owner[r];
+            r_stamp[r] = pt.ring_stamp[r];
+            r_seq[r] = pt.ring_seq[r];
+        }
+        uint64_t clock = *pt.clock, fseq = *pt.fill_seq;
+        int64_t nev = *pt.n_events;
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+            if (k >= K) continue;
+            const int32_t key = kbase + sel_e[k];
+            int slot;
+            uint64_t wseq = 0;
+            if (pin_slot[k] >= 0) {
+                slot = pin_slot[k];
+                ++n_pin;
+            } else {
+                ++n_cold;
+                int hit = -1;
+                for (int base = 0; base < R && hit < 0; base += 64) {
+                    const int r = base + lane;
+                    const uint64_t m = __ballot(r < R && r_owner[r] == key);
+                    if (m) hit = base + __builtin_ctzll(m);
+                }
+                if (hit >= 0) {
+                    // A ring entry was filled by an earlier route call whose
+                    // expert kernels waited for that copy; it is resident.
+                    ++n_ring;
+                    ++clock;
+                    if (lane == 0) r_stamp[hit] = clock;
+                    slot = (int)(pt.P + hit);
+                } else {
+                    int v = -1;
+                    for (int base = 0; base < R && v < 0; base += 64) {
+                        const int r = base + lane;
+                        const uint64_t m = __ballot(r < R && r_owner[r] < 0);
+                        if (m) v = base + __builtin_ctzll(m);
+                    }
+                    if (v < 0) {  // least recently used: smallest stamp (stamps are unique)
+                        uint64_t bs = ~0ull;
+                        int bi = 0x7fffffff;
+                        for (int r = lane; r < R; r += 64)
+                            if (r_stamp[r] < bs) { bs = r_stamp[r]; bi = r; }
+#pragma unroll
+                        for (int m = 32; m >= 1; m >>= 1) {
+                            const uint64_t os = __shfl_xor(bs, m, 64);
+                            const int oi = __shfl_xor(bi, m, 64);
+                            if (os < bs || (os == bs && oi < bi)) { bs = os; bi = oi; }
+                        }
+                        v = bi;
+                    }
+                    const int32_t victim = r_owner[v];
+                    if (victim >= 0) ++n_evict;
+                    ++clock;
+                    ++fseq;
+                    ++n_fill;
+                    if (lane == 0) {
+                        r_owner[v] = key;
+                        r_stamp[v] = clock;
+                        r_seq[v] = fseq;
+                        if (nev < pt.event_cap) {
+                            moe_spark_event ev;
+                            ev.seq = (int64_t)fseq;
+                            ev.layer = a.layer;
+                            ev.expert = sel_e[k];
+                            ev.slot = (int32_t)(pt.P + v);
+                            ev.kind = MOE_SPARK_EV_FILL;
+                            ev.victim = victim;
+                            ev.pad = 0;
+                            pt.events[nev] = ev;
+                        }
+                        FifoEntry* fe = pt.fifo + ((fseq - 1) % kFifoCap);
+                        fe->key = key;
+                        fe->ring = v;
+                        __threadfence_system();
+                        __hip_atomic_store(&fe->seq, fseq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+                    }
+                    ++nev;
+                    wseq = fseq;
+                    slot = (int)(pt.P + v);
+                }
+            }
+            if (lane == k) { my_slot = slot; my_wait = wseq; }
+        }
+        for (int r = lane; r < R; r += 64) {
+            pt.ring_owner[r] = r_owner[r];
+            pt.ring_stamp[r] = r_stamp[r];
+            pt.ring_seq[r] = r_seq[r];
+        }
+        if (lane == 0) {
+            *pt.clock = clock;
+            *pt.fill_seq = fseq;
+            *pt.n_events = nev;
+        }
+    }
+    if (lane == 0) {
+        pt.stats[DS_ACC] += K;
+        pt.stats[DS_PIN] += n_pin;
+        pt.stats[DS_COLD] += n_cold;
+        pt.stats[DS_RING] += n_ring;
+        pt.stats[DS_FILL] += n_fill;
+        pt.stats[DS_EVICT] += n_evict;
+        pt.stats[DS_H2D] += n_fill * pt.slot_bytes;
+        a.sel->inv_rms = inv;
+    }
+    if (lane < K) {
+        int myk = 0;
+        float myg = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k)
+            if (k == lane) { myk = sel_e[k]; myg = gk[k]; }
+        a.sel->idx[lane] = myk;
+        a.sel->slot[lane] = my_slot;
+        a.sel->gate[lane] = myg;
+        a.sel->wait[lane] = my_wait;
+        const int ttok = tok_value(a.trace_tok);
+        if (a.tr_topk && ttok < a.tr_cap) {
+            const int64_t o = ((int64_t)ttok * a.L + a.layer) * K + lane;
+            a.tr_topk[o] = myk;
+            a.tr_gates[o] = myg;
+        }
+        if (a.topk_out) {
+            a.topk_out[(int64_t)tok * K + lane] = myk;
+            a.gates_out[(int64_t)tok * K + lane] = myg;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- Q4_0 gate/up
+
+// Grid (f/16, K).  Work-group g of expert k owns rows 16g..16g+15 of gate
+// (waves 0, 1) and of up (waves 2, 3); each wave 8 rows; lane b = block b.
+// Slot layout of the chunk (36,864 B): codes at ((w*8 + i)*64 + b)*16, then
+// scales at 32768 + (w*64 + b)*16 + i*2 — every load is a coalesced 1 KiB.
+__global__ __launch_bounds__(256) void gateup_q4_kernel(ExpertArgs a) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = blockIdx.x, k = blockIdx.y;
+    const int slot = a.sel->slot[k];
+    const uint64_t wseq = a.sel->wait[k];
+    if (slot < 0 || slot >= a.n_slots) {  // never expected: refuse rather than fault
+        if (threadIdx.x == 0) atomicOr(a.error, (int)ERR_BAD_SLOT);
+        return;
+    }
+    if (wseq && slot >= a.P) wait_fill(a, (int)(slot - a.P), wseq);
+
+    const uint8_t* chunk = a.slots + (int64_t)slot * a.slot_bytes + (int64_t)g * kGUChunk;
+    const u32x4* cp = reinterpret_cast<const u32x4*>(chunk) + w * 8 * 64 + lane;
+    u32x4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_nontemporal_load(cp + i * 64);
+    const u32x4 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(chunk + 32768) + w * 64 + lane);
+
+    f32x4 uu[8];
+    const f32x4* ut = reinterpret_cast<const f32x4*>(a.ut);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) uu[j] = ut[j * 64 + lane];
+    const float U8 = 8.0f * block_sum(uu);
+
+    const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float s = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
+        v[i] = s * (q4_dot(c[i], uu) - U8);
+    }
+    // 8 rows x 64 lanes -> one row per group of 8 lanes (fixed tree)
+    {
+        const bool h32 = lane & 32;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float send = h32 ? v[t] : v[t + 4];
+            const float keep = h32 ? v[t + 4] : v[t];
+            v[t] = keep + __shfl_xor(send, 32, 64);
+        }
+        const bool h16 = lane & 16;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float send = h16 ? v[t] : v[t + 2];
+            const float keep = h16 ? v[t + 2] : v[t];
+            v[t] = keep + __shfl_xor(send, 16, 64);
+        }
+        const bool h8 = lane & 8;
+        const float send = h8 ? v[0] : v[1];
+        const float keep = h8 ? v[1] : v[0];
+        v[0] = keep + __shfl_xor(send, 8, 64);
+        v[0] += __shfl_xor(v[0], 4, 64);
+        v[0] += __shfl_xor(v[0], 2, 64);
+        v[0] += __shfl_xor(v[0], 1, 64);
+    }
+    __shared__ float red[32];
+    if ((lane & 7) == 0) red[w * 8 + (lane >> 3)] = v[0];  // row (lane>>5)*4 + ((lane>>4)&1)*2 + ((lane>>3)&1)
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int j = threadIdx.x;
+        const float h = silu(red[j]) * red[16 + j];
+        // h layout for the down kernel: f32x4 (k*8 + jj)*16 + b holds h[32b + 4jj .. +3]
+        const int n = g * 16 + j;
+        const int b = n >> 5, jj = (n >> 2) & 7, cc = n & 3;
+        a.h[(((int64_t)k * 8 + jj) * 16 + b) * 4 + cc] = h;
+    }
+}
+
+// ---------------------------------------------------------------- Q4_0 down + combine
+
+// Grid d/8.  Work-group g owns rows 8g..8g+7; wave w covers experts
+// (w&1)*4 .. +3 and rows 8g + (w>>1)*4 .. +3; lane = (expert kl, block b).
+// Slot down region: codes [r][b][16 B], scales [(r/4)][b][4] fp16.
+__global__ __launch_bounds__(256) void down_q4_kernel(ExpertArgs a) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = blockIdx.x;
+    const int eh = w & 1, rq = w >> 1;
+    const int kl = lane >> 4, b = lane & 15;
+    const int k = eh * 4 + kl;
+    const bool act = k < a.K;
+    const int r0 = g * kDownRowsPerWG + rq * 4;
+    const int tok = tok_value(a.tok);
+
+    float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int slot = act ? a.sel->slot[k] : 0;
+    if (act && (slot < 0 || slot >= a.n_slots)) {
+        atomicOr(a.error, (int)ERR_BAD_SLOT);
+    } else if (act) {
+        const uint8_t* base = a.slots + (int64_t)slot * a.slot_bytes + kGURegion;
+        u32x4 c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + i) * 256) + b);
+        const u32x2 sc = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + b);
+        f32x4 hh[8];
+        const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hh[j] = h4[(k * 8 + j) * 16 + b];
+        const float H8 = 8.0f * block_sum(hh);
+        const uint32_t sw[2] = {sc.x, sc.y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
+            z[i] = s * (q4_dot(c[i], hh) - H8);
+        }
+    }
+    // 4 rows x 16 lanes -> one row per group of 4 lanes
+    {
+        const bool h8 = lane & 8;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float send = h8 ? z[t] : z[t + 2];
+            const float keep = h8 ? z[t + 2] : z[t];
+            z[t] = keep + __shfl_xor(send, 8, 64);
+        }
+        const bool h4b = lane & 4;
+        const float send = h4b ? z[0] : z[1];
+        const float keep = h4b ? z[1] : z[0];
+        z[0] = keep + __shfl_xor(send, 4, 64);
+        z[0] += __shfl_xor(z[0], 2, 64);
+        z[0] += __shfl_xor(z[0], 1, 64);
+    }
+    __shared__ float zs[kQ4MaxK][kDownRowsPerWG];
+    if ((lane & 3) == 0) zs[k][rq * 4 + ((lane >> 2) & 3)] = z[0];
+    __syncthreads();
+    if (threadIdx.x < kDownRowsPerWG) {
+        const int r = g * kDownRowsPerWG + threadIdx.x;
+        float y = 0.0f;
+        for (int kk = 0; kk < a.K; ++kk) y += a.sel->gate[kk] * zs[kk][threadIdx.x];
+        const int64_t o = (int64_t)tok * a.d + r;
+        a.y_base[o] = a.residual ? a.x_base[o] + y : y;
+    }
+    if (a.advance) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __threadfence();
+            const unsigned prev = atomicAdd(a.done, 1u);
+            if (prev == gridDim.x - 1) {
+                atomicExch(a.done, 0u);
+                a.cursors[0] += 1;
+                a.cursors[1] += 1;
+                a.stats[DS_TOKENS] += 1;
+                __threadfence();
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- fp32 experts
+
+// Grid (ceil(f/4), K); wave w computes row 4*bx + w of gate and up.
+__global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int k = blockIdx.y;
+    const int slot = a.sel->slot[k];
+    const uint64_t wseq = a.sel->wait[k];
+    if (slot < 0 || slot >= a.n_slots) {
+        if (threadIdx.x == 0) atomicOr(a.error, (int)ERR_BAD_SLOT);
+        return;
+    }
+    if (wseq && slot >= a.P) wait_fill(a, (int)(slot - a.P), wseq);
+    const int n = blockIdx.x * 4 + w;
+    if (n >= a.f) return;
+    const int d4 = a.d / 4;
+    const float* base = reinterpret_cast<const float*>(a.slots + (int64_t)slot * a.slot_bytes);
+    const f32x4* gr = reinterpret_cast<const f32x4*>(base + (int64_t)n * a.d);
+    const f32x4* ur = reinterpret_cast<const f32x4*>(base + (int64_t)a.f * a.d + (int64_t)n * a.d);
+    const f32x4* u4 = reinterpret_cast<const f32x4*>(a.u);
+    float ag = 0.0f, au = 0.0f;
+    for (int c = lane; c < d4; c += 64) {
+        const f32x4 uv = u4[c], gv = gr[c], vv = ur[c];
+        ag += (gv.x * uv.x + gv.y * uv.y) + (gv.z * uv.z + gv.w * uv.w);
+        au += (vv.x * uv.x + vv.y * uv.y) + (vv.z * uv.z + vv.w * uv.w);
+    }
+    ag = wave_sum(ag);
+    au = wave_sum(au);
+    if (lane == 0) a.h[(int64_t)k * a.f + n] = silu(ag) * au;
+}
+
+// Grid ceil(d/4); wave w computes output row 4*bx + w over all K experts.
+__global__ __launch_bounds__(256) void down_f32_kernel(ExpertArgs a) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = blockIdx.x * 4 + w;
+    const int tok = tok_value(a.tok);
+    if (r < a.d) {
+        const int f4 = a.f / 4;
+        float y = 0.0f;
+        for (int kk = 0; kk < a.K; ++kk) {
+            int slot = a.sel->slot[kk];
+            if (slot < 0 || slot >= a.n_slots) {
+                if (lane == 0) atomicOr(a.error, (int)ERR_BAD_SLOT);
+                slot = 0;
+            }
+            const float* base = reinterpret_cast<const float*>(a.slots + (int64_t)slot * a.slot_bytes);
+            const f32x4* dr = reinterpret_cast<const f32x4*>(base + 2 * (int64_t)a.f * a.d + (int64_t)r * a.f);
+            const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h + (int64_t)kk * a.f);
+            float zz = 0.0f;
+            for (int c = lane; c < f4; c += 64) {
+                const f32x4 dv = dr[c], hv = h4[c];
+                zz += (dv.x * hv.x + dv.y * hv.y) + (dv.z * hv.z + dv.w * hv.w);
+            }
+            zz = wave_sum(zz);
+            y += a.sel->gate[kk] * zz;
+        }
+        if (lane == 0) {
+            const int64_t o = (int64_t)tok * a.d + r;
+            a.y_base[o] = a.residual ? a.x_base[o] + y : y;
+        }
+    }
+    if (a.advance) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __threadfence();
+            const unsigned prev = atomicAdd(a.done, 1u);
+            if (prev == gridDim.x - 1) {
+                atomicExch(a.done, 0u);
+                a.cursors[0] += 1;
+                a.cursors[1] += 1;
+                a.stats[DS_TOKENS] += 1;
+                __threadfence();
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+    const dim3 grid((a.E + 3) / 4), block(256);
+    switch (a.d / 256) {
+        case 1: hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL(route_kernel<32>, grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gateup(const ExpertArgs& a, int wfmt, hipStream_t s) {
+    if (wfmt == MOE_SPARK_W_Q4_0) {
+        hipLaunchKernelGGL(gateup_q4_kernel, dim3(kQF / kGURows, a.K), dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(gateup_f32_kernel, dim3((a.f + 3) / 4, a.K), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_down(const ExpertArgs& a, int wfmt, hipStream_t s) {
+    if (wfmt == MOE_SPARK_W_Q4_0) {
+        hipLaunchKernelGGL(down_q4_kernel, dim3(kQD / kDownRowsPerWG), dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(down_f32_kernel, dim3((a.d + 3) / 4), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

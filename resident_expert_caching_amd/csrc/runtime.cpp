@@ -1,0 +1,970 @@
+// Host runtime of the moe_spark C ABI: arenas, weight repacking, placement
+// (uniform and calibrated), the fill agent that serves cold-expert copies,
+// eager layer forward, and the whole-token decode graph.
+//
+// Method: "Luce Spark runs 35B MoE models on 16GB GPU without speed loss"
+// (theneuralfeed.com), paragraph "The key components":
+//  (1) calibrated placement pins the most-used experts — moe_spark_calibrate;
+//  (2) a fixed ring of spare GPU slots, filled on a cold hit by an
+//      asynchronous copy from pinned host memory while the LRU entry is
+//      evicted — the route kernel decides (device tables), the fill agent
+//      thread below issues hipMemcpyAsync on the copy stream and publishes a
+//      ready flag that only the work-groups needing that slot wait for;
+//  (3) the entire token runs as one graph — moe_spark_decode captures all
+//      layers' kernels once per (x, bias_row) and replays the graph per token;
+//      placement lives in device tables, so the graph never needs recapture.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+#include "moe_spark.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kThrottle = 8;  // decode tokens in flight at most
+
+struct GraphEntry {
+    float* x = nullptr;
+    const int32_t* bias_row = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+int64_t now_ns() {
+    return std::chrono::duration_cast<std::chrono::nanoseconds>(
+               std::chrono::steady_clock::now().time_since_epoch())
+        .count();
+}
+
+}  // namespace
+
+struct moe_spark_ctx {
+    moe_spark_config cfg{};
+    int device = 0;
+    int64_t slot_bytes = 0;
+    int64_t n_slots = 0;  // P + R
+    int64_t n_experts_total = 0;
+    hipStream_t compute = nullptr, copy = nullptr;
+    bool own_compute = false, own_copy = false;
+
+    uint8_t* d_slots = nullptr;
+    uint8_t* h_arena = nullptr;
+    float* d_router = nullptr;
+    float* d_bias = nullptr;
+
+    // device tables
+    int32_t* d_slot_of = nullptr;
+    int32_t* d_ring_owner = nullptr;
+    uint64_t* d_ring_stamp = nullptr;
+    uint64_t* d_ring_seq = nullptr;
+    uint64_t* d_clock = nullptr;  // [2]: clock, fill_seq
+    int64_t* d_counts = nullptr;
+    int64_t* d_stats = nullptr;
+    moe_spark_event* d_events = nullptr;
+    int64_t* d_n_events = nullptr;
+    int32_t* d_error = nullptr;
+    int32_t* d_cursors = nullptr;   // [2]
+    uint32_t* d_done = nullptr;     // [2*L + 4] last-block counters
+    LayerSel* d_sel = nullptr;      // [L] + 1 scratch
+    float* d_logits = nullptr;      // [E]
+    float* d_u = nullptr;           // [d]
+    float* d_ut = nullptr;          // [d]
+    float* d_h = nullptr;           // [kMaxK * f]
+    float* d_xscratch = nullptr;    // [d]
+
+    // host-mapped
+    FifoEntry* h_fifo = nullptr;
+    FifoEntry* d_fifo = nullptr;
+    uint64_t* h_ready = nullptr;
+    uint64_t* d_ready = nullptr;
+
+    // host mirrors / state
+    std::vector<uint8_t> router_set, expert_set;
+    int64_t n_router_set = 0, n_expert_set = 0;
+    bool placed = false;
+    std::vector<int32_t> slot_of;  // host copy of the placement
+
+    float* tr_x = nullptr;
+    int32_t* tr_topk = nullptr;
+    float* tr_gates = nullptr;
+    int64_t tr_cap = 0;
+
+    std::vector<GraphEntry> graphs;
+    hipEvent_t tok_ev[kThrottle] = {};
+    int64_t tok_launched = 0;
+    uint64_t spin_ticks = 0;
+
+    // fill agent
+    std::thread agent;
+    std::atomic<bool> stop{false};
+    std::atomic<int64_t> fill_ns_sum{0}, fill_ns_max{0};
+    std::atomic<int> agent_error{0};
+    std::string agent_msg;
+    int64_t calib_uploads = 0;
+
+    std::string err;
+
+    moe_spark_status fail(moe_spark_status st, const char* fmt, ...) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        err = buf;
+        return st;
+    }
+};
+
+#define HIPCHK(call)                                                                           \
+    do {                                                                                       \
+        hipError_t e_ = (call);                                                                \
+        if (e_ != hipSuccess)                                                                  \
+            return ctx->fail(MOE_SPARK_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+namespace {
+
+thread_local std::string g_create_err;
+
+// ---------------------------------------------------------------- repacking
+
+// GGUF Q4_0 (gate, up [f][d/32][18]; down [d][f/32][18]) -> slot layout read
+// by the Q4_0 kernels (values unchanged, only moved).
+void repack_q4(const uint8_t* gate, const uint8_t* up, const uint8_t* down, uint8_t* dst) {
+    for (int g = 0; g < kQF / kGURows; ++g) {
+        uint8_t* chunk = dst + (int64_t)g * kGUChunk;
+        for (int w = 0; w < 4; ++w) {
+            const uint8_t* mat = (w >> 1) ? up : gate;
+            for (int i = 0; i < 8; ++i) {
+                const int row = g * kGURows + (w & 1) * 8 + i;
+                for (int b = 0; b < kQNBD; ++b) {
+                    const uint8_t* blk = mat + ((int64_t)row * kQNBD + b) * 18;
+                    memcpy(chunk + ((int64_t)(w * 8 + i) * 64 + b) * 16, blk + 2, 16);
+                    memcpy(chunk + 32768 + (int64_t)(w * 64 + b) * 16 + i * 2, blk, 2);
+                }
+            }
+        }
+    }
+    uint8_t* dc = dst + kGURegion;
+    uint8_t* ds = dc + kDownCodes;
+    for (int r = 0; r < kQD; ++r) {
+        for (int b = 0; b < kQNBF; ++b) {
+            const uint8_t* blk = down + ((int64_t)r * kQNBF + b) * 18;
+            memcpy(dc + (int64_t)r * 256 + b * 16, blk + 2, 16);
+            memcpy(ds + ((int64_t)(r >> 2) * 16 + b) * 8 + (r & 3) * 2, blk, 2);
+        }
+    }
+}
+
+int64_t matrix_bytes(int rows, int cols, int wfmt) {
+    return wfmt == MOE_SPARK_W_F32 ? (int64_t)rows * cols * 4 : (int64_t)rows * (cols / 32) * 18;
+}
+
+void pack_expert(const moe_spark_ctx* ctx, const void* gate, const void* up, const void* down,
+                 uint8_t* dst) {
+    const int d = ctx->cfg.d_model, f = ctx->cfg.d_ff;
+    if (ctx->cfg.wfmt == MOE_SPARK_W_Q4_0) {
+        repack_q4((const uint8_t*)gate, (const uint8_t*)up, (const uint8_t*)down, dst);
+    } else {
+        const int64_t mb = (int64_t)f * d * 4;
+        memcpy(dst, gate, mb);
+        memcpy(dst + mb, up, mb);
+        memcpy(dst + 2 * mb, down, (int64_t)d * f * 4);
+    }
+}
+
+int64_t quota(int L, int64_t P, int l) { return P / L + ((int64_t)l < P % L ? 1 : 0); }
+
+// ---------------------------------------------------------------- fill agent
+
+void agent_loop(moe_spark_ctx* ctx) {
+    hipSetDevice(ctx->device);
+    struct Pending {
+        uint64_t seq;
+        int ring;
+        hipEvent_t ev;
+        int64_t t0;
+    };
+    std::deque<Pending> pend;
+    std::vector<hipEvent_t> pool;
+    uint64_t next = 1;
+    int idle = 0;
+    const int64_t P = ctx->cfg.resident_cap, SB = ctx->slot_bytes;
+    while (!ctx->stop.load(std::memory_order_relaxed)) {
+        bool did = false;
+        for (;;) {
+            FifoEntry* fe = ctx->h_fifo + ((next - 1) % kFifoCap);
+            const uint64_t s = __atomic_load_n(&fe->seq, __ATOMIC_ACQUIRE);
+            if (s != next) break;
+            const int key = fe->key, ring = fe->ring;
+            const int64_t t0 = now_ns();
+            hipEvent_t ev;
+            if (pool.empty()) {
+                if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) ev = nullptr;
+            } else {
+                ev = pool.back();
+                pool.pop_back();
+            }
+            bool ok = key >= 0 && key < ctx->n_experts_total && ring >= 0 && ring < ctx->cfg.ring_slots;
+            if (ok)
+                ok = hipMemcpyAsync(ctx->d_slots + (P + ring) * SB, ctx->h_arena + (int64_t)key * SB, SB,
+                                    hipMemcpyHostToDevice, ctx->copy) == hipSuccess;
+            if (ok && ev) ok = hipEventRecord(ev, ctx->copy) == hipSuccess;
+            if (!ok) {
+                ctx->agent_error.store(1);
+                if (ev) pool.push_back(ev);
+                // publish anyway: the data is wrong but nothing waits forever
+                __atomic_store_n(ctx->h_ready + (ring >= 0 && ring < ctx->cfg.ring_slots ? ring : 0), next,
+                                 __ATOMIC_RELEASE);
+            } else {
+                pend.push_back({next, ring, ev, t0});
+            }
+            ++next;
+            did = true;
+        }
+        while (!pend.empty()) {
+            Pending& p = pend.front();
+            const hipError_t q = p.ev ? hipEventQuery(p.ev) : hipStreamQuery(ctx->copy);
+            if (q == hipErrorNotReady) break;
+            if (q != hipSuccess) ctx->agent_error.store(1);
+            __atomic_store_n(ctx->h_ready + p.ring, p.seq, __ATOMIC_RELEASE);
+            const int64_t dt = now_ns() - p.t0;
+            ctx->fill_ns_sum.fetch_add(dt);
+            int64_t m = ctx->fill_ns_max.load();
+            while (dt > m && !ctx->fill_ns_max.compare_exchange_weak(m, dt)) {
+            }
+            if (p.ev) pool.push_back(p.ev);
+            pend.pop_front();
+            did = true;
+        }
+        if (did) {
+            idle = 0;
+        } else if (++idle > 20000) {
+            std::this_thread::sleep_for(std::chrono::microseconds(20));
+        } else {
+            __builtin_ia32_pause();
+        }
+    }
+    for (auto& p : pend)
+        if (p.ev) hipEventDestroy(p.ev);
+    for (auto ev : pool) hipEventDestroy(ev);
+}
+
+moe_spark_status check_config(const moe_spark_config* c, std::string& why) {
+    char buf[256];
+    auto bad = [&](const char* m) {
+        why = m;
+        return MOE_SPARK_E_INVALID;
+    };
+    if (!c) return bad("config is NULL");
+    if (c->n_layers <= 0) return bad("n_layers must be > 0");
+    if (c->n_experts <= 0 || c->n_experts > kMaxE || c->n_experts % 4)
+        return bad("n_experts must be a multiple of 4 in [4, 1024]");
+    if (c->top_k <= 0 || c->top_k > c->n_experts || c->top_k > kMaxK)
+        return bad("top_k must be in [1, min(n_experts, 16)]");
+    if (c->d_model <= 0 || c->d_model % 256 || c->d_model > 8192)
+        return bad("d_model must be a multiple of 256 up to 8192");
+    if (c->d_ff <= 0 || c->d_ff % 4 || c->d_ff > 8192) return bad("d_ff must be a multiple of 4 up to 8192");
+    if (c->wfmt != MOE_SPARK_W_F32 && c->wfmt != MOE_SPARK_W_Q4_0) return bad("unknown weight format");
+    if (c->wfmt == MOE_SPARK_W_Q4_0 && (c->d_model != kQD || c->d_ff != kQF || c->top_k > kQ4MaxK)) {
+        snprintf(buf, sizeof buf, "Q4_0 kernels are built for d_model=%d, d_ff=%d, top_k<=%d", kQD, kQF,
+                 kQ4MaxK);
+        why = buf;
+        return MOE_SPARK_E_INVALID;
+    }
+    const int64_t LE = (int64_t)c->n_layers * c->n_experts;
+    if (c->resident_cap < 0 || c->resident_cap > LE) return bad("resident_cap must be in [0, L*E]");
+    if (c->ring_slots < 0 || c->ring_slots > kMaxR) return bad("ring_slots must be in [0, 1024]");
+    if (c->resident_cap < LE && c->ring_slots < c->top_k)
+        return bad("ring_slots must be >= top_k when not every expert is pinned");
+    if (c->n_bias_rows < 0) return bad("n_bias_rows must be >= 0");
+    if (c->max_tokens < 0) return bad("max_tokens must be >= 0");
+    if (c->event_cap < 0) return bad("event_cap must be >= 0");
+    if (!(c->rms_eps >= 0.0f)) return bad("rms_eps must be >= 0");
+    return MOE_SPARK_OK;
+}
+
+void free_all(moe_spark_ctx* ctx) {
+    if (ctx->agent.joinable()) {
+        ctx->stop.store(true);
+        ctx->agent.join();
+    }
+    for (auto& g : ctx->graphs) {
+        if (g.exec) hipGraphExecDestroy(g.exec);
+        if (g.graph) hipGraphDestroy(g.graph);
+    }
+    ctx->graphs.clear();
+    for (auto& e : ctx->tok_ev)
+        if (e) hipEventDestroy(e);
+    void* dptrs[] = {ctx->d_slots,  ctx->d_router,   ctx->d_bias,   ctx->d_slot_of, ctx->d_ring_owner,
+                     ctx->d_ring_stamp, ctx->d_ring_seq, ctx->d_clock, ctx->d_counts, ctx->d_stats,
+                     ctx->d_events, ctx->d_n_events, ctx->d_error,  ctx->d_cursors, ctx->d_done,
+                     ctx->d_sel,    ctx->d_logits,   ctx->d_u,      ctx->d_ut,      ctx->d_h,
+                     ctx->d_xscratch};
+    for (void* p : dptrs)
+        if (p) hipFree(p);
+    if (ctx->h_arena) hipHostFree(ctx->h_arena);
+    if (ctx->h_fifo) hipHostFree(ctx->h_fifo);
+    if (ctx->h_ready) hipHostFree(ctx->h_ready);
+    if (ctx->own_compute && ctx->compute) hipStreamDestroy(ctx->compute);
+    if (ctx->own_copy && ctx->copy) hipStreamDestroy(ctx->copy);
+}
+
+template <typename T>
+hipError_t dalloc(T** p, size_t n) {
+    return hipMalloc((void**)p, n * sizeof(T) > 0 ? n * sizeof(T) : 16);
+}
+
+PolicyTables tables(const moe_spark_ctx* ctx) {
+    PolicyTables t;
+    t.slot_of = ctx->d_slot_of;
+    t.ring_owner = ctx->d_ring_owner;
+    t.ring_stamp = ctx->d_ring_stamp;
+    t.ring_seq = ctx->d_ring_seq;
+    t.clock = ctx->d_clock;
+    t.fill_seq = ctx->d_clock + 1;
+    t.counts = ctx->d_counts;
+    t.stats = ctx->d_stats;
+    t.events = ctx->d_events;
+    t.n_events = ctx->d_n_events;
+    t.event_cap = ctx->cfg.event_cap;
+    t.fifo = ctx->d_fifo;
+    t.error = ctx->d_error;
+    t.P = ctx->cfg.resident_cap;
+    t.R = ctx->cfg.ring_slots;
+    t.E = ctx->cfg.n_experts;
+    t.slot_bytes = ctx->slot_bytes;
+    return t;
+}
+
+RouteArgs route_args(const moe_spark_ctx* ctx, int layer, const float* x, TokRef tok, TokRef ttok,
+                     const int32_t* bias_row, int norm, int32_t* topk_out, float* gates_out) {
+    const auto& c = ctx->cfg;
+    RouteArgs a{};
+    a.x_base = x;
+    a.tok = tok;
+    a.trace_tok = ttok;
+    a.d = c.d_model;
+    a.E = c.n_experts;
+    a.K = c.top_k;
+    a.layer = layer;
+    a.L = c.n_layers;
+    a.norm = norm;
+    a.eps = c.rms_eps;
+    a.wr = ctx->d_router + (int64_t)layer * c.n_experts * c.d_model;
+    a.bias = c.n_bias_rows > 0 ? ctx->d_bias + (int64_t)layer * c.n_bias_rows * c.n_experts : nullptr;
+    a.bias_row = bias_row;
+    a.n_bias_rows = c.n_bias_rows;
+    a.logits = ctx->d_logits;
+    a.done = ctx->d_done + 2 * layer;
+    a.sel = ctx->d_sel + layer;
+    a.u = ctx->d_u;
+    a.ut = ctx->d_ut;
+    a.pt = tables(ctx);
+    a.tr_x = ctx->tr_x;
+    a.tr_topk = ctx->tr_topk;
+    a.tr_gates = ctx->tr_gates;
+    a.tr_cap = ctx->tr_cap;
+    a.topk_out = topk_out;
+    a.gates_out = gates_out;
+    a.q4 = c.wfmt == MOE_SPARK_W_Q4_0;
+    return a;
+}
+
+ExpertArgs expert_args(const moe_spark_ctx* ctx, int layer, const float* x, float* y, TokRef tok,
+                       int residual, int advance) {
+    const auto& c = ctx->cfg;
+    ExpertArgs a{};
+    a.slots = ctx->d_slots;
+    a.slot_bytes = ctx->slot_bytes;
+    a.sel = ctx->d_sel + layer;
+    a.ready = ctx->d_ready;
+    a.P = c.resident_cap;
+    a.n_slots = ctx->n_slots;
+    a.R = c.ring_slots;
+    a.d = c.d_model;
+    a.f = c.d_ff;
+    a.K = c.top_k;
+    a.u = ctx->d_u;
+    a.ut = ctx->d_ut;
+    a.h = ctx->d_h;
+    a.x_base = x;
+    a.y_base = y;
+    a.tok = tok;
+    a.residual = residual;
+    a.advance = advance;
+    a.cursors = ctx->d_cursors;
+    a.done = ctx->d_done + 2 * layer + 1;
+    a.stats = ctx->d_stats;
+    a.error = ctx->d_error;
+    a.spin_limit_ticks = ctx->spin_ticks;
+    return a;
+}
+
+moe_spark_status ready_check(moe_spark_ctx* ctx) {
+    if (ctx->n_router_set != ctx->cfg.n_layers || ctx->n_expert_set != ctx->n_experts_total)
+        return ctx->fail(MOE_SPARK_E_STATE, "every router and expert must be set first (%lld/%d routers, %lld/%lld experts)",
+                         (long long)ctx->n_router_set, ctx->cfg.n_layers, (long long)ctx->n_expert_set,
+                         (long long)ctx->n_experts_total);
+    if (!ctx->placed) return ctx->fail(MOE_SPARK_E_STATE, "no placement yet: call moe_spark_place_uniform");
+    return MOE_SPARK_OK;
+}
+
+// Upload experts into pinned slots: (slot, key) pairs, coalescing runs that are
+// contiguous in both arenas.
+moe_spark_status upload_pinned(moe_spark_ctx* ctx, std::vector<std::pair<int32_t, int32_t>> moves) {
+    std::sort(moves.begin(), moves.end(), [](auto a, auto b) { return a.first < b.first; });
+    const int64_t SB = ctx->slot_bytes;
+    size_t i = 0;
+    while (i < moves.size()) {
+        size_t j = i + 1;
+        while (j < moves.size() && moves[j].first == moves[j - 1].first + 1 &&
+               moves[j].second == moves[j - 1].second + 1)
+            ++j;
+        const int64_t n = (int64_t)(j - i);
+        HIPCHK(hipMemcpyAsync(ctx->d_slots + (int64_t)moves[i].first * SB,
+                              ctx->h_arena + (int64_t)moves[i].second * SB, n * SB, hipMemcpyHostToDevice,
+                              ctx->copy));
+        i = j;
+    }
+    HIPCHK(hipStreamSynchronize(ctx->copy));
+    return MOE_SPARK_OK;
+}
+
+void drop_graphs(moe_spark_ctx* ctx) {
+    hipStreamSynchronize(ctx->compute);
+    for (auto& g : ctx->graphs) {
+        if (g.exec) hipGraphExecDestroy(g.exec);
+        if (g.graph) hipGraphDestroy(g.graph);
+    }
+    ctx->graphs.clear();
+}
+
+moe_spark_status launch_token_kernels(moe_spark_ctx* ctx, float* x, const int32_t* bias_row) {
+    const int L = ctx->cfg.n_layers, wfmt = ctx->cfg.wfmt;
+    const TokRef tok{ctx->d_cursors, 0}, ttok{ctx->d_cursors + 1, 0};
+    for (int l = 0; l < L; ++l) {
+        const RouteArgs ra = route_args(ctx, l, x, tok, ttok, bias_row, 1, nullptr, nullptr);
+        HIPCHK(launch_route(ra, ctx->compute));
+        const ExpertArgs ea = expert_args(ctx, l, x, x, tok, 1, l == L - 1);
+        HIPCHK(launch_gateup(ea, wfmt, ctx->compute));
+        HIPCHK(launch_down(ea, wfmt, ctx->compute));
+    }
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status get_graph(moe_spark_ctx* ctx, float* x, const int32_t* bias_row, hipGraphExec_t* out) {
+    for (auto& g : ctx->graphs)
+        if (g.x == x && g.bias_row == bias_row) {
+            *out = g.exec;
+            return MOE_SPARK_OK;
+        }
+    if (ctx->graphs.size() >= 4) {
+        HIPCHK(hipStreamSynchronize(ctx->compute));
+        auto& g = ctx->graphs.front();
+        hipGraphExecDestroy(g.exec);
+        hipGraphDestroy(g.graph);
+        ctx->graphs.erase(ctx->graphs.begin());
+    }
+    GraphEntry ge;
+    ge.x = x;
+    ge.bias_row = bias_row;
+    HIPCHK(hipStreamBeginCapture(ctx->compute, hipStreamCaptureModeThreadLocal));
+    moe_spark_status st = launch_token_kernels(ctx, x, bias_row);
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(ctx->compute, &graph);
+    if (st != MOE_SPARK_OK) {
+        if (graph) hipGraphDestroy(graph);
+        return st;
+    }
+    if (ec != hipSuccess) return ctx->fail(MOE_SPARK_E_HIP, "graph capture failed: %s", hipGetErrorString(ec));
+    ge.graph = graph;
+    const hipError_t ei = hipGraphInstantiate(&ge.exec, graph, nullptr, nullptr, 0);
+    if (ei != hipSuccess) {
+        hipGraphDestroy(graph);
+        return ctx->fail(MOE_SPARK_E_HIP, "graph instantiate failed: %s", hipGetErrorString(ei));
+    }
+    ctx->graphs.push_back(ge);
+    *out = ge.exec;
+    return MOE_SPARK_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_stream, void* copy_stream,
+                                  moe_spark_ctx** out) {
+    if (!out) return MOE_SPARK_E_INVALID;
+    *out = nullptr;
+    std::string why;
+    moe_spark_status st = check_config(cfg, why);
+    if (st != MOE_SPARK_OK) {
+        g_create_err = why;
+        return st;
+    }
+    auto* ctx = new moe_spark_ctx();
+    ctx->cfg = *cfg;
+    if (ctx->cfg.event_cap == 0) ctx->cfg.event_cap = 1 << 20;
+    const auto& c = ctx->cfg;
+    const int d = c.d_model, f = c.d_ff, E = c.n_experts, L = c.n_layers;
+    ctx->slot_bytes = c.wfmt == MOE_SPARK_W_Q4_0 ? kQ4SlotBytes : (int64_t)3 * f * d * 4;
+    ctx->n_experts_total = (int64_t)L * E;
+    ctx->n_slots = c.resident_cap + c.ring_slots;
+    ctx->router_set.assign(L, 0);
+    ctx->expert_set.assign(ctx->n_experts_total, 0);
+    ctx->slot_of.assign(ctx->n_experts_total, -1);
+
+    auto fail_create = [&](moe_spark_status s, const std::string& m) {
+        g_create_err = m;
+        free_all(ctx);
+        delete ctx;
+        return s;
+    };
+    hipError_t e = hipGetDevice(&ctx->device);
+    if (e != hipSuccess) return fail_create(MOE_SPARK_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    int rate_khz = 0;
+    if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, ctx->device) != hipSuccess || rate_khz <= 0)
+        rate_khz = 100000;
+    ctx->spin_ticks = (uint64_t)rate_khz * 1000ull * 2ull;  // 2 s
+    if (compute_stream) {
+        ctx->compute = (hipStream_t)compute_stream;
+    } else {
+        if (hipStreamCreateWithFlags(&ctx->compute, hipStreamNonBlocking) != hipSuccess)
+            return fail_create(MOE_SPARK_E_HIP, "hipStreamCreate failed");
+        ctx->own_compute = true;
+    }
+    if (copy_stream) {
+        ctx->copy = (hipStream_t)copy_stream;
+    } else {
+        if (hipStreamCreateWithFlags(&ctx->copy, hipStreamNonBlocking) != hipSuccess)
+            return fail_create(MOE_SPARK_E_HIP, "hipStreamCreate failed");
+        ctx->own_copy = true;
+    }
+    if (hipMalloc((void**)&ctx->d_slots, (size_t)std::max<int64_t>(ctx->n_slots, 1) * ctx->slot_bytes) != hipSuccess) {
+        ctx->d_slots = nullptr;
+        return fail_create(MOE_SPARK_E_NOMEM, "slot arena allocation failed");
+    }
+    if (hipHostMalloc((void**)&ctx->h_arena, (size_t)ctx->n_experts_total * ctx->slot_bytes, hipHostMallocDefault) !=
+        hipSuccess) {
+        ctx->h_arena = nullptr;
+        return fail_create(MOE_SPARK_E_NOMEM, "pinned host arena allocation failed");
+    }
+    const int R = c.ring_slots;
+    bool ok = true;
+    ok &= dalloc(&ctx->d_router, (size_t)L * E * d) == hipSuccess;
+    ok &= dalloc(&ctx->d_bias, (size_t)L * std::max(c.n_bias_rows, 1) * E) == hipSuccess;
+    ok &= dalloc(&ctx->d_slot_of, (size_t)L * E) == hipSuccess;
+    ok &= dalloc(&ctx->d_ring_owner, (size_t)std::max(R, 1)) == hipSuccess;
+    ok &= dalloc(&ctx->d_ring_stamp, (size_t)std::max(R, 1)) == hipSuccess;
+    ok &= dalloc(&ctx->d_ring_seq, (size_t)std::max(R, 1)) == hipSuccess;
+    ok &= dalloc(&ctx->d_clock, 2) == hipSuccess;
+    ok &= dalloc(&ctx->d_counts, (size_t)L * E) == hipSuccess;
+    ok &= dalloc(&ctx->d_stats, DS_N) == hipSuccess;
+    ok &= dalloc(&ctx->d_events, (size_t)c.event_cap) == hipSuccess;
+    ok &= dalloc(&ctx->d_n_events, 1) == hipSuccess;
+    ok &= dalloc(&ctx->d_error, 1) == hipSuccess;
+    ok &= dalloc(&ctx->d_cursors, 2) == hipSuccess;
+    ok &= dalloc(&ctx->d_done, (size_t)2 * L + 4) == hipSuccess;
+    ok &= dalloc(&ctx->d_sel, (size_t)L + 1) == hipSuccess;
+    ok &= dalloc(&ctx->d_logits, (size_t)E) == hipSuccess;
+    ok &= dalloc(&ctx->d_u, (size_t)d) == hipSuccess;
+    ok &= dalloc(&ctx->d_ut, (size_t)d) == hipSuccess;
+    ok &= dalloc(&ctx->d_h, (size_t)kMaxK * f) == hipSuccess;
+    ok &= dalloc(&ctx->d_xscratch, (size_t)d) == hipSuccess;
+    if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "device table allocation failed");
+    if (hipHostMalloc((void**)&ctx->h_fifo, sizeof(FifoEntry) * kFifoCap, hipHostMallocMapped | hipHostMallocCoherent) !=
+            hipSuccess ||
+        hipHostMalloc((void**)&ctx->h_ready, sizeof(uint64_t) * std::max(R, 1),
+                      hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
+        return fail_create(MOE_SPARK_E_NOMEM, "mapped host allocation failed");
+    memset(ctx->h_fifo, 0, sizeof(FifoEntry) * kFifoCap);
+    memset(ctx->h_ready, 0, sizeof(uint64_t) * std::max(R, 1));
+    if (hipHostGetDevicePointer((void**)&ctx->d_fifo, ctx->h_fifo, 0) != hipSuccess ||
+        hipHostGetDevicePointer((void**)&ctx->d_ready, ctx->h_ready, 0) != hipSuccess)
+        return fail_create(MOE_SPARK_E_HIP, "hipHostGetDevicePointer failed");
+    // zero every table
+    ok &= hipMemset(ctx->d_slot_of, 0xff, sizeof(int32_t) * L * E) == hipSuccess;
+    ok &= hipMemset(ctx->d_ring_owner, 0xff, sizeof(int32_t) * std::max(R, 1)) == hipSuccess;
+    ok &= hipMemset(ctx->d_ring_stamp, 0, sizeof(uint64_t) * std::max(R, 1)) == hipSuccess;
+    ok &= hipMemset(ctx->d_ring_seq, 0, sizeof(uint64_t) * std::max(R, 1)) == hipSuccess;
+    ok &= hipMemset(ctx->d_clock, 0, sizeof(uint64_t) * 2) == hipSuccess;
+    ok &= hipMemset(ctx->d_counts, 0, sizeof(int64_t) * L * E) == hipSuccess;
+    ok &= hipMemset(ctx->d_stats, 0, sizeof(int64_t) * DS_N) == hipSuccess;
+    ok &= hipMemset(ctx->d_n_events, 0, sizeof(int64_t)) == hipSuccess;
+    ok &= hipMemset(ctx->d_error, 0, sizeof(int32_t)) == hipSuccess;
+    ok &= hipMemset(ctx->d_cursors, 0, sizeof(int32_t) * 2) == hipSuccess;
+    ok &= hipMemset(ctx->d_done, 0, sizeof(uint32_t) * (2 * L + 4)) == hipSuccess;
+    ok &= hipMemset(ctx->d_sel, 0, sizeof(LayerSel) * (L + 1)) == hipSuccess;
+    ok &= hipMemset(ctx->d_bias, 0, sizeof(float) * L * std::max(c.n_bias_rows, 1) * E) == hipSuccess;
+    ok &= hipMemset(ctx->d_xscratch, 0, sizeof(float) * d) == hipSuccess;
+    ok &= hipMemset(ctx->d_u, 0, sizeof(float) * d) == hipSuccess;
+    ok &= hipMemset(ctx->d_ut, 0, sizeof(float) * d) == hipSuccess;
+    ok &= hipMemset(ctx->d_h, 0, sizeof(float) * kMaxK * f) == hipSuccess;
+    for (auto& ev : ctx->tok_ev) ok &= hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess;
+    ok &= hipDeviceSynchronize() == hipSuccess;
+    if (!ok) return fail_create(MOE_SPARK_E_HIP, "table initialisation failed");
+    if (R > 0) ctx->agent = std::thread(agent_loop, ctx);
+    *out = ctx;
+    return MOE_SPARK_OK;
+}
+
+void moe_spark_destroy(moe_spark_ctx* ctx) {
+    if (!ctx) return;
+    if (ctx->compute) hipStreamSynchronize(ctx->compute);
+    if (ctx->copy) hipStreamSynchronize(ctx->copy);
+    free_all(ctx);
+    delete ctx;
+}
+
+const char* moe_spark_last_error(const moe_spark_ctx* ctx) {
+    return ctx ? ctx->err.c_str() : g_create_err.c_str();
+}
+
+int64_t moe_spark_slot_bytes(const moe_spark_ctx* ctx) { return ctx ? ctx->slot_bytes : 0; }
+
+moe_spark_status moe_spark_set_router(moe_spark_ctx* ctx, int32_t layer, const float* w, const float* bias) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    const auto& c = ctx->cfg;
+    if (layer < 0 || layer >= c.n_layers || !w) return ctx->fail(MOE_SPARK_E_INVALID, "bad layer or NULL weights");
+    if ((c.n_bias_rows > 0) != (bias != nullptr))
+        return ctx->fail(MOE_SPARK_E_INVALID, "bias must be given iff n_bias_rows > 0");
+    const int64_t ED = (int64_t)c.n_experts * c.d_model;
+    HIPCHK(hipMemcpy(ctx->d_router + layer * ED, w, ED * sizeof(float), hipMemcpyHostToDevice));
+    if (bias) {
+        const int64_t RE = (int64_t)c.n_bias_rows * c.n_experts;
+        HIPCHK(hipMemcpy(ctx->d_bias + layer * RE, bias, RE * sizeof(float), hipMemcpyHostToDevice));
+    }
+    if (!ctx->router_set[layer]) {
+        ctx->router_set[layer] = 1;
+        ++ctx->n_router_set;
+    }
+    return MOE_SPARK_OK;
+}
+
+static moe_spark_status refresh_pinned(moe_spark_ctx* ctx, int64_t first, int64_t n) {
+    if (!ctx->placed) return MOE_SPARK_OK;
+    std::vector<std::pair<int32_t, int32_t>> moves;
+    for (int64_t i = first; i < first + n; ++i)
+        if (ctx->slot_of[i] >= 0) moves.push_back({ctx->slot_of[i], (int32_t)i});
+    if (moves.empty()) return MOE_SPARK_OK;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    return upload_pinned(ctx, moves);
+}
+
+moe_spark_status moe_spark_set_expert(moe_spark_ctx* ctx, int32_t layer, int32_t expert, const void* gate,
+                                      const void* up, const void* down) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    const auto& c = ctx->cfg;
+    if (layer < 0 || layer >= c.n_layers || expert < 0 || expert >= c.n_experts || !gate || !up || !down)
+        return ctx->fail(MOE_SPARK_E_INVALID, "bad layer/expert or NULL weights");
+    const int64_t key = (int64_t)layer * c.n_experts + expert;
+    pack_expert(ctx, gate, up, down, ctx->h_arena + key * ctx->slot_bytes);
+    if (!ctx->expert_set[key]) {
+        ctx->expert_set[key] = 1;
+        ++ctx->n_expert_set;
+    }
+    return refresh_pinned(ctx, key, 1);
+}
+
+moe_spark_status moe_spark_set_experts(moe_spark_ctx* ctx, int64_t first, int64_t n, const void* blob) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    const auto& c = ctx->cfg;
+    if (first < 0 || n < 0 || first + n > ctx->n_experts_total || (!blob && n > 0))
+        return ctx->fail(MOE_SPARK_E_INVALID, "expert range out of bounds");
+    const int d = c.d_model, f = c.d_ff;
+    const int64_t mb = matrix_bytes(f, d, c.wfmt), db = matrix_bytes(d, f, c.wfmt);
+    const int64_t per = 2 * mb + db;
+    const uint8_t* src = (const uint8_t*)blob;
+    unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    std::vector<std::thread> th;
+    for (unsigned t = 0; t < nt; ++t)
+        th.emplace_back([&, t] {
+            for (int64_t i = t; i < n; i += nt) {
+                const uint8_t* p = src + i * per;
+                pack_expert(ctx, p, p + mb, p + 2 * mb, ctx->h_arena + (first + i) * ctx->slot_bytes);
+            }
+        });
+    for (auto& x : th) x.join();
+    for (int64_t i = first; i < first + n; ++i)
+        if (!ctx->expert_set[i]) {
+            ctx->expert_set[i] = 1;
+            ++ctx->n_expert_set;
+        }
+    return refresh_pinned(ctx, first, n);
+}
+
+moe_spark_status moe_spark_place_uniform(moe_spark_ctx* ctx) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    if (ctx->n_expert_set != ctx->n_experts_total || ctx->n_router_set != ctx->cfg.n_layers)
+        return ctx->fail(MOE_SPARK_E_STATE, "set every router and expert before placing");
+    const auto& c = ctx->cfg;
+    const int L = c.n_layers, E = c.n_experts, R = c.ring_slots;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    std::vector<std::pair<int32_t, int32_t>> moves;
+    int32_t next = 0;
+    for (int l = 0; l < L; ++l) {
+        const int64_t q = quota(L, c.resident_cap, l);
+        for (int e = 0; e < E; ++e) {
+            const int32_t key = l * E + e;
+            ctx->slot_of[key] = e < q ? next++ : -1;
+            if (e < q) moves.push_back({ctx->slot_of[key], key});
+        }
+    }
+    HIPCHK(hipMemcpy(ctx->d_slot_of, ctx->slot_of.data(), sizeof(int32_t) * L * E, hipMemcpyHostToDevice));
+    HIPCHK(hipMemset(ctx->d_ring_owner, 0xff, sizeof(int32_t) * std::max(R, 1)));
+    HIPCHK(hipMemset(ctx->d_ring_stamp, 0, sizeof(uint64_t) * std::max(R, 1)));
+    moe_spark_status st = upload_pinned(ctx, moves);
+    if (st != MOE_SPARK_OK) return st;
+    ctx->placed = true;
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    const auto& c = ctx->cfg;
+    const int L = c.n_layers, E = c.n_experts, R = c.ring_slots;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    HIPCHK(hipStreamSynchronize(ctx->copy));
+    std::vector<int64_t> counts((size_t)L * E);
+    std::vector<int32_t> owner(std::max(R, 1));
+    std::vector<uint64_t> stamp(std::max(R, 1));
+    HIPCHK(hipMemcpy(counts.data(), ctx->d_counts, sizeof(int64_t) * L * E, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(owner.data(), ctx->d_ring_owner, sizeof(int32_t) * std::max(R, 1), hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(stamp.data(), ctx->d_ring_stamp, sizeof(uint64_t) * std::max(R, 1), hipMemcpyDeviceToHost));
+    // target pinned set: per layer, the q_l most-counted experts (count desc, id asc)
+    std::vector<uint8_t> want((size_t)L * E, 0);
+    std::vector<int> order(E);
+    for (int l = 0; l < L; ++l) {
+        for (int e = 0; e < E; ++e) order[e] = e;
+        const int64_t* cl = counts.data() + (int64_t)l * E;
+        std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cl[a] > cl[b]; });
+        const int64_t q = quota(L, c.resident_cap, l);
+        for (int64_t i = 0; i < q; ++i) want[(int64_t)l * E + order[i]] = 1;
+    }
+    std::vector<int32_t> freed;
+    for (int64_t key = 0; key < (int64_t)L * E; ++key)
+        if (ctx->slot_of[key] >= 0 && !want[key]) {
+            freed.push_back(ctx->slot_of[key]);
+            ctx->slot_of[key] = -1;
+        }
+    std::sort(freed.begin(), freed.end());
+    std::vector<std::pair<int32_t, int32_t>> moves;
+    size_t nf = 0;
+    for (int64_t key = 0; key < (int64_t)L * E; ++key) {
+        if (!want[key] || ctx->slot_of[key] >= 0) continue;
+        ctx->slot_of[key] = freed[nf++];
+        moves.push_back({ctx->slot_of[key], (int32_t)key});
+        for (int r = 0; r < R; ++r)
+            if (owner[r] == (int32_t)key) {
+                owner[r] = -1;
+                stamp[r] = 0;
+            }
+    }
+    st = upload_pinned(ctx, moves);
+    if (st != MOE_SPARK_OK) return st;
+    ctx->calib_uploads += (int64_t)moves.size();
+    HIPCHK(hipMemcpy(ctx->d_slot_of, ctx->slot_of.data(), sizeof(int32_t) * L * E, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(ctx->d_ring_owner, owner.data(), sizeof(int32_t) * std::max(R, 1), hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(ctx->d_ring_stamp, stamp.data(), sizeof(uint64_t) * std::max(R, 1), hipMemcpyHostToDevice));
+    if (reset_counts) HIPCHK(hipMemset(ctx->d_counts, 0, sizeof(int64_t) * L * E));
+    HIPCHK(hipDeviceSynchronize());
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, const float* x, float* y,
+                                         int32_t n_tokens, const int32_t* bias_row, uint32_t flags,
+                                         int32_t* topk_out, float* gates_out) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    const auto& c = ctx->cfg;
+    if (layer < 0 || layer >= c.n_layers || n_tokens < 0 || (n_tokens > 0 && (!x || !y)))
+        return ctx->fail(MOE_SPARK_E_INVALID, "bad layer, token count or NULL buffer");
+    if (flags & ~(MOE_SPARK_PRE_RMSNORM | MOE_SPARK_RESIDUAL)) return ctx->fail(MOE_SPARK_E_INVALID, "unknown flags");
+    if ((topk_out == nullptr) != (gates_out == nullptr))
+        return ctx->fail(MOE_SPARK_E_INVALID, "topk_out and gates_out go together");
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    const int norm = (flags & MOE_SPARK_PRE_RMSNORM) != 0, res = (flags & MOE_SPARK_RESIDUAL) != 0;
+    for (int t = 0; t < n_tokens; ++t) {
+        const TokRef tok{nullptr, t};
+        const RouteArgs ra = route_args(ctx, layer, x, tok, tok, bias_row, norm, topk_out, gates_out);
+        HIPCHK(launch_route(ra, ctx->compute));
+        const ExpertArgs ea = expert_args(ctx, layer, x, y, tok, res, 0);
+        HIPCHK(launch_gateup(ea, c.wfmt, ctx->compute));
+        HIPCHK(launch_down(ea, c.wfmt, ctx->compute));
+    }
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens, const int32_t* bias_row) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    if (n_tokens < 0 || (n_tokens > 0 && !x)) return ctx->fail(MOE_SPARK_E_INVALID, "bad token count or NULL x");
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    if (n_tokens == 0) return MOE_SPARK_OK;
+    hipGraphExec_t exec;
+    st = get_graph(ctx, x, bias_row, &exec);
+    if (st != MOE_SPARK_OK) return st;
+    HIPCHK(hipMemsetAsync(ctx->d_cursors, 0, sizeof(int32_t), ctx->compute));
+    for (int t = 0; t < n_tokens; ++t) {
+        hipEvent_t& ev = ctx->tok_ev[ctx->tok_launched % kThrottle];
+        if (ctx->tok_launched >= kThrottle) HIPCHK(hipEventSynchronize(ev));
+        HIPCHK(hipGraphLaunch(exec, ctx->compute));
+        HIPCHK(hipEventRecord(ev, ctx->compute));
+        ++ctx->tok_launched;
+    }
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int32_t* bias_row) {
+    return moe_spark_decode(ctx, x, 1, bias_row);
+}
+
+moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_tokens, const int32_t* bias_row) {
+    (void)x;
+    (void)n_tokens;
+    (void)bias_row;
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    return ctx->fail(MOE_SPARK_E_STATE, "prefill is not available in this build");
+}
+
+moe_spark_status moe_spark_set_trace(moe_spark_ctx* ctx, float* x_layers, int32_t* topk, float* gates,
+                                     int64_t cap_tokens) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    if (cap_tokens < 0 || ((topk == nullptr) != (gates == nullptr)))
+        return ctx->fail(MOE_SPARK_E_INVALID, "bad trace buffers");
+    drop_graphs(ctx);
+    ctx->tr_x = x_layers;
+    ctx->tr_topk = topk;
+    ctx->tr_gates = gates;
+    ctx->tr_cap = (x_layers || topk) ? cap_tokens : 0;
+    HIPCHK(hipMemset(ctx->d_cursors + 1, 0, sizeof(int32_t)));
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_get_stats(moe_spark_ctx* ctx, moe_spark_stats* out) {
+    if (!ctx || !out) return MOE_SPARK_E_INVALID;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    int64_t s[DS_N];
+    HIPCHK(hipMemcpy(s, ctx->d_stats, sizeof s, hipMemcpyDeviceToHost));
+    out->accesses = s[DS_ACC];
+    out->pinned_hits = s[DS_PIN];
+    out->cold_hits = s[DS_COLD];
+    out->ring_hits = s[DS_RING];
+    out->fills = s[DS_FILL];
+    out->evictions = s[DS_EVICT];
+    out->h2d_bytes = s[DS_H2D];
+    out->fill_ns_sum = ctx->fill_ns_sum.load();
+    out->fill_ns_max = ctx->fill_ns_max.load();
+    out->calib_uploads = ctx->calib_uploads;
+    out->tokens = s[DS_TOKENS];
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_reset_stats(moe_spark_ctx* ctx) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    HIPCHK(hipMemset(ctx->d_stats, 0, sizeof(int64_t) * DS_N));
+    HIPCHK(hipDeviceSynchronize());
+    ctx->fill_ns_sum.store(0);
+    ctx->fill_ns_max.store(0);
+    ctx->calib_uploads = 0;
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_get_placement(moe_spark_ctx* ctx, int32_t* slot_of, int32_t* ring_owner,
+                                         int64_t* ring_stamp, int64_t* counts) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    const auto& c = ctx->cfg;
+    const int64_t LE = (int64_t)c.n_layers * c.n_experts;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    if (slot_of) HIPCHK(hipMemcpy(slot_of, ctx->d_slot_of, sizeof(int32_t) * LE, hipMemcpyDeviceToHost));
+    if (ring_owner && c.ring_slots > 0)
+        HIPCHK(hipMemcpy(ring_owner, ctx->d_ring_owner, sizeof(int32_t) * c.ring_slots, hipMemcpyDeviceToHost));
+    if (ring_stamp && c.ring_slots > 0)
+        HIPCHK(hipMemcpy(ring_stamp, ctx->d_ring_stamp, sizeof(int64_t) * c.ring_slots, hipMemcpyDeviceToHost));
+    if (counts) HIPCHK(hipMemcpy(counts, ctx->d_counts, sizeof(int64_t) * LE, hipMemcpyDeviceToHost));
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_get_events(moe_spark_ctx* ctx, moe_spark_event* out, int64_t cap, int64_t* n_total) {
+    if (!ctx || cap < 0 || (cap > 0 && !out)) return MOE_SPARK_E_INVALID;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    int64_t n = 0;
+    HIPCHK(hipMemcpy(&n, ctx->d_n_events, sizeof n, hipMemcpyDeviceToHost));
+    if (n_total) *n_total = n;
+    const int64_t m = std::min(std::min(n, cap), ctx->cfg.event_cap);
+    if (m > 0) HIPCHK(hipMemcpy(out, ctx->d_events, sizeof(moe_spark_event) * m, hipMemcpyDeviceToHost));
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_synchronize(moe_spark_ctx* ctx) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    HIPCHK(hipStreamSynchronize(ctx->copy));
+    int32_t e = 0;
+    HIPCHK(hipMemcpy(&e, ctx->d_error, sizeof e, hipMemcpyDeviceToHost));
+    if (e & ERR_FILL_TIMEOUT) return ctx->fail(MOE_SPARK_E_HIP, "a cold-expert fill did not arrive in time");
+    if (e & ERR_BAD_SLOT) return ctx->fail(MOE_SPARK_E_HIP, "an expert kernel was handed an invalid slot");
+    if (e) return ctx->fail(MOE_SPARK_E_HIP, "device error flags 0x%x", e);
+    if (ctx->agent_error.load()) return ctx->fail(MOE_SPARK_E_HIP, "fill agent: a host-to-device copy failed");
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_time_expert_kernels(moe_spark_ctx* ctx, int32_t iters, float* us_gateup, float* us_down,
+                                               float* us_route) {
+    if (!ctx || iters <= 0) return MOE_SPARK_E_INVALID;
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    const auto& c = ctx->cfg;
+    const int L = c.n_layers;
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    hipEvent_t e0, e1, e2;
+    HIPCHK(hipEventCreate(&e0));
+    HIPCHK(hipEventCreate(&e1));
+    HIPCHK(hipEventCreate(&e2));
+    const TokRef tok{nullptr, 0};
+    HIPCHK(hipEventRecord(e0, ctx->compute));
+    for (int it = 0; it < iters; ++it)
+        for (int l = 0; l < L; ++l) {
+            ExpertArgs ea = expert_args(ctx, l, ctx->d_xscratch, ctx->d_xscratch, tok, 1, 0);
+            HIPCHK(launch_gateup(ea, c.wfmt, ctx->compute));
+        }
+    HIPCHK(hipEventRecord(e1, ctx->compute));
+    for (int it = 0; it < iters; ++it)
+        for (int l = 0; l < L; ++l) {
+            ExpertArgs ea = expert_args(ctx, l, ctx->d_xscratch, ctx->d_xscratch, tok, 1, 0);
+            HIPCHK(launch_down(ea, c.wfmt, ctx->compute));
+        }
+    HIPCHK(hipEventRecord(e2, ctx->compute));
+    HIPCHK(hipEventSynchronize(e2));
+    float ms1 = 0, ms2 = 0;
+    HIPCHK(hipEventElapsedTime(&ms1, e0, e1));
+    HIPCHK(hipEventElapsedTime(&ms2, e1, e2));
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    hipEventDestroy(e2);
+    const float n = (float)iters * L;
+    if (us_gateup) *us_gateup = ms1 * 1000.0f / n;
+    if (us_down) *us_down = ms2 * 1000.0f / n;
+    if (us_route) *us_route = -1.0f;
+    return MOE_SPARK_OK;
+}
+
+}  // extern "C"

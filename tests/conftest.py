@@ -16,3 +16,22 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def _ensure_built():
+    """Build the three libraries if a fresh checkout has none (build() is the
+    normal route; this only covers a missing .so)."""
+    import importlib
+    for mod, path in (("workload", "workload/libworkload.so"), ("oracle", "oracle/liboracle.so")):
+        if not os.path.exists(os.path.join(ROOT, path)):
+            importlib.import_module(mod).build()
+    if not os.path.exists(os.path.join(ROOT, "resident_expert_caching_amd", "libmoe_spark.so")):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_moe_build", os.path.join(ROOT, "resident_expert_caching_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
+        b.build()
+
+
+_ensure_built()
