@@ -168,7 +168,7 @@ moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, cons
 /* Decode n_tokens independent tokens through all L layers, one graph launch
  * per token: x_{l+1} = x_l + MoE_l(RMSNorm(x_l)).  x [T][d] fp32 device,
  * updated in place; bias_row [T] int32 device or NULL.  The graph for a given
- * (x, bias_row) pair is built once and replayed. */
+ * (x, bias_row) pair is built once and replayed; n_tokens = 0 only builds it. */
 moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens,
                                   const int32_t* bias_row);
 

@@ -817,10 +817,10 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
     if (n_tokens < 0 || (n_tokens > 0 && !x)) return ctx->fail(MOE_SPARK_E_INVALID, "bad token count or NULL x");
     moe_spark_status st = ready_check(ctx);
     if (st != MOE_SPARK_OK) return st;
-    if (n_tokens == 0) return MOE_SPARK_OK;
+    if (!x) return MOE_SPARK_OK;
     hipGraphExec_t exec;
-    st = get_graph(ctx, x, bias_row, &exec);
-    if (st != MOE_SPARK_OK) return st;
+    st = get_graph(ctx, x, bias_row, &exec);  // n_tokens == 0 only prepares the graph
+    if (st != MOE_SPARK_OK || n_tokens == 0) return st;
     HIPCHK(hipMemsetAsync(ctx->d_cursors, 0, sizeof(int32_t), ctx->compute));
     for (int t = 0; t < n_tokens; ++t) {
         hipEvent_t& ev = ctx->tok_ev[ctx->tok_launched % kThrottle];
