@@ -188,7 +188,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gateup_q4_kernel (K=8 experts: gate+up GEMV + SwiGLU)",
+            "kernel": "q4_gateup_kernel (router-partial reduce, top-8, gate+up GEMV of 8 Q4_0 experts + SwiGLU)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

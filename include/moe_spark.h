@@ -210,10 +210,14 @@ moe_spark_status moe_spark_get_events(moe_spark_ctx* ctx, moe_spark_event* out, 
 /* Wait for all work of the context; report device-side errors. */
 moe_spark_status moe_spark_synchronize(moe_spark_ctx* ctx);
 
-/* Time the expert kernels in isolation: replays the gate/up and down kernels
- * of every layer with the last decoded token's selections, round-robin over
- * layers, `iters` passes, bracketed by HIP events on the compute stream.
- * Outputs microseconds per launch.  Writes only context scratch buffers. */
+/* Time the decode kernels in isolation: replays the gate/up and down kernels
+ * of every layer with each layer's last published selection (no placement
+ * policy, no fills), round-robin over layers, `iters` passes, bracketed by
+ * HIP events on the compute stream.  Outputs microseconds per launch:
+ * us_gateup (for Q4_0: router-partial reduce + top-k + gate/up GEMV + SwiGLU),
+ * us_down (down GEMV + combine + residual + next layer's router partials) and
+ * us_route (Q4_0: the first layer's router-partial kernel; fp32: -1).
+ * Writes only context scratch buffers.  Call between tokens. */
 moe_spark_status moe_spark_time_expert_kernels(moe_spark_ctx* ctx, int32_t iters,
                                                float* us_gateup, float* us_down,
                                                float* us_route);

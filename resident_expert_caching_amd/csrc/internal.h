@@ -26,6 +26,10 @@ constexpr int64_t kDownCodes = (int64_t)kQD * kQNBF * 16;          // 524,288 B
 constexpr int64_t kDownScales = (int64_t)kQD * kQNBF * 2;          // 65,536 B
 constexpr int64_t kQ4SlotBytes = kGURegion + kDownCodes + kDownScales;  // 1,769,472 B
 constexpr int kDownRowsPerWG = 8;
+// Router partial logits: a work-group owns kRW consecutive rows of x and
+// writes the router dot products restricted to those rows for every expert.
+constexpr int kRW = 16;
+constexpr int kNP = kQD / kRW;   // 128 partial rows
 
 // Device statistics counters (int64 each).
 enum DevStat { DS_ACC = 0, DS_PIN, DS_COLD, DS_RING, DS_FILL, DS_EVICT, DS_H2D, DS_TOKENS, DS_N };
@@ -125,6 +129,48 @@ struct ExpertArgs {
     int32_t* error;
     uint64_t spin_limit_ticks;  // fill wait limit, in wall-clock ticks (100 MHz)
 };
+
+// Arguments of the Q4_0 decode kernels (q4_decode.hip).  Per token-layer:
+// gate/up (reduce router partials, top-k, policy, gate/up GEMV + SwiGLU),
+// then down (down GEMV, gate-weighted combine, residual, router partials of
+// the next layer).  The first layer's partials come from the router-partial
+// kernel.
+struct Q4Args {
+    const float* x_base;     // [T][d] layer input (residual)
+    float* y_base;           // [T][d] layer output (may equal x_base)
+    TokRef tok;
+    TokRef trace_tok;
+    int32_t layer, L, E, K;
+    int32_t norm;            // RMSNorm before router and experts
+    int32_t residual;        // y = x + MoE
+    int32_t replay;          // timing replay: reuse the published selection, no policy
+    float eps;
+    float* pl;               // [kNP][E] router partial logits
+    float* ps;               // [kNP] partial sums of squares
+    const float* wr_part;    // packed router [kNP][E][kRW] whose partials this kernel writes, or null
+    const float* bias;       // this layer's router bias [n_bias_rows][E] or null
+    const int32_t* bias_row; // [T] or null
+    int32_t n_bias_rows;
+    const uint8_t* slots;
+    int64_t slot_bytes, P, n_slots;
+    const uint64_t* ready;   // host-mapped ring ready flags (device address)
+    LayerSel* sel;           // this layer's published selection
+    uint32_t* pub;           // this layer's publish flag
+    float* h;                // [K][f] in the down kernel's transposed layout
+    PolicyTables pt;
+    float* tr_x;
+    int32_t* tr_topk;
+    float* tr_gates;
+    int64_t tr_cap;
+    int32_t* topk_out;
+    float* gates_out;
+    uint64_t spin_limit_ticks;
+};
+
+hipError_t launch_q4_router_partial(const Q4Args& a, hipStream_t s);
+hipError_t launch_q4_gateup(const Q4Args& a, hipStream_t s);
+hipError_t launch_q4_down(const Q4Args& a, hipStream_t s);
+hipError_t launch_advance(int32_t* cursors, int64_t* stats, hipStream_t s);
 
 // Launchers (kernels.hip).
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

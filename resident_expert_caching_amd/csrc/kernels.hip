@@ -1,4 +1,5 @@
-// gfx950 kernels of the resident-expert-caching MoE decode path.
+// gfx950 kernels of the resident-expert-caching MoE decode path, fp32-weight
+// variant (the small configuration); Q4_0 decode runs in q4_decode.hip.
 //
 // Per layer and token (decode, batch 1):
 //   route   RMSNorm, router GEMV (+ Zipf bias), top-k, renormalised softmax,
@@ -21,59 +22,12 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace moe {
 
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xffffu));
-}
-
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
-
-__device__ __forceinline__ int tok_value(const TokRef& t) { return t.base + (t.ptr ? *t.ptr : 0); }
-
-// Dot product of one Q4_0 block's 32 codes (16 bytes, GGUF nibble order:
-// weight j in the low nibble of byte j, weight j+16 in the high nibble) with
-// the block's activations u[0..31] held as 8 f32x4 (uu[j] = u[4j..4j+3]).
-__device__ __forceinline__ float q4_dot(const u32x4 c, const f32x4* uu) {
-    const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
-    float acc = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint32_t lo = wd[m] & 0x0F0F0F0Fu;
-        const uint32_t hi = (wd[m] >> 4) & 0x0F0F0F0Fu;
-        const f32x4 ul = uu[m], uh = uu[4 + m];
-        acc += (float)(lo & 0xffu) * ul.x;
-        acc += (float)((lo >> 8) & 0xffu) * ul.y;
-        acc += (float)((lo >> 16) & 0xffu) * ul.z;
-        acc += (float)(lo >> 24) * ul.w;
-        acc += (float)(hi & 0xffu) * uh.x;
-        acc += (float)((hi >> 8) & 0xffu) * uh.y;
-        acc += (float)((hi >> 16) & 0xffu) * uh.z;
-        acc += (float)(hi >> 24) * uh.w;
-    }
-    return acc;
-}
-
-__device__ __forceinline__ float block_sum(const f32x4* uu) {
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s += (uu[j].x + uu[j].y) + (uu[j].z + uu[j].w);
-    return s;
-}
 
 // Wait until ring slot `ring` holds fill number `seq` (written by the host
 // fill agent after its copy completed).  Bounded: after `limit` wall-clock
@@ -382,161 +336,6 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- Q4_0 gate/up
-
-// Grid (f/16, K).  Work-group g of expert k owns rows 16g..16g+15 of gate
-// (waves 0, 1) and of up (waves 2, 3); each wave 8 rows; lane b = block b.
-// Slot layout of the chunk (36,864 B): codes at ((w*8 + i)*64 + b)*16, then
-// scales at 32768 + (w*64 + b)*16 + i*2 — every load is a coalesced 1 KiB.
-__global__ __launch_bounds__(256) void gateup_q4_kernel(ExpertArgs a) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int g = blockIdx.x, k = blockIdx.y;
-    const int slot = a.sel->slot[k];
-    const uint64_t wseq = a.sel->wait[k];
-    if (slot < 0 || slot >= a.n_slots) {  // never expected: refuse rather than fault
-        if (threadIdx.x == 0) atomicOr(a.error, (int)ERR_BAD_SLOT);
-        return;
-    }
-    if (wseq && slot >= a.P) wait_fill(a, (int)(slot - a.P), wseq);
-
-    const uint8_t* chunk = a.slots + (int64_t)slot * a.slot_bytes + (int64_t)g * kGUChunk;
-    const u32x4* cp = reinterpret_cast<const u32x4*>(chunk) + w * 8 * 64 + lane;
-    u32x4 c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = __builtin_nontemporal_load(cp + i * 64);
-    const u32x4 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(chunk + 32768) + w * 64 + lane);
-
-    f32x4 uu[8];
-    const f32x4* ut = reinterpret_cast<const f32x4*>(a.ut);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) uu[j] = ut[j * 64 + lane];
-    const float U8 = 8.0f * block_sum(uu);
-
-    const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float s = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
-        v[i] = s * (q4_dot(c[i], uu) - U8);
-    }
-    // 8 rows x 64 lanes -> one row per group of 8 lanes (fixed tree)
-    {
-        const bool h32 = lane & 32;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float send = h32 ? v[t] : v[t + 4];
-            const float keep = h32 ? v[t + 4] : v[t];
-            v[t] = keep + __shfl_xor(send, 32, 64);
-        }
-        const bool h16 = lane & 16;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float send = h16 ? v[t] : v[t + 2];
-            const float keep = h16 ? v[t + 2] : v[t];
-            v[t] = keep + __shfl_xor(send, 16, 64);
-        }
-        const bool h8 = lane & 8;
-        const float send = h8 ? v[0] : v[1];
-        const float keep = h8 ? v[1] : v[0];
-        v[0] = keep + __shfl_xor(send, 8, 64);
-        v[0] += __shfl_xor(v[0], 4, 64);
-        v[0] += __shfl_xor(v[0], 2, 64);
-        v[0] += __shfl_xor(v[0], 1, 64);
-    }
-    __shared__ float red[32];
-    if ((lane & 7) == 0) red[w * 8 + (lane >> 3)] = v[0];  // row (lane>>5)*4 + ((lane>>4)&1)*2 + ((lane>>3)&1)
-    __syncthreads();
-    if (threadIdx.x < 16) {
-        const int j = threadIdx.x;
-        const float h = silu(red[j]) * red[16 + j];
-        // h layout for the down kernel: f32x4 (k*8 + jj)*16 + b holds h[32b + 4jj .. +3]
-        const int n = g * 16 + j;
-        const int b = n >> 5, jj = (n >> 2) & 7, cc = n & 3;
-        a.h[(((int64_t)k * 8 + jj) * 16 + b) * 4 + cc] = h;
-    }
-}
-
-// ---------------------------------------------------------------- Q4_0 down + combine
-
-// Grid d/8.  Work-group g owns rows 8g..8g+7; wave w covers experts
-// (w&1)*4 .. +3 and rows 8g + (w>>1)*4 .. +3; lane = (expert kl, block b).
-// Slot down region: codes [r][b][16 B], scales [(r/4)][b][4] fp16.
-__global__ __launch_bounds__(256) void down_q4_kernel(ExpertArgs a) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int g = blockIdx.x;
-    const int eh = w & 1, rq = w >> 1;
-    const int kl = lane >> 4, b = lane & 15;
-    const int k = eh * 4 + kl;
-    const bool act = k < a.K;
-    const int r0 = g * kDownRowsPerWG + rq * 4;
-    const int tok = tok_value(a.tok);
-
-    float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int slot = act ? a.sel->slot[k] : 0;
-    if (act && (slot < 0 || slot >= a.n_slots)) {
-        atomicOr(a.error, (int)ERR_BAD_SLOT);
-    } else if (act) {
-        const uint8_t* base = a.slots + (int64_t)slot * a.slot_bytes + kGURegion;
-        u32x4 c[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + i) * 256) + b);
-        const u32x2 sc = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + b);
-        f32x4 hh[8];
-        const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hh[j] = h4[(k * 8 + j) * 16 + b];
-        const float H8 = 8.0f * block_sum(hh);
-        const uint32_t sw[2] = {sc.x, sc.y};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float s = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
-            z[i] = s * (q4_dot(c[i], hh) - H8);
-        }
-    }
-    // 4 rows x 16 lanes -> one row per group of 4 lanes
-    {
-        const bool h8 = lane & 8;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float send = h8 ? z[t] : z[t + 2];
-            const float keep = h8 ? z[t + 2] : z[t];
-            z[t] = keep + __shfl_xor(send, 8, 64);
-        }
-        const bool h4b = lane & 4;
-        const float send = h4b ? z[0] : z[1];
-        const float keep = h4b ? z[1] : z[0];
-        z[0] = keep + __shfl_xor(send, 4, 64);
-        z[0] += __shfl_xor(z[0], 2, 64);
-        z[0] += __shfl_xor(z[0], 1, 64);
-    }
-    __shared__ float zs[kQ4MaxK][kDownRowsPerWG];
-    if ((lane & 3) == 0) zs[k][rq * 4 + ((lane >> 2) & 3)] = z[0];
-    __syncthreads();
-    if (threadIdx.x < kDownRowsPerWG) {
-        const int r = g * kDownRowsPerWG + threadIdx.x;
-        float y = 0.0f;
-        for (int kk = 0; kk < a.K; ++kk) y += a.sel->gate[kk] * zs[kk][threadIdx.x];
-        const int64_t o = (int64_t)tok * a.d + r;
-        a.y_base[o] = a.residual ? a.x_base[o] + y : y;
-    }
-    if (a.advance) {
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            __threadfence();
-            const unsigned prev = atomicAdd(a.done, 1u);
-            if (prev == gridDim.x - 1) {
-                atomicExch(a.done, 0u);
-                a.cursors[0] += 1;
-                a.cursors[1] += 1;
-                a.stats[DS_TOKENS] += 1;
-                __threadfence();
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------- fp32 experts
 
 // Grid (ceil(f/4), K); wave w computes row 4*bx + w of gate and up.
@@ -631,20 +430,14 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gateup(const ExpertArgs& a, int wfmt, hipStream_t s) {
-    if (wfmt == MOE_SPARK_W_Q4_0) {
-        hipLaunchKernelGGL(gateup_q4_kernel, dim3(kQF / kGURows, a.K), dim3(256), 0, s, a);
-    } else {
-        hipLaunchKernelGGL(gateup_f32_kernel, dim3((a.f + 3) / 4, a.K), dim3(256), 0, s, a);
-    }
+    if (wfmt != MOE_SPARK_W_F32) return hipErrorInvalidValue;  // Q4_0 runs in q4_decode.hip
+    hipLaunchKernelGGL(gateup_f32_kernel, dim3((a.f + 3) / 4, a.K), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_down(const ExpertArgs& a, int wfmt, hipStream_t s) {
-    if (wfmt == MOE_SPARK_W_Q4_0) {
-        hipLaunchKernelGGL(down_q4_kernel, dim3(kQD / kDownRowsPerWG), dim3(256), 0, s, a);
-    } else {
-        hipLaunchKernelGGL(down_f32_kernel, dim3((a.d + 3) / 4), dim3(256), 0, s, a);
-    }
+    if (wfmt != MOE_SPARK_W_F32) return hipErrorInvalidValue;  // Q4_0 runs in q4_decode.hip
+    hipLaunchKernelGGL(down_f32_kernel, dim3((a.d + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

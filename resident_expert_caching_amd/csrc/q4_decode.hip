@@ -1,0 +1,639 @@
+// gfx950 Q4_0 decode kernels: one token-layer is two launches.
+//
+//   gateup  every work-group rebuilds the router logits from the partial
+//           dot products the previous launch left behind, runs the top-k and
+//           the renormalised softmax itself ("Luce Spark runs 35B MoE models
+//           on 16GB GPU without speed loss", opening paragraph: each token
+//           picks about 8 of 256 experts), looks its expert up in the slot
+//           table, and computes h = silu(Wg u) * (Wu u) for 16 rows of one
+//           expert.  Work-group (0,0) also runs the placement policy of the
+//           same page's paragraph "The key components" — per-expert counts,
+//           pinned set, the LRU spare-slot ring and the fill request — and
+//           publishes the slot of every cold expert; only work-groups of cold
+//           experts wait for that, and for the fill to land.
+//   down    the down GEMV of all K experts for 16 output rows, the
+//           gate-weighted combine in rank order, the residual, and the
+//           router partial logits of the next layer over those 16 rows.
+//
+// A router logit l_e = inv_rms * sum_i Wr[e][i] x_i + b_e is assembled from
+// kNP partial sums over 16-row slices of x, each written by the work-group
+// that produced those rows, so the router never needs a launch of its own.
+// Reductions have fixed trees and fixed orders; there are no floating-point
+// atomics; the slot a weight is read from never changes the arithmetic, so
+// outputs are bit-identical at every residency (same paragraph: full
+// residency is bit-identical to all-GPU execution).
+//
+// Q4_0 inner product per row: sum_i s (q_i - 8) u_i = s (sum_i q_i u_i - 8 U_b)
+// with U_b the block's activation sum, so the offset and the scale leave the
+// inner loop.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+static_assert(kNP == 128, "the gate/up kernel sums the partial squares with two loads per lane");
+
+__device__ __forceinline__ bool spin_expired(const Q4Args& a, uint64_t t0) {
+    return wall_clock64() - t0 > a.spin_limit_ticks ||
+           (__hip_atomic_load(a.pt.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ERR_FILL_TIMEOUT);
+}
+
+// Partial router logits over one 16-row slice: pl[p][e] = sum_i Wr[e][16p+i] xs[i]
+// and ps[p] = sum_i xs[i]^2.  wpre holds this thread's first expert's weights.
+__device__ __forceinline__ void router_partial(const Q4Args& a, int p, const float* xs, const f32x4* wpre) {
+    const int t = threadIdx.x, E = a.E;
+    for (int e = t; e < E; e += kThreads) {
+        f32x4 w[4];
+        if (e == t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = wpre[i];
+        } else {
+            const f32x4* w4 = reinterpret_cast<const f32x4*>(a.wr_part + ((int64_t)p * E + e) * kRW);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = w4[i];
+        }
+        float q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q[i] = (w[i].x * xs[4 * i] + w[i].y * xs[4 * i + 1]) + (w[i].z * xs[4 * i + 2] + w[i].w * xs[4 * i + 3]);
+        a.pl[(int64_t)p * E + e] = (q[0] + q[1]) + (q[2] + q[3]);
+    }
+    if (t == 0) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kRW; ++i) s += xs[i] * xs[i];
+        a.ps[p] = s;
+    }
+}
+
+__device__ __forceinline__ void load_wpre(const Q4Args& a, int p, f32x4* wpre) {
+    const int t = threadIdx.x;
+    if (a.wr_part && t < a.E) {
+        const f32x4* w4 = reinterpret_cast<const f32x4*>(a.wr_part + ((int64_t)p * a.E + t) * kRW);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wpre[i] = w4[i];
+    }
+}
+
+// ---------------------------------------------------------------- router partials (first layer)
+
+// Grid kNP.  Work-group p reads rows 16p..16p+15 of the token's x.
+__global__ __launch_bounds__(kThreads) void q4_router_partial_kernel(Q4Args a) {
+    const int p = blockIdx.x, t = threadIdx.x;
+    f32x4 wpre[4];
+    load_wpre(a, p, wpre);
+    __shared__ float xs[kRW];
+    if (t < kRW) xs[t] = a.x_base[(int64_t)tok_value(a.tok) * kQD + p * kRW + t];
+    __syncthreads();
+    router_partial(a, p, xs, wpre);
+}
+
+// ---------------------------------------------------------------- placement policy
+
+// Single wave of work-group (0,0): counts, slot lookup, the LRU ring and fill
+// requests, in rank order; then the selection is published for the cold
+// experts' work-groups and the down launch.
+__device__ void run_policy(const Q4Args& a, const int* sel_e, const float* gk, const int32_t* sof, int tok,
+                           float inv, int32_t* r_owner, uint64_t* r_stamp, uint64_t* r_seq) {
+    // sel_e, gk, sof live in LDS: the rank loop stays a loop (no unrolled copies)
+    const int lane = threadIdx.x;
+    const PolicyTables& pt = a.pt;
+    const int K = a.K, E = a.E;
+    const int32_t kbase = a.layer * E;
+    int my_slot = -1;
+    uint64_t my_wait = 0;
+    int any_cold = 0;
+    for (int k = 0; k < K; ++k) any_cold |= sof[sel_e[k]] < 0;
+    int64_t n_pin = 0, n_cold = 0, n_ring = 0, n_fill = 0, n_evict = 0;
+    if (!any_cold) {
+        if (lane < K) my_slot = sof[sel_e[lane]];
+        n_pin = K;
+    } else {
+        const int R = pt.R;
+        for (int r = lane; r < R; r += 64) {
+            r_owner[r] = pt.ring_owner[r];
+            r_stamp[r] = pt.ring_stamp[r];
+            r_seq[r] = pt.ring_seq[r];
+        }
+        uint64_t clock = *pt.clock, fseq = *pt.fill_seq;
+        int64_t nev = *pt.n_events;
+#pragma nounroll
+        for (int k = 0; k < K; ++k) {
+            const int32_t key = kbase + sel_e[k];
+            const int pin = sof[sel_e[k]];
+            int slot;
+            uint64_t wseq = 0;
+            if (pin >= 0) {
+                slot = pin;
+                ++n_pin;
+            } else {
+                ++n_cold;
+                int hit = -1;
+                for (int base = 0; base < R && hit < 0; base += 64) {
+                    const int r = base + lane;
+                    const uint64_t m = __ballot(r < R && r_owner[r] == key);
+                    if (m) hit = base + __builtin_ctzll(m);
+                }
+                if (hit >= 0) {
+                    // filled by an earlier token-layer whose kernels waited for the copy
+                    ++n_ring;
+                    ++clock;
+                    if (lane == 0) r_stamp[hit] = clock;
+                    slot = (int)(pt.P + hit);
+                } else {
+                    int v = -1;
+                    for (int base = 0; base < R && v < 0; base += 64) {
+                        const int r = base + lane;
+                        const uint64_t m = __ballot(r < R && r_owner[r] < 0);
+                        if (m) v = base + __builtin_ctzll(m);
+                    }
+                    if (v < 0) {  // least recently used: smallest stamp (stamps are unique)
+                        uint64_t bs = ~0ull;
+                        int bi = 0x7fffffff;
+                        for (int r = lane; r < R; r += 64)
+                            if (r_stamp[r] < bs) { bs = r_stamp[r]; bi = r; }
+#pragma unroll
+                        for (int m = 32; m >= 1; m >>= 1) {
+                            const uint64_t os = __shfl_xor(bs, m, 64);
+                            const int oi = __shfl_xor(bi, m, 64);
+                            if (os < bs || (os == bs && oi < bi)) { bs = os; bi = oi; }
+                        }
+                        v = bi;
+                    }
+                    const int32_t victim = r_owner[v];
+                    if (victim >= 0) ++n_evict;
+                    ++clock;
+                    ++fseq;
+                    ++n_fill;
+                    if (lane == 0) {
+                        r_owner[v] = key;
+                        r_stamp[v] = clock;
+                        r_seq[v] = fseq;
+                        if (nev < pt.event_cap) {
+                            moe_spark_event ev;
+                            ev.seq = (int64_t)fseq;
+                            ev.layer = a.layer;
+                            ev.expert = sel_e[k];
+                            ev.slot = (int32_t)(pt.P + v);
+                            ev.kind = MOE_SPARK_EV_FILL;
+                            ev.victim = victim;
+                            ev.pad = 0;
+                            pt.events[nev] = ev;
+                        }
+                        FifoEntry* fe = pt.fifo + ((fseq - 1) % kFifoCap);
+                        fe->key = key;
+                        fe->ring = v;
+                        __threadfence_system();
+                        __hip_atomic_store(&fe->seq, fseq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+                    }
+                    ++nev;
+                    wseq = fseq;
+                    slot = (int)(pt.P + v);
+                }
+            }
+            if (lane == k) { my_slot = slot; my_wait = wseq; }
+        }
+        for (int r = lane; r < R; r += 64) {
+            pt.ring_owner[r] = r_owner[r];
+            pt.ring_stamp[r] = r_stamp[r];
+            pt.ring_seq[r] = r_seq[r];
+        }
+        if (lane == 0) {
+            *pt.clock = clock;
+            *pt.fill_seq = fseq;
+            *pt.n_events = nev;
+        }
+    }
+    if (lane < K) {
+        const int myk = sel_e[lane];
+        const float myg = gk[lane];
+        atomicAdd(reinterpret_cast<unsigned long long*>(pt.counts + kbase + myk), 1ull);
+        a.sel->idx[lane] = myk;
+        a.sel->slot[lane] = my_slot;
+        a.sel->gate[lane] = myg;
+        a.sel->wait[lane] = my_wait;
+        const int ttok = tok_value(a.trace_tok);
+        if (a.tr_topk && ttok < a.tr_cap) {
+            const int64_t o = ((int64_t)ttok * a.L + a.layer) * K + lane;
+            a.tr_topk[o] = myk;
+            a.tr_gates[o] = myg;
+        }
+        if (a.topk_out) {
+            a.topk_out[(int64_t)tok * K + lane] = myk;
+            a.gates_out[(int64_t)tok * K + lane] = myg;
+        }
+    }
+    if (lane == 0) {
+        a.sel->inv_rms = inv;
+        unsigned long long* st = reinterpret_cast<unsigned long long*>(pt.stats);
+        atomicAdd(st + DS_ACC, (unsigned long long)K);
+        if (n_pin) atomicAdd(st + DS_PIN, (unsigned long long)n_pin);
+        if (n_cold) atomicAdd(st + DS_COLD, (unsigned long long)n_cold);
+        if (n_ring) atomicAdd(st + DS_RING, (unsigned long long)n_ring);
+        if (n_fill) {
+            atomicAdd(st + DS_FILL, (unsigned long long)n_fill);
+            atomicAdd(st + DS_H2D, (unsigned long long)(n_fill * pt.slot_bytes));
+        }
+        if (n_evict) atomicAdd(st + DS_EVICT, (unsigned long long)n_evict);
+    }
+    if (any_cold) {
+        // only work-groups of cold experts read the selection inside this
+        // launch; the down launch sees it at the kernel boundary
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) __hip_atomic_store(a.pub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------- gate/up
+
+// Grid (f/16, K).  Work-group (g, k) owns rows 16g..16g+15 of the gate and up
+// matrices of the rank-k expert: waves 0, 1 gate rows, waves 2, 3 up rows,
+// 8 rows per wave, lane b = Q4_0 block b along d.  Slot chunk g (36,864 B):
+// codes at ((w*8 + i)*64 + b)*16, scales at 32768 + (w*64 + b)*16 + 2i, so
+// every load of a wave is one coalesced 1 KiB line.
+__global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int g = blockIdx.x, k = blockIdx.y;
+    const int E = a.E, K = a.K;
+    const int tok = tok_value(a.tok);
+
+    __shared__ __align__(16) float lg[kMaxE];
+    __shared__ int32_t sof[kMaxE];
+    __shared__ __align__(16) float xt[kQD / 32 * 36];
+    __shared__ __align__(16) float lg_pad[kThreads];
+    __shared__ __align__(16) float cand_v[kMaxE / 64 * kQ4MaxK + 4];
+    __shared__ __align__(16) int32_t cand_e[kMaxE / 64 * kQ4MaxK + 4];
+    __shared__ int s_e[kMaxK];
+    __shared__ float s_l[kMaxK];
+    __shared__ float s_g[kMaxK];
+    __shared__ float s_z;
+    __shared__ float s_inv;
+    __shared__ int s_slot;
+    __shared__ unsigned long long s_wseq;
+    __shared__ float red[32];
+    __shared__ __align__(16) float red4[4][kThreads];
+    __shared__ int32_t r_owner[kMaxR];
+    __shared__ uint64_t r_stamp[kMaxR];
+    __shared__ uint64_t r_seq[kMaxR];
+
+    // Independent loads first: this lane's activation block, the slot table
+    // row, the partial logits.
+    // x is read once per work-group, coalesced, and transposed through LDS:
+    // Q4_0 block b (32 floats) sits at float 36*b, so that the per-lane
+    // 16-byte reads of a block are free of bank conflicts.
+    {
+        const f32x4* x4 = reinterpret_cast<const f32x4*>(a.x_base + (int64_t)tok * kQD);
+        const f32x4 v0 = x4[t], v1 = x4[t + kThreads];
+        *reinterpret_cast<f32x4*>(&xt[36 * (t >> 3) + 4 * (t & 7)]) = v0;
+        *reinterpret_cast<f32x4*>(&xt[36 * ((t + kThreads) >> 3) + 4 * (t & 7)]) = v1;
+    }
+    for (int e = t; e < E; e += kThreads) sof[e] = a.pt.slot_of[(int64_t)a.layer * E + e];
+    // Router logits from the partials: wave w sums partial rows w, w+4, ...
+    // for experts 4*lane..4*lane+3 of each 256-expert chunk, all 32 loads of
+    // a chunk in flight at once; the 4 wave sums are added in LDS in wave order.
+    float ss = 0.0f;
+    if (w == 0) ss = a.ps[lane] + a.ps[lane + 64];
+    for (int e0 = 0; e0 < E; e0 += kThreads) {
+        const int e = e0 + 4 * lane;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (e < E) {
+            f32x4 v[kNP / 4];
+#pragma unroll
+            for (int j = 0; j < kNP / 4; ++j)
+                v[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(w + 4 * j) * E + e);
+#pragma unroll
+            for (int j = 0; j < kNP / 4; ++j) acc += v[j];
+        }
+        __syncthreads();  // the previous chunk's lg reads are done
+        if (e < E) *reinterpret_cast<f32x4*>(&red4[w][4 * lane]) = acc;
+        __syncthreads();
+        if (e0 + t < E) lg[e0 + t] = (red4[0][t] + red4[1][t]) + (red4[2][t] + red4[3][t]);
+    }
+    if (w == 0) {
+        ss = wave_sum(ss);
+        if (lane == 0) s_inv = a.norm ? 1.0f / sqrtf(ss / (float)kQD + a.eps) : 1.0f;
+    }
+    __syncthreads();
+    const float inv = s_inv;
+    f32x4 xx[8];  // this lane's Q4_0 block of x
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xx[j] = *reinterpret_cast<const f32x4*>(&xt[36 * lane + 4 * j]);
+    {
+        const float* brow = nullptr;
+        if (a.bias) {
+            int row = a.bias_row ? a.bias_row[tok] : 0;
+            row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
+            brow = a.bias + (int64_t)row * E;
+        }
+        for (int e = t; e < E; e += kThreads) lg[e] = lg[e] * inv + (brow ? brow[e] : 0.0f);
+    }
+    if (t < K) {  // defined even if NaN logits leave a rank unfilled
+        s_e[t] = 0;
+        s_l[t] = -INFINITY;
+    }
+    __syncthreads();
+
+    // top-k over (logit desc, index asc), exact, in two ranking passes:
+    //  1. wave w ranks each 64-expert chunk c = w, w+4, ... within the chunk;
+    //     the chunk's first K become candidates (padding lanes past E hold
+    //     -inf with an index >= E, so they rank below every real expert);
+    //  2. the candidates are ranked among themselves.
+    // The global top K lie among the candidates, and a candidate's rank among
+    // candidates is its global rank whenever that is below K.
+    const int n_chunks = (E + 63) >> 6;
+    for (int c = w; c < n_chunks; c += 4) {
+        const int e = c * 64 + lane;
+        const float v = e < E ? lg[e] : -INFINITY;
+        lg_pad[lane + 64 * w] = v;
+        __builtin_amdgcn_wave_barrier();
+        int r = 0;
+#pragma unroll 4
+        for (int j = 0; j < 64; j += 4) {
+            const f32x4 q = *reinterpret_cast<const f32x4*>(&lg_pad[64 * w + j]);
+            r += (int)(q.x > v) + (int)((q.x == v) & (j < lane));
+            r += (int)(q.y > v) + (int)((q.y == v) & (j + 1 < lane));
+            r += (int)(q.z > v) + (int)((q.z == v) & (j + 2 < lane));
+            r += (int)(q.w > v) + (int)((q.w == v) & (j + 3 < lane));
+        }
+        if (r < K) {
+            cand_v[c * K + r] = v;
+            cand_e[c * K + r] = e;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (t < 4) {  // padding past the candidates: -inf with an index no expert has
+        cand_v[n_chunks * K + t] = -INFINITY;
+        cand_e[n_chunks * K + t] = 0x7fffffff;
+    }
+    __syncthreads();
+    {
+        const int nc = n_chunks * K;
+        for (int i = t; i < nc; i += kThreads) {
+            const float v = cand_v[i];
+            const int e = cand_e[i];
+            int r = 0;
+#pragma unroll 2
+            for (int j = 0; j < nc; j += 4) {  // entries past nc are padding that ranks last
+                const f32x4 q = *reinterpret_cast<const f32x4*>(&cand_v[j]);
+                const int4 qe = *reinterpret_cast<const int4*>(&cand_e[j]);
+                r += (int)(q.x > v) + (int)((q.x == v) & (qe.x < e));
+                r += (int)(q.y > v) + (int)((q.y == v) & (qe.y < e));
+                r += (int)(q.z > v) + (int)((q.z == v) & (qe.z < e));
+                r += (int)(q.w > v) + (int)((q.w == v) & (qe.w < e));
+            }
+            if (r < K && e >= 0 && e < E) {
+                s_e[r] = e;
+                s_l[r] = v;
+            }
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        if (g == 0 && k == 0 && !a.replay) {
+            // gates: softmax over the chosen logits, shifted by the largest
+            if (lane < K) s_g[lane] = expf(s_l[lane] - s_l[0]);
+            if (lane == 0) {
+                float z = 0.0f;
+                for (int kk = 0; kk < K; ++kk) z += s_g[kk];
+                s_z = z;
+            }
+            if (lane < K) s_g[lane] = s_g[lane] / s_z;
+            const int ttok = tok_value(a.trace_tok);
+            if (a.tr_x && ttok < a.tr_cap) {
+                f32x4* t4 = reinterpret_cast<f32x4*>(a.tr_x + ((int64_t)ttok * a.L + a.layer) * kQD);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) t4[lane * 8 + j] = xx[j];
+            }
+            run_policy(a, s_e, s_g, sof, tok, inv, r_owner, r_stamp, r_seq);
+        }
+    }
+    __syncthreads();
+
+    int slot;
+    uint64_t wseq = 0;
+    if (a.replay) {
+        slot = a.sel->slot[k];
+    } else {
+        slot = sof[s_e[k]];
+        if (slot < 0) {  // cold expert: take the slot work-group (0,0) chose
+            if (t == 0) {
+                const uint64_t t0 = wall_clock64();
+                while (__hip_atomic_load(a.pub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (spin_expired(a, t0)) {
+                        atomicOr(a.pt.error, (int)ERR_FILL_TIMEOUT);
+                        break;
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                s_slot = a.sel->slot[k];
+                s_wseq = a.sel->wait[k];
+            }
+            __syncthreads();
+            slot = s_slot;
+            wseq = s_wseq;
+        }
+    }
+    if (slot < 0 || slot >= a.n_slots) {  // never expected: refuse rather than fault
+        if (t == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
+        return;
+    }
+    if (wseq && slot >= a.P) {
+        // ring slot still filling: wait for the host agent's ready flag
+        if (t == 0) {
+            const uint64_t* flag = a.ready + (slot - a.P);
+            const uint64_t t0 = wall_clock64();
+            while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < wseq) {
+                __builtin_amdgcn_s_sleep(4);
+                if (spin_expired(a, t0)) {
+                    atomicOr(a.pt.error, (int)ERR_FILL_TIMEOUT);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+    }
+
+    const uint8_t* chunk = a.slots + (int64_t)slot * a.slot_bytes + (int64_t)g * kGUChunk;
+    const u32x4* cp = reinterpret_cast<const u32x4*>(chunk) + w * 8 * 64 + lane;
+    u32x4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_nontemporal_load(cp + i * 64);
+    const u32x4 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(chunk + 32768) + w * 64 + lane);
+
+    f32x4 uu[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) uu[j] = xx[j] * inv;
+    const float U8 = 8.0f * block_sum(uu);
+
+    const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float s = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
+        v[i] = s * (q4_dot(c[i], uu) - U8);
+    }
+    // 8 rows x 64 lanes -> one row per group of 8 lanes (fixed tree)
+    {
+        const bool h32 = lane & 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float send = h32 ? v[q] : v[q + 4];
+            const float keep = h32 ? v[q + 4] : v[q];
+            v[q] = keep + __shfl_xor(send, 32, 64);
+        }
+        const bool h16 = lane & 16;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float send = h16 ? v[q] : v[q + 2];
+            const float keep = h16 ? v[q + 2] : v[q];
+            v[q] = keep + __shfl_xor(send, 16, 64);
+        }
+        const bool h8 = lane & 8;
+        const float send = h8 ? v[0] : v[1];
+        const float keep = h8 ? v[1] : v[0];
+        v[0] = keep + __shfl_xor(send, 8, 64);
+        v[0] += __shfl_xor(v[0], 4, 64);
+        v[0] += __shfl_xor(v[0], 2, 64);
+        v[0] += __shfl_xor(v[0], 1, 64);
+    }
+    // lane group (lane >> 3) holds row (lane>>5)*4 + ((lane>>4)&1)*2 + ((lane>>3)&1) of the wave
+    if ((lane & 7) == 0) red[w * 8 + (lane >> 3)] = v[0];
+    __syncthreads();
+    if (t < 16) {
+        const int j = t;
+        const float hv = silu(red[j]) * red[16 + j];
+        // h layout for the down kernel: f32x4 (k*8 + jj)*16 + b holds h[32b + 4jj .. +3]
+        const int n = g * 16 + j;
+        const int b = n >> 5, jj = (n >> 2) & 7, cc = n & 3;
+        a.h[(((int64_t)k * 8 + jj) * 16 + b) * 4 + cc] = hv;
+    }
+}
+
+// ---------------------------------------------------------------- down + combine + next router partials
+
+// Grid kNP.  Work-group p owns output rows 16p..16p+15.  Thread t: expert rank
+// (t >> 5), row half ((t >> 4) & 1), Q4_0 block (t & 15) along f; 8 rows each.
+// Slot down region: codes [r][b][16 B], scales [r/4][b][4] fp16.
+__global__ __launch_bounds__(kThreads) void q4_down_kernel(Q4Args a) {
+    const int t = threadIdx.x, lane = t & 63;
+    const int p = blockIdx.x;
+    const int kq = t >> 5, half = (lane >> 4) & 1, b = lane & 15;
+    const int r0 = p * kRW + half * 8;
+    const int tok = tok_value(a.tok);
+    const int K = a.K;
+
+    f32x4 wpre[4];
+    load_wpre(a, p, wpre);
+    float xr = 0.0f;
+    if (t < kRW && a.residual) xr = a.x_base[(int64_t)tok * kQD + p * kRW + t];
+
+    const bool act = kq < K;
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = 0.0f;
+    const int slot = act ? a.sel->slot[kq] : 0;
+    if (act && (slot < 0 || slot >= a.n_slots)) {
+        if (b == 0 && half == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
+    } else if (act) {
+        const uint8_t* base = a.slots + (int64_t)slot * a.slot_bytes + kGURegion;
+        u32x4 c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + i) * 256) + b);
+        const u32x2 s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + b);
+        const u32x2 s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + ((r0 >> 2) + 1) * 16 + b);
+        f32x4 hh[8];
+        const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hh[j] = h4[(kq * 8 + j) * 16 + b];
+        const float H8 = 8.0f * block_sum(hh);
+        const uint32_t sw[4] = {s0.x, s0.y, s1.x, s1.y};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float s = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
+            z[i] = s * (q4_dot(c[i], hh) - H8);
+        }
+    }
+    // 8 rows x 16 lanes -> one row per pair of lanes (fixed tree)
+    {
+        const bool h8 = lane & 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float send = h8 ? z[q] : z[q + 4];
+            const float keep = h8 ? z[q + 4] : z[q];
+            z[q] = keep + __shfl_xor(send, 8, 64);
+        }
+        const bool h4 = lane & 4;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float send = h4 ? z[q] : z[q + 2];
+            const float keep = h4 ? z[q + 2] : z[q];
+            z[q] = keep + __shfl_xor(send, 4, 64);
+        }
+        const bool h2 = lane & 2;
+        const float send = h2 ? z[0] : z[1];
+        const float keep = h2 ? z[1] : z[0];
+        z[0] = keep + __shfl_xor(send, 2, 64);
+        z[0] += __shfl_xor(z[0], 1, 64);
+    }
+    __shared__ float zs[kQ4MaxK][kRW];
+    __shared__ float xn[kRW];
+    if ((lane & 1) == 0)
+        zs[kq][half * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1)] = z[0];
+    __syncthreads();
+    if (t < kRW) {
+        float y = 0.0f;
+        for (int kk = 0; kk < K; ++kk) y += a.sel->gate[kk] * zs[kk][t];  // rank order
+        const float o = a.residual ? xr + y : y;
+        a.y_base[(int64_t)tok * kQD + p * kRW + t] = o;
+        xn[t] = o;
+    }
+    if (p == 0 && t == 0 && !a.replay) *a.pub = 0u;  // every gate/up work-group of this layer has finished
+    if (a.wr_part) {
+        __syncthreads();
+        router_partial(a, p, xn, wpre);
+    }
+}
+
+__global__ void advance_kernel(int32_t* cursors, int64_t* stats) {
+    if (threadIdx.x == 0) {
+        cursors[0] += 1;
+        cursors[1] += 1;
+        stats[DS_TOKENS] += 1;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_q4_router_partial(const Q4Args& a, hipStream_t s) {
+    if (!a.wr_part || a.E > kMaxE) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(q4_router_partial_kernel, dim3(kNP), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_gateup(const Q4Args& a, hipStream_t s) {
+    if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE || a.E < a.K) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(q4_gateup_kernel, dim3(kQF / kGURows, a.K), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_down(const Q4Args& a, hipStream_t s) {
+    if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(q4_down_kernel, dim3(kNP), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_advance(int32_t* cursors, int64_t* stats, hipStream_t s) {
+    hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, cursors, stats);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -21,6 +21,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdlib>
 #include <deque>
 #include <string>
 #include <thread>
@@ -83,6 +84,9 @@ struct moe_spark_ctx {
     float* d_ut = nullptr;          // [d]
     float* d_h = nullptr;           // [kMaxK * f]
     float* d_xscratch = nullptr;    // [d]
+    float* d_pl = nullptr;          // [kNP][E] router partial logits (Q4_0)
+    float* d_ps = nullptr;          // [kNP] partial sums of squares (Q4_0)
+    uint32_t* d_pub = nullptr;      // [L] selection-published flags (Q4_0)
 
     // host-mapped
     FifoEntry* h_fifo = nullptr;
@@ -105,6 +109,7 @@ struct moe_spark_ctx {
     hipEvent_t tok_ev[kThrottle] = {};
     int64_t tok_launched = 0;
     uint64_t spin_ticks = 0;
+    bool stream_decode = false;  // MOE_SPARK_DECODE_STREAM=1: per-kernel launches instead of the token graph
 
     // fill agent
     std::thread agent;
@@ -312,7 +317,7 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_ring_stamp, ctx->d_ring_seq, ctx->d_clock, ctx->d_counts, ctx->d_stats,
                      ctx->d_events, ctx->d_n_events, ctx->d_error,  ctx->d_cursors, ctx->d_done,
                      ctx->d_sel,    ctx->d_logits,   ctx->d_u,      ctx->d_ut,      ctx->d_h,
-                     ctx->d_xscratch};
+                     ctx->d_xscratch, ctx->d_pl,     ctx->d_ps,     ctx->d_pub};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
@@ -413,6 +418,50 @@ ExpertArgs expert_args(const moe_spark_ctx* ctx, int layer, const float* x, floa
     return a;
 }
 
+// Arguments of the Q4_0 decode kernels of one token-layer.  wr_layer: the
+// layer whose packed router the launch turns into partial logits (-1: none).
+Q4Args q4_args(const moe_spark_ctx* ctx, int layer, const float* x, float* y, TokRef tok, TokRef ttok,
+               const int32_t* bias_row, int norm, int residual, int wr_layer, int32_t* topk_out,
+               float* gates_out, int replay) {
+    const auto& c = ctx->cfg;
+    Q4Args a{};
+    a.x_base = x;
+    a.y_base = y;
+    a.tok = tok;
+    a.trace_tok = ttok;
+    a.layer = layer;
+    a.L = c.n_layers;
+    a.E = c.n_experts;
+    a.K = c.top_k;
+    a.norm = norm;
+    a.residual = residual;
+    a.replay = replay;
+    a.eps = c.rms_eps;
+    a.pl = ctx->d_pl;
+    a.ps = ctx->d_ps;
+    a.wr_part = wr_layer >= 0 ? ctx->d_router + (int64_t)wr_layer * c.n_experts * c.d_model : nullptr;
+    a.bias = c.n_bias_rows > 0 ? ctx->d_bias + (int64_t)layer * c.n_bias_rows * c.n_experts : nullptr;
+    a.bias_row = bias_row;
+    a.n_bias_rows = c.n_bias_rows;
+    a.slots = ctx->d_slots;
+    a.slot_bytes = ctx->slot_bytes;
+    a.P = c.resident_cap;
+    a.n_slots = ctx->n_slots;
+    a.ready = ctx->d_ready;
+    a.sel = ctx->d_sel + layer;
+    a.pub = ctx->d_pub + layer;
+    a.h = ctx->d_h;
+    a.pt = tables(ctx);
+    a.tr_x = replay ? nullptr : ctx->tr_x;
+    a.tr_topk = replay ? nullptr : ctx->tr_topk;
+    a.tr_gates = replay ? nullptr : ctx->tr_gates;
+    a.tr_cap = ctx->tr_cap;
+    a.topk_out = topk_out;
+    a.gates_out = gates_out;
+    a.spin_limit_ticks = ctx->spin_ticks;
+    return a;
+}
+
 moe_spark_status ready_check(moe_spark_ctx* ctx) {
     if (ctx->n_router_set != ctx->cfg.n_layers || ctx->n_expert_set != ctx->n_experts_total)
         return ctx->fail(MOE_SPARK_E_STATE, "every router and expert must be set first (%lld/%d routers, %lld/%lld experts)",
@@ -455,6 +504,18 @@ void drop_graphs(moe_spark_ctx* ctx) {
 moe_spark_status launch_token_kernels(moe_spark_ctx* ctx, float* x, const int32_t* bias_row) {
     const int L = ctx->cfg.n_layers, wfmt = ctx->cfg.wfmt;
     const TokRef tok{ctx->d_cursors, 0}, ttok{ctx->d_cursors + 1, 0};
+    if (wfmt == MOE_SPARK_W_Q4_0) {
+        HIPCHK(launch_q4_router_partial(q4_args(ctx, 0, x, x, tok, ttok, bias_row, 1, 1, 0, nullptr, nullptr, 0),
+                                        ctx->compute));
+        for (int l = 0; l < L; ++l) {
+            const Q4Args a = q4_args(ctx, l, x, x, tok, ttok, bias_row, 1, 1, l + 1 < L ? l + 1 : -1, nullptr,
+                                     nullptr, 0);
+            HIPCHK(launch_q4_gateup(a, ctx->compute));
+            HIPCHK(launch_q4_down(a, ctx->compute));
+        }
+        HIPCHK(launch_advance(ctx->d_cursors, ctx->d_stats, ctx->compute));
+        return MOE_SPARK_OK;
+    }
     for (int l = 0; l < L; ++l) {
         const RouteArgs ra = route_args(ctx, l, x, tok, ttok, bias_row, 1, nullptr, nullptr);
         HIPCHK(launch_route(ra, ctx->compute));
@@ -541,6 +602,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, ctx->device) != hipSuccess || rate_khz <= 0)
         rate_khz = 100000;
     ctx->spin_ticks = (uint64_t)rate_khz * 1000ull * 2ull;  // 2 s
+    if (const char* ev = getenv("MOE_SPARK_DECODE_STREAM")) ctx->stream_decode = ev[0] == '1';
     if (compute_stream) {
         ctx->compute = (hipStream_t)compute_stream;
     } else {
@@ -586,6 +648,9 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= dalloc(&ctx->d_ut, (size_t)d) == hipSuccess;
     ok &= dalloc(&ctx->d_h, (size_t)kMaxK * f) == hipSuccess;
     ok &= dalloc(&ctx->d_xscratch, (size_t)d) == hipSuccess;
+    ok &= dalloc(&ctx->d_pl, (size_t)kNP * E) == hipSuccess;
+    ok &= dalloc(&ctx->d_ps, (size_t)kNP) == hipSuccess;
+    ok &= dalloc(&ctx->d_pub, (size_t)L) == hipSuccess;
     if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "device table allocation failed");
     if (hipHostMalloc((void**)&ctx->h_fifo, sizeof(FifoEntry) * kFifoCap, hipHostMallocMapped | hipHostMallocCoherent) !=
             hipSuccess ||
@@ -615,6 +680,9 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= hipMemset(ctx->d_u, 0, sizeof(float) * d) == hipSuccess;
     ok &= hipMemset(ctx->d_ut, 0, sizeof(float) * d) == hipSuccess;
     ok &= hipMemset(ctx->d_h, 0, sizeof(float) * kMaxK * f) == hipSuccess;
+    ok &= hipMemset(ctx->d_pl, 0, sizeof(float) * kNP * E) == hipSuccess;
+    ok &= hipMemset(ctx->d_ps, 0, sizeof(float) * kNP) == hipSuccess;
+    ok &= hipMemset(ctx->d_pub, 0, sizeof(uint32_t) * L) == hipSuccess;
     for (auto& ev : ctx->tok_ev) ok &= hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess;
     ok &= hipDeviceSynchronize() == hipSuccess;
     if (!ok) return fail_create(MOE_SPARK_E_HIP, "table initialisation failed");
@@ -644,7 +712,17 @@ moe_spark_status moe_spark_set_router(moe_spark_ctx* ctx, int32_t layer, const f
     if ((c.n_bias_rows > 0) != (bias != nullptr))
         return ctx->fail(MOE_SPARK_E_INVALID, "bias must be given iff n_bias_rows > 0");
     const int64_t ED = (int64_t)c.n_experts * c.d_model;
-    HIPCHK(hipMemcpy(ctx->d_router + layer * ED, w, ED * sizeof(float), hipMemcpyHostToDevice));
+    if (c.wfmt == MOE_SPARK_W_Q4_0) {
+        // [p][e][i] = w[e][16p + i]: one 16-row slice of every router row per partial work-group
+        std::vector<float> packed((size_t)ED);
+        const int E = c.n_experts;
+        for (int p = 0; p < kNP; ++p)
+            for (int e = 0; e < E; ++e)
+                memcpy(&packed[((size_t)p * E + e) * kRW], w + (int64_t)e * c.d_model + p * kRW, kRW * sizeof(float));
+        HIPCHK(hipMemcpy(ctx->d_router + layer * ED, packed.data(), ED * sizeof(float), hipMemcpyHostToDevice));
+    } else {
+        HIPCHK(hipMemcpy(ctx->d_router + layer * ED, w, ED * sizeof(float), hipMemcpyHostToDevice));
+    }
     if (bias) {
         const int64_t RE = (int64_t)c.n_bias_rows * c.n_experts;
         HIPCHK(hipMemcpy(ctx->d_bias + layer * RE, bias, RE * sizeof(float), hipMemcpyHostToDevice));
@@ -801,6 +879,18 @@ moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, cons
     moe_spark_status st = ready_check(ctx);
     if (st != MOE_SPARK_OK) return st;
     const int norm = (flags & MOE_SPARK_PRE_RMSNORM) != 0, res = (flags & MOE_SPARK_RESIDUAL) != 0;
+    if (c.wfmt == MOE_SPARK_W_Q4_0) {
+        for (int t = 0; t < n_tokens; ++t) {
+            const TokRef tok{nullptr, t};
+            const Q4Args a = q4_args(ctx, layer, x, y, tok, tok, bias_row, norm, res, -1, topk_out, gates_out, 0);
+            Q4Args ap = a;
+            ap.wr_part = ctx->d_router + (int64_t)layer * c.n_experts * c.d_model;
+            HIPCHK(launch_q4_router_partial(ap, ctx->compute));
+            HIPCHK(launch_q4_gateup(a, ctx->compute));
+            HIPCHK(launch_q4_down(a, ctx->compute));
+        }
+        return MOE_SPARK_OK;
+    }
     for (int t = 0; t < n_tokens; ++t) {
         const TokRef tok{nullptr, t};
         const RouteArgs ra = route_args(ctx, layer, x, tok, tok, bias_row, norm, topk_out, gates_out);
@@ -818,6 +908,15 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
     moe_spark_status st = ready_check(ctx);
     if (st != MOE_SPARK_OK) return st;
     if (!x) return MOE_SPARK_OK;
+    if (ctx->stream_decode) {
+        if (n_tokens == 0) return MOE_SPARK_OK;
+        HIPCHK(hipMemsetAsync(ctx->d_cursors, 0, sizeof(int32_t), ctx->compute));
+        for (int t = 0; t < n_tokens; ++t) {
+            st = launch_token_kernels(ctx, x, bias_row);
+            if (st != MOE_SPARK_OK) return st;
+        }
+        return MOE_SPARK_OK;
+    }
     hipGraphExec_t exec;
     st = get_graph(ctx, x, bias_row, &exec);  // n_tokens == 0 only prepares the graph
     if (st != MOE_SPARK_OK || n_tokens == 0) return st;
@@ -939,31 +1038,52 @@ moe_spark_status moe_spark_time_expert_kernels(moe_spark_ctx* ctx, int32_t iters
     HIPCHK(hipEventCreate(&e0));
     HIPCHK(hipEventCreate(&e1));
     HIPCHK(hipEventCreate(&e2));
+    hipEvent_t e3;
+    HIPCHK(hipEventCreate(&e3));
     const TokRef tok{nullptr, 0};
+    const bool q4 = c.wfmt == MOE_SPARK_W_Q4_0;
+    float* xs = ctx->d_xscratch;
     HIPCHK(hipEventRecord(e0, ctx->compute));
     for (int it = 0; it < iters; ++it)
         for (int l = 0; l < L; ++l) {
-            ExpertArgs ea = expert_args(ctx, l, ctx->d_xscratch, ctx->d_xscratch, tok, 1, 0);
-            HIPCHK(launch_gateup(ea, c.wfmt, ctx->compute));
+            if (q4) {
+                HIPCHK(launch_q4_gateup(q4_args(ctx, l, xs, xs, tok, tok, nullptr, 1, 1, -1, nullptr, nullptr, 1),
+                                        ctx->compute));
+            } else {
+                HIPCHK(launch_gateup(expert_args(ctx, l, xs, xs, tok, 1, 0), c.wfmt, ctx->compute));
+            }
         }
     HIPCHK(hipEventRecord(e1, ctx->compute));
     for (int it = 0; it < iters; ++it)
         for (int l = 0; l < L; ++l) {
-            ExpertArgs ea = expert_args(ctx, l, ctx->d_xscratch, ctx->d_xscratch, tok, 1, 0);
-            HIPCHK(launch_down(ea, c.wfmt, ctx->compute));
+            if (q4) {
+                HIPCHK(launch_q4_down(q4_args(ctx, l, xs, xs, tok, tok, nullptr, 1, 1, l + 1 < L ? l + 1 : -1,
+                                              nullptr, nullptr, 1),
+                                      ctx->compute));
+            } else {
+                HIPCHK(launch_down(expert_args(ctx, l, xs, xs, tok, 1, 0), c.wfmt, ctx->compute));
+            }
         }
     HIPCHK(hipEventRecord(e2, ctx->compute));
-    HIPCHK(hipEventSynchronize(e2));
-    float ms1 = 0, ms2 = 0;
+    if (q4)
+        for (int it = 0; it < iters; ++it)
+            for (int l = 0; l < L; ++l)
+                HIPCHK(launch_q4_router_partial(q4_args(ctx, l, xs, xs, tok, tok, nullptr, 1, 1, l, nullptr, nullptr, 1),
+                                                ctx->compute));
+    HIPCHK(hipEventRecord(e3, ctx->compute));
+    HIPCHK(hipEventSynchronize(e3));
+    float ms1 = 0, ms2 = 0, ms3 = 0;
     HIPCHK(hipEventElapsedTime(&ms1, e0, e1));
     HIPCHK(hipEventElapsedTime(&ms2, e1, e2));
+    HIPCHK(hipEventElapsedTime(&ms3, e2, e3));
     hipEventDestroy(e0);
     hipEventDestroy(e1);
     hipEventDestroy(e2);
+    hipEventDestroy(e3);
     const float n = (float)iters * L;
     if (us_gateup) *us_gateup = ms1 * 1000.0f / n;
     if (us_down) *us_down = ms2 * 1000.0f / n;
-    if (us_route) *us_route = -1.0f;
+    if (us_route) *us_route = q4 ? ms3 * 1000.0f / n : -1.0f;
     return MOE_SPARK_OK;
 }
 
