@@ -175,12 +175,19 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
 /* moe_spark_decode with n_tokens = 1. */
 moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int32_t* bias_row);
 
-/* Batched prefill of n_tokens (<= max_tokens) through all L layers: per layer
- * RMSNorm, router, top-k, grouping by expert, and a grouped expert GEMM in
- * bf16 on the matrix cores with fp32 accumulation; the layer's distinct
- * experts are accessed once each in ascending id, non-pinned ones streamed
- * through the ring in chunks of at most R.  x [T][d] fp32 device, in place;
- * bias_row [T] int32 device or NULL.  Synchronises once per layer. */
+/* Batched prefill of n_tokens (1 <= n_tokens <= max_tokens) through all L
+ * layers, Q4_0 contexts only.  Per layer: RMSNorm, router GEMM (fp32), exact
+ * top-K with the softmax renormalised over the chosen experts, routing counts,
+ * a deterministic sort of the (token, rank) assignments by expert, then a
+ * grouped expert GEMM on the matrix cores: Q4_0 weights dequantised to bf16,
+ * bf16 activations, fp32 accumulation (gate/up with SwiGLU, then down); the
+ * rank-order combine adds the result to x.  The layer's distinct experts are
+ * accessed once each in ascending id; non-pinned ones stream through the
+ * spare-slot ring in chunks of at most R, filled asynchronously as in decode.
+ * x [T][d] fp32 device, updated in place; bias_row [T] int32 device or NULL.
+ * Synchronises the compute stream once per layer (the host plans each layer
+ * from its expert histogram).  Errors: E_INVALID (format, n_tokens, x),
+ * E_STATE (max_tokens was 0 at create, weights or placement missing). */
 moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_tokens,
                                    const int32_t* bias_row);
 

@@ -85,6 +85,72 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     i = bi;
 }
 
+// Exact top-K of lg[0..E) under (value desc, index asc), for a 256-thread
+// work-group (K <= kQ4MaxK).  Two ranking passes, all comparisons branch-free:
+//  1. wave w ranks each 64-expert chunk c = w, w+4, ... within the chunk and
+//     keeps the chunk's first K as candidates (padding lanes past E hold -inf
+//     with an index >= E, so they rank below every real expert);
+//  2. every candidate is ranked among the candidates.
+// The global top K are all candidates, and a candidate's rank among the
+// candidates equals its global rank whenever that is below K.  Result:
+// s_e[r], s_l[r] for r < K.  LDS scratch: lg_pad[256],
+// cand_v/cand_e[kMaxE/64*kQ4MaxK + 4] (16-byte aligned).  Contains barriers:
+// every thread of the work-group must call it.
+__device__ inline void block_topk(const float* lg, int E, int K, float* lg_pad, float* cand_v, int32_t* cand_e,
+                                  int* s_e, float* s_l) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    if (t < K) {  // defined even if NaN logits leave a rank unfilled
+        s_e[t] = 0;
+        s_l[t] = -INFINITY;
+    }
+    const int n_chunks = (E + 63) >> 6;
+    for (int c = w; c < n_chunks; c += 4) {
+        const int e = c * 64 + lane;
+        const float v = e < E ? lg[e] : -INFINITY;
+        lg_pad[lane + 64 * w] = v;
+        __builtin_amdgcn_wave_barrier();
+        int r = 0;
+#pragma unroll 4
+        for (int j = 0; j < 64; j += 4) {
+            const f32x4 q = *reinterpret_cast<const f32x4*>(&lg_pad[64 * w + j]);
+            r += (int)(q.x > v) + (int)((q.x == v) & (j < lane));
+            r += (int)(q.y > v) + (int)((q.y == v) & (j + 1 < lane));
+            r += (int)(q.z > v) + (int)((q.z == v) & (j + 2 < lane));
+            r += (int)(q.w > v) + (int)((q.w == v) & (j + 3 < lane));
+        }
+        if (r < K) {
+            cand_v[c * K + r] = v;
+            cand_e[c * K + r] = e;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (t < 4) {  // padding past the candidates: -inf with an index no expert has
+        cand_v[n_chunks * K + t] = -INFINITY;
+        cand_e[n_chunks * K + t] = 0x7fffffff;
+    }
+    __syncthreads();
+    const int nc = n_chunks * K;
+    for (int i = t; i < nc; i += 256) {
+        const float v = cand_v[i];
+        const int e = cand_e[i];
+        int r = 0;
+#pragma unroll 2
+        for (int j = 0; j < nc; j += 4) {  // entries past nc are padding that ranks last
+            const f32x4 q = *reinterpret_cast<const f32x4*>(&cand_v[j]);
+            const int4 qe = *reinterpret_cast<const int4*>(&cand_e[j]);
+            r += (int)(q.x > v) + (int)((q.x == v) & (qe.x < e));
+            r += (int)(q.y > v) + (int)((q.y == v) & (qe.y < e));
+            r += (int)(q.z > v) + (int)((q.z == v) & (qe.z < e));
+            r += (int)(q.w > v) + (int)((q.w == v) & (qe.w < e));
+        }
+        if (r < K && e >= 0 && e < E) {
+            s_e[r] = e;
+            s_l[r] = v;
+        }
+    }
+    __syncthreads();
+}
+
 __device__ __forceinline__ float block_sum(const f32x4* uu) {
     float s = 0.0f;
 #pragma unroll

@@ -172,6 +172,49 @@ hipError_t launch_q4_gateup(const Q4Args& a, hipStream_t s);
 hipError_t launch_q4_down(const Q4Args& a, hipStream_t s);
 hipError_t launch_advance(int32_t* cursors, int64_t* stats, hipStream_t s);
 
+// Arguments of the batched-prefill kernels (prefill.hip), one layer.
+struct PfArgs {
+    float* x;                 // [T][d] residual stream, updated in place
+    int32_t T, layer, L, E, K;
+    int32_t norm;
+    float eps;
+    const float* wr;          // this layer's packed router [kNP][E][kRW]
+    const float* bias;        // this layer's router bias [n_bias_rows][E] or null
+    const int32_t* bias_row;  // [T] or null
+    int32_t n_bias_rows;
+    uint16_t* u;              // [T][d] normalised input, bf16 bits
+    float* inv;               // [T] 1 / rms
+    float* logits;            // [T][E]
+    int32_t* topk;            // [T][K]
+    float* gates;             // [T][K]
+    int32_t* hist;            // [E] assignments per expert
+    const int32_t* goff;      // [E+1] first sorted position of each expert's group
+    int32_t* perm;            // [T*K] token of each sorted position
+    int32_t* apos;            // [T][K] sorted position of assignment (t, k)
+    const int32_t* items;     // [n_items][2] GEMM work items: (expert, first row of the tile)
+    int32_t n_items;
+    const int32_t* pf_experts;  // the chunk's experts, ascending, for the policy
+    int32_t n_pf_experts;
+    int32_t* pslot;           // [E] slot chosen for each expert this layer
+    uint64_t* pwait;          // [E] fill number to wait for (0: resident)
+    uint16_t* h;              // [T*K][f] SwiGLU output, bf16 bits
+    float* y;                 // [T*K][d] expert outputs
+    const uint8_t* slots;
+    int64_t slot_bytes, P, n_slots;
+    const uint64_t* ready;
+    PolicyTables pt;
+    float* tr_x;
+    int32_t* tr_topk;
+    float* tr_gates;
+    int64_t tr_cap;
+    uint64_t spin_limit_ticks;
+};
+
+hipError_t launch_pf_front(const PfArgs& a, hipStream_t s);    // norm, router, top-k + counts + histogram
+hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s);  // sort assignments by (expert, token)
+hipError_t launch_pf_chunk(const PfArgs& a, hipStream_t s);    // policy, gate/up GEMM, down GEMM of one chunk
+hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s);  // rank-order combine + residual
+
 // Launchers (kernels.hip).
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_gateup(const ExpertArgs& a, int wfmt, hipStream_t s);

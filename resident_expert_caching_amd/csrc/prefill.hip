@@ -1,0 +1,514 @@
+// gfx950 batched prefill of the Q4_0 MoE stack: T tokens through one layer
+// at a time.
+//
+//   norm     RMSNorm per token; the normalised input in bf16 for the expert
+//            GEMMs, 1/rms kept in fp32 for the router.
+//   router   logits[t][e] = inv_rms[t] * x[t]·Wr[e] + bias, fp32 FMA.
+//   topk     exact top-K per token and the softmax renormalised over the
+//            chosen experts ("Luce Spark runs 35B MoE models on 16GB GPU
+//            without speed loss", opening paragraph: about 8 of 256 experts
+//            per token); per-expert routing counts (paragraph "The key
+//            components", item 1) and the per-expert assignment histogram.
+//   scatter  deterministic counting sort of the (token, rank) assignments by
+//            (expert, token).
+//   policy   one wave: the layer's distinct experts in ascending id, each
+//            accessed once through the pinned set or the spare-slot ring
+//            (same paragraph, item 2); the host runs it in chunks of at most
+//            R cold experts, so every expert of a chunk is resident while the
+//            chunk's GEMMs run.
+//   gateup   grouped GEMM on the matrix cores: H = silu(U Wg^T) * (U Wu^T)
+//            per expert group; Q4_0 weights are dequantised to bf16 in LDS,
+//            v_mfma_f32_16x16x32_bf16 accumulates in fp32.
+//   down     grouped GEMM Y = H Wd^T, same scheme.
+//   combine  x[t] += sum_k g[t][k] Y[pos(t,k)] in rank order.
+//
+// Every reduction order is fixed and no result depends on the slot a weight
+// is read from, so prefill outputs are bit-identical at every residency.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+#include "policy.h"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kPfThreads = 256;
+constexpr int kBM = 128;       // tokens per GEMM tile
+constexpr int kBK = 64;        // K per pipeline step (two Q4_0 blocks)
+constexpr int kLdsRow = 72;    // bf16 per LDS tile row (64 + 8 padding)
+
+__device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+}
+
+// 32 weights of one Q4_0 block (GGUF nibble order) as bf16 (q - 8) * s into
+// dst[0..31] (LDS, 16-byte aligned).
+__device__ __forceinline__ void dequant_block_bf16(const u32x4 c, float s, uint16_t* dst) {
+    const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+    uint32_t lo[8], hi[8];
+    const float m8 = -8.0f * s;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t x = wd[m];
+        // bytes 4m..4m+3: low nibbles are weights 4m..4m+3, high nibbles 4m+16..4m+19
+        const float l0 = fmaf((float)(x & 0xfu), s, m8), l1 = fmaf((float)((x >> 8) & 0xfu), s, m8);
+        const float l2 = fmaf((float)((x >> 16) & 0xfu), s, m8), l3 = fmaf((float)((x >> 24) & 0xfu), s, m8);
+        const float h0 = fmaf((float)((x >> 4) & 0xfu), s, m8), h1 = fmaf((float)((x >> 12) & 0xfu), s, m8);
+        const float h2 = fmaf((float)((x >> 20) & 0xfu), s, m8), h3 = fmaf((float)(x >> 28), s, m8);
+        lo[2 * m] = pack_bf16(l0, l1);
+        lo[2 * m + 1] = pack_bf16(l2, l3);
+        hi[2 * m] = pack_bf16(h0, h1);
+        hi[2 * m + 1] = pack_bf16(h2, h3);
+    }
+    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+    d4[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    d4[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+    d4[2] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    d4[3] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+}
+
+// ---------------------------------------------------------------- norm
+
+// Grid T, 256 threads: one token per work-group.
+__global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(a.x + (int64_t)t * kQD);
+    const f32x4 v0 = x4[tid], v1 = x4[tid + kPfThreads];
+    float ss = (v0.x * v0.x + v0.y * v0.y) + (v0.z * v0.z + v0.w * v0.w);
+    ss += (v1.x * v1.x + v1.y * v1.y) + (v1.z * v1.z + v1.w * v1.w);
+    ss = wave_sum(ss);
+    __shared__ float part[4];
+    if (lane == 0) part[w] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = a.norm ? 1.0f / sqrtf(tot / (float)kQD + a.eps) : 1.0f;
+    if (tid == 0) a.inv[t] = inv;
+    uint32_t* u2 = reinterpret_cast<uint32_t*>(a.u + (int64_t)t * kQD);
+    u2[2 * tid] = pack_bf16(v0.x * inv, v0.y * inv);
+    u2[2 * tid + 1] = pack_bf16(v0.z * inv, v0.w * inv);
+    u2[2 * (tid + kPfThreads)] = pack_bf16(v1.x * inv, v1.y * inv);
+    u2[2 * (tid + kPfThreads) + 1] = pack_bf16(v1.z * inv, v1.w * inv);
+    if (a.tr_x && t < a.tr_cap) {
+        f32x4* tr = reinterpret_cast<f32x4*>(a.tr_x + ((int64_t)t * a.L + a.layer) * kQD);
+        tr[tid] = v0;
+        tr[tid + kPfThreads] = v1;
+    }
+}
+
+// ---------------------------------------------------------------- router
+
+// Grid (ceil(T/32), ceil(E/64)), 256 threads.  Work-group tile: 32 tokens x
+// 64 experts; thread (ty, tx) = (tid >> 4, tid & 15) owns tokens 2ty, 2ty+1
+// and experts 4tx..4tx+3.  K steps of 32 through LDS; the router is read in
+// its packed layout [d/16][E][16].
+__global__ __launch_bounds__(kPfThreads) void pf_router_kernel(PfArgs a) {
+    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
+    const int E = a.E;
+    __shared__ __align__(16) float xs[32][36];
+    __shared__ __align__(16) float ws[64][36];
+    float acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int k0 = 0; k0 < kQD; k0 += 32) {
+        {   // x tile: 32 tokens x 32 floats, one f32x4 per thread
+            const int r = tid >> 3, c = (tid & 7) * 4;
+            const int tok = t0 + r;
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (tok < a.T) v = *reinterpret_cast<const f32x4*>(a.x + (int64_t)tok * kQD + k0 + c);
+            *reinterpret_cast<f32x4*>(&xs[r][c]) = v;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // router tile: 64 experts x 32, packed [k0/16 + h][e][16]
+            const int e = tid >> 2, c = (tid & 3) * 4;
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (e0 + e < E)
+                v = *reinterpret_cast<const f32x4*>(a.wr + ((int64_t)(k0 / kRW + h) * E + e0 + e) * kRW + c);
+            *reinterpret_cast<f32x4*>(&ws[e][h * 16 + c]) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 32; k += 4) {
+            const f32x4 xa = *reinterpret_cast<const f32x4*>(&xs[2 * ty][k]);
+            const f32x4 xb = *reinterpret_cast<const f32x4*>(&xs[2 * ty + 1][k]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 wv = *reinterpret_cast<const f32x4*>(&ws[4 * tx + j][k]);
+                acc[0][j] += xa.x * wv.x;
+                acc[0][j] += xa.y * wv.y;
+                acc[0][j] += xa.z * wv.z;
+                acc[0][j] += xa.w * wv.w;
+                acc[1][j] += xb.x * wv.x;
+                acc[1][j] += xb.y * wv.y;
+                acc[1][j] += xb.z * wv.z;
+                acc[1][j] += xb.w * wv.w;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tok = t0 + 2 * ty + i;
+        if (tok >= a.T) continue;
+        const float inv = a.inv[tok];
+        const float* brow = nullptr;
+        if (a.bias) {
+            int row = a.bias_row ? a.bias_row[tok] : 0;
+            row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
+            brow = a.bias + (int64_t)row * E;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + 4 * tx + j;
+            if (e < E) a.logits[(int64_t)tok * E + e] = acc[i][j] * inv + (brow ? brow[e] : 0.0f);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- top-k
+
+// Grid T, 256 threads: top-K and gates of one token; routing counts and the
+// assignment histogram (integer atomics: the totals are exact).
+__global__ __launch_bounds__(kPfThreads) void pf_topk_kernel(PfArgs a) {
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const int E = a.E, K = a.K;
+    __shared__ __align__(16) float lg[kMaxE];
+    __shared__ __align__(16) float lg_pad[kPfThreads];
+    __shared__ __align__(16) float cand_v[kMaxE / 64 * kQ4MaxK + 4];
+    __shared__ __align__(16) int32_t cand_e[kMaxE / 64 * kQ4MaxK + 4];
+    __shared__ int s_e[kMaxK];
+    __shared__ float s_l[kMaxK];
+    for (int e = tid; e < E; e += kPfThreads) lg[e] = a.logits[(int64_t)t * E + e];
+    __syncthreads();
+    block_topk(lg, E, K, lg_pad, cand_v, cand_e, s_e, s_l);
+    if (tid < K) {
+        const int e = s_e[tid];
+        float z = 0.0f;
+        for (int kk = 0; kk < K; ++kk) z += expf(s_l[kk] - s_l[0]);
+        const float g = expf(s_l[tid] - s_l[0]) / z;
+        a.topk[(int64_t)t * K + tid] = e;
+        a.gates[(int64_t)t * K + tid] = g;
+        atomicAdd(reinterpret_cast<unsigned long long*>(a.pt.counts + (int64_t)a.layer * E + e), 1ull);
+        atomicAdd(a.hist + e, 1);
+        if (a.tr_topk && t < a.tr_cap) {
+            const int64_t o = ((int64_t)t * a.L + a.layer) * K + tid;
+            a.tr_topk[o] = e;
+            a.tr_gates[o] = g;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- scatter
+
+// Grid E, 256 threads: work-group e lists the tokens that chose expert e, in
+// ascending token order, at positions goff[e] .. goff[e+1]-1.
+__global__ __launch_bounds__(kPfThreads) void pf_scatter_kernel(PfArgs a) {
+    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int K = a.K;
+    if (a.goff[e + 1] == a.goff[e]) return;
+    __shared__ int wtot[4];
+    int base = a.goff[e];
+    for (int t0 = 0; t0 < a.T; t0 += kPfThreads) {
+        const int t = t0 + tid;
+        int kk = -1;
+        if (t < a.T)
+            for (int q = 0; q < K; ++q)
+                if (a.topk[(int64_t)t * K + q] == e) kk = q;
+        const uint64_t m = __ballot(kk >= 0);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (lane == 0) wtot[w] = __builtin_popcountll(m);
+        __syncthreads();
+        int off = base;
+        for (int q = 0; q < w; ++q) off += wtot[q];
+        if (kk >= 0) {
+            const int pos = off + before;
+            a.perm[pos] = t;
+            a.apos[(int64_t)t * K + kk] = pos;
+        }
+        base += (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- policy
+
+// One wave: the chunk's experts (ascending id) through the placement policy.
+__global__ __launch_bounds__(64) void pf_policy_kernel(PfArgs a) {
+    __shared__ int32_t r_owner[kMaxR];
+    __shared__ uint64_t r_stamp[kMaxR];
+    __shared__ uint64_t r_seq[kMaxR];
+    const PolicyTables& pt = a.pt;
+    RingState rs{};
+    ring_load(pt, r_owner, r_stamp, r_seq, rs);
+    for (int i = 0; i < a.n_pf_experts; ++i) {
+        const int e = a.pf_experts[i];
+        int slot;
+        uint64_t wseq;
+        ring_access(pt, a.layer, e, pt.slot_of[(int64_t)a.layer * a.E + e], r_owner, r_stamp, r_seq, rs, slot,
+                    wseq);
+        if (threadIdx.x == 0) {
+            a.pslot[e] = slot;
+            a.pwait[e] = wseq;
+        }
+    }
+    ring_store(pt, r_owner, r_stamp, r_seq, rs);
+    stats_flush(pt, a.n_pf_experts, rs);
+}
+
+// ---------------------------------------------------------------- grouped GEMMs
+
+// Resolve a GEMM work item: expert, first row of its group, rows in the tile,
+// slot.  Waits (bounded) for a fill that is still in flight.  Returns false
+// if the work-group has nothing valid to do.
+__device__ bool pf_item(const PfArgs& a, int item, int& e, int& pos0, int& rows, const uint8_t*& S) {
+    e = a.items[2 * item];
+    const int m0 = a.items[2 * item + 1];
+    const int n_e = a.goff[e + 1] - a.goff[e];
+    pos0 = a.goff[e] + m0;
+    rows = min(kBM, n_e - m0);
+    const int slot = a.pslot[e];
+    const uint64_t wseq = a.pwait[e];
+    if (rows <= 0 || slot < 0 || slot >= a.n_slots) {
+        if (threadIdx.x == 0 && rows > 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
+        return false;
+    }
+    if (wseq && slot >= a.P) {
+        if (threadIdx.x == 0) {
+            const uint64_t* flag = a.ready + (slot - a.P);
+            const uint64_t t0 = wall_clock64();
+            while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < wseq) {
+                __builtin_amdgcn_s_sleep(4);
+                if (wall_clock64() - t0 > a.spin_limit_ticks ||
+                    (__hip_atomic_load(a.pt.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ERR_FILL_TIMEOUT)) {
+                    atomicOr(a.pt.error, (int)ERR_FILL_TIMEOUT);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+    }
+    S = a.slots + (int64_t)slot * a.slot_bytes;
+    return true;
+}
+
+// MFMA tile compute of one kBK step: wave (wm, wn) owns rows wm*64..+63 and
+// the 4 16-column groups listed in cols[]; acc[mi][nj] is 16x16.
+__device__ __forceinline__ void mfma_step(const uint16_t* As, const uint16_t* Bs, int wm, const int* cols,
+                                          f32x4 (&acc)[4][4]) {
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 15, lk = (lane >> 4) * 8;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+        bf16x8 af[4], bfr[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            af[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + mi * 16 + lr) * kLdsRow + kh * 32 + lk);
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+            bfr[nj] = *reinterpret_cast<const bf16x8*>(Bs + (cols[nj] + lr) * kLdsRow + kh * 32 + lk);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj)
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
+    }
+}
+
+// Grid (n_items, f/64), 256 threads.  Work-group tile: kBM tokens of one
+// expert group x (64 gate rows + the same 64 up rows); wave w: rows
+// (w&1)*64.., gate and up columns (w>>1)*32..; SwiGLU in the epilogue.
+// B rows come from the slot's gate/up region (chunk g = row/16: codes at
+// ((ww*8 + i)*64 + b)*16, scales at 32768 + (ww*64 + b)*16 + 2i).
+__global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(PfArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n0 = blockIdx.y * 64;
+    int e, pos0, rows;
+    const uint8_t* S;
+    if (!pf_item(a, blockIdx.x, e, pos0, rows, S)) return;
+    __shared__ __align__(16) uint16_t As[kBM * kLdsRow];
+    __shared__ __align__(16) uint16_t Bs[128 * kLdsRow];
+    __shared__ int tok[kBM];
+    if (tid < kBM) tok[tid] = tid < rows ? a.perm[pos0 + tid] : -1;
+    __syncthreads();
+    // A loads: row tid>>1, 32 bf16 (64 B) at column half (tid&1)*32
+    const int ar = tid >> 1, ah = (tid & 1) * 32;
+    const int atok = tok[ar];
+    const u32x4* arow = atok >= 0 ? reinterpret_cast<const u32x4*>(a.u + (int64_t)atok * kQD + ah) : nullptr;
+    // B loads: row br = tid>>1 (gate rows 0..63, up rows 64..127), block (tid&1) of the step
+    const int br = tid >> 1, bb = tid & 1;
+    const int mrow = n0 + (br & 63);
+    const int ww = (br >= 64 ? 2 : 0) + ((mrow >> 3) & 1);
+    const uint8_t* bchunk = S + (int64_t)(mrow >> 4) * kGUChunk;
+    const int bi = mrow & 7;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int wm = w & 1, wn = w >> 1;
+    const int cols[4] = {wn * 32, wn * 32 + 16, 64 + wn * 32, 64 + wn * 32 + 16};
+
+    u32x4 ra[4], rc;
+    uint32_t rsc;
+    auto load = [&](int k0) {
+        const int b = k0 / 32 + bb;
+        if (arow) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = arow[k0 / 8 + j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+        rc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bchunk + ((ww * 8 + bi) * 64 + b) * 16));
+        rsc = *reinterpret_cast<const uint16_t*>(bchunk + 32768 + (ww * 64 + b) * 16 + bi * 2);
+    };
+    load(0);
+    for (int k0 = 0; k0 < kQD; k0 += kBK) {
+        __syncthreads();
+        {
+            u32x4* ad = reinterpret_cast<u32x4*>(As + ar * kLdsRow + ah);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ad[j] = ra[j];
+            dequant_block_bf16(rc, half_bits_to_float(rsc), Bs + br * kLdsRow + bb * 32);
+        }
+        __syncthreads();
+        if (k0 + kBK < kQD) load(k0 + kBK);
+        mfma_step(As, Bs, wm, cols, acc);
+    }
+    // epilogue: h = silu(gate) * up, bf16
+    const int lr = lane & 15, lq = (lane >> 4) * 4;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * 64 + mi * 16 + lq + r;
+                if (row < rows) {
+                    const float g = acc[mi][nj][r], u = acc[mi][nj + 2][r];
+                    a.h[(int64_t)(pos0 + row) * kQF + n0 + wn * 32 + nj * 16 + lr] = bf16_bits(silu(g) * u);
+                }
+            }
+}
+
+// Grid (n_items, d/128), 256 threads.  Work-group tile: kBM tokens x 128
+// down rows; wave w: rows (w&1)*64.., columns (w>>1)*64...  B rows from the
+// slot's down region: codes [r][b][16 B], scales [r/4][b][4] fp16.
+__global__ __launch_bounds__(kPfThreads) void pf_down_kernel(PfArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n0 = blockIdx.y * 128;
+    int e, pos0, rows;
+    const uint8_t* S;
+    if (!pf_item(a, blockIdx.x, e, pos0, rows, S)) return;
+    __shared__ __align__(16) uint16_t As[kBM * kLdsRow];
+    __shared__ __align__(16) uint16_t Bs[128 * kLdsRow];
+    const int ar = tid >> 1, ah = (tid & 1) * 32;
+    const u32x4* arow = ar < rows ? reinterpret_cast<const u32x4*>(a.h + (int64_t)(pos0 + ar) * kQF + ah) : nullptr;
+    const int br = tid >> 1, bb = tid & 1;
+    const int drow = n0 + br;
+    const uint8_t* dcodes = S + kGURegion + (int64_t)drow * 256;
+    const uint8_t* dscales = S + kGURegion + kDownCodes + (int64_t)(drow >> 2) * 128 + (drow & 3) * 2;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int wm = w & 1, wn = w >> 1;
+    const int cols[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+
+    u32x4 ra[4], rc;
+    uint32_t rsc;
+    auto load = [&](int k0) {
+        const int b = k0 / 32 + bb;
+        if (arow) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = arow[k0 / 8 + j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+        rc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dcodes + b * 16));
+        rsc = *reinterpret_cast<const uint16_t*>(dscales + b * 8);
+    };
+    load(0);
+    for (int k0 = 0; k0 < kQF; k0 += kBK) {
+        __syncthreads();
+        {
+            u32x4* ad = reinterpret_cast<u32x4*>(As + ar * kLdsRow + ah);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ad[j] = ra[j];
+            dequant_block_bf16(rc, half_bits_to_float(rsc), Bs + br * kLdsRow + bb * 32);
+        }
+        __syncthreads();
+        if (k0 + kBK < kQF) load(k0 + kBK);
+        mfma_step(As, Bs, wm, cols, acc);
+    }
+    const int lr = lane & 15, lq = (lane >> 4) * 4;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * 64 + mi * 16 + lq + r;
+                if (row < rows) a.y[(int64_t)(pos0 + row) * kQD + n0 + cols[nj] + lr] = acc[mi][nj][r];
+            }
+}
+
+// ---------------------------------------------------------------- combine
+
+// Grid (T, d/256): x[t][i] += sum_k g[t][k] Y[pos(t,k)][i], rank order.
+__global__ __launch_bounds__(kPfThreads) void pf_combine_kernel(PfArgs a) {
+    const int t = blockIdx.x, i = blockIdx.y * kPfThreads + threadIdx.x;
+    const int K = a.K;
+    float y = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const int pos = a.apos[(int64_t)t * K + k];
+        y += a.gates[(int64_t)t * K + k] * a.y[(int64_t)pos * kQD + i];
+    }
+    float* xp = a.x + (int64_t)t * kQD + i;
+    *xp = *xp + y;
+}
+
+}  // namespace
+
+hipError_t launch_pf_front(const PfArgs& a, hipStream_t s) {
+    if (a.T <= 0 || a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pf_norm_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
+    hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (a.E + 63) / 64), dim3(kPfThreads), 0, s, a);
+    hipLaunchKernelGGL(pf_topk_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(pf_scatter_kernel, dim3(a.E), dim3(kPfThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_chunk(const PfArgs& a, hipStream_t s) {
+    if (a.n_pf_experts > 0) hipLaunchKernelGGL(pf_policy_kernel, dim3(1), dim3(64), 0, s, a);
+    if (a.n_items > 0) {
+        hipLaunchKernelGGL(pf_gateup_kernel, dim3(a.n_items, kQF / 64), dim3(kPfThreads), 0, s, a);
+        hipLaunchKernelGGL(pf_down_kernel, dim3(a.n_items, kQD / 128), dim3(kPfThreads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(pf_combine_kernel, dim3(a.T, kQD / kPfThreads), dim3(kPfThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -31,6 +31,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "policy.h"
 
 namespace moe {
 
@@ -98,10 +99,9 @@ __global__ __launch_bounds__(kThreads) void q4_router_partial_kernel(Q4Args a) {
 
 // Single wave of work-group (0,0): counts, slot lookup, the LRU ring and fill
 // requests, in rank order; then the selection is published for the cold
-// experts' work-groups and the down launch.
+// experts' work-groups and the down launch.  sel_e, gk and sof live in LDS.
 __device__ void run_policy(const Q4Args& a, const int* sel_e, const float* gk, const int32_t* sof, int tok,
                            float inv, int32_t* r_owner, uint64_t* r_stamp, uint64_t* r_seq) {
-    // sel_e, gk, sof live in LDS: the rank loop stays a loop (no unrolled copies)
     const int lane = threadIdx.x;
     const PolicyTables& pt = a.pt;
     const int K = a.K, E = a.E;
@@ -110,105 +110,23 @@ __device__ void run_policy(const Q4Args& a, const int* sel_e, const float* gk, c
     uint64_t my_wait = 0;
     int any_cold = 0;
     for (int k = 0; k < K; ++k) any_cold |= sof[sel_e[k]] < 0;
-    int64_t n_pin = 0, n_cold = 0, n_ring = 0, n_fill = 0, n_evict = 0;
+    RingState rs{};
     if (!any_cold) {
         if (lane < K) my_slot = sof[sel_e[lane]];
-        n_pin = K;
+        rs.n_pin = K;
     } else {
-        const int R = pt.R;
-        for (int r = lane; r < R; r += 64) {
-            r_owner[r] = pt.ring_owner[r];
-            r_stamp[r] = pt.ring_stamp[r];
-            r_seq[r] = pt.ring_seq[r];
-        }
-        uint64_t clock = *pt.clock, fseq = *pt.fill_seq;
-        int64_t nev = *pt.n_events;
+        ring_load(pt, r_owner, r_stamp, r_seq, rs);
 #pragma nounroll
         for (int k = 0; k < K; ++k) {
-            const int32_t key = kbase + sel_e[k];
-            const int pin = sof[sel_e[k]];
             int slot;
-            uint64_t wseq = 0;
-            if (pin >= 0) {
-                slot = pin;
-                ++n_pin;
-            } else {
-                ++n_cold;
-                int hit = -1;
-                for (int base = 0; base < R && hit < 0; base += 64) {
-                    const int r = base + lane;
-                    const uint64_t m = __ballot(r < R && r_owner[r] == key);
-                    if (m) hit = base + __builtin_ctzll(m);
-                }
-                if (hit >= 0) {
-                    // filled by an earlier token-layer whose kernels waited for the copy
-                    ++n_ring;
-                    ++clock;
-                    if (lane == 0) r_stamp[hit] = clock;
-                    slot = (int)(pt.P + hit);
-                } else {
-                    int v = -1;
-                    for (int base = 0; base < R && v < 0; base += 64) {
-                        const int r = base + lane;
-                        const uint64_t m = __ballot(r < R && r_owner[r] < 0);
-                        if (m) v = base + __builtin_ctzll(m);
-                    }
-                    if (v < 0) {  // least recently used: smallest stamp (stamps are unique)
-                        uint64_t bs = ~0ull;
-                        int bi = 0x7fffffff;
-                        for (int r = lane; r < R; r += 64)
-                            if (r_stamp[r] < bs) { bs = r_stamp[r]; bi = r; }
-#pragma unroll
-                        for (int m = 32; m >= 1; m >>= 1) {
-                            const uint64_t os = __shfl_xor(bs, m, 64);
-                            const int oi = __shfl_xor(bi, m, 64);
-                            if (os < bs || (os == bs && oi < bi)) { bs = os; bi = oi; }
-                        }
-                        v = bi;
-                    }
-                    const int32_t victim = r_owner[v];
-                    if (victim >= 0) ++n_evict;
-                    ++clock;
-                    ++fseq;
-                    ++n_fill;
-                    if (lane == 0) {
-                        r_owner[v] = key;
-                        r_stamp[v] = clock;
-                        r_seq[v] = fseq;
-                        if (nev < pt.event_cap) {
-                            moe_spark_event ev;
-                            ev.seq = (int64_t)fseq;
-                            ev.layer = a.layer;
-                            ev.expert = sel_e[k];
-                            ev.slot = (int32_t)(pt.P + v);
-                            ev.kind = MOE_SPARK_EV_FILL;
-                            ev.victim = victim;
-                            ev.pad = 0;
-                            pt.events[nev] = ev;
-                        }
-                        FifoEntry* fe = pt.fifo + ((fseq - 1) % kFifoCap);
-                        fe->key = key;
-                        fe->ring = v;
-                        __threadfence_system();
-                        __hip_atomic_store(&fe->seq, fseq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-                    }
-                    ++nev;
-                    wseq = fseq;
-                    slot = (int)(pt.P + v);
-                }
+            uint64_t wseq;
+            ring_access(pt, a.layer, sel_e[k], sof[sel_e[k]], r_owner, r_stamp, r_seq, rs, slot, wseq);
+            if (lane == k) {
+                my_slot = slot;
+                my_wait = wseq;
             }
-            if (lane == k) { my_slot = slot; my_wait = wseq; }
         }
-        for (int r = lane; r < R; r += 64) {
-            pt.ring_owner[r] = r_owner[r];
-            pt.ring_stamp[r] = r_stamp[r];
-            pt.ring_seq[r] = r_seq[r];
-        }
-        if (lane == 0) {
-            *pt.clock = clock;
-            *pt.fill_seq = fseq;
-            *pt.n_events = nev;
-        }
+        ring_store(pt, r_owner, r_stamp, r_seq, rs);
     }
     if (lane < K) {
         const int myk = sel_e[lane];
@@ -229,19 +147,8 @@ __device__ void run_policy(const Q4Args& a, const int* sel_e, const float* gk, c
             a.gates_out[(int64_t)tok * K + lane] = myg;
         }
     }
-    if (lane == 0) {
-        a.sel->inv_rms = inv;
-        unsigned long long* st = reinterpret_cast<unsigned long long*>(pt.stats);
-        atomicAdd(st + DS_ACC, (unsigned long long)K);
-        if (n_pin) atomicAdd(st + DS_PIN, (unsigned long long)n_pin);
-        if (n_cold) atomicAdd(st + DS_COLD, (unsigned long long)n_cold);
-        if (n_ring) atomicAdd(st + DS_RING, (unsigned long long)n_ring);
-        if (n_fill) {
-            atomicAdd(st + DS_FILL, (unsigned long long)n_fill);
-            atomicAdd(st + DS_H2D, (unsigned long long)(n_fill * pt.slot_bytes));
-        }
-        if (n_evict) atomicAdd(st + DS_EVICT, (unsigned long long)n_evict);
-    }
+    if (lane == 0) a.sel->inv_rms = inv;
+    stats_flush(pt, K, rs);
     if (any_cold) {
         // only work-groups of cold experts read the selection inside this
         // launch; the down launch sees it at the kernel boundary
@@ -333,67 +240,9 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
         }
         for (int e = t; e < E; e += kThreads) lg[e] = lg[e] * inv + (brow ? brow[e] : 0.0f);
     }
-    if (t < K) {  // defined even if NaN logits leave a rank unfilled
-        s_e[t] = 0;
-        s_l[t] = -INFINITY;
-    }
     __syncthreads();
 
-    // top-k over (logit desc, index asc), exact, in two ranking passes:
-    //  1. wave w ranks each 64-expert chunk c = w, w+4, ... within the chunk;
-    //     the chunk's first K become candidates (padding lanes past E hold
-    //     -inf with an index >= E, so they rank below every real expert);
-    //  2. the candidates are ranked among themselves.
-    // The global top K lie among the candidates, and a candidate's rank among
-    // candidates is its global rank whenever that is below K.
-    const int n_chunks = (E + 63) >> 6;
-    for (int c = w; c < n_chunks; c += 4) {
-        const int e = c * 64 + lane;
-        const float v = e < E ? lg[e] : -INFINITY;
-        lg_pad[lane + 64 * w] = v;
-        __builtin_amdgcn_wave_barrier();
-        int r = 0;
-#pragma unroll 4
-        for (int j = 0; j < 64; j += 4) {
-            const f32x4 q = *reinterpret_cast<const f32x4*>(&lg_pad[64 * w + j]);
-            r += (int)(q.x > v) + (int)((q.x == v) & (j < lane));
-            r += (int)(q.y > v) + (int)((q.y == v) & (j + 1 < lane));
-            r += (int)(q.z > v) + (int)((q.z == v) & (j + 2 < lane));
-            r += (int)(q.w > v) + (int)((q.w == v) & (j + 3 < lane));
-        }
-        if (r < K) {
-            cand_v[c * K + r] = v;
-            cand_e[c * K + r] = e;
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
-    if (t < 4) {  // padding past the candidates: -inf with an index no expert has
-        cand_v[n_chunks * K + t] = -INFINITY;
-        cand_e[n_chunks * K + t] = 0x7fffffff;
-    }
-    __syncthreads();
-    {
-        const int nc = n_chunks * K;
-        for (int i = t; i < nc; i += kThreads) {
-            const float v = cand_v[i];
-            const int e = cand_e[i];
-            int r = 0;
-#pragma unroll 2
-            for (int j = 0; j < nc; j += 4) {  // entries past nc are padding that ranks last
-                const f32x4 q = *reinterpret_cast<const f32x4*>(&cand_v[j]);
-                const int4 qe = *reinterpret_cast<const int4*>(&cand_e[j]);
-                r += (int)(q.x > v) + (int)((q.x == v) & (qe.x < e));
-                r += (int)(q.y > v) + (int)((q.y == v) & (qe.y < e));
-                r += (int)(q.z > v) + (int)((q.z == v) & (qe.z < e));
-                r += (int)(q.w > v) + (int)((q.w == v) & (qe.w < e));
-            }
-            if (r < K && e >= 0 && e < E) {
-                s_e[r] = e;
-                s_l[r] = v;
-            }
-        }
-    }
-    __syncthreads();
+    block_topk(lg, E, K, lg_pad, cand_v, cand_e, s_e, s_l);
     if (w == 0) {
         if (g == 0 && k == 0 && !a.replay) {
             // gates: softmax over the chosen logits, shifted by the largest

@@ -88,6 +88,24 @@ struct moe_spark_ctx {
     float* d_ps = nullptr;          // [kNP] partial sums of squares (Q4_0)
     uint32_t* d_pub = nullptr;      // [L] selection-published flags (Q4_0)
 
+    // batched prefill (allocated when max_tokens > 0)
+    uint16_t* d_pu = nullptr;       // [Tmax][d] bf16
+    float* d_pinv = nullptr;        // [Tmax]
+    float* d_plog = nullptr;        // [Tmax][E]
+    int32_t* d_ptopk = nullptr;     // [Tmax][K]
+    float* d_pgate = nullptr;       // [Tmax][K]
+    int32_t* d_phist = nullptr;     // [E]
+    int32_t* d_pperm = nullptr;     // [Tmax*K]
+    int32_t* d_papos = nullptr;     // [Tmax][K]
+    int32_t* d_pslot = nullptr;     // [E]
+    uint64_t* d_pwait = nullptr;    // [E]
+    uint16_t* d_ph = nullptr;       // [Tmax*K][f] bf16
+    float* d_py = nullptr;          // [Tmax*K][d]
+    int32_t* d_pmeta = nullptr;     // goff [E+1] | experts [E] | items [2*max_items]
+    int32_t* h_pmeta = nullptr;     // pinned staging of the same
+    int32_t* h_phist = nullptr;     // pinned [E]
+    int64_t pf_max_items = 0;
+
     // host-mapped
     FifoEntry* h_fifo = nullptr;
     FifoEntry* d_fifo = nullptr;
@@ -317,12 +335,17 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_ring_stamp, ctx->d_ring_seq, ctx->d_clock, ctx->d_counts, ctx->d_stats,
                      ctx->d_events, ctx->d_n_events, ctx->d_error,  ctx->d_cursors, ctx->d_done,
                      ctx->d_sel,    ctx->d_logits,   ctx->d_u,      ctx->d_ut,      ctx->d_h,
-                     ctx->d_xscratch, ctx->d_pl,     ctx->d_ps,     ctx->d_pub};
+                     ctx->d_xscratch, ctx->d_pl,     ctx->d_ps,     ctx->d_pub,     ctx->d_pu,
+                     ctx->d_pinv,     ctx->d_plog,   ctx->d_ptopk,  ctx->d_pgate,   ctx->d_phist,
+                     ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_ph,
+                     ctx->d_py,       ctx->d_pmeta};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
     if (ctx->h_fifo) hipHostFree(ctx->h_fifo);
     if (ctx->h_ready) hipHostFree(ctx->h_ready);
+    if (ctx->h_pmeta) hipHostFree(ctx->h_pmeta);
+    if (ctx->h_phist) hipHostFree(ctx->h_phist);
     if (ctx->own_compute && ctx->compute) hipStreamDestroy(ctx->compute);
     if (ctx->own_copy && ctx->copy) hipStreamDestroy(ctx->copy);
 }
@@ -652,6 +675,28 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= dalloc(&ctx->d_ps, (size_t)kNP) == hipSuccess;
     ok &= dalloc(&ctx->d_pub, (size_t)L) == hipSuccess;
     if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "device table allocation failed");
+    if (c.max_tokens > 0) {
+        const size_t T = (size_t)c.max_tokens, K = (size_t)c.top_k;
+        ctx->pf_max_items = (int64_t)(T * K / 128 + E + 1);
+        ok &= dalloc(&ctx->d_pu, T * d) == hipSuccess;
+        ok &= dalloc(&ctx->d_pinv, T) == hipSuccess;
+        ok &= dalloc(&ctx->d_plog, T * E) == hipSuccess;
+        ok &= dalloc(&ctx->d_ptopk, T * K) == hipSuccess;
+        ok &= dalloc(&ctx->d_pgate, T * K) == hipSuccess;
+        ok &= dalloc(&ctx->d_phist, (size_t)E) == hipSuccess;
+        ok &= dalloc(&ctx->d_pperm, T * K) == hipSuccess;
+        ok &= dalloc(&ctx->d_papos, T * K) == hipSuccess;
+        ok &= dalloc(&ctx->d_pslot, (size_t)E) == hipSuccess;
+        ok &= dalloc(&ctx->d_pwait, (size_t)E) == hipSuccess;
+        ok &= dalloc(&ctx->d_ph, T * K * f) == hipSuccess;
+        ok &= dalloc(&ctx->d_py, T * K * d) == hipSuccess;
+        const size_t meta = (size_t)(2 * E + 1 + 2 * ctx->pf_max_items);
+        ok &= dalloc(&ctx->d_pmeta, meta) == hipSuccess;
+        if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "prefill buffer allocation failed");
+        if (hipHostMalloc((void**)&ctx->h_pmeta, meta * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+            hipHostMalloc((void**)&ctx->h_phist, (size_t)E * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
+            return fail_create(MOE_SPARK_E_NOMEM, "prefill staging allocation failed");
+    }
     if (hipHostMalloc((void**)&ctx->h_fifo, sizeof(FifoEntry) * kFifoCap, hipHostMallocMapped | hipHostMallocCoherent) !=
             hipSuccess ||
         hipHostMalloc((void**)&ctx->h_ready, sizeof(uint64_t) * std::max(R, 1),
@@ -936,11 +981,114 @@ moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int
 }
 
 moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_tokens, const int32_t* bias_row) {
-    (void)x;
-    (void)n_tokens;
-    (void)bias_row;
     if (!ctx) return MOE_SPARK_E_INVALID;
-    return ctx->fail(MOE_SPARK_E_STATE, "prefill is not available in this build");
+    const auto& c = ctx->cfg;
+    if (c.wfmt != MOE_SPARK_W_Q4_0) return ctx->fail(MOE_SPARK_E_INVALID, "prefill runs the Q4_0 expert format");
+    if (c.max_tokens <= 0) return ctx->fail(MOE_SPARK_E_STATE, "prefill needs max_tokens > 0 at create");
+    if (n_tokens < 1 || n_tokens > c.max_tokens || !x)
+        return ctx->fail(MOE_SPARK_E_INVALID, "n_tokens must be in [1, max_tokens] and x non-NULL");
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    const int L = c.n_layers, E = c.n_experts, K = c.top_k, R = c.ring_slots;
+    const int32_t T = n_tokens;
+    int32_t* goff = ctx->h_pmeta;
+    int32_t* experts = goff + E + 1;
+    int32_t* items = experts + E;
+    int32_t* d_goff = ctx->d_pmeta;
+    int32_t* d_experts = d_goff + E + 1;
+    int32_t* d_items = d_experts + E;
+    for (int l = 0; l < L; ++l) {
+        PfArgs a{};
+        a.x = x;
+        a.T = T;
+        a.layer = l;
+        a.L = L;
+        a.E = E;
+        a.K = K;
+        a.norm = 1;
+        a.eps = c.rms_eps;
+        a.wr = ctx->d_router + (int64_t)l * E * c.d_model;
+        a.bias = c.n_bias_rows > 0 ? ctx->d_bias + (int64_t)l * c.n_bias_rows * E : nullptr;
+        a.bias_row = bias_row;
+        a.n_bias_rows = c.n_bias_rows;
+        a.u = ctx->d_pu;
+        a.inv = ctx->d_pinv;
+        a.logits = ctx->d_plog;
+        a.topk = ctx->d_ptopk;
+        a.gates = ctx->d_pgate;
+        a.hist = ctx->d_phist;
+        a.goff = d_goff;
+        a.perm = ctx->d_pperm;
+        a.apos = ctx->d_papos;
+        a.pslot = ctx->d_pslot;
+        a.pwait = ctx->d_pwait;
+        a.h = ctx->d_ph;
+        a.y = ctx->d_py;
+        a.slots = ctx->d_slots;
+        a.slot_bytes = ctx->slot_bytes;
+        a.P = c.resident_cap;
+        a.n_slots = ctx->n_slots;
+        a.ready = ctx->d_ready;
+        a.pt = tables(ctx);
+        a.tr_x = ctx->tr_x;
+        a.tr_topk = ctx->tr_topk;
+        a.tr_gates = ctx->tr_gates;
+        a.tr_cap = ctx->tr_cap;
+        a.spin_limit_ticks = ctx->spin_ticks;
+        // 1. routing of all tokens; the assignment histogram comes back to plan the layer
+        HIPCHK(hipMemsetAsync(ctx->d_phist, 0, sizeof(int32_t) * E, ctx->compute));
+        HIPCHK(launch_pf_front(a, ctx->compute));
+        HIPCHK(hipMemcpyAsync(ctx->h_phist, ctx->d_phist, sizeof(int32_t) * E, hipMemcpyDeviceToHost, ctx->compute));
+        HIPCHK(hipStreamSynchronize(ctx->compute));
+        // 2. plan: groups in expert order; distinct experts ascending, cut into
+        //    chunks of at most R cold (non-pinned) experts, so that every
+        //    expert of a chunk sits in the ring while the chunk computes
+        goff[0] = 0;
+        for (int e = 0; e < E; ++e) goff[e + 1] = goff[e] + ctx->h_phist[e];
+        struct Chunk {
+            int e_begin, e_end, i_begin, i_end;
+        };
+        std::vector<Chunk> chunks;
+        int ne = 0, ni = 0, cold = 0;
+        Chunk cur{0, 0, 0, 0};
+        for (int e = 0; e < E; ++e) {
+            const int n_e = ctx->h_phist[e];
+            if (n_e == 0) continue;
+            const bool is_cold = ctx->slot_of[(int64_t)l * E + e] < 0;
+            if (is_cold && cold == R) {
+                cur.e_end = ne;
+                cur.i_end = ni;
+                chunks.push_back(cur);
+                cur = Chunk{ne, ne, ni, ni};
+                cold = 0;
+            }
+            cold += is_cold;
+            experts[ne++] = e;
+            for (int m0 = 0; m0 < n_e; m0 += 128) {
+                if (ni >= ctx->pf_max_items) return ctx->fail(MOE_SPARK_E_STATE, "prefill work list overflow");
+                items[2 * ni] = e;
+                items[2 * ni + 1] = m0;
+                ++ni;
+            }
+        }
+        cur.e_end = ne;
+        cur.i_end = ni;
+        if (cur.e_end > cur.e_begin) chunks.push_back(cur);
+        const size_t meta = (size_t)(2 * E + 1) + 2 * (size_t)ni;
+        HIPCHK(hipMemcpyAsync(d_goff, goff, meta * sizeof(int32_t), hipMemcpyHostToDevice, ctx->compute));
+        // 3. sort assignments, run each chunk, combine
+        HIPCHK(launch_pf_scatter(a, ctx->compute));
+        for (const Chunk& ch : chunks) {
+            PfArgs b = a;
+            b.pf_experts = d_experts + ch.e_begin;
+            b.n_pf_experts = ch.e_end - ch.e_begin;
+            b.items = d_items + 2 * ch.i_begin;
+            b.n_items = ch.i_end - ch.i_begin;
+            HIPCHK(launch_pf_chunk(b, ctx->compute));
+        }
+        HIPCHK(launch_pf_combine(a, ctx->compute));
+    }
+    return MOE_SPARK_OK;
 }
 
 moe_spark_status moe_spark_set_trace(moe_spark_ctx* ctx, float* x_layers, int32_t* topk, float* gates,
