@@ -1,13 +1,31 @@
-"""Decode benchmark of resident expert caching on one MI355X.
+"""Benchmark of resident expert caching on one MI355X.
 
-Workload: a 40-layer stack of MoE layers (d=2048, 256 experts, top-8, SwiGLU
-f=512, Q4_0 experts from N(0, 0.02), fp32 router N(0, 0.02)), residual
-x += MoE(RMSNorm(x)), attention omitted, Zipf-routed (logit bias 2 ln p_r,
-p_r ~ r^-1.1 over a per-layer seeded permutation).  Expert residency is capped
-at 60% of the 10,240 experts (P = 6144 pinned slots) with a 32-slot LRU spare
-ring; placement is calibrated from a 256-token warm-up trace run under uniform
-placement.  A step is one decode token through all 40 layers (one graph
-launch).  The same protocol at full residency is run first for the ratio.
+Headline (the JSON line's `value`): decode tok/s of a 40-layer stack of MoE
+layers at 60% expert residency.
+ - Layer shape: d=2048, 256 experts, top-8, SwiGLU f=512.
+ - Weights: Q4_0 experts drawn from N(0, 0.02); fp32 router N(0, 0.02).
+ - Stack: residual x += MoE(RMSNorm(x)); attention omitted.
+ - Routing: Zipf-skewed (logit bias 2 ln p_r, p_r ~ r^-1.1 over a per-layer
+   seeded permutation).
+ - Residency: P = 6144 of 10,240 experts pinned, plus a 32-slot LRU spare
+   ring.
+ - Placement: calibrated from a 256-token warm-up run under uniform placement.
+A step is one decode token through all 40 layers (one graph launch).  The
+same protocol at full residency runs first, giving the ratio and the
+bit-identity check.
+
+Nested in the same line:
+ - `sweep`: residency 100/60/30% x {uniform static, calibrated + ring}, with
+   tok/s, cold-hit %, fill %, PCIe bytes and bit-identity of the outputs.
+ - `prefill`: 2048 tokens through the stack in one batch, 60% residency.
+   1. Placement is calibrated from the decode warm-up under permutation A.
+   2. The Zipf permutation switches to B at token 1024.
+   3. Then a 256-token decode probe under B runs before and after
+      recalibration.
+ - `roofline`: the dominant decode kernel, timed by HIP events over isolated
+   replays.
+ - `h2d_link`: a pinned host-to-device copy probe of the PCIe link.
+ - `cpu_baseline`: the fp64 oracle on a bounded sample of the decode stream.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -24,8 +42,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tok/s @60% expert residency; expert GEMV HBM GB/s; cold-hit %"
 HBM_PEAK_GBPS = 8000.0
-GATEUP_BYTES = 8 * 2 * 589_824   # algorithmic bytes of one gate/up launch (K experts)
-DOWN_BYTES = 8 * 589_824
+BF16_PEAK_TFLOPS = 2500.0
+EXPERT_BYTES = 1_769_472          # one Q4_0 expert: gate | up | down
+GATEUP_BYTES = 8 * 2 * 589_824    # algorithmic bytes of one gate/up launch (8 experts)
+DOWN_BYTES = 8 * 589_824 + 256 * 2048 * 4  # down weights of 8 experts + the next layer's router
+TOKEN_BYTES_PER_LAYER = 8 * EXPERT_BYTES + 256 * 2048 * 4
 
 
 def log(*a):
@@ -33,7 +54,7 @@ def log(*a):
 
 
 class Model:
-    """Host copy of the workload's weights and a loader into a context."""
+    """Host copy of the stack's weights and a loader into a context."""
 
     def __init__(self, w):
         import workload as wl
@@ -47,27 +68,34 @@ class Model:
         return [self.wl.split_expert(self.blob[layer * w.E + e], w.d, w.f, w.wfmt)
                 for e in range(w.E)]
 
-    def make_ctx(self, P, R):
+    def make_ctx(self, P, R, biases=None, max_tokens=0):
         import resident_expert_caching_amd as ms
         w = self.w
+        biases = self.biases if biases is None else biases
         cfg = ms.Config(n_layers=w.L, d_model=w.d, n_experts=w.E, top_k=w.K, d_ff=w.f,
-                        wfmt=w.wfmt, rms_eps=1e-6, n_bias_rows=len(w.bias_seeds),
-                        resident_cap=P, ring_slots=R, max_tokens=0, event_cap=0)
+                        wfmt=w.wfmt, rms_eps=1e-6, n_bias_rows=biases[0].shape[0],
+                        resident_cap=P, ring_slots=R, max_tokens=max_tokens, event_cap=0)
         ctx = ms.moe_spark_create(cfg)
         for l in range(w.L):
             ms.moe_spark_set_router(ctx, l, self.routers[l].ctypes.data,
-                                    np.ascontiguousarray(self.biases[l]).ctypes.data)
+                                    np.ascontiguousarray(biases[l]).ctypes.data)
         ms.moe_spark_set_experts(ctx, 0, w.L * w.E, self.blob.ctypes.data)
         ms.moe_spark_place_uniform(ctx)
         return ctx
 
 
-def run_decode(ms, torch, model, P, R, warm, meas, row, calibrate, kernel_iters=10):
-    """One residency setting: warm-up (uniform), optional calibration, timed decode."""
-    w = model.w
+def rates(st):
+    acc = max(st["accesses"], 1)
+    return dict(cold_hit_pct=round(100.0 * st["cold_hits"] / acc, 4),
+                fill_pct=round(100.0 * st["fills"] / acc, 4))
+
+
+def run_decode(ms, torch, model, P, R, warm, meas, row, calibrate, kernel_iters=0):
+    """One residency setting: warm-up under uniform placement, optional
+    calibration, then the timed decode of `meas`."""
     t0 = time.time()
     ctx = model.make_ctx(P=P, R=R)
-    log(f"P={P} R={R}: context ready in {time.time() - t0:.1f}s")
+    log(f"P={P} R={R} calibrated={calibrate}: context ready in {time.time() - t0:.1f}s")
     try:
         xw = torch.from_numpy(warm).cuda()
         xm = torch.from_numpy(meas).cuda()
@@ -84,30 +112,96 @@ def run_decode(ms, torch, model, P, R, warm, meas, row, calibrate, kernel_iters=
         torch.cuda.synchronize()
         dt = time.perf_counter() - t1
         st = ms.moe_spark_get_stats(ctx)
-        us_gu, us_dn, _ = ms.moe_spark_time_expert_kernels(ctx, kernel_iters)
         out = dict(tok_s=xm.shape[0] / dt, ms_per_tok=dt * 1e3 / xm.shape[0], stats=st,
-                   us_gateup=us_gu, us_down=us_dn, x_out=xm.cpu().numpy())
-        log(f"P={P}: {out['tok_s']:.1f} tok/s, cold {st['cold_hits'] / max(st['accesses'], 1):.4%}, "
-            f"fills {st['fills']}, gate/up {us_gu:.2f} us, down {us_dn:.2f} us")
+                   elapsed_s=dt, x_out=xm.cpu().numpy())
+        if kernel_iters:
+            out["us_gateup"], out["us_down"], out["us_route"] = \
+                ms.moe_spark_time_expert_kernels(ctx, kernel_iters)
+        r = rates(st)
+        log(f"P={P} calibrated={calibrate}: {out['tok_s']:.1f} tok/s, cold {r['cold_hit_pct']}%, "
+            f"fills {st['fills']}")
         return out
     finally:
         ms.moe_spark_destroy(ctx)
 
 
-def cpu_baseline(model, tokens, row, budget_s):
+def run_prefill(ms, torch, model, P, R, warm, probe, layers):
+    """Batched prefill with a popularity shift, then recalibration."""
+    import workload as wl
+    wp = wl.prefill(layers)
+    biases = [wp.bias_rows(l) for l in range(model.w.L)]  # rows: permutation A, permutation B
+    X = wp.tokens()
+    T = X.shape[0]
+    rows = torch.from_numpy((np.arange(T) >= T // 2).astype(np.int32)).cuda()
+    row_a = torch.zeros(max(warm.shape[0], probe.shape[0]), dtype=torch.int32, device="cuda")
+    row_b = torch.ones_like(row_a)
+    ctx = model.make_ctx(P=P, R=R, biases=biases, max_tokens=T)
+    try:
+        xw = torch.from_numpy(warm).cuda()
+        ms.moe_spark_decode(ctx, xw.data_ptr(), xw.shape[0], row_a.data_ptr())
+        ms.moe_spark_calibrate(ctx, True)
+        ms.moe_spark_reset_stats(ctx)
+        xd = torch.from_numpy(X).cuda()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms.moe_spark_prefill(ctx, xd.data_ptr(), T, rows.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        dt = time.perf_counter() - t1
+        st = ms.moe_spark_get_stats(ctx)
+
+        def probe_decode():
+            ms.moe_spark_reset_stats(ctx)
+            xp = torch.from_numpy(probe).cuda()
+            ms.moe_spark_decode(ctx, xp.data_ptr(), xp.shape[0], row_b.data_ptr())
+            ms.moe_spark_synchronize(ctx)
+            return rates(ms.moe_spark_get_stats(ctx))["cold_hit_pct"]
+
+        before = probe_decode()
+        ms.moe_spark_calibrate(ctx, True)
+        after = probe_decode()
+        gflop = 2.0 * T * model.w.K * (3 * model.w.d * model.w.f) * model.w.L / 1e9
+        out = dict(tokens=T, layers=model.w.L, tok_s=round(T / dt, 1), ms=round(dt * 1e3, 3),
+                   expert_gflop=round(gflop, 1), expert_tflops_end_to_end=round(gflop / dt / 1e3, 2),
+                   accesses=st["accesses"], fills=st["fills"], evictions=st["evictions"],
+                   h2d_bytes=st["h2d_bytes"], cold_hit_pct=rates(st)["cold_hit_pct"],
+                   probe_cold_hit_pct_before_recalibration=before,
+                   probe_cold_hit_pct_after_recalibration=after,
+                   arithmetic="Q4_0->bf16 dequant in LDS, bf16 activations, MFMA fp32 accumulation")
+        log(f"prefill: {out['tok_s']} tok/s, fills {st['fills']}, cold probe {before}% -> {after}%")
+        return out
+    finally:
+        ms.moe_spark_destroy(ctx)
+
+
+def h2d_probe(torch, mib=256, reps=5):
+    """Pinned host -> device copy rate (the cold-fill link)."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    best = 1e9
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src, non_blocking=True)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    return dict(bytes=mib << 20, gbps=round((mib << 20) / best / 1e9, 2))
+
+
+def cpu_baseline(model, tokens, budget_s):
     """The fp64 oracle on a bounded sample of the same decode stream."""
     import oracle
     w = model.w
     experts = [model.experts(l) for l in range(w.L)]
-    biases = model.biases
     n, t0 = 0, time.perf_counter()
     while n < tokens.shape[0] and (n < 2 or time.perf_counter() - t0 < budget_s):
-        oracle.stack(tokens[n:n + 1].astype(np.float64), model.routers, biases, experts, K=w.K,
+        oracle.stack(tokens[n:n + 1].astype(np.float64), model.routers, model.biases, experts, K=w.K,
                      wfmt=w.wfmt, bias_row=np.zeros(1, np.int32))
         n += 1
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=n / dt, unit="tok/s", cores=cores, kind="oracle",
+    return dict(value=round(n / dt, 3), unit="tok/s", cores=oracle.num_threads(), kind="oracle",
                 sample=f"{n} decode tokens of the 40-layer stack (fp64, all layers), "
                        f"{dt:.1f} s of CPU work")
 
@@ -121,6 +215,9 @@ def main():
     ap.add_argument("--residency", type=float, default=0.6)
     ap.add_argument("--ring", type=int, default=32)
     ap.add_argument("--no-full", action="store_true", help="skip the full-residency run")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the residency sweep")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the batched prefill")
+    ap.add_argument("--kernel-iters", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemv_traffic.json"))
@@ -144,15 +241,13 @@ def main():
     row = torch.zeros(max(args.warmup, args.steps, 1), dtype=torch.int32, device="cuda")
     LE = w.L * w.E
     P = int(round(args.residency * LE))
+    R = args.ring if P < LE else 0
 
     full = None
     if not args.no_full and P < LE:
         full = run_decode(ms, torch, model, LE, 0, warm, meas, row, calibrate=False)
-    part = run_decode(ms, torch, model, P, args.ring if P < LE else 0, warm, meas, row,
-                      calibrate=True)
-    if full is not None:
-        same = bool(np.array_equal(full["x_out"], part["x_out"]))
-        log(f"outputs bit-identical to full residency: {same}")
+    part = run_decode(ms, torch, model, P, R, warm, meas, row, calibrate=True,
+                      kernel_iters=args.kernel_iters)
 
     st = part["stats"]
     us = part["us_gateup"]
@@ -160,10 +255,10 @@ def main():
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
-            tj = json.load(open(args.traffic_json))
-            traffic = tj.get("gateup_hbm_bytes_per_launch")
-        except Exception:
+            traffic = json.load(open(args.traffic_json)).get("gateup_hbm_bytes_per_launch")
+        except (OSError, ValueError):
             traffic = None
+    token_gbps = TOKEN_BYTES_PER_LAYER * w.L * part["tok_s"] / 1e9
     res = {
         "metric": METRIC,
         "value": round(part["tok_s"], 2),
@@ -188,7 +283,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "q4_gateup_kernel (router-partial reduce, top-8, gate+up GEMV of 8 Q4_0 experts + SwiGLU)",
+            "kernel": "q4_gateup_kernel (router-partial reduce, top-8, gate+up GEMV of 8 Q4_0 "
+                      "experts + SwiGLU)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -196,22 +292,51 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": GATEUP_BYTES,
             "avg_launch_us": round(us, 3),
+            "down_kernel_us": round(part["us_down"], 3),
+            "down_kernel_gbps": round(DOWN_BYTES / (part["us_down"] * 1e-6) / 1e9, 1),
+            "token_algorithmic_bytes": TOKEN_BYTES_PER_LAYER * w.L,
+            "token_gbps": round(token_gbps, 1),
+            "token_frac": round(token_gbps / HBM_PEAK_GBPS, 4),
         },
-        "cold_hit_pct": round(100.0 * st["cold_hits"] / max(st["accesses"], 1), 4),
-        "fill_pct": round(100.0 * st["fills"] / max(st["accesses"], 1), 4),
         "fills": st["fills"],
         "h2d_bytes": st["h2d_bytes"],
         "h2d_gbps_per_fill": round(st["h2d_bytes"] / st["fill_ns_sum"], 3) if st["fill_ns_sum"] else None,
-        "down_kernel_us": round(part["us_down"], 3),
-        "down_kernel_gbps": round(DOWN_BYTES / (part["us_down"] * 1e-6) / 1e9, 1),
     }
+    res.update(rates(st))
     if full is not None:
         res["full_residency_tok_s"] = round(full["tok_s"], 2)
         res["ratio_to_full"] = round(part["tok_s"] / full["tok_s"], 4)
         res["bit_identical_to_full"] = bool(np.array_equal(full["x_out"], part["x_out"]))
+        log(f"outputs bit-identical to full residency: {res['bit_identical_to_full']}")
+    if not args.no_sweep:
+        rows = []
+        ref = full["x_out"] if full is not None else part["x_out"]
+        for frac in (1.0, 0.6, 0.3):
+            Pf = int(round(frac * LE))
+            for calibrated in (False, True):
+                if frac == 1.0 and calibrated:
+                    continue
+                if frac == 1.0 and full is not None:
+                    r = full
+                elif frac == args.residency and calibrated:
+                    r = part
+                else:
+                    r = run_decode(ms, torch, model, Pf, args.ring if Pf < LE else 0, warm, meas, row,
+                                   calibrate=calibrated)
+                s = r["stats"]
+                rows.append(dict(residency=frac, placement="calibrated" if calibrated else "uniform",
+                                 resident_cap=Pf, tok_s=round(r["tok_s"], 2), **rates(s),
+                                 fills=s["fills"], h2d_bytes=s["h2d_bytes"],
+                                 h2d_gbps=round(s["h2d_bytes"] / r["elapsed_s"] / 1e9, 3),
+                                 bit_identical=bool(np.array_equal(r["x_out"], ref))))
+        res["sweep"] = rows
+    if not args.no_prefill:
+        probe = wl.stack(args.layers).tokens(args.warmup + args.steps, 256)
+        res["prefill"] = run_prefill(ms, torch, model, P, args.ring, warm, probe, args.layers)
+    res["h2d_link"] = h2d_probe(torch)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same stream")
-        res["cpu_baseline"] = cpu_baseline(model, meas, row, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(model, meas, args.cpu_budget)
     print(json.dumps(res), flush=True)
 
 

@@ -47,6 +47,7 @@ def lib():
             build()
         L = ctypes.CDLL(_LIB_PATH)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.oracle_num_threads.restype = i32
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f64.restype = dbl
         L.oracle_q4_0_block.argtypes = [vp, vp]
@@ -95,6 +96,10 @@ def _f32(a):
 
 def _ptrs(arrs):
     return (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+
+
+def num_threads():
+    return int(lib().oracle_num_threads())
 
 
 def f16_to_f64(h):

@@ -20,11 +20,15 @@
  * the thread count.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include "oracle.h"
+
+/* Threads the OpenMP loops of this library use (for reporting). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* IEEE binary16 -> fp64, exact (sign, 5-bit exponent, 10-bit fraction). */
 double oracle_f16_to_f64(uint16_t h) {

@@ -40,6 +40,9 @@ typedef struct {
     double eps;    /* RMSNorm epsilon */
 } oracle_shape;
 
+/* threads the OpenMP loops use (reporting only) */
+int oracle_num_threads(void);
+
 /* ---- elementary steps ---- */
 double oracle_f16_to_f64(uint16_t h);
 void oracle_q4_0_block(const uint8_t* blk18, double* w32);
