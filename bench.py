@@ -30,6 +30,7 @@ Nested in the same line:
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -221,6 +222,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemv_traffic.json"))
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="end with a 256 MiB device-to-device copy (a known-size kernel for "
+                         "calibrating the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -252,10 +256,15 @@ def main():
     st = part["stats"]
     us = part["us_gateup"]
     achieved = GATEUP_BYTES / (us * 1e-6) / 1e9
-    traffic = None
+    traffic = None  # counter-measured HBM bytes, only while the kernel source is the one measured
     if os.path.exists(args.traffic_json):
         try:
-            traffic = json.load(open(args.traffic_json)).get("gateup_hbm_bytes_per_launch")
+            tj = json.load(open(args.traffic_json))
+            h = hashlib.sha256()
+            for f in tj.get("kernel_sources", []):
+                h.update(open(os.path.join(ROOT, "resident_expert_caching_amd", "csrc", f), "rb").read())
+            if tj.get("kernel_source_sha256") == h.hexdigest():
+                traffic = tj.get("gateup_hbm_bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
     token_gbps = TOKEN_BYTES_PER_LAYER * w.L * part["tok_s"] / 1e9
@@ -334,6 +343,12 @@ def main():
         probe = wl.stack(args.layers).tokens(args.warmup + args.steps, 256)
         res["prefill"] = run_prefill(ms, torch, model, P, args.ring, warm, probe, args.layers)
     res["h2d_link"] = h2d_probe(torch)
+    if args.copy_probe:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same stream")
         res["cpu_baseline"] = cpu_baseline(model, meas, args.cpu_budget)
