@@ -193,9 +193,10 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
 
 /* Trace buffers (device, or NULL to stop tracing) filled by decode,
  * token_forward and prefill: x_layers [cap][L][d] fp32 (input of each layer),
- * topk [cap][L][K] int32, gates [cap][L][K] fp32; token index counts from 0
- * at this call; tokens past cap are not traced.  layer_forward traces into
- * the same buffers at [token][layer]. */
+ * topk [cap][L][K] int32, gates [cap][L][K] fp32.  Rows follow a trace cursor
+ * that starts at 0 at this call and advances by one per decoded token and by
+ * n_tokens per prefill batch; rows at or past cap are not written.
+ * layer_forward traces token t of its call at row t, layer `layer`. */
 moe_spark_status moe_spark_set_trace(moe_spark_ctx* ctx, float* x_layers, int32_t* topk,
                                      float* gates, int64_t cap_tokens);
 

@@ -203,10 +203,11 @@ struct PfArgs {
     int64_t slot_bytes, P, n_slots;
     const uint64_t* ready;
     PolicyTables pt;
-    float* tr_x;
+    float* tr_x;              // traces: token t goes to row *tr_base + t
     int32_t* tr_topk;
     float* tr_gates;
     int64_t tr_cap;
+    const int32_t* tr_base;   // the context's trace cursor
     uint64_t spin_limit_ticks;
 };
 
@@ -214,6 +215,7 @@ hipError_t launch_pf_front(const PfArgs& a, hipStream_t s);    // norm, router, 
 hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s);  // sort assignments by (expert, token)
 hipError_t launch_pf_chunk(const PfArgs& a, hipStream_t s);    // policy, gate/up GEMM, down GEMM of one chunk
 hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s);  // rank-order combine + residual
+hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s);
 
 // Launchers (kernels.hip).
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

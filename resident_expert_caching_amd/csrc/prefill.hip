@@ -95,8 +95,9 @@ __global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
     u2[2 * tid + 1] = pack_bf16(v0.z * inv, v0.w * inv);
     u2[2 * (tid + kPfThreads)] = pack_bf16(v1.x * inv, v1.y * inv);
     u2[2 * (tid + kPfThreads) + 1] = pack_bf16(v1.z * inv, v1.w * inv);
-    if (a.tr_x && t < a.tr_cap) {
-        f32x4* tr = reinterpret_cast<f32x4*>(a.tr_x + ((int64_t)t * a.L + a.layer) * kQD);
+    const int64_t tt = (int64_t)*a.tr_base + t;
+    if (a.tr_x && tt < a.tr_cap) {
+        f32x4* tr = reinterpret_cast<f32x4*>(a.tr_x + (tt * a.L + a.layer) * kQD);
         tr[tid] = v0;
         tr[tid + kPfThreads] = v1;
     }
@@ -199,8 +200,9 @@ __global__ __launch_bounds__(kPfThreads) void pf_topk_kernel(PfArgs a) {
         a.gates[(int64_t)t * K + tid] = g;
         atomicAdd(reinterpret_cast<unsigned long long*>(a.pt.counts + (int64_t)a.layer * E + e), 1ull);
         atomicAdd(a.hist + e, 1);
-        if (a.tr_topk && t < a.tr_cap) {
-            const int64_t o = ((int64_t)t * a.L + a.layer) * K + tid;
+        const int64_t tt = (int64_t)*a.tr_base + t;
+        if (a.tr_topk && tt < a.tr_cap) {
+            const int64_t o = (tt * a.L + a.layer) * K + tid;
             a.tr_topk[o] = e;
             a.tr_gates[o] = g;
         }
@@ -482,7 +484,16 @@ __global__ __launch_bounds__(kPfThreads) void pf_combine_kernel(PfArgs a) {
     *xp = *xp + y;
 }
 
+__global__ void cursor_add_kernel(int32_t* cursor, int32_t n) {
+    if (threadIdx.x == 0) *cursor += n;
+}
+
 }  // namespace
+
+hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s) {
+    hipLaunchKernelGGL(cursor_add_kernel, dim3(1), dim3(64), 0, s, cursor, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_pf_front(const PfArgs& a, hipStream_t s) {
     if (a.T <= 0 || a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE) return hipErrorInvalidValue;

@@ -1034,6 +1034,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         a.tr_topk = ctx->tr_topk;
         a.tr_gates = ctx->tr_gates;
         a.tr_cap = ctx->tr_cap;
+        a.tr_base = ctx->d_cursors + 1;
         a.spin_limit_ticks = ctx->spin_ticks;
         // 1. routing of all tokens; the assignment histogram comes back to plan the layer
         HIPCHK(hipMemsetAsync(ctx->d_phist, 0, sizeof(int32_t) * E, ctx->compute));
@@ -1048,32 +1049,43 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         struct Chunk {
             int e_begin, e_end, i_begin, i_end;
         };
+        // Within a chunk the GEMM tiles of pinned experts come first and those
+        // of cold experts (in fill order) last, so the matrix cores work while
+        // the fills cross PCIe.
         std::vector<Chunk> chunks;
+        std::vector<int> chunk_experts;
         int ne = 0, ni = 0, cold = 0;
         Chunk cur{0, 0, 0, 0};
+        auto close_chunk = [&]() -> bool {
+            for (int pass = 0; pass < 2; ++pass)
+                for (int e : chunk_experts) {
+                    const bool is_cold = ctx->slot_of[(int64_t)l * E + e] < 0;
+                    if (is_cold != (pass == 1)) continue;
+                    for (int m0 = 0; m0 < ctx->h_phist[e]; m0 += 128) {
+                        if (ni >= ctx->pf_max_items) return false;
+                        items[2 * ni] = e;
+                        items[2 * ni + 1] = m0;
+                        ++ni;
+                    }
+                }
+            cur.e_end = ne;
+            cur.i_end = ni;
+            if (cur.e_end > cur.e_begin) chunks.push_back(cur);
+            cur = Chunk{ne, ne, ni, ni};
+            chunk_experts.clear();
+            cold = 0;
+            return true;
+        };
         for (int e = 0; e < E; ++e) {
-            const int n_e = ctx->h_phist[e];
-            if (n_e == 0) continue;
+            if (ctx->h_phist[e] == 0) continue;
             const bool is_cold = ctx->slot_of[(int64_t)l * E + e] < 0;
-            if (is_cold && cold == R) {
-                cur.e_end = ne;
-                cur.i_end = ni;
-                chunks.push_back(cur);
-                cur = Chunk{ne, ne, ni, ni};
-                cold = 0;
-            }
+            if (is_cold && cold == R && !close_chunk())
+                return ctx->fail(MOE_SPARK_E_STATE, "prefill work list overflow");
             cold += is_cold;
             experts[ne++] = e;
-            for (int m0 = 0; m0 < n_e; m0 += 128) {
-                if (ni >= ctx->pf_max_items) return ctx->fail(MOE_SPARK_E_STATE, "prefill work list overflow");
-                items[2 * ni] = e;
-                items[2 * ni + 1] = m0;
-                ++ni;
-            }
+            chunk_experts.push_back(e);
         }
-        cur.e_end = ne;
-        cur.i_end = ni;
-        if (cur.e_end > cur.e_begin) chunks.push_back(cur);
+        if (!close_chunk()) return ctx->fail(MOE_SPARK_E_STATE, "prefill work list overflow");
         const size_t meta = (size_t)(2 * E + 1) + 2 * (size_t)ni;
         HIPCHK(hipMemcpyAsync(d_goff, goff, meta * sizeof(int32_t), hipMemcpyHostToDevice, ctx->compute));
         // 3. sort assignments, run each chunk, combine
@@ -1088,6 +1100,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         }
         HIPCHK(launch_pf_combine(a, ctx->compute));
     }
+    HIPCHK(launch_cursor_add(ctx->d_cursors + 1, T, ctx->compute));  // trace rows continue after the batch
     return MOE_SPARK_OK;
 }
 

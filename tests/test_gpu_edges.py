@@ -1,0 +1,189 @@
+"""GPU edge cases of the Q4_0 path through the C ABI, checked against the
+oracle and the placement simulator.
+
+ * top-k extremes and expert counts that are not a multiple of the 64-expert
+   ranking chunk: (E, K) = (16, 1), (100, 2), (100, 8), and E = 1024, the
+   largest supported;
+ * no pinned slot at all (every access goes through a ring of exactly K
+   slots) next to full residency: bit-identical outputs;
+ * prefill of a single token, and prefills whose layers need many ring
+   chunks (far more cold experts than ring slots);
+ * error paths: prefill beyond max_tokens, prefill without prefill buffers,
+   forward before placement.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as wl
+from spark_harness import (STAT_KEYS, TIE_GAP, Model, events, oracle_topk_and_gap, placement,
+                           sim_events)
+
+pytestmark = pytest.mark.gpu
+
+ms = pytest.importorskip("resident_expert_caching_amd")
+
+
+def _wl(E, K, L=1, n_tokens=24, bias=True):
+    return wl.Workload(f"edge-E{E}-K{K}", d=2048, E=E, K=K, f=512, L=L, wfmt=wl.FMT_Q4_0, norm=True,
+                       seed=5 + E + K, n_tokens=n_tokens, token_stream=9,
+                       bias_seeds=(3, 1003) if bias else ())
+
+
+def _layer_run(model, P, R, x):
+    w = model.w
+    T = x.shape[0]
+    ctx = model.make_ctx(P=P, R=R)
+    try:
+        xd = torch.from_numpy(x.copy()).cuda()
+        yd = torch.empty_like(xd)
+        topk = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+        gates = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
+        rows = torch.from_numpy((np.arange(T) % 2).astype(np.int32)).cuda()
+        ms.moe_spark_layer_forward(ctx, 0, xd.data_ptr(), yd.data_ptr(), T, rows.data_ptr(),
+                                   ms.PRE_RMSNORM | ms.RESIDUAL, topk.data_ptr(), gates.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        return dict(y=yd.cpu().numpy(), topk=topk.cpu().numpy(), gates=gates.cpu().numpy(),
+                    stats=ms.moe_spark_get_stats(ctx), events=events(ctx),
+                    placement=placement(ctx, w, R), slot_bytes=ms.moe_spark_slot_bytes(ctx))
+    finally:
+        ms.moe_spark_destroy(ctx)
+
+
+@pytest.mark.parametrize("E,K", [(16, 1), (100, 2), (100, 8), (1024, 8)])
+def test_layer_extremes_against_oracle_and_simulator(E, K):
+    w = _wl(E, K)
+    model = Model(w)
+    x = w.tokens()
+    T = x.shape[0]
+    rows = (np.arange(T) % 2).astype(np.int32)
+    print(f"layer E={E} K={K}: full residency and no pinned slot (ring of {K})", flush=True)
+    full = _layer_run(model, E, 0, x)
+    none = _layer_run(model, 0, K, x)
+    assert np.array_equal(full["y"], none["y"]) and np.array_equal(full["topk"], none["topk"])
+    assert none["stats"]["pinned_hits"] == 0 and none["stats"]["cold_hits"] == T * K
+    # bookkeeping of the ring-only run
+    sim = oracle.Sim(1, E, 0, K, none["slot_bytes"])
+    sim.place_uniform()
+    for t in range(T):
+        sim.decode_layer(0, none["topk"][t])
+    assert {k: none["stats"][k] for k in STAT_KEYS} == sim.stats()
+    assert none["events"] == sim_events(sim)
+    for got, ref in zip(none["placement"], sim.placement()):
+        assert np.array_equal(got, ref)
+    # routing and outputs against the oracle
+    wr, bias = model.routers[0], model.biases[0]
+    forced = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        lg = oracle.router(wr, oracle.rmsnorm(x[t]), bias[rows[t]])
+        ref_idx, gap = oracle_topk_and_gap(lg, K)
+        if gap < TIE_GAP:
+            forced[t] = full["topk"][t]
+        else:
+            assert np.array_equal(full["topk"][t], ref_idx), (t, full["topk"][t], ref_idx)
+    if K == 1:
+        assert np.all(full["gates"] == 1.0)
+    assert np.abs(full["gates"].sum(axis=1) - 1).max() <= 1e-6
+    sample = np.arange(0, T, 3)
+    yref, _, gref, _ = oracle.layer(x[sample].astype(np.float64), wr, model.experts(0), K=K,
+                                    wfmt=w.wfmt, norm=True, bias=bias, bias_row=rows[sample],
+                                    forced=forced[sample])
+    np.testing.assert_allclose(full["gates"][sample], gref, rtol=2e-5, atol=1e-6)
+    got = full["y"][sample].astype(np.float64) - x[sample]
+    err = np.abs(got - yref).max()
+    assert err <= 2e-3 * np.abs(yref).max(), err
+
+
+def _prefill_run(model, P, R, x, rows, max_tokens):
+    w = model.w
+    T = x.shape[0]
+    ctx = model.make_ctx(P=P, R=R, max_tokens=max_tokens)
+    try:
+        tr_x = torch.zeros((T, w.L, w.d), dtype=torch.float32, device="cuda")
+        tr_k = torch.zeros((T, w.L, w.K), dtype=torch.int32, device="cuda")
+        tr_g = torch.zeros((T, w.L, w.K), dtype=torch.float32, device="cuda")
+        ms.moe_spark_set_trace(ctx, tr_x.data_ptr(), tr_k.data_ptr(), tr_g.data_ptr(), T)
+        xd = torch.from_numpy(x.copy()).cuda()
+        rd = torch.from_numpy(rows).cuda()
+        ms.moe_spark_prefill(ctx, xd.data_ptr(), T, rd.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        return dict(x=xd.cpu().numpy(), tr_x=tr_x.cpu().numpy(), tr_k=tr_k.cpu().numpy(),
+                    stats=ms.moe_spark_get_stats(ctx), events=events(ctx),
+                    placement=placement(ctx, w, R), slot_bytes=ms.moe_spark_slot_bytes(ctx))
+    finally:
+        ms.moe_spark_destroy(ctx)
+
+
+@pytest.mark.parametrize("T", [1, 130])
+def test_prefill_ring_only_many_chunks(T):
+    """E = 100 experts per layer, nothing pinned, a ring of K = 8 slots: a
+    layer's distinct experts stream through the ring in many chunks."""
+    w = _wl(100, 8, L=2, n_tokens=T)
+    model = Model(w)
+    x = w.tokens()
+    rows = (np.arange(T) >= T // 2).astype(np.int32)
+    print(f"prefill T={T}: full residency vs ring only", flush=True)
+    full = _prefill_run(model, w.L * w.E, 0, x, rows, max_tokens=max(T, 4))
+    ring = _prefill_run(model, 0, 8, x, rows, max_tokens=T)
+    assert np.array_equal(full["x"], ring["x"]) and np.array_equal(full["tr_k"], ring["tr_k"])
+    sim = oracle.Sim(w.L, w.E, 0, 8, ring["slot_bytes"])
+    sim.place_uniform()
+    for l in range(w.L):
+        sim.prefill_layer(l, ring["tr_k"][:, l, :])
+    assert {k: ring["stats"][k] for k in STAT_KEYS} == sim.stats()
+    assert ring["events"] == sim_events(sim)
+    for got, ref in zip(ring["placement"], sim.placement()):
+        assert np.array_equal(got, ref)
+    distinct = sum(len(np.unique(ring["tr_k"][:, l, :])) for l in range(w.L))
+    assert ring["stats"]["accesses"] == distinct and ring["stats"]["pinned_hits"] == 0
+    # teacher-forced output of the last layer on a few tokens
+    l = w.L - 1
+    for t in sorted({0, T // 2, T - 1}):
+        xl = full["tr_x"][t, l].astype(np.float64)
+        lg = oracle.router(model.routers[l], oracle.rmsnorm(xl), model.biases[l][rows[t]])
+        ref_idx, gap = oracle_topk_and_gap(lg, w.K)
+        forced = full["tr_k"][t, l][None] if gap < TIE_GAP else None
+        if forced is None:
+            assert np.array_equal(full["tr_k"][t, l], ref_idx)
+        yref, _, _, _ = oracle.layer(xl[None], model.routers[l], model.experts(l), K=w.K, wfmt=w.wfmt,
+                                     norm=True, bias=model.biases[l], bias_row=rows[t:t + 1], forced=forced)
+        ref_next = xl + yref[0]
+        err = np.abs(full["x"][t].astype(np.float64) - ref_next).max()
+        assert err <= 2e-3 * np.abs(ref_next).max(), (t, err)
+
+
+def test_error_paths():
+    w = _wl(16, 2, n_tokens=8)
+    model = Model(w)
+    x = torch.zeros((8, w.d), dtype=torch.float32, device="cuda")
+    ctx = model.make_ctx(P=16, R=0, max_tokens=4)
+    try:
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_prefill(ctx, x.data_ptr(), 5, None)
+        assert ei.value.status == ms.E_INVALID
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_prefill(ctx, x.data_ptr(), 0, None)
+        assert ei.value.status == ms.E_INVALID
+    finally:
+        ms.moe_spark_destroy(ctx)
+    ctx = model.make_ctx(P=16, R=0, max_tokens=0)
+    try:
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_prefill(ctx, x.data_ptr(), 1, None)
+        assert ei.value.status == ms.E_STATE
+    finally:
+        ms.moe_spark_destroy(ctx)
+    # forward before any placement
+    ctx = ms.moe_spark_create(ms.Config(n_layers=1, d_model=2048, n_experts=16, top_k=2, d_ff=512,
+                                        wfmt=ms.W_Q4_0, rms_eps=1e-6, n_bias_rows=0, resident_cap=16,
+                                        ring_slots=0, max_tokens=0, event_cap=0))
+    try:
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_layer_forward(ctx, 0, x.data_ptr(), x.data_ptr(), 1, None, 0, None, None)
+        assert ei.value.status == ms.E_STATE
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_decode(ctx, x.data_ptr(), 1, None)
+        assert ei.value.status == ms.E_STATE
+    finally:
+        ms.moe_spark_destroy(ctx)

@@ -1,0 +1,196 @@
+"""GPU parity at the benchmark's full sizes and launch configuration.
+
+ * Decode of the 40-layer stack (d=2048, 256 experts, top-8, f=512, Q4_0,
+   Zipf routing) at 60% residency with a 32-slot ring, calibrated from a
+   256-token warm-up, 128 measured tokens — the configuration bench.py times.
+ * Batched prefill of 2048 tokens through the same stack at 60% residency,
+   the Zipf permutation switching at token 1024, placement calibrated from
+   the decode warm-up.
+
+Top-k is checked on a sample of token-layers against the oracle's router
+(near-ties excepted), layer outputs on sampled (token, layer) pairs,
+teacher-forced, and all bookkeeping against the simulator replaying the GPU's
+top-k trace.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as wl
+from spark_harness import (STAT_KEYS, TIE_GAP, Model, events, oracle_topk_and_gap, placement,
+                           sim_events)
+
+pytestmark = pytest.mark.gpu
+
+ms = pytest.importorskip("resident_expert_caching_amd")
+
+WARM, MEAS = 256, 128
+
+
+@pytest.fixture(scope="module")
+def stack_model():
+    print("drawing the 40-layer stack (18.1 GB of Q4_0 experts)", flush=True)
+    return Model(wl.stack(40))
+
+
+def _check_layer_samples(model, tr_x, tr_k, x_final, rows, bias_sel, samples, rel_tol, what):
+    """Teacher-forced output parity of sampled (token, layer) pairs."""
+    w = model.w
+    worst = 0.0
+    for t, l in samples:
+        xl = tr_x[t, l].astype(np.float64)
+        xn = (tr_x[t, l + 1] if l + 1 < w.L else x_final[t]).astype(np.float64)
+        b = model.biases[l] if bias_sel is None else bias_sel[l]
+        lg = oracle.router(model.routers[l], oracle.rmsnorm(xl), b[rows[t]])
+        ref_idx, gap = oracle_topk_and_gap(lg, w.K)
+        forced = tr_k[t, l][None] if gap < TIE_GAP else None
+        yref, _, _, _ = oracle.layer(xl[None], model.routers[l], model.experts(l), K=w.K, wfmt=w.wfmt,
+                                     norm=True, bias=b, bias_row=rows[t:t + 1], forced=forced)
+        ref_next = xl + yref[0]
+        err = np.abs(xn - ref_next).max()
+        scale = np.abs(ref_next).max()
+        worst = max(worst, err / scale)
+        assert err <= rel_tol * scale, (what, t, l, err, scale)
+    print(f"{what}: worst teacher-forced error {worst:.2e} of max|x_next|", flush=True)
+
+
+def _check_topk_sample(model, tr_x, tr_k, rows, bias_sel, tokens):
+    w = model.w
+    ties = 0
+    for t in tokens:
+        for l in range(w.L):
+            b = model.biases[l] if bias_sel is None else bias_sel[l]
+            lg = oracle.router(model.routers[l], oracle.rmsnorm(tr_x[t, l]), b[rows[t]])
+            ref_idx, gap = oracle_topk_and_gap(lg, w.K)
+            if gap < TIE_GAP:
+                ties += 1
+            else:
+                assert np.array_equal(tr_k[t, l], ref_idx), (t, l, tr_k[t, l], ref_idx)
+    assert ties <= max(1, len(tokens) * w.L // 50)
+    return ties
+
+
+def test_decode_full_stack_60pct_calibrated(stack_model):
+    model = stack_model
+    w = model.w
+    LE = w.L * w.E
+    P, R = int(round(0.6 * LE)), 32
+    x = w.tokens(0, WARM + MEAS)
+    ctx = model.make_ctx(P=P, R=R)
+    try:
+        cap = WARM + MEAS
+        tr_x = torch.zeros((cap, w.L, w.d), dtype=torch.float32, device="cuda")
+        tr_k = torch.zeros((cap, w.L, w.K), dtype=torch.int32, device="cuda")
+        tr_g = torch.zeros((cap, w.L, w.K), dtype=torch.float32, device="cuda")
+        ms.moe_spark_set_trace(ctx, tr_x.data_ptr(), tr_k.data_ptr(), tr_g.data_ptr(), cap)
+        xw = torch.from_numpy(x[:WARM].copy()).cuda()
+        xm = torch.from_numpy(x[WARM:].copy()).cuda()
+        row = torch.zeros(WARM, dtype=torch.int32, device="cuda")
+        print("decode: warm-up under uniform placement", flush=True)
+        ms.moe_spark_decode(ctx, xw.data_ptr(), WARM, row.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        ms.moe_spark_calibrate(ctx, True)
+        ms.moe_spark_reset_stats(ctx)
+        print("decode: measured tokens after calibration", flush=True)
+        ms.moe_spark_decode(ctx, xm.data_ptr(), MEAS, row.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        st = ms.moe_spark_get_stats(ctx)
+        ev = events(ctx)
+        pl = placement(ctx, w, R)
+        slot_bytes = ms.moe_spark_slot_bytes(ctx)
+        trx, trk = tr_x.cpu().numpy(), tr_k.cpu().numpy()
+        x_final = np.concatenate([xw.cpu().numpy(), xm.cpu().numpy()])
+    finally:
+        ms.moe_spark_destroy(ctx)
+    sim = oracle.Sim(w.L, w.E, P, R, slot_bytes)
+    sim.place_uniform()
+    for t in range(WARM):
+        sim.decode_token(trk[t])
+    sim.calibrate(True)
+    sim.reset_stats()
+    for t in range(WARM, WARM + MEAS):
+        sim.decode_token(trk[t])
+    assert {k: st[k] for k in STAT_KEYS} == sim.stats()
+    assert st["tokens"] == MEAS
+    assert ev == sim_events(sim)
+    for got, ref in zip(pl, sim.placement()):
+        assert np.array_equal(got, ref)
+    print(f"decode stats {st}", flush=True)
+    rows = np.zeros(WARM + MEAS, np.int32)
+    rng = np.random.default_rng(7)
+    _check_topk_sample(model, trx, trk, rows, None, rng.choice(WARM + MEAS, 24, replace=False))
+    samples = [(0, 0), (5, 39), (WARM, 0), (WARM + 1, 20), (WARM + MEAS - 1, 39)] + \
+              [(int(t), int(l)) for t, l in zip(rng.integers(0, WARM + MEAS, 5), rng.integers(0, w.L, 5))]
+    _check_layer_samples(model, trx, trk, x_final, rows, None, samples, 2e-3, "decode")
+
+
+def test_prefill_full_stack_popularity_shift(stack_model):
+    model = stack_model
+    w = model.w
+    wp = wl.prefill(40)
+    biases = [wp.bias_rows(l) for l in range(w.L)]
+    LE = w.L * w.E
+    P, R = int(round(0.6 * LE)), 32
+    T = wp.n_tokens
+    X = wp.tokens()
+    rows = (np.arange(T) >= T // 2).astype(np.int32)
+    warm = w.tokens(0, WARM)
+    import resident_expert_caching_amd as m
+    cfg = m.Config(n_layers=w.L, d_model=w.d, n_experts=w.E, top_k=w.K, d_ff=w.f, wfmt=w.wfmt,
+                   rms_eps=1e-6, n_bias_rows=2, resident_cap=P, ring_slots=R, max_tokens=T,
+                   event_cap=0)
+    ctx = ms.moe_spark_create(cfg)
+    try:
+        for l in range(w.L):
+            ms.moe_spark_set_router(ctx, l, model.routers[l].ctypes.data,
+                                    np.ascontiguousarray(biases[l]).ctypes.data)
+        ms.moe_spark_set_experts(ctx, 0, LE, model.blob.ctypes.data)
+        ms.moe_spark_place_uniform(ctx)
+        cap = WARM + T
+        tr_x = torch.zeros((cap, w.L, w.d), dtype=torch.float32, device="cuda")
+        tr_k = torch.zeros((cap, w.L, w.K), dtype=torch.int32, device="cuda")
+        tr_g = torch.zeros((cap, w.L, w.K), dtype=torch.float32, device="cuda")
+        ms.moe_spark_set_trace(ctx, tr_x.data_ptr(), tr_k.data_ptr(), tr_g.data_ptr(), cap)
+        xw = torch.from_numpy(warm.copy()).cuda()
+        row0 = torch.zeros(WARM, dtype=torch.int32, device="cuda")
+        print("prefill: calibrating from the decode warm-up", flush=True)
+        ms.moe_spark_decode(ctx, xw.data_ptr(), WARM, row0.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        ms.moe_spark_calibrate(ctx, True)
+        ms.moe_spark_reset_stats(ctx)
+        xd = torch.from_numpy(X.copy()).cuda()
+        rd = torch.from_numpy(rows).cuda()
+        print("prefill: 2048 tokens through 40 layers", flush=True)
+        ms.moe_spark_prefill(ctx, xd.data_ptr(), T, rd.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        st = ms.moe_spark_get_stats(ctx)
+        ev = events(ctx)
+        pl = placement(ctx, w, R)
+        slot_bytes = ms.moe_spark_slot_bytes(ctx)
+        trx, trk = tr_x.cpu().numpy(), tr_k.cpu().numpy()
+        x_out = xd.cpu().numpy()
+    finally:
+        ms.moe_spark_destroy(ctx)
+    print(f"prefill stats {st}", flush=True)
+    assert st["fills"] > 0 and st["evictions"] > 0
+    sim = oracle.Sim(w.L, w.E, P, R, slot_bytes)
+    sim.place_uniform()
+    for t in range(WARM):
+        sim.decode_token(trk[t])
+    sim.calibrate(True)
+    sim.reset_stats()
+    for l in range(w.L):
+        sim.prefill_layer(l, trk[WARM:, l, :])
+    assert {k: st[k] for k in STAT_KEYS} == sim.stats()
+    assert ev == sim_events(sim)
+    for got, ref in zip(pl, sim.placement()):
+        assert np.array_equal(got, ref)
+    trx, trk = trx[WARM:], trk[WARM:]
+    rng = np.random.default_rng(11)
+    _check_topk_sample(model, trx, trk, rows, biases,
+                       np.concatenate([rng.choice(T // 2, 12, replace=False),
+                                       T // 2 + rng.choice(T // 2, 12, replace=False)]))
+    samples = [(0, 0), (1023, 10), (1024, 10), (2047, 39)] + \
+              [(int(t), int(l)) for t, l in zip(rng.integers(0, T, 6), rng.integers(0, w.L, 6))]
+    _check_layer_samples(model, trx, trk, x_out, rows, biases, samples, 2e-3, "prefill")
