@@ -49,42 +49,6 @@ __device__ __forceinline__ float q4_dot(const u32x4 c, const f32x4* uu) {
     return acc;
 }
 
-// (value, index) argmax across a wave64: the larger value wins, the lower
-// index on equal values.  That is a total order, so the result does not depend
-// on the reduction tree.  Within each 16-lane row the partner values move by
-// DPP (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
-// row_mirror); the four row results are then combined from scalar reads.
-// The result is wave-uniform.
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
-    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-    const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
-    if (ov > v || (ov == v && oi < i)) {
-        v = ov;
-        i = oi;
-    }
-}
-
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-    argmax_dpp_step<0xB1>(v, i);
-    argmax_dpp_step<0x4E>(v, i);
-    argmax_dpp_step<0x141>(v, i);
-    argmax_dpp_step<0x140>(v, i);
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-        if (rv > bv || (rv == bv && ri < bi)) {
-            bv = rv;
-            bi = ri;
-        }
-    }
-    v = bv;
-    i = bi;
-}
-
 // Exact top-K of lg[0..E) under (value desc, index asc), for a 256-thread
 // work-group (K <= kQ4MaxK).  Two ranking passes, all comparisons branch-free:
 //  1. wave w ranks each 64-expert chunk c = w, w+4, ... within the chunk and

@@ -167,6 +167,19 @@ struct Q4Args {
     uint64_t spin_limit_ticks;
 };
 
+// Token staging of the Q4_0 decode graph (q4_decode.hip).
+struct TokenIO {
+    float* x;                  // caller's [T][d] tokens
+    const int32_t* bias_row;   // caller's [T] router-bias rows or null
+    float* xbuf;               // [d] the current token
+    int32_t* tokrow;           // [1] its bias row
+    int32_t* cursors;          // [2] token cursor, trace cursor
+    int32_t* ntok;             // [1] tokens of this decode call
+    int64_t* stats;
+};
+hipError_t launch_token_begin(const TokenIO& io, int32_t n_tokens, hipStream_t s);
+hipError_t launch_token_end(const TokenIO& io, hipStream_t s);
+
 hipError_t launch_q4_router_partial(const Q4Args& a, hipStream_t s);
 hipError_t launch_q4_gateup(const Q4Args& a, hipStream_t s);
 hipError_t launch_q4_down(const Q4Args& a, hipStream_t s);

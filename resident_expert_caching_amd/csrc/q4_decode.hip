@@ -136,11 +136,13 @@ __device__ void run_policy(const Q4Args& a, const int* sel_e, const float* gk, c
         a.sel->slot[lane] = my_slot;
         a.sel->gate[lane] = myg;
         a.sel->wait[lane] = my_wait;
-        const int ttok = tok_value(a.trace_tok);
-        if (a.tr_topk && ttok < a.tr_cap) {
-            const int64_t o = ((int64_t)ttok * a.L + a.layer) * K + lane;
-            a.tr_topk[o] = myk;
-            a.tr_gates[o] = myg;
+        if (a.tr_topk) {
+            const int ttok = tok_value(a.trace_tok);
+            if (ttok < a.tr_cap) {
+                const int64_t o = ((int64_t)ttok * a.L + a.layer) * K + lane;
+                a.tr_topk[o] = myk;
+                a.tr_gates[o] = myg;
+            }
         }
         if (a.topk_out) {
             a.topk_out[(int64_t)tok * K + lane] = myk;
@@ -180,7 +182,6 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     __shared__ float s_l[kMaxK];
     __shared__ float s_g[kMaxK];
     __shared__ float s_z;
-    __shared__ float s_inv;
     __shared__ int s_slot;
     __shared__ unsigned long long s_wseq;
     __shared__ float red[32];
@@ -189,58 +190,63 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     __shared__ uint64_t r_stamp[kMaxR];
     __shared__ uint64_t r_seq[kMaxR];
 
-    // Independent loads first: this lane's activation block, the slot table
-    // row, the partial logits.
-    // x is read once per work-group, coalesced, and transposed through LDS:
-    // Q4_0 block b (32 floats) sits at float 36*b, so that the per-lane
-    // 16-byte reads of a block are free of bank conflicts.
-    {
-        const f32x4* x4 = reinterpret_cast<const f32x4*>(a.x_base + (int64_t)tok * kQD);
-        const f32x4 v0 = x4[t], v1 = x4[t + kThreads];
-        *reinterpret_cast<f32x4*>(&xt[36 * (t >> 3) + 4 * (t & 7)]) = v0;
-        *reinterpret_cast<f32x4*>(&xt[36 * ((t + kThreads) >> 3) + 4 * (t & 7)]) = v1;
+    // Every global load the routing needs is issued before the first LDS
+    // store or barrier, so their latencies overlap: x, the slot-table row,
+    // the partial sums of squares, the first 256 experts' partial logits
+    // (wave w sums partial rows w, w+4, ... for experts 4*lane..4*lane+3),
+    // and the bias row index, then the bias values that depend on it.
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(a.x_base + (int64_t)tok * kQD);
+    const f32x4 xv0 = x4[t], xv1 = x4[t + kThreads];
+    const int32_t sof0 = t < E ? a.pt.slot_of[(int64_t)a.layer * E + t] : -1;
+    const float ps0 = a.ps[lane], ps1 = a.ps[lane + 64];
+    f32x4 pv[kNP / 4];
+    if (4 * lane < E) {
+#pragma unroll
+        for (int j = 0; j < kNP / 4; ++j)
+            pv[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(w + 4 * j) * E + 4 * lane);
     }
-    for (int e = t; e < E; e += kThreads) sof[e] = a.pt.slot_of[(int64_t)a.layer * E + e];
-    // Router logits from the partials: wave w sums partial rows w, w+4, ...
-    // for experts 4*lane..4*lane+3 of each 256-expert chunk, all 32 loads of
-    // a chunk in flight at once; the 4 wave sums are added in LDS in wave order.
-    float ss = 0.0f;
-    if (w == 0) ss = a.ps[lane] + a.ps[lane + 64];
+    const float* brow = nullptr;
+    if (a.bias) {
+        int row = a.bias_row ? a.bias_row[tok] : 0;
+        row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
+        brow = a.bias + (int64_t)row * E;
+    }
+    const float b0 = (brow && t < E) ? brow[t] : 0.0f;
+
+    // x is transposed through LDS: Q4_0 block b (32 floats) sits at float
+    // 36*b, so the per-lane 16-byte reads of a block are free of bank conflicts.
+    *reinterpret_cast<f32x4*>(&xt[36 * (t >> 3) + 4 * (t & 7)]) = xv0;
+    *reinterpret_cast<f32x4*>(&xt[36 * ((t + kThreads) >> 3) + 4 * (t & 7)]) = xv1;
+    if (t < E) sof[t] = sof0;
+    for (int e = t + kThreads; e < E; e += kThreads) sof[e] = a.pt.slot_of[(int64_t)a.layer * E + e];
+    // 1 / rms, in every wave
+    const float ss = wave_sum(ps0 + ps1);
+    const float inv = a.norm ? 1.0f / sqrtf(ss / (float)kQD + a.eps) : 1.0f;
+    // logits = inv * (sum of the partials, 4 wave sums added in wave order) + bias
     for (int e0 = 0; e0 < E; e0 += kThreads) {
         const int e = e0 + 4 * lane;
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         if (e < E) {
-            f32x4 v[kNP / 4];
+            if (e0 > 0) {  // experts past the first 256
 #pragma unroll
-            for (int j = 0; j < kNP / 4; ++j)
-                v[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(w + 4 * j) * E + e);
+                for (int j = 0; j < kNP / 4; ++j)
+                    pv[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(w + 4 * j) * E + e);
+            }
 #pragma unroll
-            for (int j = 0; j < kNP / 4; ++j) acc += v[j];
+            for (int j = 0; j < kNP / 4; ++j) acc += pv[j];
         }
-        __syncthreads();  // the previous chunk's lg reads are done
+        __syncthreads();  // the previous chunk's red4 reads are done
         if (e < E) *reinterpret_cast<f32x4*>(&red4[w][4 * lane]) = acc;
         __syncthreads();
-        if (e0 + t < E) lg[e0 + t] = (red4[0][t] + red4[1][t]) + (red4[2][t] + red4[3][t]);
-    }
-    if (w == 0) {
-        ss = wave_sum(ss);
-        if (lane == 0) s_inv = a.norm ? 1.0f / sqrtf(ss / (float)kQD + a.eps) : 1.0f;
+        if (e0 + t < E) {
+            const float bias = e0 == 0 ? b0 : (brow ? brow[e0 + t] : 0.0f);
+            lg[e0 + t] = ((red4[0][t] + red4[1][t]) + (red4[2][t] + red4[3][t])) * inv + bias;
+        }
     }
     __syncthreads();
-    const float inv = s_inv;
     f32x4 xx[8];  // this lane's Q4_0 block of x
 #pragma unroll
     for (int j = 0; j < 8; ++j) xx[j] = *reinterpret_cast<const f32x4*>(&xt[36 * lane + 4 * j]);
-    {
-        const float* brow = nullptr;
-        if (a.bias) {
-            int row = a.bias_row ? a.bias_row[tok] : 0;
-            row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
-            brow = a.bias + (int64_t)row * E;
-        }
-        for (int e = t; e < E; e += kThreads) lg[e] = lg[e] * inv + (brow ? brow[e] : 0.0f);
-    }
-    __syncthreads();
 
     block_topk(lg, E, K, lg_pad, cand_v, cand_e, s_e, s_l);
     if (w == 0) {
@@ -253,11 +259,13 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
                 s_z = z;
             }
             if (lane < K) s_g[lane] = s_g[lane] / s_z;
-            const int ttok = tok_value(a.trace_tok);
-            if (a.tr_x && ttok < a.tr_cap) {
-                f32x4* t4 = reinterpret_cast<f32x4*>(a.tr_x + ((int64_t)ttok * a.L + a.layer) * kQD);
+            if (a.tr_x) {
+                const int ttok = tok_value(a.trace_tok);
+                if (ttok < a.tr_cap) {
+                    f32x4* t4 = reinterpret_cast<f32x4*>(a.tr_x + ((int64_t)ttok * a.L + a.layer) * kQD);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) t4[lane * 8 + j] = xx[j];
+                    for (int j = 0; j < 8; ++j) t4[lane * 8 + j] = xx[j];
+                }
             }
             run_policy(a, s_e, s_g, sof, tok, inv, r_owner, r_stamp, r_seq);
         }
@@ -460,6 +468,42 @@ __global__ void advance_kernel(int32_t* cursors, int64_t* stats) {
     }
 }
 
+// Decode stages the current token in a fixed buffer so that every kernel of
+// the token graph finds x (and the token's router-bias row) at a fixed
+// address, with no dependent load of the token cursor.
+// Before the first token of a decode call: cursor 0, token count, stage x[0].
+__global__ __launch_bounds__(kThreads) void token_begin_kernel(TokenIO io, int32_t n_tokens) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(io.x);
+    f32x4* dst = reinterpret_cast<f32x4*>(io.xbuf);
+    for (int i = threadIdx.x; i < kQD / 4; i += kThreads) dst[i] = src[i];
+    if (threadIdx.x == 0) {
+        io.cursors[0] = 0;
+        *io.ntok = n_tokens;
+        *io.tokrow = io.bias_row ? io.bias_row[0] : 0;
+    }
+}
+
+// Last node of a token graph: write the token's result back to x[t], stage
+// x[t+1] and its bias row, advance the cursors.
+__global__ __launch_bounds__(kThreads) void token_end_kernel(TokenIO io) {
+    const int t = io.cursors[0];
+    const int n = *io.ntok;
+    f32x4* xb = reinterpret_cast<f32x4*>(io.xbuf);
+    f32x4* xt = reinterpret_cast<f32x4*>(io.x + (int64_t)t * kQD);
+    const bool more = t + 1 < n;
+    for (int i = threadIdx.x; i < kQD / 4; i += kThreads) {
+        xt[i] = xb[i];
+        if (more) xb[i] = xt[i + kQD / 4];
+    }
+    if (threadIdx.x == 0 && more) *io.tokrow = io.bias_row ? io.bias_row[t + 1] : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        io.cursors[0] = t + 1;
+        io.cursors[1] += 1;
+        io.stats[DS_TOKENS] += 1;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_q4_router_partial(const Q4Args& a, hipStream_t s) {
@@ -477,6 +521,16 @@ hipError_t launch_q4_gateup(const Q4Args& a, hipStream_t s) {
 hipError_t launch_q4_down(const Q4Args& a, hipStream_t s) {
     if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE) return hipErrorInvalidValue;
     hipLaunchKernelGGL(q4_down_kernel, dim3(kNP), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_begin(const TokenIO& io, int32_t n_tokens, hipStream_t s) {
+    hipLaunchKernelGGL(token_begin_kernel, dim3(1), dim3(kThreads), 0, s, io, n_tokens);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_end(const TokenIO& io, hipStream_t s) {
+    hipLaunchKernelGGL(token_end_kernel, dim3(1), dim3(kThreads), 0, s, io);
     return hipGetLastError();
 }
 

@@ -87,6 +87,9 @@ struct moe_spark_ctx {
     float* d_pl = nullptr;          // [kNP][E] router partial logits (Q4_0)
     float* d_ps = nullptr;          // [kNP] partial sums of squares (Q4_0)
     uint32_t* d_pub = nullptr;      // [L] selection-published flags (Q4_0)
+    float* d_xbuf = nullptr;        // [d] token staged for the Q4_0 decode graph
+    int32_t* d_tokrow = nullptr;    // [1] its router-bias row
+    int32_t* d_ntok = nullptr;      // [1] tokens of the current decode call
 
     // batched prefill (allocated when max_tokens > 0)
     uint16_t* d_pu = nullptr;       // [Tmax][d] bf16
@@ -338,7 +341,7 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_xscratch, ctx->d_pl,     ctx->d_ps,     ctx->d_pub,     ctx->d_pu,
                      ctx->d_pinv,     ctx->d_plog,   ctx->d_ptopk,  ctx->d_pgate,   ctx->d_phist,
                      ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_ph,
-                     ctx->d_py,       ctx->d_pmeta};
+                     ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
@@ -524,19 +527,45 @@ void drop_graphs(moe_spark_ctx* ctx) {
     ctx->graphs.clear();
 }
 
+TokenIO token_io(const moe_spark_ctx* ctx, float* x, const int32_t* bias_row) {
+    TokenIO io;
+    io.x = x;
+    io.bias_row = bias_row;
+    io.xbuf = ctx->d_xbuf;
+    io.tokrow = ctx->d_tokrow;
+    io.cursors = ctx->d_cursors;
+    io.ntok = ctx->d_ntok;
+    io.stats = ctx->d_stats;
+    return io;
+}
+
+// Reset the token cursor for a decode call of n tokens (Q4_0: also stage the
+// first token).
+moe_spark_status begin_decode(moe_spark_ctx* ctx, float* x, const int32_t* bias_row, int32_t n) {
+    if (ctx->cfg.wfmt == MOE_SPARK_W_Q4_0) {
+        HIPCHK(launch_token_begin(token_io(ctx, x, bias_row), n, ctx->compute));
+    } else {
+        HIPCHK(hipMemsetAsync(ctx->d_cursors, 0, sizeof(int32_t), ctx->compute));
+    }
+    return MOE_SPARK_OK;
+}
+
 moe_spark_status launch_token_kernels(moe_spark_ctx* ctx, float* x, const int32_t* bias_row) {
     const int L = ctx->cfg.n_layers, wfmt = ctx->cfg.wfmt;
     const TokRef tok{ctx->d_cursors, 0}, ttok{ctx->d_cursors + 1, 0};
     if (wfmt == MOE_SPARK_W_Q4_0) {
-        HIPCHK(launch_q4_router_partial(q4_args(ctx, 0, x, x, tok, ttok, bias_row, 1, 1, 0, nullptr, nullptr, 0),
+        // the token sits in xbuf, its bias row in tokrow (fixed addresses)
+        float* xb = ctx->d_xbuf;
+        const TokRef t0{nullptr, 0};
+        HIPCHK(launch_q4_router_partial(q4_args(ctx, 0, xb, xb, t0, ttok, ctx->d_tokrow, 1, 1, 0, nullptr, nullptr, 0),
                                         ctx->compute));
         for (int l = 0; l < L; ++l) {
-            const Q4Args a = q4_args(ctx, l, x, x, tok, ttok, bias_row, 1, 1, l + 1 < L ? l + 1 : -1, nullptr,
+            const Q4Args a = q4_args(ctx, l, xb, xb, t0, ttok, ctx->d_tokrow, 1, 1, l + 1 < L ? l + 1 : -1, nullptr,
                                      nullptr, 0);
             HIPCHK(launch_q4_gateup(a, ctx->compute));
             HIPCHK(launch_q4_down(a, ctx->compute));
         }
-        HIPCHK(launch_advance(ctx->d_cursors, ctx->d_stats, ctx->compute));
+        HIPCHK(launch_token_end(token_io(ctx, x, bias_row), ctx->compute));
         return MOE_SPARK_OK;
     }
     for (int l = 0; l < L; ++l) {
@@ -674,6 +703,9 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= dalloc(&ctx->d_pl, (size_t)kNP * E) == hipSuccess;
     ok &= dalloc(&ctx->d_ps, (size_t)kNP) == hipSuccess;
     ok &= dalloc(&ctx->d_pub, (size_t)L) == hipSuccess;
+    ok &= dalloc(&ctx->d_xbuf, (size_t)d) == hipSuccess;
+    ok &= dalloc(&ctx->d_tokrow, 1) == hipSuccess;
+    ok &= dalloc(&ctx->d_ntok, 1) == hipSuccess;
     if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "device table allocation failed");
     if (c.max_tokens > 0) {
         const size_t T = (size_t)c.max_tokens, K = (size_t)c.top_k;
@@ -728,6 +760,9 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= hipMemset(ctx->d_pl, 0, sizeof(float) * kNP * E) == hipSuccess;
     ok &= hipMemset(ctx->d_ps, 0, sizeof(float) * kNP) == hipSuccess;
     ok &= hipMemset(ctx->d_pub, 0, sizeof(uint32_t) * L) == hipSuccess;
+    ok &= hipMemset(ctx->d_xbuf, 0, sizeof(float) * d) == hipSuccess;
+    ok &= hipMemset(ctx->d_tokrow, 0, sizeof(int32_t)) == hipSuccess;
+    ok &= hipMemset(ctx->d_ntok, 0, sizeof(int32_t)) == hipSuccess;
     for (auto& ev : ctx->tok_ev) ok &= hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess;
     ok &= hipDeviceSynchronize() == hipSuccess;
     if (!ok) return fail_create(MOE_SPARK_E_HIP, "table initialisation failed");
@@ -955,7 +990,8 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
     if (!x) return MOE_SPARK_OK;
     if (ctx->stream_decode) {
         if (n_tokens == 0) return MOE_SPARK_OK;
-        HIPCHK(hipMemsetAsync(ctx->d_cursors, 0, sizeof(int32_t), ctx->compute));
+        st = begin_decode(ctx, x, bias_row, n_tokens);
+        if (st != MOE_SPARK_OK) return st;
         for (int t = 0; t < n_tokens; ++t) {
             st = launch_token_kernels(ctx, x, bias_row);
             if (st != MOE_SPARK_OK) return st;
@@ -965,7 +1001,8 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
     hipGraphExec_t exec;
     st = get_graph(ctx, x, bias_row, &exec);  // n_tokens == 0 only prepares the graph
     if (st != MOE_SPARK_OK || n_tokens == 0) return st;
-    HIPCHK(hipMemsetAsync(ctx->d_cursors, 0, sizeof(int32_t), ctx->compute));
+    st = begin_decode(ctx, x, bias_row, n_tokens);
+    if (st != MOE_SPARK_OK) return st;
     for (int t = 0; t < n_tokens; ++t) {
         hipEvent_t& ev = ctx->tok_ev[ctx->tok_launched % kThrottle];
         if (ctx->tok_launched >= kThrottle) HIPCHK(hipEventSynchronize(ev));
