@@ -26,28 +26,61 @@ __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
 __device__ __forceinline__ int tok_value(const TokRef& t) { return t.base + (t.ptr ? *t.ptr : 0); }
 
-// Dot product of one Q4_0 block's 32 codes (16 bytes, GGUF nibble order:
-// weight j in the low nibble of byte j, weight j+16 in the high nibble) with
-// the block's activations u[0..31] held as 8 f32x4 (uu[j] = u[4j..4j+3]).
-__device__ __forceinline__ float q4_dot(const u32x4 c, const f32x4* uu) {
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// One Q4_0 block's 32 activations u[0..31] (uu[j] = u[4j..4j+3]) rounded to
+// fp16 and paired in the order q4_dot forms its nibble pairs: for word m of
+// the codes, a[4m] = (u[4m], u[4m+2]), a[4m+1] = (u[4m+1], u[4m+3]),
+// a[4m+2] = (u[16+4m], u[18+4m]), a[4m+3] = (u[17+4m], u[19+4m]).
+// Returns the fp32 sum of the rounded values, taken from the packed pairs
+// themselves: a second, unpacked rounding of u could be contracted with the
+// product that formed u and round some element differently.
+__device__ __forceinline__ float q4_pairs(const f32x4* uu, f16x2* a) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const f32x4 lo = uu[m], hi = uu[4 + m];
+        a[4 * m + 0] = f16x2{(_Float16)lo.x, (_Float16)lo.z};
+        a[4 * m + 1] = f16x2{(_Float16)lo.y, (_Float16)lo.w};
+        a[4 * m + 2] = f16x2{(_Float16)hi.x, (_Float16)hi.z};
+        a[4 * m + 3] = f16x2{(_Float16)hi.y, (_Float16)hi.w};
+    }
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float U = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) U = __builtin_amdgcn_fdot2(a[i], one, U, false);
+    return U;
+}
+
+// Sum over one Q4_0 block of (1024 + q_i) * a_i, for 32 codes (16 bytes,
+// GGUF nibble order: weight j in the low nibble of byte j, weight j+16 in
+// the high nibble) against the fp16 pairs of q4_pairs.  The nibbles of a
+// code word are masked into bytes, and a byte permute sets each code byte
+// under the byte 0x64: (0x64 << 8) | q is the fp16 1024 + q exactly, so two
+// codes two bytes apart form one fp16 pair, consumed by one fp16 dot product
+// with fp32 accumulation.  The caller subtracts (1024 + 8) * U to obtain
+// sum_i (q_i - 8) a_i.
+__device__ __forceinline__ float q4_dot(const u32x4 c, const f16x2* a) {
     const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+    constexpr uint32_t kHi = 0x64646464u;
+    // v_perm_b32 selectors over {kHi : nibble bytes}: 0-3 pick a nibble byte, 4 a 0x64
+    constexpr uint32_t kEven = 0x04020400u, kOdd = 0x04030401u;
     float acc = 0.0f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const uint32_t lo = wd[m] & 0x0F0F0F0Fu;
-        const uint32_t hi = (wd[m] >> 4) & 0x0F0F0F0Fu;
-        const f32x4 ul = uu[m], uh = uu[4 + m];
-        acc += (float)(lo & 0xffu) * ul.x;
-        acc += (float)((lo >> 8) & 0xffu) * ul.y;
-        acc += (float)((lo >> 16) & 0xffu) * ul.z;
-        acc += (float)(lo >> 24) * ul.w;
-        acc += (float)(hi & 0xffu) * uh.x;
-        acc += (float)((hi >> 8) & 0xffu) * uh.y;
-        acc += (float)((hi >> 16) & 0xffu) * uh.z;
-        acc += (float)(hi >> 24) * uh.w;
+        const uint32_t lo = wd[m] & 0x0F0F0F0Fu, hi = (wd[m] >> 4) & 0x0F0F0F0Fu;
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, lo, kEven)),
+                                     a[4 * m + 0], acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, lo, kOdd)),
+                                     a[4 * m + 1], acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, hi, kEven)),
+                                     a[4 * m + 2], acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, hi, kOdd)),
+                                     a[4 * m + 3], acc, false);
     }
     return acc;
 }
+
+constexpr float kQ4Offset = 1032.0f;  // 1024 from the fp16 encoding + the Q4_0 zero point 8
 
 // Exact top-K of lg[0..E) under (value desc, index asc), for a 256-thread
 // work-group (K <= kQ4MaxK).  Two ranking passes, all comparisons branch-free:
@@ -113,13 +146,6 @@ __device__ inline void block_topk(const float* lg, int E, int K, float* lg_pad, 
         }
     }
     __syncthreads();
-}
-
-__device__ __forceinline__ float block_sum(const f32x4* uu) {
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s += (uu[j].x + uu[j].y) + (uu[j].z + uu[j].w);
-    return s;
 }
 
 }  // namespace moe

@@ -328,14 +328,15 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     f32x4 uu[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) uu[j] = xx[j] * inv;
-    const float U8 = 8.0f * block_sum(uu);
+    f16x2 ua[16];
+    const float UO = kQ4Offset * q4_pairs(uu, ua);
 
     const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float s = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
-        v[i] = s * (q4_dot(c[i], uu) - U8);
+        v[i] = s * (q4_dot(c[i], ua) - UO);
     }
     // 8 rows x 64 lanes -> one row per group of 8 lanes (fixed tree)
     {
@@ -411,12 +412,13 @@ __global__ __launch_bounds__(kThreads) void q4_down_kernel(Q4Args a) {
         const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
 #pragma unroll
         for (int j = 0; j < 8; ++j) hh[j] = h4[(kq * 8 + j) * 16 + b];
-        const float H8 = 8.0f * block_sum(hh);
+        f16x2 ha[16];
+        const float HO = kQ4Offset * q4_pairs(hh, ha);
         const uint32_t sw[4] = {s0.x, s0.y, s1.x, s1.y};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float s = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
-            z[i] = s * (q4_dot(c[i], hh) - H8);
+            z[i] = s * (q4_dot(c[i], ha) - HO);
         }
     }
     // 8 rows x 16 lanes -> one row per pair of lanes (fixed tree)
