@@ -82,67 +82,70 @@ __device__ __forceinline__ float q4_dot(const u32x4 c, const f16x2* a) {
 
 constexpr float kQ4Offset = 1032.0f;  // 1024 from the fp16 encoding + the Q4_0 zero point 8
 
+// Total-order key of (logit v, expert e) for the top-K: larger key = larger
+// value, or equal value and smaller index.  High word: the float's bits made
+// monotone as an unsigned integer (-0 is first folded into +0, so the two
+// compare equal); low word: ~e.  Every real expert's key is above 0, the key
+// of padding entries.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
+
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+    const uint32_t o = (uint32_t)(key >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 // Exact top-K of lg[0..E) under (value desc, index asc), for a 256-thread
-// work-group (K <= kQ4MaxK).  Two ranking passes, all comparisons branch-free:
+// work-group (K <= kQ4MaxK).  Keys are unique, so an entry's rank is the
+// number of keys above it.  Two ranking passes:
 //  1. wave w ranks each 64-expert chunk c = w, w+4, ... within the chunk and
-//     keeps the chunk's first K as candidates (padding lanes past E hold -inf
-//     with an index >= E, so they rank below every real expert);
+//     keeps the chunk's first K as candidates (lanes past E hold key 0);
 //  2. every candidate is ranked among the candidates.
 // The global top K are all candidates, and a candidate's rank among the
-// candidates equals its global rank whenever that is below K.  Result:
-// s_e[r], s_l[r] for r < K.  LDS scratch: lg_pad[256],
-// cand_v/cand_e[kMaxE/64*kQ4MaxK + 4] (16-byte aligned).  Contains barriers:
-// every thread of the work-group must call it.
-__device__ inline void block_topk(const float* lg, int E, int K, float* lg_pad, float* cand_v, int32_t* cand_e,
-                                  int* s_e, float* s_l) {
+// candidates equals its global rank whenever that is below K.  A NaN logit
+// ranks above every number.  Result: s_e[r], s_l[r] for r < K.  LDS scratch:
+// kpad[256] and cand[kMaxE/64*kQ4MaxK + 2] (16-byte aligned).  Contains
+// barriers: every thread of the work-group must call it.
+__device__ inline void block_topk(const float* lg, int E, int K, uint64_t* kpad, uint64_t* cand, int* s_e,
+                                  float* s_l) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    if (t < K) {  // defined even if NaN logits leave a rank unfilled
+    if (t < K) {  // defined even when fewer than K experts exist
         s_e[t] = 0;
         s_l[t] = -INFINITY;
     }
     const int n_chunks = (E + 63) >> 6;
     for (int c = w; c < n_chunks; c += 4) {
         const int e = c * 64 + lane;
-        const float v = e < E ? lg[e] : -INFINITY;
-        lg_pad[lane + 64 * w] = v;
+        const uint64_t key = e < E ? topk_key(lg[e], e) : 0ull;
+        kpad[lane + 64 * w] = key;
+        if (lane < K) cand[c * K + lane] = 0ull;  // a chunk may hold fewer than K experts
         __builtin_amdgcn_wave_barrier();
         int r = 0;
-#pragma unroll 4
-        for (int j = 0; j < 64; j += 4) {
-            const f32x4 q = *reinterpret_cast<const f32x4*>(&lg_pad[64 * w + j]);
-            r += (int)(q.x > v) + (int)((q.x == v) & (j < lane));
-            r += (int)(q.y > v) + (int)((q.y == v) & (j + 1 < lane));
-            r += (int)(q.z > v) + (int)((q.z == v) & (j + 2 < lane));
-            r += (int)(q.w > v) + (int)((q.w == v) & (j + 3 < lane));
+#pragma unroll 8
+        for (int j = 0; j < 64; j += 2) {
+            const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(&kpad[64 * w + j]);
+            r += (int)(q.x > key) + (int)(q.y > key);
         }
-        if (r < K) {
-            cand_v[c * K + r] = v;
-            cand_e[c * K + r] = e;
-        }
+        if (r < K && e < E) cand[c * K + r] = key;
         __builtin_amdgcn_wave_barrier();
     }
-    if (t < 4) {  // padding past the candidates: -inf with an index no expert has
-        cand_v[n_chunks * K + t] = -INFINITY;
-        cand_e[n_chunks * K + t] = 0x7fffffff;
-    }
+    if (t < 2) cand[n_chunks * K + t] = 0ull;  // padding past the candidates
     __syncthreads();
     const int nc = n_chunks * K;
     for (int i = t; i < nc; i += 256) {
-        const float v = cand_v[i];
-        const int e = cand_e[i];
+        const uint64_t key = cand[i];
         int r = 0;
-#pragma unroll 2
-        for (int j = 0; j < nc; j += 4) {  // entries past nc are padding that ranks last
-            const f32x4 q = *reinterpret_cast<const f32x4*>(&cand_v[j]);
-            const int4 qe = *reinterpret_cast<const int4*>(&cand_e[j]);
-            r += (int)(q.x > v) + (int)((q.x == v) & (qe.x < e));
-            r += (int)(q.y > v) + (int)((q.y == v) & (qe.y < e));
-            r += (int)(q.z > v) + (int)((q.z == v) & (qe.z < e));
-            r += (int)(q.w > v) + (int)((q.w == v) & (qe.w < e));
+#pragma unroll 4
+        for (int j = 0; j < nc; j += 2) {  // an entry past nc is padding that ranks last
+            const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(&cand[j]);
+            r += (int)(q.x > key) + (int)(q.y > key);
         }
-        if (r < K && e >= 0 && e < E) {
-            s_e[r] = e;
-            s_l[r] = v;
+        if (r < K && key != 0ull) {
+            s_e[r] = (int)~(uint32_t)key;
+            s_l[r] = topk_key_value(key);
         }
     }
     __syncthreads();

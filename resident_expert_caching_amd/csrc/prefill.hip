@@ -183,14 +183,13 @@ __global__ __launch_bounds__(kPfThreads) void pf_topk_kernel(PfArgs a) {
     const int t = blockIdx.x, tid = threadIdx.x;
     const int E = a.E, K = a.K;
     __shared__ __align__(16) float lg[kMaxE];
-    __shared__ __align__(16) float lg_pad[kPfThreads];
-    __shared__ __align__(16) float cand_v[kMaxE / 64 * kQ4MaxK + 4];
-    __shared__ __align__(16) int32_t cand_e[kMaxE / 64 * kQ4MaxK + 4];
+    __shared__ __align__(16) uint64_t kpad[kPfThreads];
+    __shared__ __align__(16) uint64_t cand[kMaxE / 64 * kQ4MaxK + 2];
     __shared__ int s_e[kMaxK];
     __shared__ float s_l[kMaxK];
     for (int e = tid; e < E; e += kPfThreads) lg[e] = a.logits[(int64_t)t * E + e];
     __syncthreads();
-    block_topk(lg, E, K, lg_pad, cand_v, cand_e, s_e, s_l);
+    block_topk(lg, E, K, kpad, cand, s_e, s_l);
     if (tid < K) {
         const int e = s_e[tid];
         float z = 0.0f;

@@ -175,9 +175,8 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     __shared__ __align__(16) float lg[kMaxE];
     __shared__ int32_t sof[kMaxE];
     __shared__ __align__(16) float xt[kQD / 32 * 36];
-    __shared__ __align__(16) float lg_pad[kThreads];
-    __shared__ __align__(16) float cand_v[kMaxE / 64 * kQ4MaxK + 4];
-    __shared__ __align__(16) int32_t cand_e[kMaxE / 64 * kQ4MaxK + 4];
+    __shared__ __align__(16) uint64_t kpad[kThreads];
+    __shared__ __align__(16) uint64_t cand[kMaxE / 64 * kQ4MaxK + 2];
     __shared__ int s_e[kMaxK];
     __shared__ float s_l[kMaxK];
     __shared__ float s_g[kMaxK];
@@ -248,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) xx[j] = *reinterpret_cast<const f32x4*>(&xt[36 * lane + 4 * j]);
 
-    block_topk(lg, E, K, lg_pad, cand_v, cand_e, s_e, s_l);
+    block_topk(lg, E, K, kpad, cand, s_e, s_l);
     if (w == 0) {
         if (g == 0 && k == 0 && !a.replay) {
             // gates: softmax over the chosen logits, shifted by the largest
