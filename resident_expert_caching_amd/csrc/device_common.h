@@ -107,7 +107,7 @@ __device__ __forceinline__ float topk_key_value(uint64_t key) {
 // The global top K are all candidates, and a candidate's rank among the
 // candidates equals its global rank whenever that is below K.  A NaN logit
 // ranks above every number.  Result: s_e[r], s_l[r] for r < K.  LDS scratch:
-// kpad[256] and cand[kMaxE/64*kQ4MaxK + 2] (16-byte aligned).  Contains
+// kpad[256] and cand[kMaxE/64*kQ4MaxK + 16] (16-byte aligned).  Contains
 // barriers: every thread of the work-group must call it.
 __device__ inline void block_topk(const float* lg, int E, int K, uint64_t* kpad, uint64_t* cand, int* s_e,
                                   float* s_l) {
@@ -132,18 +132,25 @@ __device__ inline void block_topk(const float* lg, int E, int K, uint64_t* kpad,
         if (r < K && e < E) cand[c * K + r] = key;
         __builtin_amdgcn_wave_barrier();
     }
-    if (t < 2) cand[n_chunks * K + t] = 0ull;  // padding past the candidates
-    __syncthreads();
     const int nc = n_chunks * K;
-    for (int i = t; i < nc; i += 256) {
-        const uint64_t key = cand[i];
+    const int part = ((nc + 15) & ~15) >> 3;  // candidates each of 8 threads compares against (even)
+    if (t < 8 * part - nc) cand[nc + t] = 0ull;  // padding past the candidates ranks last
+    __syncthreads();
+    // 8 threads per candidate, each counting the keys above it in one eighth
+    // of the candidates; the counts meet in lanes 8c..8c+7 of one wave
+    const int sub = t & 7;
+    for (int base = 0; base < nc; base += 32) {
+        const int i = base + (t >> 3);
+        const uint64_t key = i < nc ? cand[i] : 0ull;
         int r = 0;
-#pragma unroll 4
-        for (int j = 0; j < nc; j += 2) {  // an entry past nc is padding that ranks last
+        for (int j = sub * part; j < (sub + 1) * part; j += 2) {
             const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(&cand[j]);
             r += (int)(q.x > key) + (int)(q.y > key);
         }
-        if (r < K && key != 0ull) {
+        r += __shfl_xor(r, 1, 64);
+        r += __shfl_xor(r, 2, 64);
+        r += __shfl_xor(r, 4, 64);
+        if (sub == 0 && r < K && key != 0ull) {
             s_e[r] = (int)~(uint32_t)key;
             s_l[r] = topk_key_value(key);
         }

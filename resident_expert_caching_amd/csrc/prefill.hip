@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_topk_kernel(PfArgs a) {
     const int E = a.E, K = a.K;
     __shared__ __align__(16) float lg[kMaxE];
     __shared__ __align__(16) uint64_t kpad[kPfThreads];
-    __shared__ __align__(16) uint64_t cand[kMaxE / 64 * kQ4MaxK + 2];
+    __shared__ __align__(16) uint64_t cand[kMaxE / 64 * kQ4MaxK + 16];
     __shared__ int s_e[kMaxK];
     __shared__ float s_l[kMaxK];
     for (int e = tid; e < E; e += kPfThreads) lg[e] = a.logits[(int64_t)t * E + e];

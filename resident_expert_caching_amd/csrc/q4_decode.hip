@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     __shared__ int32_t sof[kMaxE];
     __shared__ __align__(16) float xt[kQD / 32 * 36];
     __shared__ __align__(16) uint64_t kpad[kThreads];
-    __shared__ __align__(16) uint64_t cand[kMaxE / 64 * kQ4MaxK + 2];
+    __shared__ __align__(16) uint64_t cand[kMaxE / 64 * kQ4MaxK + 16];
     __shared__ int s_e[kMaxK];
     __shared__ float s_l[kMaxK];
     __shared__ float s_g[kMaxK];
@@ -396,7 +396,17 @@ __global__ __launch_bounds__(kThreads) void q4_down_kernel(Q4Args a) {
     float z[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) z[i] = 0.0f;
+    // loads that do not depend on the slot go out together with the slot
     const int slot = act ? a.sel->slot[kq] : 0;
+    f32x4 hh[8];
+    if (act) {
+        const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hh[j] = h4[(kq * 8 + j) * 16 + b];
+    }
+    float gk[kQ4MaxK];  // the combine's gates, in rank order
+#pragma unroll
+    for (int kk = 0; kk < kQ4MaxK; ++kk) gk[kk] = (t < kRW && kk < K) ? a.sel->gate[kk] : 0.0f;
     if (act && (slot < 0 || slot >= a.n_slots)) {
         if (b == 0 && half == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
     } else if (act) {
@@ -407,10 +417,6 @@ __global__ __launch_bounds__(kThreads) void q4_down_kernel(Q4Args a) {
             c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + i) * 256) + b);
         const u32x2 s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + b);
         const u32x2 s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + ((r0 >> 2) + 1) * 16 + b);
-        f32x4 hh[8];
-        const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hh[j] = h4[(kq * 8 + j) * 16 + b];
         f16x2 ha[16];
         const float HO = kQ4Offset * q4_pairs(hh, ha);
         const uint32_t sw[4] = {s0.x, s0.y, s1.x, s1.y};
@@ -449,7 +455,9 @@ __global__ __launch_bounds__(kThreads) void q4_down_kernel(Q4Args a) {
     __syncthreads();
     if (t < kRW) {
         float y = 0.0f;
-        for (int kk = 0; kk < K; ++kk) y += a.sel->gate[kk] * zs[kk][t];  // rank order
+#pragma unroll
+        for (int kk = 0; kk < kQ4MaxK; ++kk)
+            if (kk < K) y += gk[kk] * zs[kk][t];  // rank order
         const float o = a.residual ? xr + y : y;
         a.y_base[(int64_t)tok * kQD + p * kRW + t] = o;
         xn[t] = o;
