@@ -279,7 +279,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "q4_0*f16->f32",  # Q4_0 codes times fp16 activations, fp32 accumulation; router and norms fp32
         "data": "synthetic",
         "config": {
             "workload": f"{w.L}-layer Q4_0 MoE stack decode, batch 1: d=2048, 256 experts, top-8, "
