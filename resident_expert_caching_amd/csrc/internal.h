@@ -28,6 +28,10 @@ constexpr int64_t kQ4SlotBytes = kGURegion + kDownCodes + kDownScales;  // 1,769
 constexpr int kDownRowsPerWG = 8;
 // Router partial logits: a work-group owns kRW consecutive rows of x and
 // writes the router dot products restricted to those rows for every expert.
+// Streams the fill agent spreads ring fills over (the caller's copy stream and
+// kCopyStreams - 1 of the context's own).
+constexpr int kCopyStreams = 2;
+
 constexpr int kRW = 16;
 constexpr int kNP = kQD / kRW;   // 128 partial rows
 

@@ -59,6 +59,9 @@ struct moe_spark_ctx {
     int64_t n_experts_total = 0;
     hipStream_t compute = nullptr, copy = nullptr;
     bool own_compute = false, own_copy = false;
+    // fills of ring slot r go to copy_streams[r % kCopyStreams]: copies into one
+    // slot stay ordered, copies into different slots use several DMA engines
+    hipStream_t copy_x[kCopyStreams - 1] = {};
 
     uint8_t* d_slots = nullptr;
     uint8_t* h_arena = nullptr;
@@ -215,12 +218,28 @@ int64_t quota(int L, int64_t P, int l) { return P / L + ((int64_t)l < P % L ? 1 
 
 // ---------------------------------------------------------------- fill agent
 
+hipStream_t fill_stream(const moe_spark_ctx* ctx, int ring) {
+    const int i = ring % kCopyStreams;
+    return i == 0 ? ctx->copy : ctx->copy_x[i - 1];
+}
+
+hipError_t sync_copies(const moe_spark_ctx* ctx) {
+    hipError_t e = ctx->copy ? hipStreamSynchronize(ctx->copy) : hipSuccess;
+    for (hipStream_t st : ctx->copy_x)
+        if (st) {
+            const hipError_t f = hipStreamSynchronize(st);
+            if (e == hipSuccess) e = f;
+        }
+    return e;
+}
+
 void agent_loop(moe_spark_ctx* ctx) {
     hipSetDevice(ctx->device);
     struct Pending {
         uint64_t seq;
         int ring;
         hipEvent_t ev;
+        hipStream_t stream;
         int64_t t0;
     };
     std::deque<Pending> pend;
@@ -244,10 +263,11 @@ void agent_loop(moe_spark_ctx* ctx) {
                 pool.pop_back();
             }
             bool ok = key >= 0 && key < ctx->n_experts_total && ring >= 0 && ring < ctx->cfg.ring_slots;
+            const hipStream_t st = ok ? fill_stream(ctx, ring) : ctx->copy;
             if (ok)
                 ok = hipMemcpyAsync(ctx->d_slots + (P + ring) * SB, ctx->h_arena + (int64_t)key * SB, SB,
-                                    hipMemcpyHostToDevice, ctx->copy) == hipSuccess;
-            if (ok && ev) ok = hipEventRecord(ev, ctx->copy) == hipSuccess;
+                                    hipMemcpyHostToDevice, st) == hipSuccess;
+            if (ok && ev) ok = hipEventRecord(ev, st) == hipSuccess;
             if (!ok) {
                 ctx->agent_error.store(1);
                 if (ev) pool.push_back(ev);
@@ -255,24 +275,28 @@ void agent_loop(moe_spark_ctx* ctx) {
                 __atomic_store_n(ctx->h_ready + (ring >= 0 && ring < ctx->cfg.ring_slots ? ring : 0), next,
                                  __ATOMIC_RELEASE);
             } else {
-                pend.push_back({next, ring, ev, t0});
+                pend.push_back({next, ring, ev, st, t0});
             }
             ++next;
             did = true;
         }
-        while (!pend.empty()) {
-            Pending& p = pend.front();
-            const hipError_t q = p.ev ? hipEventQuery(p.ev) : hipStreamQuery(ctx->copy);
-            if (q == hipErrorNotReady) break;
+        // Publish every finished copy.  Copies into one ring slot share a
+        // stream, so a later fill of a slot never finishes before an earlier one.
+        for (auto it = pend.begin(); it != pend.end();) {
+            const hipError_t q = it->ev ? hipEventQuery(it->ev) : hipStreamQuery(it->stream);
+            if (q == hipErrorNotReady) {
+                ++it;
+                continue;
+            }
             if (q != hipSuccess) ctx->agent_error.store(1);
-            __atomic_store_n(ctx->h_ready + p.ring, p.seq, __ATOMIC_RELEASE);
-            const int64_t dt = now_ns() - p.t0;
+            __atomic_store_n(ctx->h_ready + it->ring, it->seq, __ATOMIC_RELEASE);
+            const int64_t dt = now_ns() - it->t0;
             ctx->fill_ns_sum.fetch_add(dt);
             int64_t m = ctx->fill_ns_max.load();
             while (dt > m && !ctx->fill_ns_max.compare_exchange_weak(m, dt)) {
             }
-            if (p.ev) pool.push_back(p.ev);
-            pend.pop_front();
+            if (it->ev) pool.push_back(it->ev);
+            it = pend.erase(it);
             did = true;
         }
         if (did) {
@@ -351,6 +375,8 @@ void free_all(moe_spark_ctx* ctx) {
     if (ctx->h_phist) hipHostFree(ctx->h_phist);
     if (ctx->own_compute && ctx->compute) hipStreamDestroy(ctx->compute);
     if (ctx->own_copy && ctx->copy) hipStreamDestroy(ctx->copy);
+    for (hipStream_t st : ctx->copy_x)
+        if (st) hipStreamDestroy(st);
 }
 
 template <typename T>
@@ -514,7 +540,7 @@ moe_spark_status upload_pinned(moe_spark_ctx* ctx, std::vector<std::pair<int32_t
                               ctx->copy));
         i = j;
     }
-    HIPCHK(hipStreamSynchronize(ctx->copy));
+    HIPCHK(sync_copies(ctx));
     return MOE_SPARK_OK;
 }
 
@@ -669,6 +695,9 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
             return fail_create(MOE_SPARK_E_HIP, "hipStreamCreate failed");
         ctx->own_copy = true;
     }
+    for (hipStream_t& st : ctx->copy_x)
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
+            return fail_create(MOE_SPARK_E_HIP, "hipStreamCreate failed");
     if (hipMalloc((void**)&ctx->d_slots, (size_t)std::max<int64_t>(ctx->n_slots, 1) * ctx->slot_bytes) != hipSuccess) {
         ctx->d_slots = nullptr;
         return fail_create(MOE_SPARK_E_NOMEM, "slot arena allocation failed");
@@ -774,7 +803,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
 void moe_spark_destroy(moe_spark_ctx* ctx) {
     if (!ctx) return;
     if (ctx->compute) hipStreamSynchronize(ctx->compute);
-    if (ctx->copy) hipStreamSynchronize(ctx->copy);
+    sync_copies(ctx);
     free_all(ctx);
     delete ctx;
 }
@@ -899,7 +928,7 @@ moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts) {
     const auto& c = ctx->cfg;
     const int L = c.n_layers, E = c.n_experts, R = c.ring_slots;
     HIPCHK(hipStreamSynchronize(ctx->compute));
-    HIPCHK(hipStreamSynchronize(ctx->copy));
+    HIPCHK(sync_copies(ctx));
     std::vector<int64_t> counts((size_t)L * E);
     std::vector<int32_t> owner(std::max(R, 1));
     std::vector<uint64_t> stamp(std::max(R, 1));
@@ -1214,7 +1243,7 @@ moe_spark_status moe_spark_get_events(moe_spark_ctx* ctx, moe_spark_event* out, 
 moe_spark_status moe_spark_synchronize(moe_spark_ctx* ctx) {
     if (!ctx) return MOE_SPARK_E_INVALID;
     HIPCHK(hipStreamSynchronize(ctx->compute));
-    HIPCHK(hipStreamSynchronize(ctx->copy));
+    HIPCHK(sync_copies(ctx));
     int32_t e = 0;
     HIPCHK(hipMemcpy(&e, ctx->d_error, sizeof e, hipMemcpyDeviceToHost));
     if (e & ERR_FILL_TIMEOUT) return ctx->fail(MOE_SPARK_E_HIP, "a cold-expert fill did not arrive in time");
