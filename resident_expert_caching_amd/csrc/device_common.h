@@ -98,39 +98,40 @@ __device__ __forceinline__ float topk_key_value(uint64_t key) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// Exact top-K of lg[0..E) under (value desc, index asc), for a 256-thread
-// work-group (K <= kQ4MaxK).  Keys are unique, so an entry's rank is the
-// number of keys above it.  Two ranking passes:
-//  1. wave w ranks each 64-expert chunk c = w, w+4, ... within the chunk and
-//     keeps the chunk's first K as candidates (lanes past E hold key 0);
-//  2. every candidate is ranked among the candidates.
+// Exact top-K under (value desc, index asc), in two ranking passes over
+// unique keys (an entry's rank is the number of keys above it):
+//  1. topk_rank_chunk: a wave ranks one chunk of 64 keys among themselves and
+//     keeps the chunk's first K as candidates cand[c*K .. c*K+K);
+//  2. topk_merge: every candidate is ranked among the candidates.
 // The global top K are all candidates, and a candidate's rank among the
 // candidates equals its global rank whenever that is below K.  A NaN logit
-// ranks above every number.  Result: s_e[r], s_l[r] for r < K.  LDS scratch:
-// kpad[256] and cand[kMaxE/64*kQ4MaxK + 16] (16-byte aligned).  Contains
-// barriers: every thread of the work-group must call it.
-__device__ inline void block_topk(const float* lg, int E, int K, uint64_t* kpad, uint64_t* cand, int* s_e,
-                                  float* s_l) {
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    if (t < K) {  // defined even when fewer than K experts exist
+// ranks above every number.  Keys of entries past E are 0 and never chosen.
+// LDS scratch: kpad[256] (64 per wave), cand[kMaxE/64*kQ4MaxK + 16]
+// (16-byte aligned).
+
+// Wave-wide: this lane's key (0 for no entry) in chunk c of wave w.
+__device__ __forceinline__ void topk_rank_chunk(uint64_t key, int c, int K, uint64_t* kpad, uint64_t* cand) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    kpad[lane + 64 * w] = key;
+    if (lane < K) cand[c * K + lane] = 0ull;  // a chunk may hold fewer than K entries
+    __builtin_amdgcn_wave_barrier();
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < 64; j += 2) {
+        const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(&kpad[64 * w + j]);
+        r += (int)(q.x > key) + (int)(q.y > key);
+    }
+    if (r < K && key != 0ull) cand[c * K + r] = key;
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Work-group-wide (256 threads, barriers inside): rank the n_chunks*K
+// candidates; result s_e[r], s_l[r] for r < K.
+__device__ inline void topk_merge(int n_chunks, int K, uint64_t* cand, int* s_e, float* s_l) {
+    const int t = threadIdx.x;
+    if (t < K) {  // defined even when fewer than K entries exist
         s_e[t] = 0;
         s_l[t] = -INFINITY;
-    }
-    const int n_chunks = (E + 63) >> 6;
-    for (int c = w; c < n_chunks; c += 4) {
-        const int e = c * 64 + lane;
-        const uint64_t key = e < E ? topk_key(lg[e], e) : 0ull;
-        kpad[lane + 64 * w] = key;
-        if (lane < K) cand[c * K + lane] = 0ull;  // a chunk may hold fewer than K experts
-        __builtin_amdgcn_wave_barrier();
-        int r = 0;
-#pragma unroll 8
-        for (int j = 0; j < 64; j += 2) {
-            const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(&kpad[64 * w + j]);
-            r += (int)(q.x > key) + (int)(q.y > key);
-        }
-        if (r < K && e < E) cand[c * K + r] = key;
-        __builtin_amdgcn_wave_barrier();
     }
     const int nc = n_chunks * K;
     const int part = ((nc + 15) & ~15) >> 3;  // candidates each of 8 threads compares against (even)
@@ -156,6 +157,19 @@ __device__ inline void block_topk(const float* lg, int E, int K, uint64_t* kpad,
         }
     }
     __syncthreads();
+}
+
+// Top-K of lg[0..E) held in LDS, for a 256-thread work-group: wave w ranks
+// the 64-expert chunks w, w+4, ...  Every thread must call it.
+__device__ inline void block_topk(const float* lg, int E, int K, uint64_t* kpad, uint64_t* cand, int* s_e,
+                                  float* s_l) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n_chunks = (E + 63) >> 6;
+    for (int c = w; c < n_chunks; c += 4) {
+        const int e = c * 64 + lane;
+        topk_rank_chunk(e < E ? topk_key(lg[e], e) : 0ull, c, K, kpad, cand);
+    }
+    topk_merge(n_chunks, K, cand, s_e, s_l);
 }
 
 }  // namespace moe

@@ -172,7 +172,6 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     const int E = a.E, K = a.K;
     const int tok = tok_value(a.tok);
 
-    __shared__ __align__(16) float lg[kMaxE];
     __shared__ int32_t sof[kMaxE];
     __shared__ __align__(16) float xt[kQD / 32 * 36];
     __shared__ __align__(16) uint64_t kpad[kThreads];
@@ -184,25 +183,28 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     __shared__ int s_slot;
     __shared__ unsigned long long s_wseq;
     __shared__ float red[32];
-    __shared__ __align__(16) float red4[4][kThreads];
     __shared__ int32_t r_owner[kMaxR];
     __shared__ uint64_t r_stamp[kMaxR];
     __shared__ uint64_t r_seq[kMaxR];
 
     // Every global load the routing needs is issued before the first LDS
-    // store or barrier, so their latencies overlap: x, the slot-table row,
-    // the partial sums of squares, the first 256 experts' partial logits
-    // (wave w sums partial rows w, w+4, ... for experts 4*lane..4*lane+3),
-    // and the bias row index, then the bias values that depend on it.
+    // store, so their latencies overlap: x, the slot-table row, the partial
+    // sums of squares, the partial logits of this wave's first 64-expert
+    // chunk, and the bias row index, then the bias values that depend on it.
+    // Wave w owns chunk w (and w+4, ... past 256 experts): lane l sums the
+    // partial rows l/16, l/16 + 4, ... of experts 64c + 4(l%16) .. +3, the
+    // four row groups meet in a butterfly, and the lane keeps the logit of
+    // expert 64c + 4(l%16) + l/16.
     const f32x4* x4 = reinterpret_cast<const f32x4*>(a.x_base + (int64_t)tok * kQD);
     const f32x4 xv0 = x4[t], xv1 = x4[t + kThreads];
     const int32_t sof0 = t < E ? a.pt.slot_of[(int64_t)a.layer * E + t] : -1;
     const float ps0 = a.ps[lane], ps1 = a.ps[lane + 64];
+    const int e4 = 64 * w + 4 * (lane & 15), rg = lane >> 4;
     f32x4 pv[kNP / 4];
-    if (4 * lane < E) {
+    if (e4 < E) {
 #pragma unroll
         for (int j = 0; j < kNP / 4; ++j)
-            pv[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(w + 4 * j) * E + 4 * lane);
+            pv[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(rg + 4 * j) * E + e4);
     }
     const float* brow = nullptr;
     if (a.bias) {
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
         row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
         brow = a.bias + (int64_t)row * E;
     }
-    const float b0 = (brow && t < E) ? brow[t] : 0.0f;
+    const float b0 = (brow && e4 + rg < E) ? brow[e4 + rg] : 0.0f;
 
     // x is transposed through LDS: Q4_0 block b (32 floats) sits at float
     // 36*b, so the per-lane 16-byte reads of a block are free of bank conflicts.
@@ -221,33 +223,37 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     // 1 / rms, in every wave
     const float ss = wave_sum(ps0 + ps1);
     const float inv = a.norm ? 1.0f / sqrtf(ss / (float)kQD + a.eps) : 1.0f;
-    // logits = inv * (sum of the partials, 4 wave sums added in wave order) + bias
-    for (int e0 = 0; e0 < E; e0 += kThreads) {
-        const int e = e0 + 4 * lane;
+    // logit = inv * (sum of the 128 partials: 32 in row order per lane, then
+    // the four row groups) + bias; every lane of a row-group quartet ends
+    // with the same bits, since each butterfly step adds the same two values
+    const int n_chunks = (E + 63) >> 6;
+    for (int c = w; c < n_chunks; c += 4) {
+        const int ec = 64 * c + 4 * (lane & 15);
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (e < E) {
-            if (e0 > 0) {  // experts past the first 256
+        if (ec < E) {
+            if (c != w) {  // chunks past the first 256 experts
 #pragma unroll
                 for (int j = 0; j < kNP / 4; ++j)
-                    pv[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(w + 4 * j) * E + e);
+                    pv[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(rg + 4 * j) * E + ec);
             }
 #pragma unroll
             for (int j = 0; j < kNP / 4; ++j) acc += pv[j];
         }
-        __syncthreads();  // the previous chunk's red4 reads are done
-        if (e < E) *reinterpret_cast<f32x4*>(&red4[w][4 * lane]) = acc;
-        __syncthreads();
-        if (e0 + t < E) {
-            const float bias = e0 == 0 ? b0 : (brow ? brow[e0 + t] : 0.0f);
-            lg[e0 + t] = ((red4[0][t] + red4[1][t]) + (red4[2][t] + red4[3][t])) * inv + bias;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[q] += __shfl_xor(acc[q], 16, 64);
+            acc[q] += __shfl_xor(acc[q], 32, 64);
         }
+        const int e = ec + rg;
+        const float bias = c == w ? b0 : ((brow && e < E) ? brow[e] : 0.0f);
+        const float v = (rg == 0 ? acc.x : rg == 1 ? acc.y : rg == 2 ? acc.z : acc.w) * inv + bias;
+        topk_rank_chunk(e < E ? topk_key(v, e) : 0ull, c, K, kpad, cand);
     }
-    __syncthreads();
+    topk_merge(n_chunks, K, cand, s_e, s_l);
     f32x4 xx[8];  // this lane's Q4_0 block of x
 #pragma unroll
     for (int j = 0; j < 8; ++j) xx[j] = *reinterpret_cast<const f32x4*>(&xt[36 * lane + 4 * j]);
 
-    block_topk(lg, E, K, kpad, cand, s_e, s_l);
     if (w == 0) {
         if (g == 0 && k == 0 && !a.replay) {
             // gates: softmax over the chosen logits, shifted by the largest
