@@ -110,9 +110,10 @@ typedef struct moe_spark_ctx moe_spark_ctx;
 /* Create a context: allocates the HBM slot arena ((P+R) slots), the pinned
  * host arena (L*E slots) and all tables, and starts the fill agent.
  * compute_stream / copy_stream: hipStream_t, or NULL to let the context make
- * its own.  The fill agent issues ring fills on copy_stream and on one more
- * stream of the context's own (fills of one ring slot always share a
- * stream); moe_spark_synchronize waits for both.  Kernels wait for fills, so
+ * its own.  The fill agent issues ring fills on copy_stream; while a prefill
+ * runs it also uses one more stream of the context's own whenever
+ * copy_stream is busy (fills of one ring slot in flight together share a
+ * stream).  moe_spark_synchronize waits for both.  Kernels wait for fills, so
  * neither copy stream may share a hardware queue with the compute stream:
  * keep the process's streams within GPU_MAX_HW_QUEUES (a fill that never
  * starts ends the wait with E_HIP "fill did not arrive in time").

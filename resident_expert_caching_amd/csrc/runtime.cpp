@@ -134,6 +134,12 @@ struct moe_spark_ctx {
     int64_t tok_launched = 0;
     uint64_t spin_ticks = 0;
     bool stream_decode = false;  // MOE_SPARK_DECODE_STREAM=1: per-kernel launches instead of the token graph
+    // Streams the fill agent may spread a burst of fills over: 1 in decode (a
+    // second queue woken for occasional fills slows the calibrated decode by
+    // about 2%), all kCopyStreams during a prefill, whose fills come in bursts.
+    // MOE_SPARK_COPY_STREAMS=1..kCopyStreams sets the decode figure.
+    int n_copy = 1;
+    std::atomic<int> burst_fills{0};
 
     // fill agent
     std::thread agent;
@@ -218,10 +224,7 @@ int64_t quota(int L, int64_t P, int l) { return P / L + ((int64_t)l < P % L ? 1 
 
 // ---------------------------------------------------------------- fill agent
 
-hipStream_t fill_stream(const moe_spark_ctx* ctx, int ring) {
-    const int i = ring % kCopyStreams;
-    return i == 0 ? ctx->copy : ctx->copy_x[i - 1];
-}
+hipStream_t copy_stream_at(const moe_spark_ctx* ctx, int i) { return i == 0 ? ctx->copy : ctx->copy_x[i - 1]; }
 
 hipError_t sync_copies(const moe_spark_ctx* ctx) {
     hipError_t e = ctx->copy ? hipStreamSynchronize(ctx->copy) : hipSuccess;
@@ -239,10 +242,24 @@ void agent_loop(moe_spark_ctx* ctx) {
         uint64_t seq;
         int ring;
         hipEvent_t ev;
-        hipStream_t stream;
+        int stream;
         int64_t t0;
     };
     std::deque<Pending> pend;
+    // Stream choice: a ring slot with a copy in flight keeps that copy's
+    // stream, so one slot's fills finish in order; otherwise the first stream
+    // unless it is busy, then the least busy one.  A lone fill therefore
+    // always takes the first stream; only bursts spread over the others.
+    std::vector<int> ring_stream(std::max(ctx->cfg.ring_slots, 1), -1), ring_pending(ring_stream.size(), 0);
+    int stream_pending[kCopyStreams] = {};
+    auto pick = [&](int ring) {
+        if (ring_pending[ring] > 0) return ring_stream[ring];
+        int best = 0;
+        const int nc = ctx->burst_fills.load(std::memory_order_relaxed) ? kCopyStreams : ctx->n_copy;
+        for (int i = 1; i < nc && stream_pending[best] > 0; ++i)
+            if (stream_pending[i] < stream_pending[best]) best = i;
+        return best;
+    };
     std::vector<hipEvent_t> pool;
     uint64_t next = 1;
     int idle = 0;
@@ -263,7 +280,8 @@ void agent_loop(moe_spark_ctx* ctx) {
                 pool.pop_back();
             }
             bool ok = key >= 0 && key < ctx->n_experts_total && ring >= 0 && ring < ctx->cfg.ring_slots;
-            const hipStream_t st = ok ? fill_stream(ctx, ring) : ctx->copy;
+            const int si = ok ? pick(ring) : 0;
+            const hipStream_t st = copy_stream_at(ctx, si);
             if (ok)
                 ok = hipMemcpyAsync(ctx->d_slots + (P + ring) * SB, ctx->h_arena + (int64_t)key * SB, SB,
                                     hipMemcpyHostToDevice, st) == hipSuccess;
@@ -275,15 +293,18 @@ void agent_loop(moe_spark_ctx* ctx) {
                 __atomic_store_n(ctx->h_ready + (ring >= 0 && ring < ctx->cfg.ring_slots ? ring : 0), next,
                                  __ATOMIC_RELEASE);
             } else {
-                pend.push_back({next, ring, ev, st, t0});
+                pend.push_back({next, ring, ev, si, t0});
+                ring_stream[ring] = si;
+                ++ring_pending[ring];
+                ++stream_pending[si];
             }
             ++next;
             did = true;
         }
-        // Publish every finished copy.  Copies into one ring slot share a
-        // stream, so a later fill of a slot never finishes before an earlier one.
+        // Publish every finished copy.  Copies into one ring slot in flight at
+        // once share a stream, so a later fill of a slot never finishes first.
         for (auto it = pend.begin(); it != pend.end();) {
-            const hipError_t q = it->ev ? hipEventQuery(it->ev) : hipStreamQuery(it->stream);
+            const hipError_t q = it->ev ? hipEventQuery(it->ev) : hipStreamQuery(copy_stream_at(ctx, it->stream));
             if (q == hipErrorNotReady) {
                 ++it;
                 continue;
@@ -296,6 +317,8 @@ void agent_loop(moe_spark_ctx* ctx) {
             while (dt > m && !ctx->fill_ns_max.compare_exchange_weak(m, dt)) {
             }
             if (it->ev) pool.push_back(it->ev);
+            --ring_pending[it->ring];
+            --stream_pending[it->stream];
             it = pend.erase(it);
             did = true;
         }
@@ -681,6 +704,10 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         rate_khz = 100000;
     ctx->spin_ticks = (uint64_t)rate_khz * 1000ull * 2ull;  // 2 s
     if (const char* ev = getenv("MOE_SPARK_DECODE_STREAM")) ctx->stream_decode = ev[0] == '1';
+    if (const char* ev = getenv("MOE_SPARK_COPY_STREAMS")) {
+        const int n = atoi(ev);
+        if (n >= 1 && n <= kCopyStreams) ctx->n_copy = n;
+    }
     if (compute_stream) {
         ctx->compute = (hipStream_t)compute_stream;
     } else {
@@ -1046,6 +1073,12 @@ moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int
     return moe_spark_decode(ctx, x, 1, bias_row);
 }
 
+struct BurstFills {  // lets the fill agent use every copy stream while a prefill runs
+    moe_spark_ctx* ctx;
+    explicit BurstFills(moe_spark_ctx* c) : ctx(c) { ctx->burst_fills.store(1); }
+    ~BurstFills() { ctx->burst_fills.store(0); }
+};
+
 moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_tokens, const int32_t* bias_row) {
     if (!ctx) return MOE_SPARK_E_INVALID;
     const auto& c = ctx->cfg;
@@ -1055,6 +1088,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         return ctx->fail(MOE_SPARK_E_INVALID, "n_tokens must be in [1, max_tokens] and x non-NULL");
     moe_spark_status st = ready_check(ctx);
     if (st != MOE_SPARK_OK) return st;
+    const BurstFills burst(ctx);
     const int L = c.n_layers, E = c.n_experts, K = c.top_k, R = c.ring_slots;
     const int32_t T = n_tokens;
     int32_t* goff = ctx->h_pmeta;
