@@ -115,12 +115,17 @@ __device__ __forceinline__ void topk_rank_chunk(uint64_t key, int c, int K, uint
     kpad[lane + 64 * w] = key;
     if (lane < K) cand[c * K + lane] = 0ull;  // a chunk may hold fewer than K entries
     __builtin_amdgcn_wave_barrier();
-    int r = 0;
-#pragma unroll 8
-    for (int j = 0; j < 64; j += 2) {
-        const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(&kpad[64 * w + j]);
-        r += (int)(q.x > key) + (int)(q.y > key);
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;  // four counts, so compares do not wait on one another
+#pragma unroll
+    for (int j = 0; j < 64; j += 8) {
+        const ulonglong2* q = reinterpret_cast<const ulonglong2*>(&kpad[64 * w + j]);
+        const ulonglong2 q0 = q[0], q1 = q[1], q2 = q[2], q3 = q[3];
+        r0 += (int)(q0.x > key) + (int)(q0.y > key);
+        r1 += (int)(q1.x > key) + (int)(q1.y > key);
+        r2 += (int)(q2.x > key) + (int)(q2.y > key);
+        r3 += (int)(q3.x > key) + (int)(q3.y > key);
     }
+    const int r = (r0 + r1) + (r2 + r3);
     if (r < K && key != 0ull) cand[c * K + r] = key;
     __builtin_amdgcn_wave_barrier();
 }
