@@ -26,6 +26,19 @@ __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
 __device__ __forceinline__ int tok_value(const TokRef& t) { return t.base + (t.ptr ? *t.ptr : 0); }
 
+// Pause between polls of a fill's ready flag, which lives in host memory:
+// every poll is a read across PCIe, the link the fill itself is using, so
+// after the first 16 quick polls (~0.1 us apart) a waiter polls about once
+// a microsecond.
+__device__ __forceinline__ void fill_poll_pause(int& polls) {
+    if (polls < 16) {
+        ++polls;
+        __builtin_amdgcn_s_sleep(4);
+    } else {
+        __builtin_amdgcn_s_sleep(32);
+    }
+}
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // One Q4_0 block's 32 activations u[0..31] (uu[j] = u[4j..4j+3]) rounded to

@@ -38,8 +38,9 @@ __device__ void wait_fill(const ExpertArgs& a, int ring, uint64_t seq) {
     if (threadIdx.x == 0) {
         const uint64_t* flag = a.ready + ring;
         const uint64_t t0 = wall_clock64();
+        int polls = 0;
         while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < seq) {
-            __builtin_amdgcn_s_sleep(4);
+            fill_poll_pause(polls);
             // once one fill has timed out, nobody waits again (no cascade of waits)
             if (wall_clock64() - t0 > a.spin_limit_ticks ||
                 (__hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ERR_FILL_TIMEOUT)) {

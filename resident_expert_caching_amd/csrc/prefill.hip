@@ -286,8 +286,9 @@ __device__ bool pf_item(const PfArgs& a, int item, int& e, int& pos0, int& rows,
         if (threadIdx.x == 0) {
             const uint64_t* flag = a.ready + (slot - a.P);
             const uint64_t t0 = wall_clock64();
+            int polls = 0;
             while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < wseq) {
-                __builtin_amdgcn_s_sleep(4);
+                fill_poll_pause(polls);
                 if (wall_clock64() - t0 > a.spin_limit_ticks ||
                     (__hip_atomic_load(a.pt.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ERR_FILL_TIMEOUT)) {
                     atomicOr(a.pt.error, (int)ERR_FILL_TIMEOUT);

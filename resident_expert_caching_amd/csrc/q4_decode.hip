@@ -311,8 +311,9 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
         if (t == 0) {
             const uint64_t* flag = a.ready + (slot - a.P);
             const uint64_t t0 = wall_clock64();
+            int polls = 0;
             while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < wseq) {
-                __builtin_amdgcn_s_sleep(4);
+                fill_poll_pause(polls);
                 if (spin_expired(a, t0)) {
                     atomicOr(a.pt.error, (int)ERR_FILL_TIMEOUT);
                     break;
