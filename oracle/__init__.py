@@ -68,6 +68,8 @@ def lib():
         L.oracle_sim_destroy.argtypes = [vp]
         L.oracle_sim_place_uniform.argtypes = [vp]
         L.oracle_sim_calibrate.argtypes = [vp, i32]
+        L.oracle_sim_retune.argtypes = [vp, i32, i32]
+        L.oracle_sim_retune.restype = ctypes.c_int64
         L.oracle_sim_decode_token.argtypes = [vp, i32, vp]
         L.oracle_sim_decode_layer.argtypes = [vp, i32, i32, vp]
         L.oracle_sim_prefill_layer.argtypes = [vp, i32, i32, i32, vp]
@@ -233,6 +235,9 @@ class Sim:
 
     def calibrate(self, reset_counts=True):
         lib().oracle_sim_calibrate(self._h, int(reset_counts))
+
+    def retune(self, hysteresis_pct, decay_shift):
+        return int(lib().oracle_sim_retune(self._h, int(hysteresis_pct), int(decay_shift)))
 
     def decode_token(self, idx):
         idx = np.ascontiguousarray(idx, dtype=np.int32)

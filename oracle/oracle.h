@@ -101,6 +101,8 @@ oracle_sim* oracle_sim_create(int L, int E, int64_t P, int R, int64_t slot_bytes
 void oracle_sim_destroy(oracle_sim* s);
 void oracle_sim_place_uniform(oracle_sim* s);
 void oracle_sim_calibrate(oracle_sim* s, int reset_counts);
+/* one online self-tuning step (hysteresis in percent, counts >>= decay_shift); returns swaps */
+int64_t oracle_sim_retune(oracle_sim* s, int hyst_pct, int decay_shift);
 void oracle_sim_decode_token(oracle_sim* s, int K, const int32_t* idx /* [L][K] */);
 void oracle_sim_decode_layer(oracle_sim* s, int layer, int K, const int32_t* idx /* [K] */);
 void oracle_sim_prefill_layer(oracle_sim* s, int layer, int T, int K, const int32_t* idx /* [T][K] */);

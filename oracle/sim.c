@@ -129,6 +129,62 @@ void oracle_sim_calibrate(oracle_sim* s, int reset_counts) {
     free(want); free(order); free(freed); free(used);
 }
 
+/* Online self-tuning step (reading of the same paragraph: the engine keeps
+ * profiling traffic and re-deciding what stays resident).  Per layer, with
+ * experts ranked by (count desc, expert asc): walk the unpinned experts from
+ * the strongest and the pinned ones from the weakest in step; the pair
+ * (x, y) swaps while 100*count[x] > (100 + hyst_pct)*count[y], and the first
+ * pair that fails ends the layer.  Freed slots then go, ascending, to the
+ * entering experts in (layer, expert) order, whose ring entries are emptied
+ * (as in calibration); finally every count is shifted right by decay_shift.
+ * Returns the number of swaps. */
+int64_t oracle_sim_retune(oracle_sim* s, int hyst_pct, int decay_shift) {
+    const int L = s->L, E = s->E;
+    int* order = (int*)malloc(sizeof(int) * (size_t)E);
+    int* outs = (int*)malloc(sizeof(int) * (size_t)E);
+    int* ins = (int*)malloc(sizeof(int) * (size_t)E);
+    char* enter = (char*)calloc((size_t)L * E, 1);
+    int32_t* freed = (int32_t*)malloc(sizeof(int32_t) * (size_t)(s->P > 0 ? s->P : 1));
+    int64_t swaps = 0, n_free = 0;
+    for (int l = 0; l < L; ++l) {
+        const int64_t base = (int64_t)l * E;
+        for (int e = 0; e < E; ++e) order[e] = e;
+        g_cnt = s->counts + base;
+        qsort(order, (size_t)E, sizeof(int), cmp_count_desc);
+        int n_out = 0, n_in = 0;
+        for (int i = 0; i < E; ++i)
+            if (s->slot_of[base + order[i]] < 0) outs[n_out++] = order[i];
+        for (int i = E - 1; i >= 0; --i)
+            if (s->slot_of[base + order[i]] >= 0) ins[n_in++] = order[i];
+        for (int i = 0; i < n_out && i < n_in; ++i) {
+            const int64_t cx = g_cnt[outs[i]], cy = g_cnt[ins[i]];
+            if (!(100 * cx > (int64_t)(100 + hyst_pct) * cy)) break;
+            enter[base + outs[i]] = 1;
+            freed[n_free++] = s->slot_of[base + ins[i]];
+            s->slot_of[base + ins[i]] = -1;
+            ++swaps;
+        }
+    }
+    /* freed slots ascending (insertion sort: a handful per step) */
+    for (int64_t i = 1; i < n_free; ++i) {
+        const int32_t v = freed[i];
+        int64_t j = i - 1;
+        while (j >= 0 && freed[j] > v) { freed[j + 1] = freed[j]; --j; }
+        freed[j + 1] = v;
+    }
+    int64_t next = 0;
+    for (int64_t i = 0; i < (int64_t)L * E; ++i) {
+        if (!enter[i]) continue;
+        s->slot_of[i] = freed[next++];
+        for (int r = 0; r < s->R; ++r)
+            if (s->ring_owner[r] == (int32_t)i) { s->ring_owner[r] = -1; s->ring_stamp[r] = 0; }
+    }
+    if (decay_shift > 0)
+        for (int64_t i = 0; i < (int64_t)L * E; ++i) s->counts[i] >>= decay_shift;
+    free(order); free(outs); free(ins); free(enter); free(freed);
+    return swaps;
+}
+
 static void log_fill(oracle_sim* s, int l, int e, int slot, int victim) {
     if (s->n_ev == s->cap_ev) {
         s->cap_ev = s->cap_ev ? 2 * s->cap_ev : 1024;

@@ -1,7 +1,8 @@
 """Pins of the placement / LRU-ring simulator: hand-worked traces (golden
 file), an independent list-based LRU model on random traces, calibration
-against a full sort, quota arithmetic, and the uniform-placement cold-hit rate
-under unbiased routing."""
+against a full sort, quota arithmetic, the uniform-placement cold-hit rate
+under unbiased routing, and the online self-tuning step (against calibration,
+and on hand-worked hysteresis, decay and ring cases)."""
 import os
 from collections import OrderedDict
 
@@ -198,3 +199,62 @@ def test_uniform_placement_cold_rate_under_unbiased_routing():
     rate = st["cold_hits"] / st["accesses"]
     q = sum(oracle.quota(L, P, l) for l in range(L)) / (L * E)
     assert abs(rate - (1 - q)) < 0.01
+
+
+def _sim_with_counts(counts, P, R):
+    """A simulator whose layers have exactly these routing counts, reached by
+    single-expert decode tokens (K = 1) in a shuffled order."""
+    L, E = counts.shape
+    sim = oracle.Sim(L, E, P, R, slot_bytes=1)
+    sim.place_uniform()
+    rng = np.random.default_rng(3)
+    per_layer = [rng.permutation(np.repeat(np.arange(E), counts[l])) for l in range(L)]
+    for t in range(max(len(p) for p in per_layer)):
+        for l in range(L):
+            if t < len(per_layer[l]):
+                sim.decode_layer(l, np.array([per_layer[l][t]], np.int32))
+    assert np.array_equal(sim.placement()[3], counts)
+    return sim
+
+
+def test_retune_without_hysteresis_reaches_the_calibrated_placement():
+    """With distinct counts, no hysteresis and no decay, the swap walk ends at
+    each layer's top q_l: the same slots, ring and counts as calibration."""
+    rng = np.random.default_rng(21)
+    L, E, P, R = 3, 16, 20, 4
+    counts = np.stack([rng.permutation(E) + 1 for _ in range(L)]).astype(np.int64)
+    a = _sim_with_counts(counts, P, R)
+    b = _sim_with_counts(counts, P, R)
+    swaps = a.retune(0, 0)
+    b.calibrate(reset_counts=False)
+    for got, ref in zip(a.placement(), b.placement()):
+        assert np.array_equal(got, ref)
+    before = _sim_with_counts(counts, P, R).placement()[0]
+    assert swaps == int(((before < 0) & (a.placement()[0] >= 0)).sum())
+
+
+def test_retune_hysteresis_decay_and_ring():
+    """Hand-worked: one layer, 4 experts, 2 pinned (experts 0 and 1 after the
+    uniform placement), counts 2, 10, 12, 1.  Ranked: 2, 1, 0, 3.  Pairs
+    (strongest unpinned, weakest pinned): (2, 0), then (3, 1)."""
+    counts = np.array([[2, 10, 12, 1]], np.int64)
+    sim = _sim_with_counts(counts, P=2, R=2)
+    slot_of, owner, _, _ = sim.placement()
+    assert slot_of[0].tolist() == [0, 1, -1, -1]
+    assert sorted(owner.tolist()) == [2, 3]   # both cold experts sit in the ring
+    # 25%: 1200 > 125*2 swaps 2 for 0; 100 > 125*10 fails and ends the layer
+    assert sim.retune(25, 1) == 1
+    slot_of, owner, stamp, cnt = sim.placement()
+    assert slot_of[0].tolist() == [-1, 1, 0, -1]   # expert 2 takes the slot expert 0 freed
+    assert 2 not in owner.tolist() and 3 in owner.tolist()
+    assert stamp[owner.tolist().index(-1)] == 0
+    assert cnt[0].tolist() == [1, 5, 6, 0]           # counts >> 1
+    # at 600% the first pair already fails (1200 > 700*2 is false): nothing moves
+    sim2 = _sim_with_counts(counts, P=2, R=2)
+    assert sim2.retune(600, 0) == 0
+    assert sim2.placement()[0][0].tolist() == [0, 1, -1, -1]
+    # equal counts never swap, even without hysteresis: counts 5, 5, 5, 1 rank
+    # 0, 1, 2, 3 and the first pair (2, 1) has 500 > 500 false
+    sim3 = _sim_with_counts(np.array([[5, 5, 5, 1]], np.int64), P=2, R=2)
+    assert sim3.retune(0, 0) == 0
+    assert sim3.placement()[0][0].tolist() == [0, 1, -1, -1]
