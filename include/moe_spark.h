@@ -92,6 +92,8 @@ typedef struct {
     int64_t fill_ns_max;
     int64_t calib_uploads; /* experts copied into pinned slots by calibration */
     int64_t tokens;        /* tokens run by the decode graph */
+    int64_t retunes;       /* online self-tuning steps taken (moe_spark_set_autotune) */
+    int64_t retune_swaps;  /* experts those steps swapped into the pinned set */
 } moe_spark_stats;
 
 typedef struct {
@@ -160,6 +162,26 @@ moe_spark_status moe_spark_place_uniform(moe_spark_ctx* ctx);
  * newly pinned expert's ring entry is emptied.  reset_counts != 0 zeroes the
  * counts afterwards.  Synchronises both streams (call between tokens). */
 moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts);
+
+/* Online self-tuning of the placement during decode.  The pages' "The key
+ * components" paragraph has the engine profile live traffic and keep
+ * re-deciding which experts stay resident; this is that loop made explicit.
+ * Once interval_tokens decode tokens have run since the placement last
+ * changed (calibration, uniform placement or the previous step), the next
+ * decode token is preceded by one step, taken on the host between tokens:
+ *  - per layer, experts are ordered by (count desc, expert asc); the
+ *    strongest unpinned expert x displaces the weakest pinned expert y while
+ *    100*count[x] > (100 + hysteresis_pct)*count[y] (the next strongest and
+ *    next weakest are then compared; the first failing pair ends the layer);
+ *  - slots move as in moe_spark_calibrate (freed slots, ascending, to the
+ *    entering experts in (layer, expert) order; their ring entries emptied);
+ *  - every count is then shifted right by decay_shift bits.
+ * interval_tokens = 0 turns it off (the default).  Only decode tokens count;
+ * a step synchronises both streams and uploads the entering experts.
+ * Errors: E_INVALID for interval < 0, hysteresis_pct outside [0, 100000] or
+ * decay_shift outside [0, 62]. */
+moe_spark_status moe_spark_set_autotune(moe_spark_ctx* ctx, int32_t interval_tokens, int32_t hysteresis_pct,
+                                        int32_t decay_shift);
 
 /* One MoE layer for n_tokens tokens, each run as a separate batch-1 decode
  * step in order (route, then experts, then combine).  Device pointers:

@@ -34,7 +34,7 @@ class Config(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "accesses", "pinned_hits", "cold_hits", "ring_hits", "fills", "evictions", "h2d_bytes",
-        "fill_ns_sum", "fill_ns_max", "calib_uploads", "tokens")]
+        "fill_ns_sum", "fill_ns_max", "calib_uploads", "tokens", "retunes", "retune_swaps")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -68,6 +68,7 @@ def _load():
         "moe_spark_set_experts": (st, [vp, i64, i64, vp]),
         "moe_spark_place_uniform": (st, [vp]),
         "moe_spark_calibrate": (st, [vp, i32]),
+        "moe_spark_set_autotune": (st, [vp, i32, i32, i32]),
         "moe_spark_layer_forward": (st, [vp, i32, vp, vp, i32, vp, u32, vp, vp]),
         "moe_spark_decode": (st, [vp, vp, i32, vp]),
         "moe_spark_token_forward": (st, [vp, vp, vp]),
@@ -134,6 +135,10 @@ def moe_spark_place_uniform(ctx):
 
 def moe_spark_calibrate(ctx, reset_counts=True):
     _check(ctx, _lib.moe_spark_calibrate(ctx, int(reset_counts)))
+
+
+def moe_spark_set_autotune(ctx, interval_tokens, hysteresis_pct=25, decay_shift=1):
+    _check(ctx, _lib.moe_spark_set_autotune(ctx, int(interval_tokens), int(hysteresis_pct), int(decay_shift)))
 
 
 def moe_spark_layer_forward(ctx, layer, x, y, n_tokens, bias_row=None, flags=0, topk_out=None,

@@ -148,6 +148,10 @@ struct moe_spark_ctx {
     std::atomic<int> agent_error{0};
     std::string agent_msg;
     int64_t calib_uploads = 0;
+    // online self-tuning (moe_spark_set_autotune)
+    int32_t at_interval = 0, at_hyst = 0, at_shift = 0;
+    int64_t at_since = 0;  // decoded tokens since the placement last changed
+    int64_t retunes = 0, retune_swaps = 0;
 
     std::string err;
 
@@ -945,33 +949,18 @@ moe_spark_status moe_spark_place_uniform(moe_spark_ctx* ctx) {
     moe_spark_status st = upload_pinned(ctx, moves);
     if (st != MOE_SPARK_OK) return st;
     ctx->placed = true;
+    ctx->at_since = 0;
     return MOE_SPARK_OK;
 }
 
-moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts) {
-    if (!ctx) return MOE_SPARK_E_INVALID;
-    moe_spark_status st = ready_check(ctx);
-    if (st != MOE_SPARK_OK) return st;
+// Move the pinned set to `want`: experts leaving it free their slots; the
+// freed slots, ascending, go to the experts entering it in (layer, expert)
+// order, and an entering expert's ring entry is emptied.  owner / stamp are
+// host copies of the ring; tables are uploaded, the moved experts copied in.
+moe_spark_status repin(moe_spark_ctx* ctx, const std::vector<uint8_t>& want, std::vector<int32_t>& owner,
+                       std::vector<uint64_t>& stamp) {
     const auto& c = ctx->cfg;
     const int L = c.n_layers, E = c.n_experts, R = c.ring_slots;
-    HIPCHK(hipStreamSynchronize(ctx->compute));
-    HIPCHK(sync_copies(ctx));
-    std::vector<int64_t> counts((size_t)L * E);
-    std::vector<int32_t> owner(std::max(R, 1));
-    std::vector<uint64_t> stamp(std::max(R, 1));
-    HIPCHK(hipMemcpy(counts.data(), ctx->d_counts, sizeof(int64_t) * L * E, hipMemcpyDeviceToHost));
-    HIPCHK(hipMemcpy(owner.data(), ctx->d_ring_owner, sizeof(int32_t) * std::max(R, 1), hipMemcpyDeviceToHost));
-    HIPCHK(hipMemcpy(stamp.data(), ctx->d_ring_stamp, sizeof(uint64_t) * std::max(R, 1), hipMemcpyDeviceToHost));
-    // target pinned set: per layer, the q_l most-counted experts (count desc, id asc)
-    std::vector<uint8_t> want((size_t)L * E, 0);
-    std::vector<int> order(E);
-    for (int l = 0; l < L; ++l) {
-        for (int e = 0; e < E; ++e) order[e] = e;
-        const int64_t* cl = counts.data() + (int64_t)l * E;
-        std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cl[a] > cl[b]; });
-        const int64_t q = quota(L, c.resident_cap, l);
-        for (int64_t i = 0; i < q; ++i) want[(int64_t)l * E + order[i]] = 1;
-    }
     std::vector<int32_t> freed;
     for (int64_t key = 0; key < (int64_t)L * E; ++key)
         if (ctx->slot_of[key] >= 0 && !want[key]) {
@@ -983,6 +972,7 @@ moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts) {
     size_t nf = 0;
     for (int64_t key = 0; key < (int64_t)L * E; ++key) {
         if (!want[key] || ctx->slot_of[key] >= 0) continue;
+        if (nf >= freed.size()) return ctx->fail(MOE_SPARK_E_STATE, "placement: more experts to pin than slots");
         ctx->slot_of[key] = freed[nf++];
         moves.push_back({ctx->slot_of[key], (int32_t)key});
         for (int r = 0; r < R; ++r)
@@ -991,14 +981,128 @@ moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts) {
                 stamp[r] = 0;
             }
     }
-    st = upload_pinned(ctx, moves);
+    moe_spark_status st = upload_pinned(ctx, moves);
     if (st != MOE_SPARK_OK) return st;
     ctx->calib_uploads += (int64_t)moves.size();
     HIPCHK(hipMemcpy(ctx->d_slot_of, ctx->slot_of.data(), sizeof(int32_t) * L * E, hipMemcpyHostToDevice));
     HIPCHK(hipMemcpy(ctx->d_ring_owner, owner.data(), sizeof(int32_t) * std::max(R, 1), hipMemcpyHostToDevice));
     HIPCHK(hipMemcpy(ctx->d_ring_stamp, stamp.data(), sizeof(uint64_t) * std::max(R, 1), hipMemcpyHostToDevice));
+    return MOE_SPARK_OK;
+}
+
+// Host copies of the routing counts and the ring, after all queued work.
+moe_spark_status read_tables(moe_spark_ctx* ctx, std::vector<int64_t>& counts, std::vector<int32_t>& owner,
+                             std::vector<uint64_t>& stamp) {
+    const auto& c = ctx->cfg;
+    const int64_t LE = (int64_t)c.n_layers * c.n_experts;
+    const int R1 = std::max(c.ring_slots, 1);
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    HIPCHK(sync_copies(ctx));
+    counts.resize(LE);
+    owner.resize(R1);
+    stamp.resize(R1);
+    HIPCHK(hipMemcpy(counts.data(), ctx->d_counts, sizeof(int64_t) * LE, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(owner.data(), ctx->d_ring_owner, sizeof(int32_t) * R1, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(stamp.data(), ctx->d_ring_stamp, sizeof(uint64_t) * R1, hipMemcpyDeviceToHost));
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    const auto& c = ctx->cfg;
+    const int L = c.n_layers, E = c.n_experts;
+    std::vector<int64_t> counts;
+    std::vector<int32_t> owner;
+    std::vector<uint64_t> stamp;
+    st = read_tables(ctx, counts, owner, stamp);
+    if (st != MOE_SPARK_OK) return st;
+    // target pinned set: per layer, the q_l most-counted experts (count desc, id asc)
+    std::vector<uint8_t> want((size_t)L * E, 0);
+    std::vector<int> order(E);
+    for (int l = 0; l < L; ++l) {
+        for (int e = 0; e < E; ++e) order[e] = e;
+        const int64_t* cl = counts.data() + (int64_t)l * E;
+        std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cl[a] > cl[b]; });
+        const int64_t q = quota(L, c.resident_cap, l);
+        for (int64_t i = 0; i < q; ++i) want[(int64_t)l * E + order[i]] = 1;
+    }
+    st = repin(ctx, want, owner, stamp);
+    if (st != MOE_SPARK_OK) return st;
     if (reset_counts) HIPCHK(hipMemset(ctx->d_counts, 0, sizeof(int64_t) * L * E));
     HIPCHK(hipDeviceSynchronize());
+    ctx->at_since = 0;
+    return MOE_SPARK_OK;
+}
+
+// One step of online self-tuning, between two decode tokens.  Per layer, in
+// the order (count desc, id asc), the strongest unpinned expert x displaces
+// the weakest pinned expert y while 100*count[x] > (100 + hysteresis)*count[y];
+// the first pair that fails ends the layer.  Then every count is shifted
+// right by decay_shift, so older traffic fades.
+moe_spark_status retune(moe_spark_ctx* ctx) {
+    const auto& c = ctx->cfg;
+    const int L = c.n_layers, E = c.n_experts;
+    std::vector<int64_t> counts;
+    std::vector<int32_t> owner;
+    std::vector<uint64_t> stamp;
+    moe_spark_status st = read_tables(ctx, counts, owner, stamp);
+    if (st != MOE_SPARK_OK) return st;
+    std::vector<uint8_t> want((size_t)L * E);
+    for (int64_t key = 0; key < (int64_t)L * E; ++key) want[key] = ctx->slot_of[key] >= 0;
+    std::vector<int> order(E), outs, ins;
+    int64_t swaps = 0;
+    for (int l = 0; l < L; ++l) {
+        const int64_t base = (int64_t)l * E;
+        for (int e = 0; e < E; ++e) order[e] = e;
+        const int64_t* cl = counts.data() + base;
+        std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cl[a] > cl[b]; });
+        outs.clear();
+        ins.clear();
+        for (int i = 0; i < E; ++i)
+            if (!want[base + order[i]]) outs.push_back(order[i]);
+        for (int i = E - 1; i >= 0; --i)
+            if (want[base + order[i]]) ins.push_back(order[i]);
+        for (size_t i = 0; i < outs.size() && i < ins.size(); ++i) {
+            const int x = outs[i], y = ins[i];
+            if (!(100 * cl[x] > (int64_t)(100 + ctx->at_hyst) * cl[y])) break;
+            want[base + x] = 1;
+            want[base + y] = 0;
+            ++swaps;
+        }
+    }
+    if (swaps) {
+        st = repin(ctx, want, owner, stamp);
+        if (st != MOE_SPARK_OK) return st;
+    }
+    if (ctx->at_shift) {
+        for (auto& v : counts) v >>= ctx->at_shift;
+        HIPCHK(hipMemcpy(ctx->d_counts, counts.data(), sizeof(int64_t) * L * E, hipMemcpyHostToDevice));
+    }
+    HIPCHK(hipDeviceSynchronize());
+    ++ctx->retunes;
+    ctx->retune_swaps += swaps;
+    ctx->at_since = 0;
+    return MOE_SPARK_OK;
+}
+
+// Before a decode token: retune once `interval` tokens have run since the
+// placement last changed.
+moe_spark_status maybe_retune(moe_spark_ctx* ctx) {
+    if (ctx->at_interval <= 0 || ctx->at_since < ctx->at_interval) return MOE_SPARK_OK;
+    return retune(ctx);
+}
+
+moe_spark_status moe_spark_set_autotune(moe_spark_ctx* ctx, int32_t interval_tokens, int32_t hysteresis_pct,
+                                        int32_t decay_shift) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    if (interval_tokens < 0 || hysteresis_pct < 0 || hysteresis_pct > 100000 || decay_shift < 0 || decay_shift > 62)
+        return ctx->fail(MOE_SPARK_E_INVALID, "interval >= 0, hysteresis in [0, 100000] %, decay shift in [0, 62]");
+    ctx->at_interval = interval_tokens;
+    ctx->at_hyst = hysteresis_pct;
+    ctx->at_shift = decay_shift;
+    ctx->at_since = 0;
     return MOE_SPARK_OK;
 }
 
@@ -1049,8 +1153,11 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
         st = begin_decode(ctx, x, bias_row, n_tokens);
         if (st != MOE_SPARK_OK) return st;
         for (int t = 0; t < n_tokens; ++t) {
+            st = maybe_retune(ctx);
+            if (st != MOE_SPARK_OK) return st;
             st = launch_token_kernels(ctx, x, bias_row);
             if (st != MOE_SPARK_OK) return st;
+            ++ctx->at_since;
         }
         return MOE_SPARK_OK;
     }
@@ -1060,11 +1167,14 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
     st = begin_decode(ctx, x, bias_row, n_tokens);
     if (st != MOE_SPARK_OK) return st;
     for (int t = 0; t < n_tokens; ++t) {
+        st = maybe_retune(ctx);
+        if (st != MOE_SPARK_OK) return st;
         hipEvent_t& ev = ctx->tok_ev[ctx->tok_launched % kThrottle];
         if (ctx->tok_launched >= kThrottle) HIPCHK(hipEventSynchronize(ev));
         HIPCHK(hipGraphLaunch(exec, ctx->compute));
         HIPCHK(hipEventRecord(ev, ctx->compute));
         ++ctx->tok_launched;
+        ++ctx->at_since;
     }
     return MOE_SPARK_OK;
 }
@@ -1233,6 +1343,8 @@ moe_spark_status moe_spark_get_stats(moe_spark_ctx* ctx, moe_spark_stats* out) {
     out->fill_ns_sum = ctx->fill_ns_sum.load();
     out->fill_ns_max = ctx->fill_ns_max.load();
     out->calib_uploads = ctx->calib_uploads;
+    out->retunes = ctx->retunes;
+    out->retune_swaps = ctx->retune_swaps;
     out->tokens = s[DS_TOKENS];
     return MOE_SPARK_OK;
 }
@@ -1245,6 +1357,8 @@ moe_spark_status moe_spark_reset_stats(moe_spark_ctx* ctx) {
     ctx->fill_ns_sum.store(0);
     ctx->fill_ns_max.store(0);
     ctx->calib_uploads = 0;
+    ctx->retunes = 0;
+    ctx->retune_swaps = 0;
     return MOE_SPARK_OK;
 }
 
