@@ -174,6 +174,53 @@ def run_prefill(ms, torch, model, P, R, warm, probe, layers):
         ms.moe_spark_destroy(ctx)
 
 
+def run_autotune(ms, torch, model, P, R, warm, meas, layers, every=64, hyst=25, shift=1):
+    """Decode through a popularity shift: calibrated on router bias row A,
+    then `meas` tokens under row B, with the placement fixed and with online
+    self-tuning (a step every `every` tokens)."""
+    import workload as wl
+    wp = wl.prefill(layers)
+    biases = [wp.bias_rows(l) for l in range(model.w.L)]  # rows: permutation A, permutation B
+    n_tail = meas.shape[0] // 4
+    row_a = torch.zeros(warm.shape[0], dtype=torch.int32, device="cuda")
+    row_b = torch.ones(meas.shape[0], dtype=torch.int32, device="cuda")
+    out = {}
+    for name, on in (("fixed", False), ("self_tuned", True)):
+        ctx = model.make_ctx(P=P, R=R, biases=biases)
+        try:
+            xw = torch.from_numpy(warm).cuda()
+            ms.moe_spark_decode(ctx, xw.data_ptr(), xw.shape[0], row_a.data_ptr())
+            ms.moe_spark_calibrate(ctx, True)
+            ms.moe_spark_reset_stats(ctx)
+            if on:
+                ms.moe_spark_set_autotune(ctx, every, hyst, shift)
+            xm = torch.from_numpy(meas).cuda()
+            head = meas.shape[0] - n_tail
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            ms.moe_spark_decode(ctx, xm.data_ptr(), head, row_b.data_ptr())
+            ms.moe_spark_synchronize(ctx)
+            s_head = ms.moe_spark_get_stats(ctx)
+            ms.moe_spark_decode(ctx, xm[head:].data_ptr(), n_tail, row_b.data_ptr())
+            ms.moe_spark_synchronize(ctx)
+            dt = time.perf_counter() - t1
+            st = ms.moe_spark_get_stats(ctx)
+            tail = {k: st[k] - s_head[k] for k in ("accesses", "cold_hits")}
+            out[name] = dict(tok_s=round(meas.shape[0] / dt, 1), **rates(st),
+                             tail_tokens=n_tail,
+                             tail_cold_hit_pct=round(100.0 * tail["cold_hits"] / max(tail["accesses"], 1), 4),
+                             fills=st["fills"], retunes=st["retunes"], retune_swaps=st["retune_swaps"],
+                             pinned_uploads=st["calib_uploads"])
+            log(f"popularity shift, {name}: {out[name]['tok_s']} tok/s, cold {out[name]['cold_hit_pct']}% "
+                f"(last {n_tail} tokens {out[name]['tail_cold_hit_pct']}%), {st['retunes']} steps, "
+                f"{st['retune_swaps']} swaps")
+        finally:
+            ms.moe_spark_destroy(ctx)
+    out["setting"] = dict(every_tokens=every, hysteresis_pct=hyst, decay_shift=shift,
+                          calibrated_on="router bias row A", measured_on="row B")
+    return out
+
+
 def h2d_probe(torch, mib=256, reps=5):
     """Pinned host -> device copy rate (the cold-fill link)."""
     src = torch.empty(mib << 20, dtype=torch.uint8, pin_memory=True)
@@ -218,6 +265,7 @@ def main():
     ap.add_argument("--no-full", action="store_true", help="skip the full-residency run")
     ap.add_argument("--no-sweep", action="store_true", help="skip the residency sweep")
     ap.add_argument("--no-prefill", action="store_true", help="skip the batched prefill")
+    ap.add_argument("--no-autotune", action="store_true", help="skip the popularity-shift self-tuning runs")
     ap.add_argument("--kernel-iters", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -342,6 +390,8 @@ def main():
     if not args.no_prefill:
         probe = wl.stack(args.layers).tokens(args.warmup + args.steps, 256)
         res["prefill"] = run_prefill(ms, torch, model, P, args.ring, warm, probe, args.layers)
+    if not args.no_autotune and P < LE:
+        res["self_tuning"] = run_autotune(ms, torch, model, P, args.ring, warm, meas, args.layers)
     res["h2d_link"] = h2d_probe(torch)
     if args.copy_probe:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
