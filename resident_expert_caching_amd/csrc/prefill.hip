@@ -3,7 +3,7 @@
 //
 //   norm     RMSNorm per token; the normalised input in bf16 for the expert
 //            GEMMs, 1/rms kept in fp32 for the router.
-//   router   logits[t][e] = inv_rms[t] * x[t]·Wr[e] + bias, fp32 FMA.
+//   router   logits[t][e] = inv_rms[t] * x[t]·Wr[e] + bias, fp32 MFMA.
 //   topk     exact top-K per token and the softmax renormalised over the
 //            chosen experts ("Luce Spark runs 35B MoE models on 16GB GPU
 //            without speed loss", opening paragraph: about 8 of 256 experts
@@ -105,72 +105,59 @@ __global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
 
 // ---------------------------------------------------------------- router
 
-// Grid (ceil(T/32), ceil(E/64)), 256 threads.  Work-group tile: 32 tokens x
-// 64 experts; thread (ty, tx) = (tid >> 4, tid & 15) owns tokens 2ty, 2ty+1
-// and experts 4tx..4tx+3.  K steps of 32 through LDS; the router is read in
-// its packed layout [d/16][E][16].
-__global__ __launch_bounds__(kPfThreads) void pf_router_kernel(PfArgs a) {
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
+// One wave per 32 tokens x 32 experts, on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: fp32 products, fp32 accumulation).  For a 16-wide
+// slice k0..k0+15 of d, lane (i, g) = (lane % 16, lane / 16) loads the four
+// consecutive values 4g..4g+3 of token row i and of expert row i (the router
+// is packed [d/16][E][16], so both are 16-byte loads); MFMA j then takes
+// k = k0 + 4g + j from lane group g on both operands, which covers the slice.
+// Output: logits[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias.
+__global__ __launch_bounds__(64) void pf_router_kernel(PfArgs a) {
+    const int lane = threadIdx.x, i = lane & 15, g = lane >> 4;
+    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
     const int E = a.E;
-    __shared__ __align__(16) float xs[32][36];
-    __shared__ __align__(16) float ws[64][36];
-    float acc[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-    for (int k0 = 0; k0 < kQD; k0 += 32) {
-        {   // x tile: 32 tokens x 32 floats, one f32x4 per thread
-            const int r = tid >> 3, c = (tid & 7) * 4;
-            const int tok = t0 + r;
-            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (tok < a.T) v = *reinterpret_cast<const f32x4*>(a.x + (int64_t)tok * kQD + k0 + c);
-            *reinterpret_cast<f32x4*>(&xs[r][c]) = v;
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {  // router tile: 64 experts x 32, packed [k0/16 + h][e][16]
-            const int e = tid >> 2, c = (tid & 3) * 4;
-            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (e0 + e < E)
-                v = *reinterpret_cast<const f32x4*>(a.wr + ((int64_t)(k0 / kRW + h) * E + e0 + e) * kRW + c);
-            *reinterpret_cast<f32x4*>(&ws[e][h * 16 + c]) = v;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 32; k += 4) {
-            const f32x4 xa = *reinterpret_cast<const f32x4*>(&xs[2 * ty][k]);
-            const f32x4 xb = *reinterpret_cast<const f32x4*>(&xs[2 * ty + 1][k]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 wv = *reinterpret_cast<const f32x4*>(&ws[4 * tx + j][k]);
-                acc[0][j] += xa.x * wv.x;
-                acc[0][j] += xa.y * wv.y;
-                acc[0][j] += xa.z * wv.z;
-                acc[0][j] += xa.w * wv.w;
-                acc[1][j] += xb.x * wv.x;
-                acc[1][j] += xb.y * wv.y;
-                acc[1][j] += xb.z * wv.z;
-                acc[1][j] += xb.w * wv.w;
-            }
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int tok = t0 + 2 * ty + i;
-        if (tok >= a.T) continue;
-        const float inv = a.inv[tok];
-        const float* brow = nullptr;
-        if (a.bias) {
-            int row = a.bias_row ? a.bias_row[tok] : 0;
-            row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
-            brow = a.bias + (int64_t)row * E;
-        }
+    const bool ta = t0 + i < a.T, tb = t0 + 16 + i < a.T;
+    const bool ea = e0 + i < E, eb = e0 + 16 + i < E;
+    const float* xa = a.x + (int64_t)(ta ? t0 + i : 0) * kQD + 4 * g;
+    const float* xb = a.x + (int64_t)(tb ? t0 + 16 + i : 0) * kQD + 4 * g;
+    const float* wa = a.wr + (int64_t)(ea ? e0 + i : 0) * kRW + 4 * g;
+    const float* wb = a.wr + (int64_t)(eb ? e0 + 16 + i : 0) * kRW + 4 * g;
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[2][2] = {{zero, zero}, {zero, zero}};
+#pragma unroll 4
+    for (int k0 = 0; k0 < kQD; k0 += kRW) {
+        const f32x4 A0 = ta ? *reinterpret_cast<const f32x4*>(xa + k0) : zero;
+        const f32x4 A1 = tb ? *reinterpret_cast<const f32x4*>(xb + k0) : zero;
+        const int64_t wo = (int64_t)(k0 / kRW) * E * kRW;
+        const f32x4 B0 = ea ? *reinterpret_cast<const f32x4*>(wa + wo) : zero;
+        const f32x4 B1 = eb ? *reinterpret_cast<const f32x4*>(wb + wo) : zero;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int e = e0 + 4 * tx + j;
-            if (e < E) a.logits[(int64_t)tok * E + e] = acc[i][j] * inv + (brow ? brow[e] : 0.0f);
+            acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(A0[j], B0[j], acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A0[j], B1[j], acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(A1[j], B0[j], acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A1[j], B1[j], acc[1][1], 0, 0, 0);
+        }
+    }
+    // D of a 16x16 tile: lane (i, g) holds rows 4g..4g+3 of column i
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = t0 + 16 * m + 4 * g + r;
+            if (tok >= a.T) continue;
+            const float inv = a.inv[tok];
+            const float* brow = nullptr;
+            if (a.bias) {
+                int row = a.bias_row ? a.bias_row[tok] : 0;
+                row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
+                brow = a.bias + (int64_t)row * E;
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int e = e0 + 16 * n + i;
+                if (e < E) a.logits[(int64_t)tok * E + e] = acc[m][n][r] * inv + (brow ? brow[e] : 0.0f);
+            }
         }
     }
 }
@@ -498,7 +485,7 @@ hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s) {
 hipError_t launch_pf_front(const PfArgs& a, hipStream_t s) {
     if (a.T <= 0 || a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pf_norm_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
-    hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (a.E + 63) / 64), dim3(kPfThreads), 0, s, a);
+    hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (a.E + 31) / 32), dim3(64), 0, s, a);
     hipLaunchKernelGGL(pf_topk_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
     return hipGetLastError();
 }
