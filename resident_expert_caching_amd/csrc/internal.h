@@ -229,6 +229,7 @@ struct PfArgs {
 };
 
 hipError_t launch_pf_front(const PfArgs& a, hipStream_t s);    // norm, router, top-k + counts + histogram
+hipError_t launch_pf_policy_first(const PfArgs& a, hipStream_t s);
 hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s);  // sort assignments by (expert, token)
 hipError_t launch_pf_chunk(const PfArgs& a, hipStream_t s);    // policy, gate/up GEMM, down GEMM of one chunk
 hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s);  // rank-order combine + residual

@@ -252,6 +252,51 @@ __global__ __launch_bounds__(64) void pf_policy_kernel(PfArgs a) {
     stats_flush(pt, a.n_pf_experts, rs);
 }
 
+// One wave, right after the routing: the first chunk's experts through the
+// placement policy, so that its fills start before the host has planned the
+// layer.  The chunk is cut by the host's rule: the layer's experts with
+// assignments (hist > 0), ascending, up to and excluding the one that would
+// be the (R+1)-th unpinned expert.
+__global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
+    __shared__ int32_t r_owner[kMaxR];
+    __shared__ uint64_t r_stamp[kMaxR];
+    __shared__ uint64_t r_seq[kMaxR];
+    const PolicyTables& pt = a.pt;
+    const int lane = threadIdx.x, E = a.E;
+    const int64_t lbase = (int64_t)a.layer * E;
+    RingState rs{};
+    ring_load(pt, r_owner, r_stamp, r_seq, rs);
+    int cold = 0, n = 0;
+    bool full = false;
+    for (int base = 0; base < E && !full; base += 64) {
+        const int e = base + lane;
+        const bool used = e < E && a.hist[e] > 0;
+        uint64_t mu = __ballot(used);
+        const uint64_t mc = __ballot(used && pt.slot_of[lbase + e] < 0);
+        while (mu) {
+            const int b = __builtin_ctzll(mu);
+            mu &= mu - 1;
+            const bool is_cold = (mc >> b) & 1ull;
+            if (is_cold && cold == pt.R) {
+                full = true;
+                break;
+            }
+            cold += is_cold;
+            const int ex = base + b;
+            int slot;
+            uint64_t wseq;
+            ring_access(pt, a.layer, ex, pt.slot_of[lbase + ex], r_owner, r_stamp, r_seq, rs, slot, wseq);
+            if (lane == 0) {
+                a.pslot[ex] = slot;
+                a.pwait[ex] = wseq;
+            }
+            ++n;
+        }
+    }
+    ring_store(pt, r_owner, r_stamp, r_seq, rs);
+    stats_flush(pt, n, rs);
+}
+
 // ---------------------------------------------------------------- grouped GEMMs
 
 // Resolve a GEMM work item: expert, first row of its group, rows in the tile,
@@ -487,6 +532,11 @@ hipError_t launch_pf_front(const PfArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(pf_norm_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
     hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (a.E + 31) / 32), dim3(64), 0, s, a);
     hipLaunchKernelGGL(pf_topk_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_policy_first(const PfArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(pf_policy_first_kernel, dim3(1), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

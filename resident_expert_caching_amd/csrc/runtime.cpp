@@ -98,6 +98,7 @@ struct moe_spark_ctx {
     uint16_t* d_pu = nullptr;       // [Tmax][d] bf16
     float* d_pinv = nullptr;        // [Tmax]
     float* d_plog = nullptr;        // [Tmax][E]
+    hipEvent_t pf_hist_ev = nullptr;  // prefill: the layer's histogram has reached the host
     int32_t* d_ptopk = nullptr;     // [Tmax][K]
     float* d_pgate = nullptr;       // [Tmax][K]
     int32_t* d_phist = nullptr;     // [E]
@@ -400,6 +401,7 @@ void free_all(moe_spark_ctx* ctx) {
     if (ctx->h_ready) hipHostFree(ctx->h_ready);
     if (ctx->h_pmeta) hipHostFree(ctx->h_pmeta);
     if (ctx->h_phist) hipHostFree(ctx->h_phist);
+    if (ctx->pf_hist_ev) hipEventDestroy(ctx->pf_hist_ev);
     if (ctx->own_compute && ctx->compute) hipStreamDestroy(ctx->compute);
     if (ctx->own_copy && ctx->copy) hipStreamDestroy(ctx->copy);
     for (hipStream_t st : ctx->copy_x)
@@ -773,6 +775,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_pu, T * d) == hipSuccess;
         ok &= dalloc(&ctx->d_pinv, T) == hipSuccess;
         ok &= dalloc(&ctx->d_plog, T * E) == hipSuccess;
+        ok &= hipEventCreateWithFlags(&ctx->pf_hist_ev, hipEventDisableTiming) == hipSuccess;
         ok &= dalloc(&ctx->d_ptopk, T * K) == hipSuccess;
         ok &= dalloc(&ctx->d_pgate, T * K) == hipSuccess;
         ok &= dalloc(&ctx->d_phist, (size_t)E) == hipSuccess;
@@ -1250,7 +1253,10 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         HIPCHK(hipMemsetAsync(ctx->d_phist, 0, sizeof(int32_t) * E, ctx->compute));
         HIPCHK(launch_pf_front(a, ctx->compute));
         HIPCHK(hipMemcpyAsync(ctx->h_phist, ctx->d_phist, sizeof(int32_t) * E, hipMemcpyDeviceToHost, ctx->compute));
-        HIPCHK(hipStreamSynchronize(ctx->compute));
+        HIPCHK(hipEventRecord(ctx->pf_hist_ev, ctx->compute));
+        // the first chunk's policy (and so its fills) starts while the host plans
+        HIPCHK(launch_pf_policy_first(a, ctx->compute));
+        HIPCHK(hipEventSynchronize(ctx->pf_hist_ev));
         // 2. plan: groups in expert order; distinct experts ascending, cut into
         //    chunks of at most R cold (non-pinned) experts, so that every
         //    expert of a chunk sits in the ring while the chunk computes
@@ -1303,7 +1309,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         for (const Chunk& ch : chunks) {
             PfArgs b = a;
             b.pf_experts = d_experts + ch.e_begin;
-            b.n_pf_experts = ch.e_end - ch.e_begin;
+            b.n_pf_experts = &ch == &chunks[0] ? 0 : ch.e_end - ch.e_begin;  // the first ran already
             b.items = d_items + 2 * ch.i_begin;
             b.n_items = ch.i_end - ch.i_begin;
             HIPCHK(launch_pf_chunk(b, ctx->compute));
