@@ -112,7 +112,11 @@ typedef struct moe_spark_ctx moe_spark_ctx;
 /* Create a context: allocates the HBM slot arena ((P+R) slots), the pinned
  * host arena (L*E slots) and all tables, and starts the fill agent.
  * compute_stream / copy_stream: hipStream_t, or NULL to let the context make
- * its own.  The fill agent issues ring fills on copy_stream; while a prefill
+ * its own.  Q4_0 decode fills are pulled by the decode kernels themselves:
+ * the cold expert's work-groups read it from the pinned host arena through its
+ * device address, compute from it and write it into the ring slot (set
+ * MOE_SPARK_PULL_FILLS=0 in the environment to hand them to the fill agent
+ * instead).  The fill agent issues the other ring fills on copy_stream; while a prefill
  * runs it also uses one more stream of the context's own whenever
  * copy_stream is busy (fills of one ring slot in flight together share a
  * stream).  moe_spark_synchronize waits for both.  Kernels wait for fills, so

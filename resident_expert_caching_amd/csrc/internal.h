@@ -44,7 +44,8 @@ enum DevError { ERR_FILL_TIMEOUT = 1, ERR_FIFO_OVERRUN = 2, ERR_BAD_SLOT = 4 };
 // One fill request, written by the route kernel into host-mapped memory.
 struct FifoEntry {
     uint64_t seq;   // written last; 0 = empty
-    int32_t key;    // layer*E + expert (index into the host arena)
+    int32_t key;    // layer*E + expert (index into the host arena); -1 - key: the
+                    // decode kernels copy this fill themselves, nothing to do
     int32_t ring;   // ring slot index 0..R-1
 };
 
@@ -82,6 +83,7 @@ struct PolicyTables {
     int32_t R;
     int32_t E;
     int64_t slot_bytes;
+    int32_t pull;          // 1: decode kernels copy their fills from the host arena themselves
 };
 
 struct RouteArgs {
@@ -155,7 +157,8 @@ struct Q4Args {
     const float* bias;       // this layer's router bias [n_bias_rows][E] or null
     const int32_t* bias_row; // [T] or null
     int32_t n_bias_rows;
-    const uint8_t* slots;
+    uint8_t* slots;          // slot arena (written by pulled fills)
+    const uint8_t* arena;    // pinned host arena (device address): the source of pulled fills
     int64_t slot_bytes, P, n_slots;
     const uint64_t* ready;   // host-mapped ring ready flags (device address)
     LayerSel* sel;           // this layer's published selection

@@ -130,7 +130,7 @@ __device__ inline void ring_access(const PolicyTables& pt, int layer, int expert
             pt.events[s.nev] = ev;
         }
         FifoEntry* fe = pt.fifo + ((s.fseq - 1) % kFifoCap);
-        fe->key = key;
+        fe->key = pt.pull ? -1 - key : key;
         fe->ring = v;
         __threadfence_system();
         __hip_atomic_store(&fe->seq, s.fseq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);

@@ -306,8 +306,11 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
         if (t == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
         return;
     }
-    if (wseq && slot >= a.P) {
-        // ring slot still filling: wait for the host agent's ready flag
+    // A fill issued for this token: in pull mode this expert's work-groups copy
+    // it from the host arena themselves (below); otherwise wait for the host
+    // agent's copy to land.
+    const bool pull = a.pt.pull && wseq && slot >= a.P;
+    if (wseq && slot >= a.P && !pull) {
         if (t == 0) {
             const uint64_t* flag = a.ready + (slot - a.P);
             const uint64_t t0 = wall_clock64();
@@ -324,12 +327,28 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
     }
 
-    const uint8_t* chunk = a.slots + (int64_t)slot * a.slot_bytes + (int64_t)g * kGUChunk;
+    const int64_t key = (int64_t)a.layer * E + s_e[k];
+    const uint8_t* chunk = (pull ? a.arena + key * a.slot_bytes : a.slots + (int64_t)slot * a.slot_bytes) +
+                           (int64_t)g * kGUChunk;
     const u32x4* cp = reinterpret_cast<const u32x4*>(chunk) + w * 8 * 64 + lane;
     u32x4 c[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) c[i] = __builtin_nontemporal_load(cp + i * 64);
     const u32x4 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(chunk + 32768) + w * 64 + lane);
+    if (pull) {
+        // the fill: this chunk of gate/up rows as read, plus 1/32 of the down
+        // region, into the ring slot (the down launch and later ring hits
+        // read the slot; nothing else reads it during this launch)
+        uint8_t* dst = a.slots + (int64_t)slot * a.slot_bytes;
+        u32x4* dp = reinterpret_cast<u32x4*>(dst + (int64_t)g * kGUChunk) + w * 8 * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(c[i], dp + i * 64);
+        __builtin_nontemporal_store(sc, reinterpret_cast<u32x4*>(dst + (int64_t)g * kGUChunk + 32768) + w * 64 + lane);
+        constexpr int kDownShare = (int)((kQ4SlotBytes - kGURegion) / (kQF / kGURows) / 16);  // 16-byte words
+        const u32x4* hs = reinterpret_cast<const u32x4*>(a.arena + key * a.slot_bytes + kGURegion) + g * kDownShare;
+        u32x4* ds = reinterpret_cast<u32x4*>(dst + kGURegion) + g * kDownShare;
+        for (int i = t; i < kDownShare; i += kThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(hs + i), ds + i);
+    }
 
     f32x4 uu[8];
 #pragma unroll

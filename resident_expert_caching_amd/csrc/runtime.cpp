@@ -65,6 +65,8 @@ struct moe_spark_ctx {
 
     uint8_t* d_slots = nullptr;
     uint8_t* h_arena = nullptr;
+    const uint8_t* d_arena = nullptr;  // the host arena's device address (pulled decode fills)
+    bool pull_fills = false;           // Q4_0 decode kernels copy their own fills
     float* d_router = nullptr;
     float* d_bias = nullptr;
 
@@ -276,6 +278,11 @@ void agent_loop(moe_spark_ctx* ctx) {
             const uint64_t s = __atomic_load_n(&fe->seq, __ATOMIC_ACQUIRE);
             if (s != next) break;
             const int key = fe->key, ring = fe->ring;
+            if (key < 0) {  // a pulled fill: the decode kernels copied it themselves
+                ++next;
+                did = true;
+                continue;
+            }
             const int64_t t0 = now_ns();
             hipEvent_t ev;
             if (pool.empty()) {
@@ -413,8 +420,9 @@ hipError_t dalloc(T** p, size_t n) {
     return hipMalloc((void**)p, n * sizeof(T) > 0 ? n * sizeof(T) : 16);
 }
 
-PolicyTables tables(const moe_spark_ctx* ctx) {
+PolicyTables tables(const moe_spark_ctx* ctx, bool pull = false) {
     PolicyTables t;
+    t.pull = pull ? 1 : 0;
     t.slot_of = ctx->d_slot_of;
     t.ring_owner = ctx->d_ring_owner;
     t.ring_stamp = ctx->d_ring_stamp;
@@ -529,10 +537,11 @@ Q4Args q4_args(const moe_spark_ctx* ctx, int layer, const float* x, float* y, To
     a.P = c.resident_cap;
     a.n_slots = ctx->n_slots;
     a.ready = ctx->d_ready;
+    a.arena = ctx->d_arena;
     a.sel = ctx->d_sel + layer;
     a.pub = ctx->d_pub + layer;
     a.h = ctx->d_h;
-    a.pt = tables(ctx);
+    a.pt = tables(ctx, ctx->pull_fills);
     a.tr_x = replay ? nullptr : ctx->tr_x;
     a.tr_topk = replay ? nullptr : ctx->tr_topk;
     a.tr_gates = replay ? nullptr : ctx->tr_gates;
@@ -739,6 +748,15 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         hipSuccess) {
         ctx->h_arena = nullptr;
         return fail_create(MOE_SPARK_E_NOMEM, "pinned host arena allocation failed");
+    }
+    {   // decode pulls its own fills from the arena through its device address
+        void* dp = nullptr;
+        const char* ev = getenv("MOE_SPARK_PULL_FILLS");
+        const bool want = !(ev && ev[0] == '0');
+        if (want && c.wfmt == MOE_SPARK_W_Q4_0 && hipHostGetDevicePointer(&dp, ctx->h_arena, 0) == hipSuccess && dp) {
+            ctx->d_arena = (const uint8_t*)dp;
+            ctx->pull_fills = true;
+        }
     }
     const int R = c.ring_slots;
     bool ok = true;
