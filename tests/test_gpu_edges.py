@@ -9,7 +9,8 @@ oracle and the placement simulator.
  * prefill of a single token, and prefills whose layers need many ring
    chunks (far more cold experts than ring slots);
  * error paths: prefill beyond max_tokens, prefill without prefill buffers,
-   forward before placement.
+   forward before placement;
+ * decode fills pulled by the kernels against fills copied by the host agent.
 """
 import numpy as np
 import pytest
@@ -187,3 +188,23 @@ def test_error_paths():
         assert ei.value.status == ms.E_STATE
     finally:
         ms.moe_spark_destroy(ctx)
+
+
+def test_pulled_and_agent_fills_agree(monkeypatch):
+    """Decode fills pulled by the kernels (the default) and fills copied by the
+    host agent (MOE_SPARK_PULL_FILLS=0, read at context creation) give the
+    same outputs, counters, fill log and placement: every access goes
+    through a ring of K = 8 slots."""
+    w = _wl(100, 8)
+    model = Model(w)
+    x = w.tokens()
+    print("ring-only layer: pulled fills, then agent fills", flush=True)
+    pulled = _layer_run(model, 0, 8, x)
+    monkeypatch.setenv("MOE_SPARK_PULL_FILLS", "0")
+    agent = _layer_run(model, 0, 8, x)
+    assert np.array_equal(pulled["y"], agent["y"]) and np.array_equal(pulled["topk"], agent["topk"])
+    assert {k: pulled["stats"][k] for k in STAT_KEYS} == {k: agent["stats"][k] for k in STAT_KEYS}
+    assert pulled["stats"]["fills"] > 0
+    assert pulled["events"] == agent["events"]
+    for a, b in zip(pulled["placement"], agent["placement"]):
+        assert np.array_equal(a, b)
