@@ -42,11 +42,14 @@ enum DevStat { DS_ACC = 0, DS_PIN, DS_COLD, DS_RING, DS_FILL, DS_EVICT, DS_H2D, 
 enum DevError { ERR_FILL_TIMEOUT = 1, ERR_FIFO_OVERRUN = 2, ERR_BAD_SLOT = 4 };
 
 // One fill request, written by the route kernel into host-mapped memory.
+// A copy request for the host fill agent.  Requests are numbered on their own
+// (fills the decode kernels copy themselves post none), and each carries the
+// fill number that the slot's ready flag must reach.
 struct FifoEntry {
-    uint64_t seq;   // written last; 0 = empty
-    int32_t key;    // layer*E + expert (index into the host arena); -1 - key: the
-                    // decode kernels copy this fill themselves, nothing to do
+    uint64_t seq;   // request number, written last; 0 = empty
+    int32_t key;    // layer*E + expert (index into the host arena)
     int32_t ring;   // ring slot index 0..R-1
+    uint64_t fill;  // fill number: ready[ring] is set to it once the copy has landed
 };
 
 // Routing decision of one layer for the current token.
@@ -72,6 +75,7 @@ struct PolicyTables {
     uint64_t* ring_seq;    // [R] fill number of the current content
     uint64_t* clock;       // LRU clock
     uint64_t* fill_seq;    // fills issued
+    uint64_t* req_seq;     // copy requests posted to the host fill agent
     int64_t* counts;       // [L*E]
     int64_t* stats;        // [DS_N]
     moe_spark_event* events;

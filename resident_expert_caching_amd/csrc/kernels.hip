@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
             r_stamp[r] = pt.ring_stamp[r];
             r_seq[r] = pt.ring_seq[r];
         }
-        uint64_t clock = *pt.clock, fseq = *pt.fill_seq;
+        uint64_t clock = *pt.clock, fseq = *pt.fill_seq, qseq = *pt.req_seq;
         int64_t nev = *pt.n_events;
 #pragma unroll
         for (int k = 0; k < kMaxK; ++k) {
@@ -280,12 +280,14 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
                             ev.pad = 0;
                             pt.events[nev] = ev;
                         }
-                        FifoEntry* fe = pt.fifo + ((fseq - 1) % kFifoCap);
+                        FifoEntry* fe = pt.fifo + (qseq % kFifoCap);
                         fe->key = key;
                         fe->ring = v;
+                        fe->fill = fseq;
                         __threadfence_system();
-                        __hip_atomic_store(&fe->seq, fseq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+                        __hip_atomic_store(&fe->seq, qseq + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
                     }
+                    ++qseq;
                     ++nev;
                     wseq = fseq;
                     slot = (int)(pt.P + v);
@@ -301,6 +303,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         if (lane == 0) {
             *pt.clock = clock;
             *pt.fill_seq = fseq;
+            *pt.req_seq = qseq;
             *pt.n_events = nev;
         }
     }

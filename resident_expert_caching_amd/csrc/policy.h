@@ -17,7 +17,7 @@
 namespace moe {
 
 struct RingState {
-    uint64_t clock, fseq;
+    uint64_t clock, fseq, qseq;
     int64_t nev;
     int64_t n_pin, n_cold, n_ring, n_fill, n_evict;
 };
@@ -33,6 +33,7 @@ __device__ inline void ring_load(const PolicyTables& pt, int32_t* r_owner, uint6
     }
     s.clock = *pt.clock;
     s.fseq = *pt.fill_seq;
+    s.qseq = *pt.req_seq;
     s.nev = *pt.n_events;
     __builtin_amdgcn_wave_barrier();
 }
@@ -50,6 +51,7 @@ __device__ inline void ring_store(const PolicyTables& pt, const int32_t* r_owner
     if (lane == 0) {
         *pt.clock = s.clock;
         *pt.fill_seq = s.fseq;
+        *pt.req_seq = s.qseq;
         *pt.n_events = s.nev;
     }
 }
@@ -129,12 +131,16 @@ __device__ inline void ring_access(const PolicyTables& pt, int layer, int expert
             ev.pad = 0;
             pt.events[s.nev] = ev;
         }
-        FifoEntry* fe = pt.fifo + ((s.fseq - 1) % kFifoCap);
-        fe->key = pt.pull ? -1 - key : key;
-        fe->ring = v;
-        __threadfence_system();
-        __hip_atomic_store(&fe->seq, s.fseq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (!pt.pull) {  // a copy for the host agent (pulled fills are copied by the decode kernels)
+            FifoEntry* fe = pt.fifo + (s.qseq % kFifoCap);
+            fe->key = key;
+            fe->ring = v;
+            fe->fill = s.fseq;
+            __threadfence_system();
+            __hip_atomic_store(&fe->seq, s.qseq + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
+    if (!pt.pull) ++s.qseq;
     __builtin_amdgcn_wave_barrier();
     ++s.nev;
     wseq = s.fseq;

@@ -75,7 +75,7 @@ struct moe_spark_ctx {
     int32_t* d_ring_owner = nullptr;
     uint64_t* d_ring_stamp = nullptr;
     uint64_t* d_ring_seq = nullptr;
-    uint64_t* d_clock = nullptr;  // [2]: clock, fill_seq
+    uint64_t* d_clock = nullptr;  // [3]: clock, fill_seq, req_seq
     int64_t* d_counts = nullptr;
     int64_t* d_stats = nullptr;
     moe_spark_event* d_events = nullptr;
@@ -278,11 +278,7 @@ void agent_loop(moe_spark_ctx* ctx) {
             const uint64_t s = __atomic_load_n(&fe->seq, __ATOMIC_ACQUIRE);
             if (s != next) break;
             const int key = fe->key, ring = fe->ring;
-            if (key < 0) {  // a pulled fill: the decode kernels copied it themselves
-                ++next;
-                did = true;
-                continue;
-            }
+            const uint64_t fill = fe->fill;
             const int64_t t0 = now_ns();
             hipEvent_t ev;
             if (pool.empty()) {
@@ -302,10 +298,10 @@ void agent_loop(moe_spark_ctx* ctx) {
                 ctx->agent_error.store(1);
                 if (ev) pool.push_back(ev);
                 // publish anyway: the data is wrong but nothing waits forever
-                __atomic_store_n(ctx->h_ready + (ring >= 0 && ring < ctx->cfg.ring_slots ? ring : 0), next,
+                __atomic_store_n(ctx->h_ready + (ring >= 0 && ring < ctx->cfg.ring_slots ? ring : 0), fill,
                                  __ATOMIC_RELEASE);
             } else {
-                pend.push_back({next, ring, ev, si, t0});
+                pend.push_back({fill, ring, ev, si, t0});
                 ring_stream[ring] = si;
                 ++ring_pending[ring];
                 ++stream_pending[si];
@@ -429,6 +425,7 @@ PolicyTables tables(const moe_spark_ctx* ctx, bool pull = false) {
     t.ring_seq = ctx->d_ring_seq;
     t.clock = ctx->d_clock;
     t.fill_seq = ctx->d_clock + 1;
+    t.req_seq = ctx->d_clock + 2;
     t.counts = ctx->d_counts;
     t.stats = ctx->d_stats;
     t.events = ctx->d_events;
@@ -766,7 +763,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= dalloc(&ctx->d_ring_owner, (size_t)std::max(R, 1)) == hipSuccess;
     ok &= dalloc(&ctx->d_ring_stamp, (size_t)std::max(R, 1)) == hipSuccess;
     ok &= dalloc(&ctx->d_ring_seq, (size_t)std::max(R, 1)) == hipSuccess;
-    ok &= dalloc(&ctx->d_clock, 2) == hipSuccess;
+    ok &= dalloc(&ctx->d_clock, 3) == hipSuccess;
     ok &= dalloc(&ctx->d_counts, (size_t)L * E) == hipSuccess;
     ok &= dalloc(&ctx->d_stats, DS_N) == hipSuccess;
     ok &= dalloc(&ctx->d_events, (size_t)c.event_cap) == hipSuccess;
@@ -825,7 +822,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= hipMemset(ctx->d_ring_owner, 0xff, sizeof(int32_t) * std::max(R, 1)) == hipSuccess;
     ok &= hipMemset(ctx->d_ring_stamp, 0, sizeof(uint64_t) * std::max(R, 1)) == hipSuccess;
     ok &= hipMemset(ctx->d_ring_seq, 0, sizeof(uint64_t) * std::max(R, 1)) == hipSuccess;
-    ok &= hipMemset(ctx->d_clock, 0, sizeof(uint64_t) * 2) == hipSuccess;
+    ok &= hipMemset(ctx->d_clock, 0, sizeof(uint64_t) * 3) == hipSuccess;
     ok &= hipMemset(ctx->d_counts, 0, sizeof(int64_t) * L * E) == hipSuccess;
     ok &= hipMemset(ctx->d_stats, 0, sizeof(int64_t) * DS_N) == hipSuccess;
     ok &= hipMemset(ctx->d_n_events, 0, sizeof(int64_t)) == hipSuccess;

@@ -83,6 +83,44 @@ def test_tiny_fp32_layer():
         ms.moe_spark_destroy(ctx)
 
 
+def test_tiny_fp32_layer_partial_residency():
+    """The fp32 layer at 50% and 0% residency with a ring of 2 (every cold
+    expert goes through host-agent fills): outputs bit-identical to full
+    residency, bookkeeping equal to the simulator."""
+    w = wl.tiny()
+    model = Model(w)
+    x = w.tokens()
+    T = x.shape[0]
+    outs = {}
+    for P, R in [(w.E, 0), (w.E // 2, 2), (0, 2)]:
+        ctx = model.make_ctx(P=P, R=R)
+        try:
+            print(f"tiny layer at P={P}, R={R}", flush=True)
+            xd = _dev(x)
+            yd = torch.empty_like(xd)
+            topk = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+            gates = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
+            ms.moe_spark_layer_forward(ctx, 0, xd.data_ptr(), yd.data_ptr(), T, None, 0, topk.data_ptr(),
+                                       gates.data_ptr())
+            ms.moe_spark_synchronize(ctx)
+            outs[P] = yd.cpu().numpy()
+            idx = topk.cpu().numpy()
+            sim = oracle.Sim(1, w.E, P, R, ms.moe_spark_slot_bytes(ctx))
+            sim.place_uniform()
+            for t in range(T):
+                sim.decode_layer(0, idx[t])
+            st = ms.moe_spark_get_stats(ctx)
+            assert {k: st[k] for k in STAT_KEYS} == sim.stats()
+            assert events(ctx) == sim_events(sim)
+            for got, ref in zip(placement(ctx, w, R), sim.placement()):
+                assert np.array_equal(got, ref)
+            if P < w.E:
+                assert st["fills"] > 0 and st["evictions"] > 0
+        finally:
+            ms.moe_spark_destroy(ctx)
+    assert np.array_equal(outs[w.E], outs[w.E // 2]) and np.array_equal(outs[w.E], outs[0])
+
+
 def test_target_layer_q4_0_full_residency():
     w = wl.layer()
     model = Model(w)
