@@ -161,6 +161,16 @@ __device__ void run_policy(const Q4Args& a, const int* sel_e, const float* gk, c
 
 // ---------------------------------------------------------------- gate/up
 
+// pv[j] = partial-logit row rg + 4j, experts e4..e4+3, loads issued from j = S on
+template <int S>
+__device__ __forceinline__ void load_partials(f32x4* pv, const float* pl, int rg, int E, int e4) {
+#pragma unroll
+    for (int jj = 0; jj < kNP / 4; ++jj) {
+        const int j = (jj + S) & (kNP / 4 - 1);
+        pv[j] = *reinterpret_cast<const f32x4*>(pl + (int64_t)(rg + 4 * j) * E + e4);
+    }
+}
+
 // Grid (f/16, K).  Work-group (g, k) owns rows 16g..16g+15 of the gate and up
 // matrices of the rank-k expert: waves 0, 1 gate rows, waves 2, 3 up rows,
 // 8 rows per wave, lane b = Q4_0 block b along d.  Slot chunk g (36,864 B):
@@ -202,9 +212,19 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     const int e4 = 64 * w + 4 * (lane & 15), rg = lane >> 4;
     f32x4 pv[kNP / 4];
     if (e4 < E) {
-#pragma unroll
-        for (int j = 0; j < kNP / 4; ++j)
-            pv[j] = *reinterpret_cast<const f32x4*>(a.pl + (int64_t)(rg + 4 * j) * E + e4);
+        // the 32 work-groups on one XCD start at 8 different rows, so they do
+        // not all ask the XCD's L2 for the same lines at the same moment (the
+        // sum below still runs in row order)
+        switch (((g >> 3) + k) & 7) {
+            case 0: load_partials<0>(pv, a.pl, rg, E, e4); break;
+            case 1: load_partials<4>(pv, a.pl, rg, E, e4); break;
+            case 2: load_partials<8>(pv, a.pl, rg, E, e4); break;
+            case 3: load_partials<12>(pv, a.pl, rg, E, e4); break;
+            case 4: load_partials<16>(pv, a.pl, rg, E, e4); break;
+            case 5: load_partials<20>(pv, a.pl, rg, E, e4); break;
+            case 6: load_partials<24>(pv, a.pl, rg, E, e4); break;
+            default: load_partials<28>(pv, a.pl, rg, E, e4); break;
+        }
     }
     const float* brow = nullptr;
     if (a.bias) {
