@@ -105,15 +105,17 @@ __global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
 
 // ---------------------------------------------------------------- router
 
-// One wave per 32 tokens x 32 experts, on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32: fp32 products, fp32 accumulation).  For a 16-wide
-// slice k0..k0+15 of d, lane (i, g) = (lane % 16, lane / 16) loads the four
-// consecutive values 4g..4g+3 of token row i and of expert row i (the router
-// is packed [d/16][E][16], so both are 16-byte loads); MFMA j then takes
-// k = k0 + 4g + j from lane group g on both operands, which covers the slice.
+// One work-group of 4 waves per 32 tokens x 32 experts, on the fp32 matrix
+// cores (v_mfma_f32_16x16x4_f32: fp32 products, fp32 accumulation).  Wave w
+// covers d in [512w, 512w + 512).  For a 16-wide slice k0..k0+15 of d, lane
+// (i, g) = (lane % 16, lane / 16) loads the four consecutive values 4g..4g+3
+// of token row i and of expert row i (the router is packed [d/16][E][16], so
+// both are 16-byte loads); MFMA j then takes k = k0 + 4g + j from lane group g
+// on both operands, which covers the slice.  The four waves' partial sums
+// meet in LDS and are added in wave order.
 // Output: logits[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias.
-__global__ __launch_bounds__(64) void pf_router_kernel(PfArgs a) {
-    const int lane = threadIdx.x, i = lane & 15, g = lane >> 4;
+__global__ __launch_bounds__(256) void pf_router_kernel(PfArgs a) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, i = lane & 15, g = lane >> 4;
     const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
     const int E = a.E;
     const bool ta = t0 + i < a.T, tb = t0 + 16 + i < a.T;
@@ -124,8 +126,9 @@ __global__ __launch_bounds__(64) void pf_router_kernel(PfArgs a) {
     const float* wb = a.wr + (int64_t)(eb ? e0 + 16 + i : 0) * kRW + 4 * g;
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x4 acc[2][2] = {{zero, zero}, {zero, zero}};
+    constexpr int kSplit = kQD / 4;
 #pragma unroll 4
-    for (int k0 = 0; k0 < kQD; k0 += kRW) {
+    for (int k0 = w * kSplit; k0 < (w + 1) * kSplit; k0 += kRW) {
         const f32x4 A0 = ta ? *reinterpret_cast<const f32x4*>(xa + k0) : zero;
         const f32x4 A1 = tb ? *reinterpret_cast<const f32x4*>(xb + k0) : zero;
         const int64_t wo = (int64_t)(k0 / kRW) * E * kRW;
@@ -139,26 +142,26 @@ __global__ __launch_bounds__(64) void pf_router_kernel(PfArgs a) {
             acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A1[j], B1[j], acc[1][1], 0, 0, 0);
         }
     }
-    // D of a 16x16 tile: lane (i, g) holds rows 4g..4g+3 of column i
+    __shared__ __align__(16) f32x4 part[4][4][64];  // [wave][tile m*2+n][lane]
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int q = 0; q < 4; ++q) part[w][q][lane] = acc[q >> 1][q & 1];
+    __syncthreads();
+    // wave w finishes tile q = w: lane (i, g) holds rows 4g..4g+3 of column i
+    const int m = w >> 1, n = w & 1;
+    const f32x4 sum = ((part[0][w][lane] + part[1][w][lane]) + part[2][w][lane]) + part[3][w][lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tok = t0 + 16 * m + 4 * g + r;
-            if (tok >= a.T) continue;
-            const float inv = a.inv[tok];
-            const float* brow = nullptr;
-            if (a.bias) {
-                int row = a.bias_row ? a.bias_row[tok] : 0;
-                row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
-                brow = a.bias + (int64_t)row * E;
-            }
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int e = e0 + 16 * n + i;
-                if (e < E) a.logits[(int64_t)tok * E + e] = acc[m][n][r] * inv + (brow ? brow[e] : 0.0f);
-            }
+    for (int r = 0; r < 4; ++r) {
+        const int tok = t0 + 16 * m + 4 * g + r;
+        const int e = e0 + 16 * n + i;
+        if (tok >= a.T || e >= E) continue;
+        const float inv = a.inv[tok];
+        float bias = 0.0f;
+        if (a.bias) {
+            int row = a.bias_row ? a.bias_row[tok] : 0;
+            row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
+            bias = a.bias[(int64_t)row * E + e];
         }
+        a.logits[(int64_t)tok * E + e] = sum[r] * inv + bias;
     }
 }
 
@@ -530,7 +533,7 @@ hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s) {
 hipError_t launch_pf_front(const PfArgs& a, hipStream_t s) {
     if (a.T <= 0 || a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pf_norm_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
-    hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (a.E + 31) / 32), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (a.E + 31) / 32), dim3(256), 0, s, a);
     hipLaunchKernelGGL(pf_topk_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
     return hipGetLastError();
 }
