@@ -72,6 +72,7 @@ def lib():
         L.oracle_sim_retune.restype = ctypes.c_int64
         L.oracle_sim_decode_token.argtypes = [vp, i32, vp]
         L.oracle_sim_decode_layer.argtypes = [vp, i32, i32, vp]
+        L.oracle_sim_decode_batch.argtypes = [vp, i32, i32, vp]
         L.oracle_sim_prefill_layer.argtypes = [vp, i32, i32, i32, vp]
         L.oracle_sim_stats.argtypes = [vp, vp]
         L.oracle_sim_reset_stats.argtypes = [vp]
@@ -243,6 +244,12 @@ class Sim:
         idx = np.ascontiguousarray(idx, dtype=np.int32)
         assert idx.shape[0] == self.L
         lib().oracle_sim_decode_token(self._h, idx.shape[1], _p(idx))
+
+    def decode_batch(self, idx):
+        """idx [B][L][K]: B tokens through the stack together."""
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        assert idx.ndim == 3 and idx.shape[1] == self.L
+        lib().oracle_sim_decode_batch(self._h, idx.shape[0], idx.shape[2], _p(idx))
 
     def decode_layer(self, layer, idx):
         idx = np.ascontiguousarray(idx, dtype=np.int32).ravel()

@@ -105,6 +105,8 @@ void oracle_sim_calibrate(oracle_sim* s, int reset_counts);
 int64_t oracle_sim_retune(oracle_sim* s, int hyst_pct, int decay_shift);
 void oracle_sim_decode_token(oracle_sim* s, int K, const int32_t* idx /* [L][K] */);
 void oracle_sim_decode_layer(oracle_sim* s, int layer, int K, const int32_t* idx /* [K] */);
+/* B tokens decoded together: accesses in (layer, token, rank) order */
+void oracle_sim_decode_batch(oracle_sim* s, int B, int K, const int32_t* idx /* [B][L][K] */);
 void oracle_sim_prefill_layer(oracle_sim* s, int layer, int T, int K, const int32_t* idx /* [T][K] */);
 void oracle_sim_stats(const oracle_sim* s, int64_t* out);
 void oracle_sim_reset_stats(oracle_sim* s);

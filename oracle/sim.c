@@ -235,6 +235,14 @@ void oracle_sim_decode_token(oracle_sim* s, int K, const int32_t* idx) {
     for (int l = 0; l < s->L; ++l) oracle_sim_decode_layer(s, l, K, idx + (int64_t)l * K);
 }
 
+/* Batched decode (reading: B tokens advance through the stack together, so a
+ * layer's accesses come from all B tokens, in batch order, before the next
+ * layer's): accesses in (layer, token, rank) order.  idx is [B][L][K]. */
+void oracle_sim_decode_batch(oracle_sim* s, int B, int K, const int32_t* idx) {
+    for (int l = 0; l < s->L; ++l)
+        for (int b = 0; b < B; ++b) oracle_sim_decode_layer(s, l, K, idx + ((int64_t)b * s->L + l) * K);
+}
+
 void oracle_sim_prefill_layer(oracle_sim* s, int l, int T, int K, const int32_t* idx) {
     char* hit = (char*)calloc((size_t)s->E, 1);
     for (int64_t i = 0; i < (int64_t)T * K; ++i) {

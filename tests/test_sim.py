@@ -258,3 +258,37 @@ def test_retune_hysteresis_decay_and_ring():
     sim3 = _sim_with_counts(np.array([[5, 5, 5, 1]], np.int64), P=2, R=2)
     assert sim3.retune(0, 0) == 0
     assert sim3.placement()[0][0].tolist() == [0, 1, -1, -1]
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_batched_decode_matches_list_lru_in_layer_token_rank_order(B):
+    """B tokens through the stack together access in (layer, token, rank)
+    order; checked against the independent list model fed in that order, and
+    B = 1 against decode_token."""
+    L, E, P, R, K = 3, 32, 40, 8, 4
+    rng = np.random.default_rng(100 + B)
+    sim = oracle.Sim(L, E, P, R, slot_bytes=1)
+    sim.place_uniform()
+    one = oracle.Sim(L, E, P, R, slot_bytes=1)
+    one.place_uniform()
+    ref = ListLRU(L, E, P, R)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    for step in range(300):
+        idx = np.stack([np.stack([rng.choice(E, size=K, replace=False, p=p) for _ in range(L)])
+                        for _ in range(B)]).astype(np.int32)
+        sim.decode_batch(idx)
+        if B == 1:
+            one.decode_token(idx[0])
+        for l in range(L):
+            for b in range(B):
+                for e in idx[b, l]:
+                    ref.access(l, int(e))
+    st = sim.stats()
+    for k, v in ref.stats.items():
+        assert st[k] == v, (k, st[k], v)
+    got = [(int(e["seq"]), int(e["layer"]), int(e["expert"]), int(e["slot"]), int(e["victim"]))
+           for e in sim.events()]
+    assert got == ref.events and st["ring_hits"] > 0 and st["evictions"] > 0
+    if B == 1:
+        assert st == one.stats()
