@@ -205,6 +205,27 @@ moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, cons
 moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens,
                                   const int32_t* bias_row);
 
+/* Batched decode: n_tokens independent tokens advance through all L layers
+ * in steps of `batch` consecutive tokens (1 <= batch <= 16; the last step
+ * takes what is left), one graph launch per step.  Each token computes
+ * x_{l+1} = x_l + MoE_l(RMSNorm(x_l)) exactly as in moe_spark_decode, so its
+ * outputs are bit-identical to batch-1 decode of the same token.  Serving
+ * several requests at once is the use the pages' "The key components"
+ * paragraph names for the engine; the expert cache is unchanged: within a
+ * step the layer's accesses are made in (token, rank) order, token by token,
+ * before the next layer's, and every counter, the fill log and the ring
+ * follow from that order.  Each distinct expert of a layer-step is read once
+ * for all the tokens that chose it.
+ * x [T][d] fp32 device, updated in place; bias_row [T] int32 device or NULL.
+ * Q4_0 contexts only.  Below full residency the ring must hold a whole
+ * step's accesses (ring_slots >= batch * top_k), so no expert a step uses is
+ * evicted before the step has read it.  The graph for a given (x, bias_row,
+ * batch) is built once and replayed; n_tokens = 0 only builds it.  Online
+ * self-tuning (moe_spark_set_autotune) runs between steps.
+ * Errors: E_INVALID (format, batch, ring size, n_tokens, x), E_STATE. */
+moe_spark_status moe_spark_decode_batched(moe_spark_ctx* ctx, float* x, int32_t n_tokens, int32_t batch,
+                                          const int32_t* bias_row);
+
 /* moe_spark_decode with n_tokens = 1. */
 moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int32_t* bias_row);
 

@@ -71,6 +71,7 @@ def _load():
         "moe_spark_set_autotune": (st, [vp, i32, i32, i32]),
         "moe_spark_layer_forward": (st, [vp, i32, vp, vp, i32, vp, u32, vp, vp]),
         "moe_spark_decode": (st, [vp, vp, i32, vp]),
+        "moe_spark_decode_batched": (st, [vp, vp, i32, i32, vp]),
         "moe_spark_token_forward": (st, [vp, vp, vp]),
         "moe_spark_prefill": (st, [vp, vp, i32, vp]),
         "moe_spark_set_trace": (st, [vp, vp, vp, vp, i64]),
@@ -149,6 +150,10 @@ def moe_spark_layer_forward(ctx, layer, x, y, n_tokens, bias_row=None, flags=0, 
 
 def moe_spark_decode(ctx, x, n_tokens, bias_row=None):
     _check(ctx, _lib.moe_spark_decode(ctx, x, n_tokens, bias_row))
+
+
+def moe_spark_decode_batched(ctx, x, n_tokens, batch, bias_row=None):
+    _check(ctx, _lib.moe_spark_decode_batched(ctx, x, n_tokens, batch, bias_row))
 
 
 def moe_spark_token_forward(ctx, x, bias_row=None):

@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libmoe_spark.so")
-SOURCES = [os.path.join(HERE, "csrc", s) for s in ("kernels.hip", "q4_decode.hip", "prefill.hip", "runtime.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", s) for s in ("kernels.hip", "q4_decode.hip", "qb_decode.hip", "prefill.hip", "runtime.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

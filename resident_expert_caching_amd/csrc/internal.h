@@ -196,6 +196,83 @@ hipError_t launch_q4_gateup(const Q4Args& a, hipStream_t s);
 hipError_t launch_q4_down(const Q4Args& a, hipStream_t s);
 hipError_t launch_advance(int32_t* cursors, int64_t* stats, hipStream_t s);
 
+// Batched decode (qb_decode.hip): B tokens advance through the stack together,
+// one step at a time.  Per layer: a route launch (router, top-k and gates per
+// token; the last work-group to finish runs the placement policy over the
+// step's accesses in (token, rank) order and groups them by distinct expert),
+// then gate/up and down launches that stream each distinct expert once for
+// all the tokens that chose it.
+constexpr int kMaxB = 16;                 // tokens per step
+constexpr int kMaxBK = kMaxB * kQ4MaxK;   // accesses per layer-step
+
+// Routing and placement of one layer for the current step.  Accesses are
+// numbered i = b*K + k; distinct experts j = 0..D-1 ascend by expert id and
+// own the accesses dent[doff[j] .. doff[j+1]) in ascending i.
+struct BatchSel {
+    int32_t idx[kMaxBK];
+    float gate[kMaxBK];
+    int32_t slot[kMaxBK];    // slot the access reads
+    float inv_rms[kMaxB];
+    int32_t D;
+    int32_t pad0;
+    int32_t dexp[kMaxBK];
+    int32_t dslot[kMaxBK];
+    uint64_t dwait[kMaxBK];  // fill number to wait for or pull (0: resident)
+    int32_t doff[kMaxBK + 1];
+    int32_t dent[kMaxBK];
+};
+
+struct QBArgs {
+    int32_t layer, L, E, K;
+    int32_t B;                // step capacity: the grid's token dimension
+    const int32_t* nb;        // tokens in the current step (device, 1..B)
+    float* xb;                // [B][d] the step's tokens: layer input, updated in place
+    const int32_t* rows;      // [B] their router-bias rows
+    int32_t norm;
+    float eps;
+    float* pl;                // [B][kNP][E] router partial logits
+    float* ps;                // [B][kNP] partial sums of squares
+    const float* wr_part;     // packed router [kNP][E][kRW] whose partials the launch writes, or null
+    const float* bias;        // this layer's router bias [n_bias_rows][E] or null
+    int32_t n_bias_rows;
+    uint32_t* ua;             // [B][64 blocks][16] normalised input as fp16 pairs (q4_pairs order)
+    float* ub;                // [B][64] per-block sums of those fp16 values
+    uint8_t* slots;
+    const uint8_t* arena;
+    int64_t slot_bytes, P, n_slots;
+    const uint64_t* ready;
+    BatchSel* sel;            // this layer's routing and placement
+    uint32_t* done;           // last-work-group ticket of the route launch
+    float* h;                 // [B*K][f] SwiGLU output, per access in the down kernel's layout
+    PolicyTables pt;
+    float* tr_x;              // traces: token b of the step goes to row *trace_base + b
+    int32_t* tr_topk;
+    float* tr_gates;
+    int64_t tr_cap;
+    const int32_t* trace_base;
+    uint64_t spin_limit_ticks;
+};
+
+// Token staging of the batched decode graph.
+struct BatchIO {
+    float* x;                 // caller's [T][d] tokens
+    const int32_t* bias_row;  // caller's [T] router-bias rows or null
+    float* xb;                // [B][d] the step's tokens
+    int32_t* rows;            // [B] their bias rows
+    int32_t* nb;              // [1] tokens in the step
+    int32_t* cursors;         // [2] first token of the step, trace cursor
+    int32_t* ntok;            // [1] tokens of this decode call
+    int64_t* stats;
+    int32_t B;
+};
+
+hipError_t launch_qb_begin(const BatchIO& io, int32_t n_tokens, hipStream_t s);
+hipError_t launch_qb_end(const BatchIO& io, hipStream_t s);
+hipError_t launch_qb_router_partial(const QBArgs& a, hipStream_t s);
+hipError_t launch_qb_route(const QBArgs& a, hipStream_t s);
+hipError_t launch_qb_gateup(const QBArgs& a, hipStream_t s);
+hipError_t launch_qb_down(const QBArgs& a, hipStream_t s);
+
 // Arguments of the batched-prefill kernels (prefill.hip), one layer.
 struct PfArgs {
     float* x;                 // [T][d] residual stream, updated in place

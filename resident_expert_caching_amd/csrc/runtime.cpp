@@ -39,6 +39,7 @@ constexpr int kThrottle = 8;  // decode tokens in flight at most
 struct GraphEntry {
     float* x = nullptr;
     const int32_t* bias_row = nullptr;
+    int32_t batch = 0;  // 0: batch-1 token graph; B: batched step graph
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
 };
@@ -95,6 +96,18 @@ struct moe_spark_ctx {
     float* d_xbuf = nullptr;        // [d] token staged for the Q4_0 decode graph
     int32_t* d_tokrow = nullptr;    // [1] its router-bias row
     int32_t* d_ntok = nullptr;      // [1] tokens of the current decode call
+
+    // batched decode (Q4_0): the step's tokens and their routing
+    float* d_bx = nullptr;          // [kMaxB][d]
+    int32_t* d_brows = nullptr;     // [kMaxB]
+    int32_t* d_bn = nullptr;        // [1] tokens in the current step
+    float* d_bpl = nullptr;         // [kMaxB][kNP][E]
+    float* d_bps = nullptr;         // [kMaxB][kNP]
+    uint32_t* d_bua = nullptr;      // [kMaxB][64][16]
+    float* d_bub = nullptr;         // [kMaxB][64]
+    BatchSel* d_bsel = nullptr;     // [L]
+    uint32_t* d_bdone = nullptr;    // [1] route launch ticket
+    float* d_bh = nullptr;          // [kMaxBK][f]
 
     // batched prefill (allocated when max_tokens > 0)
     uint16_t* d_pu = nullptr;       // [Tmax][d] bf16
@@ -396,7 +409,9 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_xscratch, ctx->d_pl,     ctx->d_ps,     ctx->d_pub,     ctx->d_pu,
                      ctx->d_pinv,     ctx->d_plog,   ctx->d_ptopk,  ctx->d_pgate,   ctx->d_phist,
                      ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_ph,
-                     ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok};
+                     ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok,
+                     ctx->d_bx,       ctx->d_brows,  ctx->d_bn,     ctx->d_bpl,     ctx->d_bps,
+                     ctx->d_bua,      ctx->d_bub,    ctx->d_bsel,   ctx->d_bdone,   ctx->d_bh};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
@@ -639,9 +654,80 @@ moe_spark_status launch_token_kernels(moe_spark_ctx* ctx, float* x, const int32_
     return MOE_SPARK_OK;
 }
 
-moe_spark_status get_graph(moe_spark_ctx* ctx, float* x, const int32_t* bias_row, hipGraphExec_t* out) {
+BatchIO batch_io(const moe_spark_ctx* ctx, float* x, const int32_t* bias_row, int32_t batch) {
+    BatchIO io;
+    io.x = x;
+    io.bias_row = bias_row;
+    io.xb = ctx->d_bx;
+    io.rows = ctx->d_brows;
+    io.nb = ctx->d_bn;
+    io.cursors = ctx->d_cursors;
+    io.ntok = ctx->d_ntok;
+    io.stats = ctx->d_stats;
+    io.B = batch;
+    return io;
+}
+
+// Arguments of the batched decode kernels of one layer.  wr_layer: the layer
+// whose packed router the launch turns into partial logits (-1: none).
+QBArgs qb_args(const moe_spark_ctx* ctx, int layer, int wr_layer, int32_t batch) {
+    const auto& c = ctx->cfg;
+    QBArgs a{};
+    a.layer = layer;
+    a.L = c.n_layers;
+    a.E = c.n_experts;
+    a.K = c.top_k;
+    a.B = batch;
+    a.nb = ctx->d_bn;
+    a.xb = ctx->d_bx;
+    a.rows = ctx->d_brows;
+    a.norm = 1;
+    a.eps = c.rms_eps;
+    a.pl = ctx->d_bpl;
+    a.ps = ctx->d_bps;
+    a.wr_part = wr_layer >= 0 ? ctx->d_router + (int64_t)wr_layer * c.n_experts * c.d_model : nullptr;
+    a.bias = c.n_bias_rows > 0 ? ctx->d_bias + (int64_t)layer * c.n_bias_rows * c.n_experts : nullptr;
+    a.n_bias_rows = c.n_bias_rows;
+    a.ua = ctx->d_bua;
+    a.ub = ctx->d_bub;
+    a.slots = ctx->d_slots;
+    a.arena = ctx->d_arena;
+    a.slot_bytes = ctx->slot_bytes;
+    a.P = c.resident_cap;
+    a.n_slots = ctx->n_slots;
+    a.ready = ctx->d_ready;
+    a.sel = ctx->d_bsel + layer;
+    a.done = ctx->d_bdone;
+    a.h = ctx->d_bh;
+    a.pt = tables(ctx, ctx->pull_fills);
+    a.tr_x = ctx->tr_x;
+    a.tr_topk = ctx->tr_topk;
+    a.tr_gates = ctx->tr_gates;
+    a.tr_cap = ctx->tr_cap;
+    a.trace_base = ctx->d_cursors + 1;
+    a.spin_limit_ticks = ctx->spin_ticks;
+    return a;
+}
+
+// One step of batched decode: the first layer's router partials, then route,
+// gate/up and down per layer, then the step's write-back and staging.
+moe_spark_status launch_step_kernels(moe_spark_ctx* ctx, float* x, const int32_t* bias_row, int32_t batch) {
+    const int L = ctx->cfg.n_layers;
+    HIPCHK(launch_qb_router_partial(qb_args(ctx, 0, 0, batch), ctx->compute));
+    for (int l = 0; l < L; ++l) {
+        const QBArgs a = qb_args(ctx, l, l + 1 < L ? l + 1 : -1, batch);
+        HIPCHK(launch_qb_route(a, ctx->compute));
+        HIPCHK(launch_qb_gateup(a, ctx->compute));
+        HIPCHK(launch_qb_down(a, ctx->compute));
+    }
+    HIPCHK(launch_qb_end(batch_io(ctx, x, bias_row, batch), ctx->compute));
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status get_graph(moe_spark_ctx* ctx, float* x, const int32_t* bias_row, int32_t batch,
+                           hipGraphExec_t* out) {
     for (auto& g : ctx->graphs)
-        if (g.x == x && g.bias_row == bias_row) {
+        if (g.x == x && g.bias_row == bias_row && g.batch == batch) {
             *out = g.exec;
             return MOE_SPARK_OK;
         }
@@ -655,8 +741,9 @@ moe_spark_status get_graph(moe_spark_ctx* ctx, float* x, const int32_t* bias_row
     GraphEntry ge;
     ge.x = x;
     ge.bias_row = bias_row;
+    ge.batch = batch;
     HIPCHK(hipStreamBeginCapture(ctx->compute, hipStreamCaptureModeThreadLocal));
-    moe_spark_status st = launch_token_kernels(ctx, x, bias_row);
+    moe_spark_status st = batch ? launch_step_kernels(ctx, x, bias_row, batch) : launch_token_kernels(ctx, x, bias_row);
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(ctx->compute, &graph);
     if (st != MOE_SPARK_OK) {
@@ -783,6 +870,18 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= dalloc(&ctx->d_xbuf, (size_t)d) == hipSuccess;
     ok &= dalloc(&ctx->d_tokrow, 1) == hipSuccess;
     ok &= dalloc(&ctx->d_ntok, 1) == hipSuccess;
+    if (c.wfmt == MOE_SPARK_W_Q4_0) {
+        ok &= dalloc(&ctx->d_bx, (size_t)kMaxB * d) == hipSuccess;
+        ok &= dalloc(&ctx->d_brows, (size_t)kMaxB) == hipSuccess;
+        ok &= dalloc(&ctx->d_bn, 1) == hipSuccess;
+        ok &= dalloc(&ctx->d_bpl, (size_t)kMaxB * kNP * E) == hipSuccess;
+        ok &= dalloc(&ctx->d_bps, (size_t)kMaxB * kNP) == hipSuccess;
+        ok &= dalloc(&ctx->d_bua, (size_t)kMaxB * 64 * 16) == hipSuccess;
+        ok &= dalloc(&ctx->d_bub, (size_t)kMaxB * 64) == hipSuccess;
+        ok &= dalloc(&ctx->d_bsel, (size_t)L) == hipSuccess;
+        ok &= dalloc(&ctx->d_bdone, 1) == hipSuccess;
+        ok &= dalloc(&ctx->d_bh, (size_t)kMaxBK * f) == hipSuccess;
+    }
     if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "device table allocation failed");
     if (c.max_tokens > 0) {
         const size_t T = (size_t)c.max_tokens, K = (size_t)c.top_k;
@@ -841,6 +940,14 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     ok &= hipMemset(ctx->d_xbuf, 0, sizeof(float) * d) == hipSuccess;
     ok &= hipMemset(ctx->d_tokrow, 0, sizeof(int32_t)) == hipSuccess;
     ok &= hipMemset(ctx->d_ntok, 0, sizeof(int32_t)) == hipSuccess;
+    if (c.wfmt == MOE_SPARK_W_Q4_0) {
+        ok &= hipMemset(ctx->d_bx, 0, sizeof(float) * kMaxB * d) == hipSuccess;
+        ok &= hipMemset(ctx->d_brows, 0, sizeof(int32_t) * kMaxB) == hipSuccess;
+        ok &= hipMemset(ctx->d_bn, 0, sizeof(int32_t)) == hipSuccess;
+        ok &= hipMemset(ctx->d_bsel, 0, sizeof(BatchSel) * L) == hipSuccess;
+        ok &= hipMemset(ctx->d_bdone, 0, sizeof(uint32_t)) == hipSuccess;
+        ok &= hipMemset(ctx->d_bh, 0, sizeof(float) * kMaxBK * f) == hipSuccess;
+    }
     for (auto& ev : ctx->tok_ev) ok &= hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess;
     ok &= hipDeviceSynchronize() == hipSuccess;
     if (!ok) return fail_create(MOE_SPARK_E_HIP, "table initialisation failed");
@@ -1180,7 +1287,7 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
         return MOE_SPARK_OK;
     }
     hipGraphExec_t exec;
-    st = get_graph(ctx, x, bias_row, &exec);  // n_tokens == 0 only prepares the graph
+    st = get_graph(ctx, x, bias_row, 0, &exec);  // n_tokens == 0 only prepares the graph
     if (st != MOE_SPARK_OK || n_tokens == 0) return st;
     st = begin_decode(ctx, x, bias_row, n_tokens);
     if (st != MOE_SPARK_OK) return st;
@@ -1199,6 +1306,45 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
 
 moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int32_t* bias_row) {
     return moe_spark_decode(ctx, x, 1, bias_row);
+}
+
+moe_spark_status moe_spark_decode_batched(moe_spark_ctx* ctx, float* x, int32_t n_tokens, int32_t batch,
+                                          const int32_t* bias_row) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    const auto& c = ctx->cfg;
+    if (c.wfmt != MOE_SPARK_W_Q4_0) return ctx->fail(MOE_SPARK_E_INVALID, "batched decode needs Q4_0 experts");
+    if (batch < 1 || batch > kMaxB) return ctx->fail(MOE_SPARK_E_INVALID, "batch %d outside [1, %d]", batch, kMaxB);
+    if (c.resident_cap < (int64_t)c.n_layers * c.n_experts && c.ring_slots < batch * c.top_k)
+        return ctx->fail(MOE_SPARK_E_INVALID,
+                         "batch %d needs a ring of at least batch * top_k = %d slots below full residency (have %d)",
+                         batch, batch * c.top_k, c.ring_slots);
+    if (n_tokens < 0 || (n_tokens > 0 && !x)) return ctx->fail(MOE_SPARK_E_INVALID, "bad token count or NULL x");
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    if (!x) return MOE_SPARK_OK;
+    hipGraphExec_t exec = nullptr;
+    if (!ctx->stream_decode) {
+        st = get_graph(ctx, x, bias_row, batch, &exec);  // n_tokens == 0 only prepares the graph
+        if (st != MOE_SPARK_OK) return st;
+    }
+    if (n_tokens == 0) return MOE_SPARK_OK;
+    HIPCHK(launch_qb_begin(batch_io(ctx, x, bias_row, batch), n_tokens, ctx->compute));
+    for (int t0 = 0; t0 < n_tokens; t0 += batch) {
+        st = maybe_retune(ctx);
+        if (st != MOE_SPARK_OK) return st;
+        if (exec) {
+            hipEvent_t& ev = ctx->tok_ev[ctx->tok_launched % kThrottle];
+            if (ctx->tok_launched >= kThrottle) HIPCHK(hipEventSynchronize(ev));
+            HIPCHK(hipGraphLaunch(exec, ctx->compute));
+            HIPCHK(hipEventRecord(ev, ctx->compute));
+            ++ctx->tok_launched;
+        } else {
+            st = launch_step_kernels(ctx, x, bias_row, batch);
+            if (st != MOE_SPARK_OK) return st;
+        }
+        ctx->at_since += std::min(batch, n_tokens - t0);
+    }
+    return MOE_SPARK_OK;
 }
 
 struct BurstFills {  // lets the fill agent use every copy stream while a prefill runs

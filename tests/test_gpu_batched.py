@@ -1,0 +1,193 @@
+"""Batched decode (moe_spark_decode_batched) through the C ABI.
+
+A 4-layer stack of the target layer shape (d=2048, 64 experts, top-8, f=512,
+Q4_0, Zipf-biased router) decodes 32 warm-up tokens batch-1 under uniform
+placement, is calibrated, and then decodes 45 tokens in steps of B tokens
+(45 is a whole number of steps for B = 1, 3 and ragged for B = 8, 16):
+
+ * outputs and top-k are bit-identical to batch-1 decode of the same tokens
+   at full residency (every token's arithmetic is the batch-1 arithmetic);
+ * bookkeeping — counters, fill/eviction log, pinned set, ring, counts —
+   equals the simulator replaying the GPU's own top-k trace with each step's
+   accesses in (layer, token, rank) order;
+ * sampled (token, layer) outputs match the fp64 oracle, teacher-forced;
+ * at 100/60/30% residency with uniform placement and the smallest ring a
+   step allows (R = B*K, so one step can turn the whole ring over), with
+   pulled and with host-agent fills, outputs stay bit-identical and
+   bookkeeping exact.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as wl
+from spark_harness import (STAT_KEYS, TIE_GAP, Model, assert_outputs_close, events,
+                           oracle_topk_and_gap, placement, sim_events)
+
+pytestmark = pytest.mark.gpu
+
+ms = pytest.importorskip("resident_expert_caching_amd")
+
+WARM, MEAS = 32, 45
+
+
+@pytest.fixture(scope="module")
+def model():
+    w = wl.Workload("batched-L4-E64", d=2048, E=64, K=8, f=512, L=4, wfmt=wl.FMT_Q4_0, norm=True,
+                    seed=51, n_tokens=WARM + MEAS, token_stream=53, bias_seeds=(5,))
+    return Model(w)
+
+
+def _run(model, P, R, B, calibrate=True, pull=True):
+    """Warm-up batch-1, optional calibration, measured tokens in steps of B
+    (B = 0: batch-1 decode).  Traced."""
+    w = model.w
+    x = w.tokens(0, WARM + MEAS)
+    old = os.environ.get("MOE_SPARK_PULL_FILLS")
+    os.environ["MOE_SPARK_PULL_FILLS"] = "1" if pull else "0"
+    try:
+        ctx = model.make_ctx(P=P, R=R)
+    finally:
+        if old is None:
+            del os.environ["MOE_SPARK_PULL_FILLS"]
+        else:
+            os.environ["MOE_SPARK_PULL_FILLS"] = old
+    try:
+        cap = WARM + MEAS
+        tr_x = torch.zeros((cap, w.L, w.d), dtype=torch.float32, device="cuda")
+        tr_k = torch.zeros((cap, w.L, w.K), dtype=torch.int32, device="cuda")
+        tr_g = torch.zeros((cap, w.L, w.K), dtype=torch.float32, device="cuda")
+        ms.moe_spark_set_trace(ctx, tr_x.data_ptr(), tr_k.data_ptr(), tr_g.data_ptr(), cap)
+        xw = torch.from_numpy(x[:WARM].copy()).cuda()
+        xm = torch.from_numpy(x[WARM:].copy()).cuda()
+        row = torch.zeros(cap, dtype=torch.int32, device="cuda")
+        ms.moe_spark_decode(ctx, xw.data_ptr(), WARM, row.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        if calibrate:
+            ms.moe_spark_calibrate(ctx, True)
+        ms.moe_spark_reset_stats(ctx)
+        if B:
+            ms.moe_spark_decode_batched(ctx, xm.data_ptr(), MEAS, B, row.data_ptr())
+        else:
+            ms.moe_spark_decode(ctx, xm.data_ptr(), MEAS, row.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        return dict(x=np.concatenate([xw.cpu().numpy(), xm.cpu().numpy()]), tr_x=tr_x.cpu().numpy(),
+                    tr_k=tr_k.cpu().numpy(), tr_g=tr_g.cpu().numpy(), stats=ms.moe_spark_get_stats(ctx),
+                    events=events(ctx), placement=placement(ctx, w, R),
+                    slot_bytes=ms.moe_spark_slot_bytes(ctx))
+    finally:
+        ms.moe_spark_destroy(ctx)
+
+
+def _check_bookkeeping(model, r, P, R, B, calibrate):
+    w = model.w
+    sim = oracle.Sim(w.L, w.E, P, R, r["slot_bytes"])
+    sim.place_uniform()
+    for t in range(WARM):
+        sim.decode_token(r["tr_k"][t])
+    if calibrate:
+        sim.calibrate(True)
+    sim.reset_stats()
+    for t0 in range(WARM, WARM + MEAS, B):
+        sim.decode_batch(r["tr_k"][t0:min(t0 + B, WARM + MEAS)])
+    st = r["stats"]
+    assert {k: st[k] for k in STAT_KEYS} == sim.stats(), (st, sim.stats())
+    assert st["tokens"] == MEAS
+    assert r["events"] == sim_events(sim)
+    for got, ref in zip(r["placement"], sim.placement()):
+        assert np.array_equal(got, ref)
+    return sim.stats()
+
+
+@pytest.fixture(scope="module")
+def batch1(model):
+    w = model.w
+    print("batch-1 reference decode at full residency", flush=True)
+    return _run(model, w.L * w.E, 0, 0, calibrate=False)
+
+
+@pytest.mark.parametrize("B", [1, 3, 8, 16])
+def test_batched_matches_batch1_and_simulator(model, batch1, B):
+    w = model.w
+    LE = w.L * w.E
+    P, R = int(round(0.6 * LE)), max(8, B * w.K)
+    print(f"batched decode B={B}: P={P} R={R}, calibrated", flush=True)
+    r = _run(model, P, R, B)
+    assert np.array_equal(r["tr_k"], batch1["tr_k"])
+    assert np.array_equal(r["x"], batch1["x"])
+    assert np.array_equal(r["tr_x"], batch1["tr_x"])
+    assert np.array_equal(r["tr_g"], batch1["tr_g"])
+    ss = _check_bookkeeping(model, r, P, R, B, True)
+    print(f"B={B}: {ss}", flush=True)
+    # teacher-forced oracle parity of sampled (token, layer) pairs of the batched run
+    tr_x, tr_k = r["tr_x"], r["tr_k"]
+    for t in (WARM, WARM + B // 2, WARM + MEAS - 1):
+        for l in range(w.L):
+            xl = tr_x[t, l].astype(np.float64)
+            xn = (tr_x[t, l + 1] if l + 1 < w.L else r["x"][t]).astype(np.float64)
+            lg = oracle.router(model.routers[l], oracle.rmsnorm(xl), model.biases[l][0])
+            ref_idx, gap = oracle_topk_and_gap(lg, w.K)
+            forced = tr_k[t, l][None] if gap < TIE_GAP else None
+            if forced is None:
+                assert np.array_equal(tr_k[t, l], ref_idx), (t, l)
+            yref, _, gref, _ = oracle.layer(xl[None], model.routers[l], model.experts(l), K=w.K,
+                                            wfmt=w.wfmt, norm=True, bias=model.biases[l],
+                                            bias_row=np.zeros(1, np.int32), forced=forced)
+            assert_outputs_close(xn - xl, yref[0], f"B={B} token {t} layer {l}")
+            np.testing.assert_allclose(r["tr_g"][t, l], gref[0], rtol=2e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("pull", [True, False], ids=["pulled-fills", "agent-fills"])
+def test_batched_residency_sweep_uniform(model, batch1, pull):
+    w = model.w
+    LE = w.L * w.E
+    B = 2
+    R = B * w.K  # the smallest ring a step allows: a step can turn it over completely
+    fills = {}
+    for frac in (1.0, 0.6, 0.3):
+        P = int(round(frac * LE))
+        RR = R if P < LE else 0
+        print(f"batched decode B={B}: P={P} R={RR}, uniform placement, pull={pull}", flush=True)
+        r = _run(model, P, RR, B, calibrate=False, pull=pull)
+        assert np.array_equal(r["x"], batch1["x"]), frac
+        assert np.array_equal(r["tr_k"], batch1["tr_k"]), frac
+        ss = _check_bookkeeping(model, r, P, RR, B, False)
+        fills[frac] = ss["fills"]
+        if P < LE:
+            assert ss["fills"] > 0 and ss["evictions"] > 0
+    print(f"fills by residency: {fills}", flush=True)
+
+
+def test_batched_rejects_bad_arguments(model):
+    w = model.w
+    LE = w.L * w.E
+    P = int(round(0.6 * LE))
+    ctx = model.make_ctx(P=P, R=16)
+    try:
+        x = torch.zeros((4, w.d), dtype=torch.float32, device="cuda")
+        for B, needle in ((0, "batch"), (17, "batch"), (3, "ring")):
+            with pytest.raises(ms.MoeSparkError) as ei:
+                ms.moe_spark_decode_batched(ctx, x.data_ptr(), 4, B, None)
+            assert ei.value.status == ms.E_INVALID and needle in str(ei.value), (B, str(ei.value))
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_decode_batched(ctx, x.data_ptr(), -1, 2, None)
+        assert ei.value.status == ms.E_INVALID
+        # a ring of 16 holds a step of 2 tokens x 8 experts
+        ms.moe_spark_decode_batched(ctx, x.data_ptr(), 4, 2, None)
+        ms.moe_spark_synchronize(ctx)
+        assert ms.moe_spark_get_stats(ctx)["tokens"] == 4
+    finally:
+        ms.moe_spark_destroy(ctx)
+    tiny = wl.tiny()
+    tm = Model(tiny)
+    ctx = tm.make_ctx(P=tiny.E, R=0)
+    try:
+        x = torch.zeros((2, tiny.d), dtype=torch.float32, device="cuda")
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_decode_batched(ctx, x.data_ptr(), 2, 2, None)
+        assert ei.value.status == ms.E_INVALID and "Q4_0" in str(ei.value)
+    finally:
+        ms.moe_spark_destroy(ctx)
