@@ -22,6 +22,9 @@ Nested in the same line:
    2. The Zipf permutation switches to B at token 1024.
    3. Then a 256-token decode probe under B runs before and after
       recalibration.
+ - `batched`: the same decode in steps of B tokens (moe_spark_decode_batched),
+   the ring widened to B*top_k slots where it is smaller; tok/s, distinct
+   experts per layer-step, algorithmic weight GB/s, bit-identity to batch 1.
  - `roofline`: the dominant decode kernel, timed by HIP events over isolated
    replays.
  - `h2d_link`: a pinned host-to-device copy probe of the PCIe link.
@@ -121,6 +124,52 @@ def run_decode(ms, torch, model, P, R, warm, meas, row, calibrate, kernel_iters=
         r = rates(st)
         log(f"P={P} calibrated={calibrate}: {out['tok_s']:.1f} tok/s, cold {r['cold_hit_pct']}%, "
             f"fills {st['fills']}")
+        return out
+    finally:
+        ms.moe_spark_destroy(ctx)
+
+
+def run_batched(ms, torch, model, P, R, B, warm, meas, row, ref_x):
+    """Batched decode: warm-up batch-1 under uniform placement, calibration,
+    then `meas` in steps of B tokens.  Each layer-step reads each of its
+    distinct experts once; the traced top-k gives their number."""
+    w = model.w
+    t0 = time.time()
+    ctx = model.make_ctx(P=P, R=R)
+    log(f"batched B={B}: P={P} R={R}: context ready in {time.time() - t0:.1f}s")
+    try:
+        T = meas.shape[0]
+        tr_k = torch.zeros((T, w.L, w.K), dtype=torch.int32, device="cuda")
+        tr_g = torch.zeros((T, w.L, w.K), dtype=torch.float32, device="cuda")
+        xw = torch.from_numpy(warm).cuda()
+        xm = torch.from_numpy(meas).cuda()
+        ms.moe_spark_decode(ctx, xw.data_ptr(), xw.shape[0], row.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        ms.moe_spark_calibrate(ctx, True)
+        ms.moe_spark_reset_stats(ctx)
+        ms.moe_spark_set_trace(ctx, None, tr_k.data_ptr(), tr_g.data_ptr(), T)
+        ms.moe_spark_decode_batched(ctx, xm.data_ptr(), 0, B, row.data_ptr())  # build the step graph
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms.moe_spark_decode_batched(ctx, xm.data_ptr(), T, B, row.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t1
+        st = ms.moe_spark_get_stats(ctx)
+        k = tr_k.cpu().numpy()
+        distinct = sum(len(np.unique(k[t0:t0 + B, l])) for t0 in range(0, T, B) for l in range(w.L))
+        steps = (T + B - 1) // B
+        weight_bytes = distinct * EXPERT_BYTES + steps * w.L * w.E * w.d * 4
+        gbps = weight_bytes / dt / 1e9
+        out = dict(batch=B, ring_slots=R, tok_s=round(T / dt, 1), ms_per_step=round(dt * 1e3 / steps, 4),
+                   **rates(st), fills=st["fills"],
+                   distinct_experts_per_layer_step=round(distinct / (steps * w.L), 2),
+                   algorithmic_bytes=weight_bytes, hbm_gbps=round(gbps, 1),
+                   hbm_frac=round(gbps / HBM_PEAK_GBPS, 4),
+                   bit_identical_to_batch1=None if ref_x is None else bool(np.array_equal(xm.cpu().numpy(), ref_x)))
+        log(f"batched B={B}: {out['tok_s']} tok/s, {out['distinct_experts_per_layer_step']} distinct experts "
+            f"per layer-step, {out['hbm_gbps']} GB/s algorithmic, cold {out['cold_hit_pct']}%, "
+            f"bit-identical {out['bit_identical_to_batch1']}")
         return out
     finally:
         ms.moe_spark_destroy(ctx)
@@ -266,6 +315,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the residency sweep")
     ap.add_argument("--no-prefill", action="store_true", help="skip the batched prefill")
     ap.add_argument("--no-autotune", action="store_true", help="skip the popularity-shift self-tuning runs")
+    ap.add_argument("--batches", default="4,16",
+                    help="batched decode step sizes to run beside batch 1 (empty: none)")
     ap.add_argument("--kernel-iters", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -387,6 +438,11 @@ def main():
                                  h2d_gbps=round(s["h2d_bytes"] / r["elapsed_s"] / 1e9, 3),
                                  bit_identical=bool(np.array_equal(r["x_out"], ref))))
         res["sweep"] = rows
+    batches = [int(b) for b in args.batches.split(",") if b.strip()]
+    if batches:
+        ref = full["x_out"] if full is not None else part["x_out"]
+        res["batched"] = [run_batched(ms, torch, model, P, max(R, b * w.K) if P < LE else 0, b, warm, meas, row,
+                                      ref) for b in batches]
     if not args.no_prefill:
         probe = wl.stack(args.layers).tokens(args.warmup + args.steps, 256)
         res["prefill"] = run_prefill(ms, torch, model, P, args.ring, warm, probe, args.layers)

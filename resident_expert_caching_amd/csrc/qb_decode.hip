@@ -1,5 +1,5 @@
 // gfx950 Q4_0 batched decode: B tokens (B <= 16) go through the stack
-// together, one step at a time, three launches per layer.
+// together, one step at a time, four launches per layer.
 //
 //   route   one work-group per token rebuilds its router logits from the
 //           partial dot products of the previous launch, takes the top-k and
@@ -10,13 +10,16 @@
 //           finish runs the placement policy of the same page's paragraph
 //           "The key components" over the step's accesses in (token, rank)
 //           order, and groups the accesses by distinct expert.
-//   gateup  work-group (g, j) streams rows 16g..16g+15 of the gate and up
-//           matrices of distinct expert j once and applies them to every
-//           token of the step that chose the expert.
-//   down    work-group p computes output rows 16p..16p+15 of every access's
-//           down GEMV (an expert chosen by several tokens is re-read from L2),
-//           the gate-weighted combine in rank order, the residual, and the
-//           next layer's router partials of every token over those rows.
+//   gateup  work-group (g, y) streams rows 16g..16g+15 of the gate and up
+//           matrices of a work item's expert (up to 4 of the tokens that
+//           chose it) and applies them to each of those tokens; a popular
+//           expert's items re-read its rows from L2.
+//   down    work-group (p, s) computes output rows 16p..16p+15 of the down
+//           GEMV of 16 accesses (an expert chosen by several tokens is
+//           re-read from L2).
+//   combine work-group p does the gate-weighted combine of those rows in rank
+//           order, the residual, and the next layer's router partials of
+//           every token over them.
 //
 // Per token, every value is formed by the same operations in the same order
 // as in the batch-1 kernels, so a token's outputs do not depend on the batch
@@ -33,7 +36,9 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPhase = 8;  // tokens whose activations a gate/up work-group stages in LDS at once
+constexpr int kDownSlice = 16;  // accesses per down work-group
+constexpr int kGURowsMax = 64;  // work-item rows of the gate/up grid (more items loop)
+typedef __attribute__((address_space(4))) const BatchSel ConstSel;
 static_assert(kNP == 128, "the route kernel sums the partial squares with two loads per lane");
 static_assert(kMaxBK <= kThreads, "one thread per access in the route kernel's policy pass");
 
@@ -115,10 +120,13 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
     __shared__ float s_g[kMaxK];
     __shared__ float s_z;
     __shared__ int s_last;
+    __shared__ int32_t sof[kMaxE];
 
-    // every routing load first (x, partial squares, partial logits, bias)
+    // every routing load first (x, slot-table row, partial squares, partial
+    // logits, bias)
     const f32x4* x4 = reinterpret_cast<const f32x4*>(a.xb + (int64_t)b * kQD);
     const f32x4 xv0 = x4[t], xv1 = x4[t + kThreads];
+    const int32_t sof0 = t < E ? a.pt.slot_of[(int64_t)a.layer * E + t] : -1;
     const float* psb = a.ps + (int64_t)b * kNP;
     const float ps0 = psb[lane], ps1 = psb[lane + 64];
     const float* plb = a.pl + (int64_t)b * kNP * E;
@@ -139,6 +147,8 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
     // x transposed through LDS: Q4_0 block q at float 36q
     *reinterpret_cast<f32x4*>(&xt[36 * (t >> 3) + 4 * (t & 7)]) = xv0;
     *reinterpret_cast<f32x4*>(&xt[36 * ((t + kThreads) >> 3) + 4 * (t & 7)]) = xv1;
+    if (t < E) sof[t] = sof0;
+    for (int e = t + kThreads; e < E; e += kThreads) sof[e] = a.pt.slot_of[(int64_t)a.layer * E + e];
     const float ss = wave_sum(ps0 + ps1);
     const float inv = a.norm ? 1.0f / sqrtf(ss / (float)kQD + a.eps) : 1.0f;
     // logit = inv * (the 128 partials: 32 in row order per lane, then the
@@ -185,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
             const float myg = s_g[lane];
             sel->idx[b * K + lane] = myk;
             sel->gate[b * K + lane] = myg;
+            sel->slot[b * K + lane] = sof[myk];  // its pinned slot or -1, for the policy
             atomicAdd(reinterpret_cast<unsigned long long*>(a.pt.counts + (int64_t)a.layer * E + myk), 1ull);
             if (a.tr_topk && ttok < a.tr_cap) {
                 const int64_t o = ((int64_t)ttok * a.L + a.layer) * K + lane;
@@ -235,6 +246,7 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
     __shared__ int32_t s_pre[kMaxE / 32];
     __shared__ int32_t s_cnt[kMaxBK];
     __shared__ int32_t s_off[kMaxBK + 1];
+    __shared__ int32_t s_ioff[kMaxBK + 1];
     __shared__ int s_D, s_cold;
     __shared__ int32_t r_owner[kMaxR];
     __shared__ uint64_t r_stamp[kMaxR];
@@ -251,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
     int e_t = -1, pin_t = -1;
     if (t < n) {
         e_t = __hip_atomic_load(&sel->idx[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        pin_t = a.pt.slot_of[(int64_t)a.layer * E + e_t];
+        pin_t = __hip_atomic_load(&sel->slot[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_idx[t] = e_t;
         s_pin[t] = pin_t;
     }
@@ -293,6 +305,19 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
         s_off[2 * lane + 1] = excl + c0;
         if (lane == 63) s_off[kMaxBK] = incl;
     }
+    if (w == 2) {  // work-item offsets: the same prefix over ceil(count / kItemTok)
+        const int c0 = (s_cnt[2 * lane] + kItemTok - 1) / kItemTok, c1 = (s_cnt[2 * lane + 1] + kItemTok - 1) / kItemTok;
+        int incl = c0 + c1;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const int o = __shfl_up(incl, m, 64);
+            if (lane >= m) incl += o;
+        }
+        const int excl = incl - (c0 + c1);
+        s_ioff[2 * lane] = excl;
+        s_ioff[2 * lane + 1] = excl + c0;
+        if (lane == 63) s_ioff[kMaxBK] = incl;
+    }
     if (w == 1) {
         // the policy, one access at a time in (token, rank) order
         RingState rs{};
@@ -328,36 +353,44 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
             sel->dslot[rank] = s_slot[t];
             sel->dwait[rank] = s_wseq[t];
         }
+        const int item = s_ioff[rank] + pos / kItemTok;
+        sel->item_acc[item][pos % kItemTok] = t;
+        if (pos % kItemTok == 0) {
+            const int left = s_cnt[rank] - pos;
+            sel->item_j[item] = rank;
+            sel->item_n[item] = left < kItemTok ? left : kItemTok;
+        }
     }
     if (t <= D) sel->doff[t] = t < D ? s_off[t] : n;
-    if (t == 0) sel->D = D;
+    if (t == 0) {
+        sel->D = D;
+        sel->NI = s_ioff[kMaxBK];
+    }
 }
 
 // ---------------------------------------------------------------- gate/up
 
-// Grid (f/16, min(B*K, E)).  Work-group (g, j) owns rows 16g..16g+15 of the
-// gate and up matrices of distinct expert j (waves 0, 1 gate rows, waves 2, 3
-// up rows, 8 rows per wave, lane q = Q4_0 block q along d), decodes its codes
-// to fp16 pairs once, and applies them to each token that chose the expert.
-__global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
+// Rows 16g..16g+15 of the gate and up matrices of one work item's expert
+// (waves 0, 1 gate rows, waves 2, 3 up rows, 8 rows per wave, lane q = Q4_0
+// block q along d), applied to the item's tokens (at most kItemTok).
+__device__ __forceinline__ void qb_gateup_item(const QBArgs& a, const ConstSel* sel, int g, int it,
+                                               u32x4 (*s_ua)[kThreads], float (*s_ub)[64], float (*red)[32]) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int g = blockIdx.x, j = blockIdx.y;
-    const BatchSel* sel = a.sel;
-    const int D = sel->D;
-    if (j >= D) return;
     const int K = a.K;
+    const int j = sel->item_j[it], cn = sel->item_n[it];
+    const bool first_item = it == 0 || sel->item_j[it - 1] != j;
     const int e = sel->dexp[j], slot = sel->dslot[j];
     const uint64_t wseq = sel->dwait[j];
-    const int c0 = sel->doff[j], cn = sel->doff[j + 1] - c0;
+    int acc_i[kItemTok];
+#pragma unroll
+    for (int q = 0; q < kItemTok; ++q) acc_i[q] = sel->item_acc[it][q];  // entries past cn: not used
 
-    __shared__ __align__(16) u32x4 s_ua[kPhase][kThreads];
-    __shared__ float s_ub[kPhase][64];
-    __shared__ float red[kMaxB][32];
-
-    if (slot < 0 || slot >= a.n_slots || cn < 1 || cn > kMaxB) {  // never expected: refuse rather than fault
+    if (slot < 0 || slot >= a.n_slots || cn < 1 || cn > kItemTok) {  // never expected: refuse rather than fault
         if (t == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
         return;
     }
+    // a fill made in this step: pulled from the host arena by every item of
+    // the expert, written into the ring slot by the first item's work-groups
     const bool pull = a.pt.pull && wseq && slot >= a.P;
     if (wseq && slot >= a.P && !pull) {  // wait for the host agent's copy
         if (t == 0) {
@@ -385,29 +418,28 @@ __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
     for (int i = 0; i < 8; ++i) c[i] = __builtin_nontemporal_load(cp + i * 64);
     const u32x4 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(chunk + 32768) + w * 64 + lane);
 
-    // the first tokens' activations, while the weights are in flight
-    auto stage = [&](int n0) {
-        u32x4 st[kPhase];
-        float su[kPhase];
+    // the tokens' fp16 pairs and block sums, while the weights are in flight
+    {
+        u32x4 st[kItemTok];
+        float su[kItemTok];
 #pragma unroll
-        for (int q = 0; q < kPhase; ++q) {
-            if (n0 + q < cn) {
-                const int bq = sel->dent[c0 + n0 + q] / K;
+        for (int q = 0; q < kItemTok; ++q) {
+            if (q < cn) {
+                const int bq = acc_i[q] / K;
                 st[q] = reinterpret_cast<const u32x4*>(a.ua + (int64_t)bq * 64 * 16)[t];
                 if (t < 64) su[q] = a.ub[(int64_t)bq * 64 + t];
             }
         }
 #pragma unroll
-        for (int q = 0; q < kPhase; ++q) {
-            if (n0 + q < cn) {
+        for (int q = 0; q < kItemTok; ++q) {
+            if (q < cn) {
                 s_ua[q][t] = st[q];
                 if (t < 64) s_ub[q][t] = su[q];
             }
         }
-    };
-    stage(0);
+    }
 
-    if (pull) {
+    if (pull && first_item) {
         // the fill: this chunk of gate/up rows as read, plus 1/32 of the down
         // region, into the ring slot (read by the down launch and later hits)
         uint8_t* dst = a.slots + (int64_t)slot * a.slot_bytes;
@@ -443,149 +475,165 @@ __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
     }
     __syncthreads();
 
-    for (int n0 = 0; n0 < cn; n0 += kPhase) {
-        if (n0) {
-            __syncthreads();  // every wave is done with the previous phase
-            stage(n0);
-            __syncthreads();
-        }
-        const int np = cn - n0 < kPhase ? cn - n0 : kPhase;
-        for (int q = 0; q < np; ++q) {
-            // this lane's block: 16 fp16 pairs, read as words
-            const uint32_t* up = reinterpret_cast<const uint32_t*>(&s_ua[q][lane * 4]);
-            f16x2 ua[16];
+    // all the item's tokens at once, so their reduction trees' cross-lane
+    // steps are in flight together
+    float v[kItemTok][8];
 #pragma unroll
-            for (int pp = 0; pp < 16; ++pp) ua[pp] = __builtin_bit_cast(f16x2, up[pp]);
-            const float UO = kQ4Offset * s_ub[q][lane];
-            float v[8];
+    for (int u = 0; u < kItemTok; ++u) {
+        const int q = u < cn ? u : cn - 1;  // past the item: recompute its last token, not stored
+        // this lane's block: 16 fp16 pairs, read as words
+        const uint32_t* up = reinterpret_cast<const uint32_t*>(&s_ua[q][lane * 4]);
+        f16x2 ua[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float acc = 0.0f;
+        for (int pp = 0; pp < 16; ++pp) ua[pp] = __builtin_bit_cast(f16x2, up[pp]);
+        const float UO = kQ4Offset * s_ub[q][lane];
 #pragma unroll
-                for (int pp = 0; pp < 16; ++pp) acc = __builtin_amdgcn_fdot2(wq[i][pp], ua[pp], acc, false);
-                v[i] = sv[i] * (acc - UO);
-            }
-            // 8 rows x 64 lanes -> one row per group of 8 lanes (fixed tree)
-            {
-                const bool h32 = lane & 32;
+        for (int i = 0; i < 8; ++i) {
+            float acc = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float send = h32 ? v[r] : v[r + 4];
-                    const float keep = h32 ? v[r + 4] : v[r];
-                    v[r] = keep + __shfl_xor(send, 32, 64);
-                }
-                const bool h16 = lane & 16;
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const float send = h16 ? v[r] : v[r + 2];
-                    const float keep = h16 ? v[r + 2] : v[r];
-                    v[r] = keep + __shfl_xor(send, 16, 64);
-                }
-                const bool h8 = lane & 8;
-                const float send = h8 ? v[0] : v[1];
-                const float keep = h8 ? v[1] : v[0];
-                v[0] = keep + __shfl_xor(send, 8, 64);
-                v[0] += __shfl_xor(v[0], 4, 64);
-                v[0] += __shfl_xor(v[0], 2, 64);
-                v[0] += __shfl_xor(v[0], 1, 64);
-            }
-            if ((lane & 7) == 0) red[n0 + q][w * 8 + (lane >> 3)] = v[0];
+            for (int pp = 0; pp < 16; ++pp) acc = __builtin_amdgcn_fdot2(wq[i][pp], ua[pp], acc, false);
+            v[u][i] = sv[i] * (acc - UO);
         }
     }
+    // 8 rows x 64 lanes -> one row per group of 8 lanes (fixed tree), per token
+    const bool h32 = lane & 32, h16 = lane & 16, h8 = lane & 8;
+#pragma unroll
+    for (int u = 0; u < kItemTok; ++u) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float send = h32 ? v[u][r] : v[u][r + 4];
+            const float keep = h32 ? v[u][r + 4] : v[u][r];
+            v[u][r] = keep + __shfl_xor(send, 32, 64);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kItemTok; ++u) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float send = h16 ? v[u][r] : v[u][r + 2];
+            const float keep = h16 ? v[u][r + 2] : v[u][r];
+            v[u][r] = keep + __shfl_xor(send, 16, 64);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kItemTok; ++u) {
+        const float send = h8 ? v[u][0] : v[u][1];
+        const float keep = h8 ? v[u][1] : v[u][0];
+        v[u][0] = keep + __shfl_xor(send, 8, 64);
+    }
+#pragma unroll
+    for (int u = 0; u < kItemTok; ++u) v[u][0] += __shfl_xor(v[u][0], 4, 64);
+#pragma unroll
+    for (int u = 0; u < kItemTok; ++u) v[u][0] += __shfl_xor(v[u][0], 2, 64);
+#pragma unroll
+    for (int u = 0; u < kItemTok; ++u) v[u][0] += __shfl_xor(v[u][0], 1, 64);
+#pragma unroll
+    for (int u = 0; u < kItemTok; ++u)
+        if (u < cn && (lane & 7) == 0) red[u][w * 8 + (lane >> 3)] = v[u][0];
     __syncthreads();
     if (t < 16 * cn) {
         const int q = t >> 4, jr = t & 15;
         const float hv = silu(red[q][jr]) * red[q][16 + jr];
-        const int acc_i = sel->dent[c0 + q];
         // h layout for the down kernel: f32x4 (i*8 + jj)*16 + blk holds h_i[32blk + 4jj .. +3]
         const int rn = g * 16 + jr;
         const int blk = rn >> 5, jj = (rn >> 2) & 7, cc = rn & 3;
-        a.h[(((int64_t)acc_i * 8 + jj) * 16 + blk) * 4 + cc] = hv;
+        a.h[(((int64_t)acc_i[q] * 8 + jj) * 16 + blk) * 4 + cc] = hv;
+    }
+}
+
+// Grid (f/16, min(B*K, 64)): work-group (g, y) takes work items y,
+// y + gridDim.y, ... of the step.
+__global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
+    __shared__ __align__(16) u32x4 s_ua[kItemTok][kThreads];
+    __shared__ float s_ub[kItemTok][64];
+    __shared__ float red[kItemTok][32];
+    // read-only here (written by the route launch): through the constant
+    // address space, so uniform reads go through the scalar cache
+    const ConstSel* sel = (const ConstSel*)a.sel;
+    const int NI = sel->NI;
+    for (int it = blockIdx.y; it < NI; it += gridDim.y) {
+        if (it != (int)blockIdx.y) __syncthreads();  // LDS reuse
+        qb_gateup_item(a, sel, blockIdx.x, it, s_ua, s_ub, red);
     }
 }
 
 // ---------------------------------------------------------------- down + combine + next router partials
 
-// Grid kNP.  Work-group p owns output rows 16p..16p+15.  Thread t: access
-// group (t >> 5), row half ((t >> 4) & 1), Q4_0 block (t & 15) along f; 8 rows
-// each.  Group q takes accesses q, q+8, ..., and loads the next one's codes,
-// scales and h while it computes the current one.
+// Grid (kNP, ceil(B*K/16)).  Work-group (p, s) computes output rows
+// 16p..16p+15 of accesses 16s..16s+15: thread t takes access 16s + (t >> 5)
+// and access 16s + 8 + (t >> 5), row half ((t >> 4) & 1), Q4_0 block (t & 15)
+// along f, 8 rows each; both accesses' codes, scales and h are loaded
+// together.  The per-access rows go to zb for the combine launch (a kernel
+// boundary is the cheaper hand-over here: a release fence at device scope in
+// each of a thousand work-groups writes back L2 every time).
 __global__ __launch_bounds__(kThreads) void qb_down_kernel(QBArgs a) {
     const int t = threadIdx.x, lane = t & 63;
-    const int p = blockIdx.x;
+    const int p = blockIdx.x, s = blockIdx.y;
     const int kq = t >> 5, half = (lane >> 4) & 1, blk = lane & 15;
     const int r0 = p * kRW + half * 8;
     const int nb = *a.nb;
     const int K = a.K, n = nb * K;
+    const int n_slices = (n + kDownSlice - 1) / kDownSlice;
+    if (s >= n_slices) return;
     const BatchSel* sel = a.sel;
 
-    __shared__ float zs[kMaxBK][kRW];
-    __shared__ float xn[kMaxB][kRW];
-    __shared__ float s_g[kMaxBK];
-
-    f32x4 wpre[4];
-    qb_load_wpre(a, p, wpre);
-    const int tb = t >> 4, tr = t & 15;  // combine: token tb, row tr
-    float xr = 0.0f;
-    if (tb < nb) xr = a.xb[(int64_t)tb * kQD + p * kRW + tr];
-    if (t < n) s_g[t] = sel->gate[t];
-
     const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
-    auto load = [&](int i, u32x4* c, u32x2& s0, u32x2& s1, f32x4* hh, bool& ok) {
-        const int slot = sel->slot[i];
-        ok = slot >= 0 && slot < a.n_slots;
+    u32x4 c[2][8];
+    u32x2 sc[2][2];
+    f32x4 hh[2][8];
+    bool ok[2] = {false, false};
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) hh[jj] = h4[((int64_t)i * 8 + jj) * 16 + blk];
-        if (ok) {
-            const uint8_t* base = a.slots + (int64_t)slot * a.slot_bytes + kGURegion;
+    for (int q = 0; q < 2; ++q) {
+        const int i = s * kDownSlice + q * 8 + kq;
+        if (i < n) {
+            const int slot = sel->slot[i];
+            ok[q] = slot >= 0 && slot < a.n_slots;
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                c[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + r) * 256) + blk);
-            s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + blk);
-            s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + ((r0 >> 2) + 1) * 16 + blk);
+            for (int jj = 0; jj < 8; ++jj) hh[q][jj] = h4[((int64_t)i * 8 + jj) * 16 + blk];
+            if (ok[q]) {
+                const uint8_t* base = a.slots + (int64_t)slot * a.slot_bytes + kGURegion;
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    c[q][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + r) * 256) + blk);
+                sc[q][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + blk);
+                sc[q][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + ((r0 >> 2) + 1) * 16 + blk);
+            } else if (blk == 0 && half == 0) {
+                atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
+            }
         }
-    };
-    u32x4 c[8];
-    u32x2 s0 = {0u, 0u}, s1 = {0u, 0u};
-    f32x4 hh[8];
-    bool ok = false;
-    if (kq < n) load(kq, c, s0, s1, hh, ok);
-    for (int i = kq; i < n; i += 8) {
-        u32x4 cn_[8];
-        u32x2 sn0 = {0u, 0u}, sn1 = {0u, 0u};
-        f32x4 hn[8];
-        bool okn = false;
-        if (i + 8 < n) load(i + 8, cn_, sn0, sn1, hn, okn);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = s * kDownSlice + q * 8 + kq;
+        if (i >= n) continue;
         float z[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) z[r] = 0.0f;
-        if (!ok) {
-            if (blk == 0 && half == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
-        } else {
+        if (ok[q]) {
             f16x2 ha[16];
-            const float HO = kQ4Offset * q4_pairs(hh, ha);
-            const uint32_t sw[4] = {s0.x, s0.y, s1.x, s1.y};
+            const float HO = kQ4Offset * q4_pairs(hh[q], ha);
+            const uint32_t sw[4] = {sc[q][0].x, sc[q][0].y, sc[q][1].x, sc[q][1].y};
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const float s = half_bits_to_float(sw[r >> 1] >> ((r & 1) * 16));
-                z[r] = s * (q4_dot(c[r], ha) - HO);
+                const float sv = half_bits_to_float(sw[r >> 1] >> ((r & 1) * 16));
+                z[r] = sv * (q4_dot(c[q][r], ha) - HO);
             }
         }
         // 8 rows x 16 lanes -> one row per pair of lanes (fixed tree)
         {
             const bool h8 = lane & 8;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float send = h8 ? z[q] : z[q + 4];
-                const float keep = h8 ? z[q + 4] : z[q];
-                z[q] = keep + __shfl_xor(send, 8, 64);
+            for (int u = 0; u < 4; ++u) {
+                const float send = h8 ? z[u] : z[u + 4];
+                const float keep = h8 ? z[u + 4] : z[u];
+                z[u] = keep + __shfl_xor(send, 8, 64);
             }
             const bool h4b = lane & 4;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const float send = h4b ? z[q] : z[q + 2];
-                const float keep = h4b ? z[q + 2] : z[q];
-                z[q] = keep + __shfl_xor(send, 4, 64);
+            for (int u = 0; u < 2; ++u) {
+                const float send = h4b ? z[u] : z[u + 2];
+                const float keep = h4b ? z[u + 2] : z[u];
+                z[u] = keep + __shfl_xor(send, 4, 64);
             }
             const bool h2 = lane & 2;
             const float send = h2 ? z[0] : z[1];
@@ -593,22 +641,41 @@ __global__ __launch_bounds__(kThreads) void qb_down_kernel(QBArgs a) {
             z[0] = keep + __shfl_xor(send, 2, 64);
             z[0] += __shfl_xor(z[0], 1, 64);
         }
-        if ((lane & 1) == 0) zs[i][half * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1)] = z[0];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            c[r] = cn_[r];
-            hh[r] = hn[r];
-        }
-        s0 = sn0;
-        s1 = sn1;
-        ok = okn;
+        if ((lane & 1) == 0)
+            a.zb[(int64_t)i * kQD + p * kRW + half * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 +
+                 ((lane >> 1) & 1)] = z[0];
     }
+
+}
+
+// Grid kNP.  Work-group p adds up rows 16p..16p+15 of each token's accesses
+// in rank order (the gate-weighted combine), adds the residual, and writes
+// the next layer's router partials of every token over those rows.
+__global__ __launch_bounds__(kThreads) void qb_combine_kernel(QBArgs a) {
+    const int t = threadIdx.x, p = blockIdx.x;
+    const int nb = *a.nb;
+    const int K = a.K, n = nb * K;
+    const BatchSel* sel = a.sel;
+    __shared__ float xn[kMaxB][kRW];
+    __shared__ float s_g[kMaxBK];
+
+    f32x4 wpre[4];
+    qb_load_wpre(a, p, wpre);
+    const int tb = t >> 4, tr = t & 15;  // token tb, row tr
+    float xr = 0.0f;
+    float zk[kQ4MaxK];
+    if (tb < nb) {
+        xr = a.xb[(int64_t)tb * kQD + p * kRW + tr];
+#pragma unroll
+        for (int kk = 0; kk < kQ4MaxK; ++kk) zk[kk] = kk < K ? a.zb[(int64_t)(tb * K + kk) * kQD + p * kRW + tr] : 0.0f;
+    }
+    if (t < n) s_g[t] = sel->gate[t];
     __syncthreads();
     if (tb < nb) {
         float y = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < kQ4MaxK; ++kk)
-            if (kk < K) y += s_g[tb * K + kk] * zs[tb * K + kk][tr];  // rank order
+            if (kk < K) y += s_g[tb * K + kk] * zk[kk];  // rank order
         const float o = xr + y;
         a.xb[(int64_t)tb * kQD + p * kRW + tr] = o;
         xn[tb][tr] = o;
@@ -688,14 +755,21 @@ hipError_t launch_qb_route(const QBArgs& a, hipStream_t s) {
 
 hipError_t launch_qb_gateup(const QBArgs& a, hipStream_t s) {
     if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE || a.B < 1 || a.B > kMaxB) return hipErrorInvalidValue;
-    const int dmax = a.B * a.K < a.E ? a.B * a.K : a.E;
-    hipLaunchKernelGGL(qb_gateup_kernel, dim3(kQF / kGURows, dmax), dim3(kThreads), 0, s, a);
+    int rows = a.B * a.K < a.E ? a.B * a.K : a.E;
+    rows = rows < kGURowsMax ? rows : kGURowsMax;
+    hipLaunchKernelGGL(qb_gateup_kernel, dim3(kQF / kGURows, rows), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_qb_combine(const QBArgs& a, hipStream_t s) {
+    if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE || a.B < 1 || a.B > kMaxB) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(qb_combine_kernel, dim3(kNP), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_qb_down(const QBArgs& a, hipStream_t s) {
     if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE || a.B < 1 || a.B > kMaxB) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(qb_down_kernel, dim3(kNP), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(qb_down_kernel, dim3(kNP, (a.B * a.K + kDownSlice - 1) / kDownSlice), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

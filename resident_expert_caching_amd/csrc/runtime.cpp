@@ -108,6 +108,7 @@ struct moe_spark_ctx {
     BatchSel* d_bsel = nullptr;     // [L]
     uint32_t* d_bdone = nullptr;    // [1] route launch ticket
     float* d_bh = nullptr;          // [kMaxBK][f]
+    float* d_bz = nullptr;          // [kMaxBK][d]
 
     // batched prefill (allocated when max_tokens > 0)
     uint16_t* d_pu = nullptr;       // [Tmax][d] bf16
@@ -411,7 +412,8 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_ph,
                      ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok,
                      ctx->d_bx,       ctx->d_brows,  ctx->d_bn,     ctx->d_bpl,     ctx->d_bps,
-                     ctx->d_bua,      ctx->d_bub,    ctx->d_bsel,   ctx->d_bdone,   ctx->d_bh};
+                     ctx->d_bua,      ctx->d_bub,    ctx->d_bsel,   ctx->d_bdone,   ctx->d_bh,
+                     ctx->d_bz};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
@@ -699,6 +701,7 @@ QBArgs qb_args(const moe_spark_ctx* ctx, int layer, int wr_layer, int32_t batch)
     a.sel = ctx->d_bsel + layer;
     a.done = ctx->d_bdone;
     a.h = ctx->d_bh;
+    a.zb = ctx->d_bz;
     a.pt = tables(ctx, ctx->pull_fills);
     a.tr_x = ctx->tr_x;
     a.tr_topk = ctx->tr_topk;
@@ -710,7 +713,7 @@ QBArgs qb_args(const moe_spark_ctx* ctx, int layer, int wr_layer, int32_t batch)
 }
 
 // One step of batched decode: the first layer's router partials, then route,
-// gate/up and down per layer, then the step's write-back and staging.
+// gate/up, down and combine per layer, then the step's write-back and staging.
 moe_spark_status launch_step_kernels(moe_spark_ctx* ctx, float* x, const int32_t* bias_row, int32_t batch) {
     const int L = ctx->cfg.n_layers;
     HIPCHK(launch_qb_router_partial(qb_args(ctx, 0, 0, batch), ctx->compute));
@@ -719,6 +722,7 @@ moe_spark_status launch_step_kernels(moe_spark_ctx* ctx, float* x, const int32_t
         HIPCHK(launch_qb_route(a, ctx->compute));
         HIPCHK(launch_qb_gateup(a, ctx->compute));
         HIPCHK(launch_qb_down(a, ctx->compute));
+        HIPCHK(launch_qb_combine(a, ctx->compute));
     }
     HIPCHK(launch_qb_end(batch_io(ctx, x, bias_row, batch), ctx->compute));
     return MOE_SPARK_OK;
@@ -881,6 +885,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_bsel, (size_t)L) == hipSuccess;
         ok &= dalloc(&ctx->d_bdone, 1) == hipSuccess;
         ok &= dalloc(&ctx->d_bh, (size_t)kMaxBK * f) == hipSuccess;
+        ok &= dalloc(&ctx->d_bz, (size_t)kMaxBK * d) == hipSuccess;
     }
     if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "device table allocation failed");
     if (c.max_tokens > 0) {
@@ -947,6 +952,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= hipMemset(ctx->d_bsel, 0, sizeof(BatchSel) * L) == hipSuccess;
         ok &= hipMemset(ctx->d_bdone, 0, sizeof(uint32_t)) == hipSuccess;
         ok &= hipMemset(ctx->d_bh, 0, sizeof(float) * kMaxBK * f) == hipSuccess;
+        ok &= hipMemset(ctx->d_bz, 0, sizeof(float) * kMaxBK * d) == hipSuccess;
     }
     for (auto& ev : ctx->tok_ev) ok &= hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess;
     ok &= hipDeviceSynchronize() == hipSuccess;

@@ -3,6 +3,8 @@
  * Decode of the 40-layer stack (d=2048, 256 experts, top-8, f=512, Q4_0,
    Zipf routing) at 60% residency with a 32-slot ring, calibrated from a
    256-token warm-up, 128 measured tokens — the configuration bench.py times.
+ * Batched decode of the same stream in steps of 16 tokens (128-slot ring):
+   bit-identical to batch 1, bookkeeping in the batched access order.
  * Batched prefill of 2048 tokens through the same stack at 60% residency,
    the Zipf permutation switching at token 1024, placement calibrated from
    the decode warm-up.
@@ -26,6 +28,7 @@ pytestmark = pytest.mark.gpu
 ms = pytest.importorskip("resident_expert_caching_amd")
 
 WARM, MEAS = 256, 128
+_BATCH1 = {}  # outputs and top-k trace of the batch-1 decode test, for the batched test
 
 
 @pytest.fixture(scope="module")
@@ -117,12 +120,90 @@ def test_decode_full_stack_60pct_calibrated(stack_model):
     for got, ref in zip(pl, sim.placement()):
         assert np.array_equal(got, ref)
     print(f"decode stats {st}", flush=True)
+    _BATCH1.update(x=x_final, trk=trk)
     rows = np.zeros(WARM + MEAS, np.int32)
     rng = np.random.default_rng(7)
     _check_topk_sample(model, trx, trk, rows, None, rng.choice(WARM + MEAS, 24, replace=False))
     samples = [(0, 0), (5, 39), (WARM, 0), (WARM + 1, 20), (WARM + MEAS - 1, 39)] + \
               [(int(t), int(l)) for t, l in zip(rng.integers(0, WARM + MEAS, 5), rng.integers(0, w.L, 5))]
     _check_layer_samples(model, trx, trk, x_final, rows, None, samples, 2e-3, "decode")
+
+
+def _batch1_decode(model, x):
+    """Batch-1 decode of the same stream at full residency (outputs do not
+    depend on residency), when the batch-1 test has not run in this session."""
+    w = model.w
+    ctx = model.make_ctx(P=w.L * w.E, R=0)
+    try:
+        tr_k = torch.zeros((WARM + MEAS, w.L, w.K), dtype=torch.int32, device="cuda")
+        tr_g = torch.zeros_like(tr_k, dtype=torch.float32)
+        ms.moe_spark_set_trace(ctx, None, tr_k.data_ptr(), tr_g.data_ptr(), WARM + MEAS)
+        xd = torch.from_numpy(x.copy()).cuda()
+        ms.moe_spark_decode(ctx, xd.data_ptr(), WARM + MEAS, None)
+        ms.moe_spark_synchronize(ctx)
+        return dict(x=xd.cpu().numpy(), trk=tr_k.cpu().numpy())
+    finally:
+        ms.moe_spark_destroy(ctx)
+
+
+def test_batched_decode_full_stack_16_tokens(stack_model):
+    """The bench's batched configuration: steps of 16 tokens at 60% residency,
+    calibrated, with a ring of 16*8 = 128 slots.  Outputs and top-k are
+    bit-identical to batch-1 decode of the same tokens; bookkeeping equals
+    the simulator in (layer, token, rank) order per step; sampled layer
+    outputs match the oracle, teacher-forced."""
+    model = stack_model
+    w = model.w
+    LE = w.L * w.E
+    B = 16
+    P, R = int(round(0.6 * LE)), B * w.K
+    x = w.tokens(0, WARM + MEAS)
+    ref = _BATCH1 if _BATCH1 else _batch1_decode(model, x)
+    ctx = model.make_ctx(P=P, R=R)
+    try:
+        cap = WARM + MEAS
+        tr_x = torch.zeros((cap, w.L, w.d), dtype=torch.float32, device="cuda")
+        tr_k = torch.zeros((cap, w.L, w.K), dtype=torch.int32, device="cuda")
+        tr_g = torch.zeros((cap, w.L, w.K), dtype=torch.float32, device="cuda")
+        ms.moe_spark_set_trace(ctx, tr_x.data_ptr(), tr_k.data_ptr(), tr_g.data_ptr(), cap)
+        xw = torch.from_numpy(x[:WARM].copy()).cuda()
+        xm = torch.from_numpy(x[WARM:].copy()).cuda()
+        row = torch.zeros(cap, dtype=torch.int32, device="cuda")
+        print("batched decode: warm-up batch-1 under uniform placement", flush=True)
+        ms.moe_spark_decode(ctx, xw.data_ptr(), WARM, row.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        ms.moe_spark_calibrate(ctx, True)
+        ms.moe_spark_reset_stats(ctx)
+        print(f"batched decode: {MEAS} tokens in steps of {B}", flush=True)
+        ms.moe_spark_decode_batched(ctx, xm.data_ptr(), MEAS, B, row.data_ptr())
+        ms.moe_spark_synchronize(ctx)
+        st = ms.moe_spark_get_stats(ctx)
+        ev = events(ctx)
+        pl = placement(ctx, w, R)
+        slot_bytes = ms.moe_spark_slot_bytes(ctx)
+        trx, trk = tr_x.cpu().numpy(), tr_k.cpu().numpy()
+        x_final = np.concatenate([xw.cpu().numpy(), xm.cpu().numpy()])
+    finally:
+        ms.moe_spark_destroy(ctx)
+    assert np.array_equal(trk, ref["trk"])
+    assert np.array_equal(x_final, ref["x"])
+    sim = oracle.Sim(w.L, w.E, P, R, slot_bytes)
+    sim.place_uniform()
+    for t in range(WARM):
+        sim.decode_token(trk[t])
+    sim.calibrate(True)
+    sim.reset_stats()
+    for t0 in range(WARM, WARM + MEAS, B):
+        sim.decode_batch(trk[t0:t0 + B])
+    assert {k: st[k] for k in STAT_KEYS} == sim.stats()
+    assert st["tokens"] == MEAS
+    assert ev == sim_events(sim)
+    for got, ref_pl in zip(pl, sim.placement()):
+        assert np.array_equal(got, ref_pl)
+    print(f"batched decode stats {st}", flush=True)
+    rows = np.zeros(WARM + MEAS, np.int32)
+    samples = [(WARM, 0), (WARM + 7, 19), (WARM + 15, 39), (WARM + MEAS - 1, 39)]
+    _check_layer_samples(model, trx, trk, x_final, rows, None, samples, 2e-3, "batched decode")
 
 
 def test_prefill_full_stack_popularity_shift(stack_model):
