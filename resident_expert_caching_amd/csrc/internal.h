@@ -200,18 +200,15 @@ hipError_t launch_advance(int32_t* cursors, int64_t* stats, hipStream_t s);
 // one step at a time.  Per layer: a route launch (router, top-k and gates per
 // token; the last work-group to finish runs the placement policy over the
 // step's accesses in (token, rank) order and groups them by distinct expert),
-// gate/up and down launches that stream each distinct expert once for all
-// the tokens that chose it, and a combine launch (rank-order combine,
-// residual, next layer's router partials).
+// then gate/up and down launches that stream each distinct expert once for
+// all the tokens that chose it (matrix-core skinny GEMMs); down also does the
+// rank-order combine, the residual and the next layer's router partials.
 constexpr int kMaxB = 16;                 // tokens per step
 constexpr int kMaxBK = kMaxB * kQ4MaxK;   // accesses per layer-step
-constexpr int kItemTok = 4;               // accesses per gate/up work item
 
 // Routing and placement of one layer for the current step.  Accesses are
 // numbered i = b*K + k; distinct experts j = 0..D-1 ascend by expert id and
-// own the accesses dent[doff[j] .. doff[j+1]) in ascending i, which are cut
-// into work items of at most kItemTok accesses (so a popular expert spreads
-// over several gate/up work-groups).
+// own the accesses dent[doff[j] .. doff[j+1]) in ascending i.
 struct BatchSel {
     int32_t idx[kMaxBK];
     float gate[kMaxBK];
@@ -224,11 +221,6 @@ struct BatchSel {
     uint64_t dwait[kMaxBK];  // fill number to wait for or pull (0: resident)
     int32_t doff[kMaxBK + 1];
     int32_t dent[kMaxBK];
-    // gate/up work items: up to kItemTok accesses of one distinct expert
-    int32_t NI;
-    int32_t item_j[kMaxBK];
-    int32_t item_n[kMaxBK];
-    int32_t item_acc[kMaxBK][4];
 };
 
 struct QBArgs {
@@ -244,16 +236,14 @@ struct QBArgs {
     const float* wr_part;     // packed router [kNP][E][kRW] whose partials the launch writes, or null
     const float* bias;        // this layer's router bias [n_bias_rows][E] or null
     int32_t n_bias_rows;
-    uint32_t* ua;             // [B][64 blocks][16] normalised input as fp16 pairs (q4_pairs order)
-    float* ub;                // [B][64] per-block sums of those fp16 values
+    uint16_t* u16;            // [B][d] normalised input, fp16 bits
     uint8_t* slots;
     const uint8_t* arena;
     int64_t slot_bytes, P, n_slots;
     const uint64_t* ready;
     BatchSel* sel;            // this layer's routing and placement
     uint32_t* done;           // last-work-group ticket of the route launch
-    float* h;                 // [B*K][f] SwiGLU output, per access in the down kernel's layout
-    float* zb;                // [B*K][d] each access's down GEMV output
+    uint16_t* h16;            // [B*K][f] SwiGLU output per access, fp16 bits
     PolicyTables pt;
     float* tr_x;              // traces: token b of the step goes to row *trace_base + b
     int32_t* tr_topk;
@@ -282,7 +272,6 @@ hipError_t launch_qb_router_partial(const QBArgs& a, hipStream_t s);
 hipError_t launch_qb_route(const QBArgs& a, hipStream_t s);
 hipError_t launch_qb_gateup(const QBArgs& a, hipStream_t s);
 hipError_t launch_qb_down(const QBArgs& a, hipStream_t s);
-hipError_t launch_qb_combine(const QBArgs& a, hipStream_t s);
 
 // Arguments of the batched-prefill kernels (prefill.hip), one layer.
 struct PfArgs {

@@ -1,29 +1,27 @@
 // gfx950 Q4_0 batched decode: B tokens (B <= 16) go through the stack
-// together, one step at a time, four launches per layer.
+// together, one step at a time, three launches per layer.
 //
 //   route   one work-group per token rebuilds its router logits from the
 //           partial dot products of the previous launch, takes the top-k and
 //           the softmax renormalised over it ("Luce Spark runs 35B MoE models
 //           on 16GB GPU without speed loss", opening paragraph: about 8 of
 //           256 experts per token), counts the choices and stores the
-//           token's normalised input as fp16 pairs.  The last work-group to
-//           finish runs the placement policy of the same page's paragraph
-//           "The key components" over the step's accesses in (token, rank)
-//           order, and groups the accesses by distinct expert.
-//   gateup  work-group (g, y) streams rows 16g..16g+15 of the gate and up
-//           matrices of a work item's expert (up to 4 of the tokens that
-//           chose it) and applies them to each of those tokens; a popular
-//           expert's items re-read its rows from L2.
-//   down    work-group (p, s) computes output rows 16p..16p+15 of the down
-//           GEMV of 16 accesses (an expert chosen by several tokens is
-//           re-read from L2).
-//   combine work-group p does the gate-weighted combine of those rows in rank
-//           order, the residual, and the next layer's router partials of
-//           every token over them.
+//           token's normalised input in fp16.  The last work-group to finish
+//           runs the placement policy of the same page's paragraph "The key
+//           components" over the step's accesses in (token, rank) order, and
+//           groups the accesses by distinct expert.
+//   gateup  work-group (g, j) streams rows 16g..16g+15 of the gate and up
+//           matrices of distinct expert j once, for all the tokens that chose
+//           it: a skinny GEMM on the matrix cores (tokens x rows, the Q4_0
+//           codes decoded exactly to fp16, each block's scale applied in fp32).
+//   down    work-group p computes output rows 16p..16p+15 of every distinct
+//           expert's down GEMV on the matrix cores the same way, then the
+//           gate-weighted combine of each token in rank order, the residual,
+//           and the next layer's router partials of every token over those rows.
 //
-// Per token, every value is formed by the same operations in the same order
-// as in the batch-1 kernels, so a token's outputs do not depend on the batch
-// it runs in nor on where its experts' weights sit.
+// A token's result does not depend on which other tokens share its step nor
+// on where its experts' weights sit: the matrix cores sum each output element
+// in a fixed order, and the combine and the router partials are per token.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -36,8 +34,13 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kDownSlice = 16;  // accesses per down work-group
-constexpr int kGURowsMax = 64;  // work-item rows of the gate/up grid (more items loop)
+constexpr int kGURowsMax = 32;  // distinct-expert rows of the gate/up grid (more experts loop)
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)hi) << 16);
+}
 typedef __attribute__((address_space(4))) const BatchSel ConstSel;
 static_assert(kNP == 128, "the route kernel sums the partial squares with two loads per lane");
 static_assert(kMaxBK <= kThreads, "one thread per access in the route kernel's policy pass");
@@ -204,8 +207,8 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
             }
         }
         if (lane == 0) sel->inv_rms[b] = inv;
-        // lane q: Q4_0 block q of x; the trace row, then the fp16 pairs of
-        // the normalised block and their sum, for the gate/up kernel
+        // lane q: Q4_0 block q of x; the trace row, then the normalised block
+        // rounded to fp16, for the gate/up kernel's matrix-core operand
         f32x4 xx[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) xx[j] = *reinterpret_cast<const f32x4*>(&xt[36 * lane + 4 * j]);
@@ -214,17 +217,13 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) t4[lane * 8 + j] = xx[j];
         }
-        f32x4 uu[8];
+        // matrix-core operand order: 16 bytes h = (u[4h..4h+3], u[16+4h..16+4h+3])
+        u32x4* dst = reinterpret_cast<u32x4*>(a.u16 + ((int64_t)b * kQD + 32 * lane));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) uu[j] = xx[j] * inv;
-        f16x2 ua[16];
-        const float U = q4_pairs(uu, ua);
-        u32x4* dst = reinterpret_cast<u32x4*>(a.ua + ((int64_t)b * 64 + lane) * 16);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            dst[m] = u32x4{__builtin_bit_cast(uint32_t, ua[4 * m]), __builtin_bit_cast(uint32_t, ua[4 * m + 1]),
-                           __builtin_bit_cast(uint32_t, ua[4 * m + 2]), __builtin_bit_cast(uint32_t, ua[4 * m + 3])};
-        a.ub[(int64_t)b * 64 + lane] = U;
+        for (int h = 0; h < 4; ++h) {
+            const f32x4 u0 = xx[h] * inv, u1 = xx[4 + h] * inv;
+            dst[h] = u32x4{pack_f16(u0.x, u0.y), pack_f16(u0.z, u0.w), pack_f16(u1.x, u1.y), pack_f16(u1.z, u1.w)};
+        }
     }
 
     // ---- the last work-group of the step places its accesses
@@ -246,7 +245,6 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
     __shared__ int32_t s_pre[kMaxE / 32];
     __shared__ int32_t s_cnt[kMaxBK];
     __shared__ int32_t s_off[kMaxBK + 1];
-    __shared__ int32_t s_ioff[kMaxBK + 1];
     __shared__ int s_D, s_cold;
     __shared__ int32_t r_owner[kMaxR];
     __shared__ uint64_t r_stamp[kMaxR];
@@ -305,19 +303,6 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
         s_off[2 * lane + 1] = excl + c0;
         if (lane == 63) s_off[kMaxBK] = incl;
     }
-    if (w == 2) {  // work-item offsets: the same prefix over ceil(count / kItemTok)
-        const int c0 = (s_cnt[2 * lane] + kItemTok - 1) / kItemTok, c1 = (s_cnt[2 * lane + 1] + kItemTok - 1) / kItemTok;
-        int incl = c0 + c1;
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const int o = __shfl_up(incl, m, 64);
-            if (lane >= m) incl += o;
-        }
-        const int excl = incl - (c0 + c1);
-        s_ioff[2 * lane] = excl;
-        s_ioff[2 * lane + 1] = excl + c0;
-        if (lane == 63) s_ioff[kMaxBK] = incl;
-    }
     if (w == 1) {
         // the policy, one access at a time in (token, rank) order
         RingState rs{};
@@ -353,44 +338,58 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
             sel->dslot[rank] = s_slot[t];
             sel->dwait[rank] = s_wseq[t];
         }
-        const int item = s_ioff[rank] + pos / kItemTok;
-        sel->item_acc[item][pos % kItemTok] = t;
-        if (pos % kItemTok == 0) {
-            const int left = s_cnt[rank] - pos;
-            sel->item_j[item] = rank;
-            sel->item_n[item] = left < kItemTok ? left : kItemTok;
-        }
     }
     if (t <= D) sel->doff[t] = t < D ? s_off[t] : n;
-    if (t == 0) {
-        sel->D = D;
-        sel->NI = s_ioff[kMaxBK];
-    }
+    if (t == 0) sel->D = D;
 }
 
 // ---------------------------------------------------------------- gate/up
 
-// Rows 16g..16g+15 of the gate and up matrices of one work item's expert
-// (waves 0, 1 gate rows, waves 2, 3 up rows, 8 rows per wave, lane q = Q4_0
-// block q along d), applied to the item's tokens (at most kItemTok).
-__device__ __forceinline__ void qb_gateup_item(const QBArgs& a, const ConstSel* sel, int g, int it,
-                                               u32x4 (*s_ua)[kThreads], float (*s_ub)[64], float (*red)[32]) {
+// Matrix-core operand order inside a Q4_0 block: position p = 8h + i (h = 0..3)
+// holds weight 4h + i for i < 4 and weight 16 + 4h + (i - 4) for i >= 4, so that
+// the four code bytes 4h..4h+3 of a row supply one lane's eight values (low
+// nibbles, then high nibbles).  Activations are stored in the same order.
+__device__ __forceinline__ int mfma_pos(int k) {  // position of weight k (0..31) of a block
+    return (k & 16) ? 8 * ((k - 16) >> 2) + 4 + (k & 3) : 8 * (k >> 2) + (k & 3);
+}
+
+// One lane's eight weights of a block as fp16 (q - 8), exact: code word w
+// (bytes 4h..4h+3 of the row's block).  A byte permute sets each code under
+// the byte 0x64, so each fp16 is 1024 + q exactly; subtracting 1032 is exact.
+__device__ __forceinline__ f16x8 q4_word_to_f16x8(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    constexpr uint32_t kHi = 0x64646464u, k01 = 0x04010400u, k23 = 0x04030402u;
+    const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, lo, k01)) - off;
+    const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, lo, k23)) - off;
+    const f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, hi, k01)) - off;
+    const f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, hi, k23)) - off;
+    return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+constexpr int kGUCodeStride = 260;  // words per chunk row in LDS (1 KiB + 16 B: rows fall on distinct banks)
+constexpr int kGUScaleStride = 66;  // fp16 scales per chunk row in LDS
+
+// Rows 16g..16g+15 of the gate (tile 0) and up (tile 1) matrices of distinct
+// expert j, for the tokens that chose it.  The chunk's codes and scales are
+// loaded with coalesced 16-byte loads and staged in LDS; then wave w runs Q4_0
+// blocks 16w..16w+15 on the matrix cores: D[token m][row n] = sum over the
+// block of u[m][k] (q[n][k] - 8), lane layout A[m = lane%16][p = 8(lane/16)+i],
+// B[p][n = lane%16], D[m = 4(lane/16) + r][n], followed by the block's fp16
+// scale of row n in fp32.  The four waves' sums are added in wave order.
+__device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, const ConstSel* sel, int g, int j,
+                                                 uint32_t* s_code, unsigned short* s_sc, float (*red)[2][16][17]) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int K = a.K;
-    const int j = sel->item_j[it], cn = sel->item_n[it];
-    const bool first_item = it == 0 || sel->item_j[it - 1] != j;
     const int e = sel->dexp[j], slot = sel->dslot[j];
     const uint64_t wseq = sel->dwait[j];
-    int acc_i[kItemTok];
-#pragma unroll
-    for (int q = 0; q < kItemTok; ++q) acc_i[q] = sel->item_acc[it][q];  // entries past cn: not used
-
-    if (slot < 0 || slot >= a.n_slots || cn < 1 || cn > kItemTok) {  // never expected: refuse rather than fault
+    const int c0 = sel->doff[j], cn = sel->doff[j + 1] - c0;
+    if (slot < 0 || slot >= a.n_slots || cn < 1 || cn > kMaxB) {  // never expected: refuse rather than fault
         if (t == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
         return;
     }
-    // a fill made in this step: pulled from the host arena by every item of
-    // the expert, written into the ring slot by the first item's work-groups
+    // a fill made in this step: read from the host arena and copied into the
+    // ring slot by this expert's work-groups (chunk g and 1/32 of the down rows)
     const bool pull = a.pt.pull && wseq && slot >= a.P;
     if (wseq && slot >= a.P && !pull) {  // wait for the host agent's copy
         if (t == 0) {
@@ -408,40 +407,24 @@ __device__ __forceinline__ void qb_gateup_item(const QBArgs& a, const ConstSel* 
         __syncthreads();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
     }
-
     const int64_t key = (int64_t)a.layer * a.E + e;
     const uint8_t* chunk = (pull ? a.arena + key * a.slot_bytes : a.slots + (int64_t)slot * a.slot_bytes) +
                            (int64_t)g * kGUChunk;
+    // wave w loads chunk rows 8w..8w+7, lane = block (one coalesced 1 KiB line per row)
     const u32x4* cp = reinterpret_cast<const u32x4*>(chunk) + w * 8 * 64 + lane;
     u32x4 c[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) c[i] = __builtin_nontemporal_load(cp + i * 64);
     const u32x4 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(chunk + 32768) + w * 64 + lane);
-
-    // the tokens' fp16 pairs and block sums, while the weights are in flight
-    {
-        u32x4 st[kItemTok];
-        float su[kItemTok];
+    // the tokens' activations of this wave's blocks, A rows = tokens
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int tok = l16 < cn ? sel->dent[c0 + l16] / K : -1;
+    f16x8 A[16];
 #pragma unroll
-        for (int q = 0; q < kItemTok; ++q) {
-            if (q < cn) {
-                const int bq = acc_i[q] / K;
-                st[q] = reinterpret_cast<const u32x4*>(a.ua + (int64_t)bq * 64 * 16)[t];
-                if (t < 64) su[q] = a.ub[(int64_t)bq * 64 + t];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < kItemTok; ++q) {
-            if (q < cn) {
-                s_ua[q][t] = st[q];
-                if (t < 64) s_ub[q][t] = su[q];
-            }
-        }
-    }
-
-    if (pull && first_item) {
-        // the fill: this chunk of gate/up rows as read, plus 1/32 of the down
-        // region, into the ring slot (read by the down launch and later hits)
+    for (int bb = 0; bb < 16; ++bb)
+        A[bb] = tok >= 0 ? *reinterpret_cast<const f16x8*>(a.u16 + (int64_t)tok * kQD + (16 * w + bb) * 32 + 8 * kg)
+                         : f16x8{};
+    if (pull) {
         uint8_t* dst = a.slots + (int64_t)slot * a.slot_bytes;
         u32x4* dp = reinterpret_cast<u32x4*>(dst + (int64_t)g * kGUChunk) + w * 8 * 64 + lane;
 #pragma unroll
@@ -452,237 +435,190 @@ __device__ __forceinline__ void qb_gateup_item(const QBArgs& a, const ConstSel* 
         u32x4* ds = reinterpret_cast<u32x4*>(dst + kGURegion) + g * kDownShare;
         for (int i = t; i < kDownShare; i += kThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(hs + i), ds + i);
     }
-
-    // codes -> fp16 (1024 + q) pairs, in the order q4_dot consumes them
-    f16x2 wq[8][16];
-    float sv[8];
+    // stage: row r = 8w + i, block = lane
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(s_code + (8 * w + i) * kGUCodeStride + lane * 4) = c[i];
     {
-        constexpr uint32_t kHi = 0x64646464u, kEven = 0x04020400u, kOdd = 0x04030401u;
         const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t wd[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t lo = wd[m] & 0x0F0F0F0Fu, hi = (wd[m] >> 4) & 0x0F0F0F0Fu;
-                wq[i][4 * m + 0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, lo, kEven));
-                wq[i][4 * m + 1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, lo, kOdd));
-                wq[i][4 * m + 2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, hi, kEven));
-                wq[i][4 * m + 3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kHi, hi, kOdd));
-            }
-            sv[i] = half_bits_to_float(sw[i >> 1] >> ((i & 1) * 16));
-        }
+        for (int i = 0; i < 8; ++i) s_sc[(8 * w + i) * kGUScaleStride + lane] = (unsigned short)(sw[i >> 1] >> ((i & 1) * 16));
     }
     __syncthreads();
-
-    // all the item's tokens at once, so their reduction trees' cross-lane
-    // steps are in flight together
-    float v[kItemTok][8];
+    f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < kItemTok; ++u) {
-        const int q = u < cn ? u : cn - 1;  // past the item: recompute its last token, not stored
-        // this lane's block: 16 fp16 pairs, read as words
-        const uint32_t* up = reinterpret_cast<const uint32_t*>(&s_ua[q][lane * 4]);
-        f16x2 ua[16];
+    for (int bb = 0; bb < 16; ++bb) {
+        const int b = 16 * w + bb;
 #pragma unroll
-        for (int pp = 0; pp < 16; ++pp) ua[pp] = __builtin_bit_cast(f16x2, up[pp]);
-        const float UO = kQ4Offset * s_ub[q][lane];
+        for (int tt = 0; tt < 2; ++tt) {
+            const int r = tt * 16 + l16;  // chunk row: gate rows 0..15, up rows 16..31
+            const f16x8 B = q4_word_to_f16x8(s_code[r * kGUCodeStride + b * 4 + kg]);
+            const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], B, zero, 0, 0, 0);
+            const float s = half_bits_to_float(s_sc[r * kGUScaleStride + b]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int pp = 0; pp < 16; ++pp) acc = __builtin_amdgcn_fdot2(wq[i][pp], ua[pp], acc, false);
-            v[u][i] = sv[i] * (acc - UO);
-        }
-    }
-    // 8 rows x 64 lanes -> one row per group of 8 lanes (fixed tree), per token
-    const bool h32 = lane & 32, h16 = lane & 16, h8 = lane & 8;
-#pragma unroll
-    for (int u = 0; u < kItemTok; ++u) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float send = h32 ? v[u][r] : v[u][r + 4];
-            const float keep = h32 ? v[u][r + 4] : v[u][r];
-            v[u][r] = keep + __shfl_xor(send, 32, 64);
+            for (int q = 0; q < 4; ++q) acc[tt][q] += s * d[q];
         }
     }
 #pragma unroll
-    for (int u = 0; u < kItemTok; ++u) {
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const float send = h16 ? v[u][r] : v[u][r + 2];
-            const float keep = h16 ? v[u][r + 2] : v[u][r];
-            v[u][r] = keep + __shfl_xor(send, 16, 64);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < kItemTok; ++u) {
-        const float send = h8 ? v[u][0] : v[u][1];
-        const float keep = h8 ? v[u][1] : v[u][0];
-        v[u][0] = keep + __shfl_xor(send, 8, 64);
-    }
-#pragma unroll
-    for (int u = 0; u < kItemTok; ++u) v[u][0] += __shfl_xor(v[u][0], 4, 64);
-#pragma unroll
-    for (int u = 0; u < kItemTok; ++u) v[u][0] += __shfl_xor(v[u][0], 2, 64);
-#pragma unroll
-    for (int u = 0; u < kItemTok; ++u) v[u][0] += __shfl_xor(v[u][0], 1, 64);
-#pragma unroll
-    for (int u = 0; u < kItemTok; ++u)
-        if (u < cn && (lane & 7) == 0) red[u][w * 8 + (lane >> 3)] = v[u][0];
+        for (int q = 0; q < 4; ++q) red[w][tt][4 * kg + q][l16] = acc[tt][q];
     __syncthreads();
-    if (t < 16 * cn) {
-        const int q = t >> 4, jr = t & 15;
-        const float hv = silu(red[q][jr]) * red[q][16 + jr];
-        // h layout for the down kernel: f32x4 (i*8 + jj)*16 + blk holds h_i[32blk + 4jj .. +3]
-        const int rn = g * 16 + jr;
-        const int blk = rn >> 5, jj = (rn >> 2) & 7, cc = rn & 3;
-        a.h[(((int64_t)acc_i[q] * 8 + jj) * 16 + blk) * 4 + cc] = hv;
+    {
+        const int m = t >> 4, n = t & 15;  // token m, row n
+        if (m < cn) {
+            const float gt = ((red[0][0][m][n] + red[1][0][m][n]) + red[2][0][m][n]) + red[3][0][m][n];
+            const float ut = ((red[0][1][m][n] + red[1][1][m][n]) + red[2][1][m][n]) + red[3][1][m][n];
+            const int acc_i = sel->dent[c0 + m];
+            const int f = g * 16 + n;  // h index, stored in the down launch's operand order
+            a.h16[(int64_t)acc_i * kQF + (f & ~31) + mfma_pos(f & 31)] =
+                __builtin_bit_cast(unsigned short, (_Float16)(silu(gt) * ut));
+        }
     }
 }
 
-// Grid (f/16, min(B*K, 64)): work-group (g, y) takes work items y,
-// y + gridDim.y, ... of the step.
+// Grid (f/16, min(B*K, E, 32)): work-group (g, y) takes distinct experts
+// y, y + gridDim.y, ... of the step.
 __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
-    __shared__ __align__(16) u32x4 s_ua[kItemTok][kThreads];
-    __shared__ float s_ub[kItemTok][64];
-    __shared__ float red[kItemTok][32];
+    __shared__ __align__(16) uint32_t s_code[32 * kGUCodeStride];
+    __shared__ unsigned short s_sc[32 * kGUScaleStride];
+    __shared__ float red[4][2][16][17];
     // read-only here (written by the route launch): through the constant
     // address space, so uniform reads go through the scalar cache
     const ConstSel* sel = (const ConstSel*)a.sel;
-    const int NI = sel->NI;
-    for (int it = blockIdx.y; it < NI; it += gridDim.y) {
-        if (it != (int)blockIdx.y) __syncthreads();  // LDS reuse
-        qb_gateup_item(a, sel, blockIdx.x, it, s_ua, s_ub, red);
+    const int D = sel->D;
+    for (int j = blockIdx.y; j < D; j += gridDim.y) {
+        if (j != (int)blockIdx.y) __syncthreads();  // LDS reuse
+        qb_gateup_expert(a, sel, blockIdx.x, j, s_code, s_sc, red);
     }
 }
 
 // ---------------------------------------------------------------- down + combine + next router partials
 
-// Grid (kNP, ceil(B*K/16)).  Work-group (p, s) computes output rows
-// 16p..16p+15 of accesses 16s..16s+15: thread t takes access 16s + (t >> 5)
-// and access 16s + 8 + (t >> 5), row half ((t >> 4) & 1), Q4_0 block (t & 15)
-// along f, 8 rows each; both accesses' codes, scales and h are loaded
-// together.  The per-access rows go to zb for the combine launch (a kernel
-// boundary is the cheaper hand-over here: a release fence at device scope in
-// each of a thousand work-groups writes back L2 every time).
-__global__ __launch_bounds__(kThreads) void qb_down_kernel(QBArgs a) {
-    const int t = threadIdx.x, lane = t & 63;
-    const int p = blockIdx.x, s = blockIdx.y;
-    const int kq = t >> 5, half = (lane >> 4) & 1, blk = lane & 15;
-    const int r0 = p * kRW + half * 8;
+constexpr int kDownThreads = 512;
+constexpr int kDCodeStride = 68;  // words per down row in a wave's LDS (256 B + 16 B)
+
+// Grid kNP, 512 threads.  Work-group p owns output rows 16p..16p+15.  Wave w
+// takes distinct experts w, w + 8, ...: it stages the expert's 16 down rows
+// (4 KiB of codes, 512 B of scales, coalesced) in its own LDS, then runs the
+// 16 Q4_0 blocks along f on the matrix cores with the tokens that chose the
+// expert as rows, as in gate/up.  Then the gate-weighted combine of each token
+// in rank order, the residual, and the next layer's router partials of every
+// token over the work-group's rows.
+__global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int p = blockIdx.x;
     const int nb = *a.nb;
-    const int K = a.K, n = nb * K;
-    const int n_slices = (n + kDownSlice - 1) / kDownSlice;
-    if (s >= n_slices) return;
-    const BatchSel* sel = a.sel;
-
-    const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
-    u32x4 c[2][8];
-    u32x2 sc[2][2];
-    f32x4 hh[2][8];
-    bool ok[2] = {false, false};
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int i = s * kDownSlice + q * 8 + kq;
-        if (i < n) {
-            const int slot = sel->slot[i];
-            ok[q] = slot >= 0 && slot < a.n_slots;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) hh[q][jj] = h4[((int64_t)i * 8 + jj) * 16 + blk];
-            if (ok[q]) {
-                const uint8_t* base = a.slots + (int64_t)slot * a.slot_bytes + kGURegion;
-#pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    c[q][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + r) * 256) + blk);
-                sc[q][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + blk);
-                sc[q][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + ((r0 >> 2) + 1) * 16 + blk);
-            } else if (blk == 0 && half == 0) {
-                atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
-            }
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int i = s * kDownSlice + q * 8 + kq;
-        if (i >= n) continue;
-        float z[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) z[r] = 0.0f;
-        if (ok[q]) {
-            f16x2 ha[16];
-            const float HO = kQ4Offset * q4_pairs(hh[q], ha);
-            const uint32_t sw[4] = {sc[q][0].x, sc[q][0].y, sc[q][1].x, sc[q][1].y};
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float sv = half_bits_to_float(sw[r >> 1] >> ((r & 1) * 16));
-                z[r] = sv * (q4_dot(c[q][r], ha) - HO);
-            }
-        }
-        // 8 rows x 16 lanes -> one row per pair of lanes (fixed tree)
-        {
-            const bool h8 = lane & 8;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float send = h8 ? z[u] : z[u + 4];
-                const float keep = h8 ? z[u + 4] : z[u];
-                z[u] = keep + __shfl_xor(send, 8, 64);
-            }
-            const bool h4b = lane & 4;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const float send = h4b ? z[u] : z[u + 2];
-                const float keep = h4b ? z[u + 2] : z[u];
-                z[u] = keep + __shfl_xor(send, 4, 64);
-            }
-            const bool h2 = lane & 2;
-            const float send = h2 ? z[0] : z[1];
-            const float keep = h2 ? z[1] : z[0];
-            z[0] = keep + __shfl_xor(send, 2, 64);
-            z[0] += __shfl_xor(z[0], 1, 64);
-        }
-        if ((lane & 1) == 0)
-            a.zb[(int64_t)i * kQD + p * kRW + half * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 +
-                 ((lane >> 1) & 1)] = z[0];
-    }
-
-}
-
-// Grid kNP.  Work-group p adds up rows 16p..16p+15 of each token's accesses
-// in rank order (the gate-weighted combine), adds the residual, and writes
-// the next layer's router partials of every token over those rows.
-__global__ __launch_bounds__(kThreads) void qb_combine_kernel(QBArgs a) {
-    const int t = threadIdx.x, p = blockIdx.x;
-    const int nb = *a.nb;
-    const int K = a.K, n = nb * K;
-    const BatchSel* sel = a.sel;
+    const int K = a.K, n = nb * K, E = a.E;
+    const ConstSel* sel = (const ConstSel*)a.sel;
+    const int D = sel->D;
+    __shared__ __align__(16) uint32_t s_code[kDownThreads / 64][16 * kDCodeStride];
+    __shared__ float s_sc[kDownThreads / 64][16][17];
+    __shared__ float zs[kMaxBK][kRW + 1];
     __shared__ float xn[kMaxB][kRW];
     __shared__ float s_g[kMaxBK];
 
+    // the next layer's router rows of this work-group's slice: thread t takes
+    // expert t % E (every expert when E divides the thread count)
+    const bool wfix = a.wr_part && (kDownThreads % E) == 0;
     f32x4 wpre[4];
-    qb_load_wpre(a, p, wpre);
-    const int tb = t >> 4, tr = t & 15;  // token tb, row tr
-    float xr = 0.0f;
-    float zk[kQ4MaxK];
-    if (tb < nb) {
-        xr = a.xb[(int64_t)tb * kQD + p * kRW + tr];
+    if (wfix) {
+        const f32x4* w4 = reinterpret_cast<const f32x4*>(a.wr_part + ((int64_t)p * E + t % E) * kRW);
 #pragma unroll
-        for (int kk = 0; kk < kQ4MaxK; ++kk) zk[kk] = kk < K ? a.zb[(int64_t)(tb * K + kk) * kQD + p * kRW + tr] : 0.0f;
+        for (int i = 0; i < 4; ++i) wpre[i] = w4[i];
     }
+    const int tb = t >> 4, tr = t & 15;  // combine: token tb, row tr
+    float xr = 0.0f;
+    if (tb < nb) xr = a.xb[(int64_t)tb * kQD + p * kRW + tr];
     if (t < n) s_g[t] = sel->gate[t];
+
+    const int l16 = lane & 15, kg = lane >> 4;
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t* wcode = s_code[w];
+    for (int j = w; j < D; j += kDownThreads / 64) {
+        const int slot = sel->dslot[j];
+        const int c0 = sel->doff[j], cn = sel->doff[j + 1] - c0;
+        if (slot < 0 || slot >= a.n_slots || cn < 1 || cn > kMaxB) {
+            if (lane == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
+            continue;
+        }
+        const uint8_t* base = a.slots + (int64_t)slot * a.slot_bytes + kGURegion;
+        // rows 16p..16p+15: 4 KiB of codes (lane: row 4q + lane/16, block lane%16) and
+        // 512 B of scales (lane: rows 4(lane/16)..+3, block lane%16)
+        const u32x4* cr = reinterpret_cast<const u32x4*>(base + (int64_t)p * kRW * 256) + lane;
+        u32x4 cc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cc[q] = __builtin_nontemporal_load(cr + q * 64);
+        const u32x2 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + p * 64 + lane);
+        const int acc_m = l16 < cn ? sel->dent[c0 + l16] : -1;  // the access of A row l16
+        f16x8 A[16];
+#pragma unroll
+        for (int bb = 0; bb < 16; ++bb)
+            A[bb] = acc_m >= 0 ? *reinterpret_cast<const f16x8*>(a.h16 + (int64_t)acc_m * kQF + bb * 32 + 8 * kg)
+                               : f16x8{};
+        __builtin_amdgcn_wave_barrier();  // the wave's LDS region is free again
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u32x4*>(wcode + (4 * q + kg) * kDCodeStride + l16 * 4) = cc[q];
+        {
+            const uint32_t sw[4] = {sc.x >> 0, sc.x >> 16, sc.y >> 0, sc.y >> 16};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_sc[w][4 * kg + i][l16] = half_bits_to_float(sw[i]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        f32x4 acc = zero;
+#pragma unroll
+        for (int bb = 0; bb < 16; ++bb) {
+            const f16x8 B = q4_word_to_f16x8(wcode[l16 * kDCodeStride + bb * 4 + kg]);
+            const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[bb], B, zero, 0, 0, 0);
+            const float s = s_sc[w][l16][bb];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] += s * d[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 4 * kg + q;
+            if (m < cn) zs[sel->dent[c0 + m]][l16] = acc[q];
+        }
+    }
     __syncthreads();
     if (tb < nb) {
         float y = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < kQ4MaxK; ++kk)
-            if (kk < K) y += s_g[tb * K + kk] * zk[kk];  // rank order
+            if (kk < K) y += s_g[tb * K + kk] * zs[tb * K + kk][tr];  // rank order
         const float o = xr + y;
         a.xb[(int64_t)tb * kQD + p * kRW + tr] = o;
         xn[tb][tr] = o;
     }
     if (a.wr_part) {
         __syncthreads();
-        for (int b = 0; b < nb; ++b) qb_router_partial(a, b, p, xn[b], wpre);
+        // pl[b][p][e] = sum_i Wr[e][16p+i] xn[b][i]; ps[b][p] = sum_i xn[b][i]^2
+        for (int q = t; q < nb * E; q += kDownThreads) {
+            const int b = q / E, e = q - b * E;
+            f32x4 wv[4];
+            if (wfix) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wv[i] = wpre[i];
+            } else {
+                const f32x4* w4 = reinterpret_cast<const f32x4*>(a.wr_part + ((int64_t)p * E + e) * kRW);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wv[i] = w4[i];
+            }
+            const float* xs = xn[b];
+            float s4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s4[i] = (wv[i].x * xs[4 * i] + wv[i].y * xs[4 * i + 1]) + (wv[i].z * xs[4 * i + 2] + wv[i].w * xs[4 * i + 3]);
+            a.pl[((int64_t)b * kNP + p) * E + e] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        }
+        if (t < nb) {
+            float s2 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kRW; ++i) s2 += xn[t][i] * xn[t][i];
+            a.ps[(int64_t)t * kNP + p] = s2;
+        }
     }
 }
 
@@ -761,15 +697,9 @@ hipError_t launch_qb_gateup(const QBArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_qb_combine(const QBArgs& a, hipStream_t s) {
-    if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE || a.B < 1 || a.B > kMaxB) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(qb_combine_kernel, dim3(kNP), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_qb_down(const QBArgs& a, hipStream_t s) {
     if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE || a.B < 1 || a.B > kMaxB) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(qb_down_kernel, dim3(kNP, (a.B * a.K + kDownSlice - 1) / kDownSlice), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(qb_down_kernel, dim3(kNP), dim3(kDownThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -103,12 +103,10 @@ struct moe_spark_ctx {
     int32_t* d_bn = nullptr;        // [1] tokens in the current step
     float* d_bpl = nullptr;         // [kMaxB][kNP][E]
     float* d_bps = nullptr;         // [kMaxB][kNP]
-    uint32_t* d_bua = nullptr;      // [kMaxB][64][16]
-    float* d_bub = nullptr;         // [kMaxB][64]
+    uint16_t* d_bu16 = nullptr;     // [kMaxB][d] fp16
     BatchSel* d_bsel = nullptr;     // [L]
     uint32_t* d_bdone = nullptr;    // [1] route launch ticket
-    float* d_bh = nullptr;          // [kMaxBK][f]
-    float* d_bz = nullptr;          // [kMaxBK][d]
+    uint16_t* d_bh16 = nullptr;     // [kMaxBK][f] fp16
 
     // batched prefill (allocated when max_tokens > 0)
     uint16_t* d_pu = nullptr;       // [Tmax][d] bf16
@@ -412,8 +410,7 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_ph,
                      ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok,
                      ctx->d_bx,       ctx->d_brows,  ctx->d_bn,     ctx->d_bpl,     ctx->d_bps,
-                     ctx->d_bua,      ctx->d_bub,    ctx->d_bsel,   ctx->d_bdone,   ctx->d_bh,
-                     ctx->d_bz};
+                     ctx->d_bu16,     ctx->d_bsel,   ctx->d_bdone,  ctx->d_bh16};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
@@ -690,8 +687,7 @@ QBArgs qb_args(const moe_spark_ctx* ctx, int layer, int wr_layer, int32_t batch)
     a.wr_part = wr_layer >= 0 ? ctx->d_router + (int64_t)wr_layer * c.n_experts * c.d_model : nullptr;
     a.bias = c.n_bias_rows > 0 ? ctx->d_bias + (int64_t)layer * c.n_bias_rows * c.n_experts : nullptr;
     a.n_bias_rows = c.n_bias_rows;
-    a.ua = ctx->d_bua;
-    a.ub = ctx->d_bub;
+    a.u16 = ctx->d_bu16;
     a.slots = ctx->d_slots;
     a.arena = ctx->d_arena;
     a.slot_bytes = ctx->slot_bytes;
@@ -700,8 +696,7 @@ QBArgs qb_args(const moe_spark_ctx* ctx, int layer, int wr_layer, int32_t batch)
     a.ready = ctx->d_ready;
     a.sel = ctx->d_bsel + layer;
     a.done = ctx->d_bdone;
-    a.h = ctx->d_bh;
-    a.zb = ctx->d_bz;
+    a.h16 = ctx->d_bh16;
     a.pt = tables(ctx, ctx->pull_fills);
     a.tr_x = ctx->tr_x;
     a.tr_topk = ctx->tr_topk;
@@ -713,7 +708,7 @@ QBArgs qb_args(const moe_spark_ctx* ctx, int layer, int wr_layer, int32_t batch)
 }
 
 // One step of batched decode: the first layer's router partials, then route,
-// gate/up, down and combine per layer, then the step's write-back and staging.
+// gate/up and down per layer, then the step's write-back and staging.
 moe_spark_status launch_step_kernels(moe_spark_ctx* ctx, float* x, const int32_t* bias_row, int32_t batch) {
     const int L = ctx->cfg.n_layers;
     HIPCHK(launch_qb_router_partial(qb_args(ctx, 0, 0, batch), ctx->compute));
@@ -722,7 +717,6 @@ moe_spark_status launch_step_kernels(moe_spark_ctx* ctx, float* x, const int32_t
         HIPCHK(launch_qb_route(a, ctx->compute));
         HIPCHK(launch_qb_gateup(a, ctx->compute));
         HIPCHK(launch_qb_down(a, ctx->compute));
-        HIPCHK(launch_qb_combine(a, ctx->compute));
     }
     HIPCHK(launch_qb_end(batch_io(ctx, x, bias_row, batch), ctx->compute));
     return MOE_SPARK_OK;
@@ -880,12 +874,10 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_bn, 1) == hipSuccess;
         ok &= dalloc(&ctx->d_bpl, (size_t)kMaxB * kNP * E) == hipSuccess;
         ok &= dalloc(&ctx->d_bps, (size_t)kMaxB * kNP) == hipSuccess;
-        ok &= dalloc(&ctx->d_bua, (size_t)kMaxB * 64 * 16) == hipSuccess;
-        ok &= dalloc(&ctx->d_bub, (size_t)kMaxB * 64) == hipSuccess;
+        ok &= dalloc(&ctx->d_bu16, (size_t)kMaxB * d) == hipSuccess;
         ok &= dalloc(&ctx->d_bsel, (size_t)L) == hipSuccess;
         ok &= dalloc(&ctx->d_bdone, 1) == hipSuccess;
-        ok &= dalloc(&ctx->d_bh, (size_t)kMaxBK * f) == hipSuccess;
-        ok &= dalloc(&ctx->d_bz, (size_t)kMaxBK * d) == hipSuccess;
+        ok &= dalloc(&ctx->d_bh16, (size_t)kMaxBK * f) == hipSuccess;
     }
     if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "device table allocation failed");
     if (c.max_tokens > 0) {
@@ -951,8 +943,8 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= hipMemset(ctx->d_bn, 0, sizeof(int32_t)) == hipSuccess;
         ok &= hipMemset(ctx->d_bsel, 0, sizeof(BatchSel) * L) == hipSuccess;
         ok &= hipMemset(ctx->d_bdone, 0, sizeof(uint32_t)) == hipSuccess;
-        ok &= hipMemset(ctx->d_bh, 0, sizeof(float) * kMaxBK * f) == hipSuccess;
-        ok &= hipMemset(ctx->d_bz, 0, sizeof(float) * kMaxBK * d) == hipSuccess;
+        ok &= hipMemset(ctx->d_bh16, 0, sizeof(uint16_t) * kMaxBK * f) == hipSuccess;
+        ok &= hipMemset(ctx->d_bu16, 0, sizeof(uint16_t) * kMaxB * d) == hipSuccess;
     }
     for (auto& ev : ctx->tok_ev) ok &= hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess;
     ok &= hipDeviceSynchronize() == hipSuccess;

@@ -5,16 +5,19 @@ Q4_0, Zipf-biased router) decodes 32 warm-up tokens batch-1 under uniform
 placement, is calibrated, and then decodes 45 tokens in steps of B tokens
 (45 is a whole number of steps for B = 1, 3 and ragged for B = 8, 16):
 
- * outputs and top-k are bit-identical to batch-1 decode of the same tokens
-   at full residency (every token's arithmetic is the batch-1 arithmetic);
+ * top-k is identical to batch-1 decode of the same tokens at full residency
+   and outputs agree with it to fp32 rounding (the matrix cores sum in
+   another order than the batch-1 dot products);
+ * outputs are bit-identical for every batch size (a token's result does not
+   depend on the tokens that share its step);
  * bookkeeping — counters, fill/eviction log, pinned set, ring, counts —
    equals the simulator replaying the GPU's own top-k trace with each step's
    accesses in (layer, token, rank) order;
  * sampled (token, layer) outputs match the fp64 oracle, teacher-forced;
  * at 100/60/30% residency with uniform placement and the smallest ring a
    step allows (R = B*K, so one step can turn the whole ring over), with
-   pulled and with host-agent fills, outputs stay bit-identical and
-   bookkeeping exact.
+   pulled and with host-agent fills, outputs stay bit-identical to the other
+   batched runs and bookkeeping exact.
 """
 import os
 
@@ -32,6 +35,8 @@ pytestmark = pytest.mark.gpu
 ms = pytest.importorskip("resident_expert_caching_amd")
 
 WARM, MEAS = 32, 45
+BATCH1_TOL = 2e-3  # max|batched - batch-1| / max|batch-1|: the parity bar; both paths also meet it against the oracle
+_BATCHED = {}      # the first batched run's outputs: every other batched run must match them bitwise
 
 
 @pytest.fixture(scope="module")
@@ -117,9 +122,15 @@ def test_batched_matches_batch1_and_simulator(model, batch1, B):
     print(f"batched decode B={B}: P={P} R={R}, calibrated", flush=True)
     r = _run(model, P, R, B)
     assert np.array_equal(r["tr_k"], batch1["tr_k"])
-    assert np.array_equal(r["x"], batch1["x"])
-    assert np.array_equal(r["tr_x"], batch1["tr_x"])
-    assert np.array_equal(r["tr_g"], batch1["tr_g"])
+    rel = np.abs(r["x"] - batch1["x"]).max() / np.abs(batch1["x"]).max()
+    print(f"B={B}: max|batched - batch-1| / max|x| = {rel:.2e}", flush=True)
+    assert rel <= BATCH1_TOL
+    np.testing.assert_allclose(r["tr_g"], batch1["tr_g"], rtol=BATCH1_TOL, atol=1e-5)
+    if _BATCHED:
+        assert np.array_equal(r["x"], _BATCHED["x"]) and np.array_equal(r["tr_x"], _BATCHED["tr_x"])
+        assert np.array_equal(r["tr_g"], _BATCHED["tr_g"])
+    else:
+        _BATCHED.update(x=r["x"], tr_x=r["tr_x"], tr_g=r["tr_g"])
     ss = _check_bookkeeping(model, r, P, R, B, True)
     print(f"B={B}: {ss}", flush=True)
     # teacher-forced oracle parity of sampled (token, layer) pairs of the batched run
@@ -152,8 +163,10 @@ def test_batched_residency_sweep_uniform(model, batch1, pull):
         RR = R if P < LE else 0
         print(f"batched decode B={B}: P={P} R={RR}, uniform placement, pull={pull}", flush=True)
         r = _run(model, P, RR, B, calibrate=False, pull=pull)
-        assert np.array_equal(r["x"], batch1["x"]), frac
         assert np.array_equal(r["tr_k"], batch1["tr_k"]), frac
+        if not _BATCHED:
+            _BATCHED.update(x=r["x"], tr_x=r["tr_x"], tr_g=r["tr_g"])
+        assert np.array_equal(r["x"], _BATCHED["x"]), frac
         ss = _check_bookkeeping(model, r, P, RR, B, False)
         fills[frac] = ss["fills"]
         if P < LE:

@@ -4,7 +4,9 @@
    Zipf routing) at 60% residency with a 32-slot ring, calibrated from a
    256-token warm-up, 128 measured tokens — the configuration bench.py times.
  * Batched decode of the same stream in steps of 16 tokens (128-slot ring):
-   bit-identical to batch 1, bookkeeping in the batched access order.
+   top-k and sampled layer outputs against the oracle on the batched run's
+   own trace, bookkeeping in the batched access order, and the share of
+   token-layers whose top-k equals batch-1 decode's.
  * Batched prefill of 2048 tokens through the same stack at 60% residency,
    the Zipf permutation switching at token 1024, placement calibrated from
    the decode warm-up.
@@ -148,10 +150,10 @@ def _batch1_decode(model, x):
 
 def test_batched_decode_full_stack_16_tokens(stack_model):
     """The bench's batched configuration: steps of 16 tokens at 60% residency,
-    calibrated, with a ring of 16*8 = 128 slots.  Outputs and top-k are
-    bit-identical to batch-1 decode of the same tokens; bookkeeping equals
-    the simulator in (layer, token, rank) order per step; sampled layer
-    outputs match the oracle, teacher-forced."""
+    calibrated, with a ring of 16*8 = 128 slots.  Bookkeeping equals the
+    simulator in (layer, token, rank) order per step; top-k on sampled tokens
+    and sampled layer outputs match the oracle, teacher-forced; at least 99%
+    of token-layers pick the same experts as batch-1 decode."""
     model = stack_model
     w = model.w
     LE = w.L * w.E
@@ -185,8 +187,12 @@ def test_batched_decode_full_stack_16_tokens(stack_model):
         x_final = np.concatenate([xw.cpu().numpy(), xm.cpu().numpy()])
     finally:
         ms.moe_spark_destroy(ctx)
-    assert np.array_equal(trk, ref["trk"])
-    assert np.array_equal(x_final, ref["x"])
+    # the matrix cores sum in another order than the batch-1 dot products, so
+    # x differs at the 1e-4 level and a router near-tie can pick the other
+    # expert; parity is against the oracle, on the batched run's own trace
+    same = float((trk == ref["trk"]).all(axis=2).mean())
+    print(f"batched decode: top-k identical to batch-1 on {same:.4%} of token-layers", flush=True)
+    assert same >= 0.99
     sim = oracle.Sim(w.L, w.E, P, R, slot_bytes)
     sim.place_uniform()
     for t in range(WARM):
@@ -202,6 +208,8 @@ def test_batched_decode_full_stack_16_tokens(stack_model):
         assert np.array_equal(got, ref_pl)
     print(f"batched decode stats {st}", flush=True)
     rows = np.zeros(WARM + MEAS, np.int32)
+    rng = np.random.default_rng(13)
+    _check_topk_sample(model, trx, trk, rows, None, WARM + rng.choice(MEAS, 16, replace=False))
     samples = [(WARM, 0), (WARM + 7, 19), (WARM + 15, 39), (WARM + MEAS - 1, 39)]
     _check_layer_samples(model, trx, trk, x_final, rows, None, samples, 2e-3, "batched decode")
 
