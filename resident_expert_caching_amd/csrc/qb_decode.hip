@@ -496,11 +496,11 @@ __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
 
 // ---------------------------------------------------------------- down + combine + next router partials
 
-constexpr int kDownThreads = 512;
+constexpr int kDownThreads = 1024;
 constexpr int kDCodeStride = 68;  // words per down row in a wave's LDS (256 B + 16 B)
 
-// Grid kNP, 512 threads.  Work-group p owns output rows 16p..16p+15.  Wave w
-// takes distinct experts w, w + 8, ...: it stages the expert's 16 down rows
+// Grid kNP, 1024 threads.  Work-group p owns output rows 16p..16p+15.  Wave w
+// takes distinct experts w, w + 16, ...: it stages the expert's 16 down rows
 // (4 KiB of codes, 512 B of scales, coalesced) in its own LDS, then runs the
 // 16 Q4_0 blocks along f on the matrix cores with the tokens that chose the
 // expert as rows, as in gate/up.  Then the gate-weighted combine of each token
@@ -519,15 +519,6 @@ __global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
     __shared__ float xn[kMaxB][kRW];
     __shared__ float s_g[kMaxBK];
 
-    // the next layer's router rows of this work-group's slice: thread t takes
-    // expert t % E (every expert when E divides the thread count)
-    const bool wfix = a.wr_part && (kDownThreads % E) == 0;
-    f32x4 wpre[4];
-    if (wfix) {
-        const f32x4* w4 = reinterpret_cast<const f32x4*>(a.wr_part + ((int64_t)p * E + t % E) * kRW);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wpre[i] = w4[i];
-    }
     const int tb = t >> 4, tr = t & 15;  // combine: token tb, row tr
     float xr = 0.0f;
     if (tb < nb) xr = a.xb[(int64_t)tb * kQD + p * kRW + tr];
@@ -581,6 +572,16 @@ __global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
             const int m = 4 * kg + q;
             if (m < cn) zs[sel->dent[c0 + m]][l16] = acc[q];
         }
+    }
+    // the next layer's router rows of this work-group's slice, in flight during
+    // the combine: thread t takes expert t % E (every expert when E divides
+    // the thread count)
+    const bool wfix = a.wr_part && (kDownThreads % E) == 0;
+    f32x4 wpre[4];
+    if (wfix) {
+        const f32x4* w4 = reinterpret_cast<const f32x4*>(a.wr_part + ((int64_t)p * E + t % E) * kRW);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wpre[i] = w4[i];
     }
     __syncthreads();
     if (tb < nb) {
