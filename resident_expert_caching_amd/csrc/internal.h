@@ -198,11 +198,11 @@ hipError_t launch_advance(int32_t* cursors, int64_t* stats, hipStream_t s);
 
 // Batched decode (qb_decode.hip): B tokens advance through the stack together,
 // one step at a time.  Per layer: a route launch (router, top-k and gates per
-// token; the last work-group to finish runs the placement policy over the
-// step's accesses in (token, rank) order and groups them by distinct expert),
-// then gate/up and down launches that stream each distinct expert once for
-// all the tokens that chose it (matrix-core skinny GEMMs); down also does the
-// rank-order combine, the residual and the next layer's router partials.
+// token), then gate/up and down launches that stream each distinct expert once
+// for all the tokens that chose it (matrix-core skinny GEMMs).  Gate/up groups
+// the accesses by distinct expert, and its work-group (0,0) runs the placement
+// policy over them in (token, rank) order; down also does the rank-order
+// combine, the residual and the next layer's router partials.
 constexpr int kMaxB = 16;                 // tokens per step
 constexpr int kMaxBK = kMaxB * kQ4MaxK;   // accesses per layer-step
 
@@ -242,7 +242,7 @@ struct QBArgs {
     int64_t slot_bytes, P, n_slots;
     const uint64_t* ready;
     BatchSel* sel;            // this layer's routing and placement
-    uint32_t* done;           // last-work-group ticket of the route launch
+    uint32_t* pub;            // this layer's flag: slots of cold experts published
     uint16_t* h16;            // [B*K][f] SwiGLU output per access, fp16 bits
     PolicyTables pt;
     float* tr_x;              // traces: token b of the step goes to row *trace_base + b

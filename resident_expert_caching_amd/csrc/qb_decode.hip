@@ -6,14 +6,15 @@
 //           the softmax renormalised over it ("Luce Spark runs 35B MoE models
 //           on 16GB GPU without speed loss", opening paragraph: about 8 of
 //           256 experts per token), counts the choices and stores the
-//           token's normalised input in fp16.  The last work-group to finish
-//           runs the placement policy of the same page's paragraph "The key
-//           components" over the step's accesses in (token, rank) order, and
-//           groups the accesses by distinct expert.
-//   gateup  work-group (g, j) streams rows 16g..16g+15 of the gate and up
-//           matrices of distinct expert j once, for all the tokens that chose
-//           it: a skinny GEMM on the matrix cores (tokens x rows, the Q4_0
-//           codes decoded exactly to fp16, each block's scale applied in fp32).
+//           token's normalised input in fp16.
+//   gateup  every work-group groups the step's accesses by distinct expert;
+//           work-group (0,0) also runs the placement policy of the same
+//           page's paragraph "The key components" over them in (token, rank)
+//           order.  Work-group (g, j) streams rows 16g..16g+15 of the gate and
+//           up matrices of distinct expert j once, for all the tokens that
+//           chose it: a skinny GEMM on the matrix cores (tokens x rows, the
+//           Q4_0 codes decoded exactly to fp16, each block's scale applied in
+//           fp32).
 //   down    work-group p computes output rows 16p..16p+15 of every distinct
 //           expert's down GEMV on the matrix cores the same way, then the
 //           gate-weighted combine of each token in rank order, the residual,
@@ -34,7 +35,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGURowsMax = 32;  // distinct-expert rows of the gate/up grid (more experts loop)
+constexpr int kGURowsMax = 24;  // distinct-expert rows of the gate/up grid (more experts loop)
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
@@ -122,7 +123,6 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
     __shared__ float s_l[kMaxK];
     __shared__ float s_g[kMaxK];
     __shared__ float s_z;
-    __shared__ int s_last;
     __shared__ int32_t sof[kMaxE];
 
     // every routing load first (x, slot-table row, partial squares, partial
@@ -225,122 +225,6 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
             dst[h] = u32x4{pack_f16(u0.x, u0.y), pack_f16(u0.z, u0.w), pack_f16(u1.x, u1.y), pack_f16(u1.z, u1.w)};
         }
     }
-
-    // ---- the last work-group of the step places its accesses
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (t == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (unsigned)nb - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-    __shared__ int32_t s_idx[kMaxBK];
-    __shared__ int32_t s_pin[kMaxBK];
-    __shared__ int32_t s_slot[kMaxBK];
-    __shared__ unsigned long long s_wseq[kMaxBK];
-    __shared__ uint32_t s_bits[kMaxE / 32];
-    __shared__ int32_t s_pre[kMaxE / 32];
-    __shared__ int32_t s_cnt[kMaxBK];
-    __shared__ int32_t s_off[kMaxBK + 1];
-    __shared__ int s_D, s_cold;
-    __shared__ int32_t r_owner[kMaxR];
-    __shared__ uint64_t r_stamp[kMaxR];
-    __shared__ uint64_t r_seq[kMaxR];
-
-    const int n = nb * K;
-    const int nw = (E + 31) >> 5;
-    if (t == 0) {
-        __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_cold = 0;
-    }
-    for (int i = t; i < nw; i += kThreads) s_bits[i] = 0u;
-    if (t < kMaxBK) s_cnt[t] = 0;
-    int e_t = -1, pin_t = -1;
-    if (t < n) {
-        e_t = __hip_atomic_load(&sel->idx[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        pin_t = __hip_atomic_load(&sel->slot[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_idx[t] = e_t;
-        s_pin[t] = pin_t;
-    }
-    __syncthreads();
-    if (t < n) {
-        atomicOr(&s_bits[e_t >> 5], 1u << (e_t & 31));
-        if (pin_t < 0) s_cold = 1;
-    }
-    __syncthreads();
-    if (w == 0) {  // exclusive prefix of the per-word popcounts: rank of an expert among the distinct
-        const int c = lane < nw ? __popc(s_bits[lane]) : 0;
-        int incl = c;
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const int o = __shfl_up(incl, m, 64);
-            if (lane >= m) incl += o;
-        }
-        if (lane < nw) s_pre[lane] = incl - c;
-        if (lane == 63) s_D = incl;
-    }
-    __syncthreads();
-    int rank = 0, pos = 0;
-    if (t < n) {
-        rank = s_pre[e_t >> 5] + __popc(s_bits[e_t >> 5] & ((1u << (e_t & 31)) - 1u));
-        for (int i = 0; i < t; ++i) pos += s_idx[i] == e_t;  // earlier accesses of the same expert
-        atomicAdd(&s_cnt[rank], 1);
-    }
-    __syncthreads();
-    if (w == 0) {  // group offsets: exclusive prefix over the distinct experts, two per lane
-        const int c0 = s_cnt[2 * lane], c1 = s_cnt[2 * lane + 1];
-        int incl = c0 + c1;
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const int o = __shfl_up(incl, m, 64);
-            if (lane >= m) incl += o;
-        }
-        const int excl = incl - (c0 + c1);
-        s_off[2 * lane] = excl;
-        s_off[2 * lane + 1] = excl + c0;
-        if (lane == 63) s_off[kMaxBK] = incl;
-    }
-    if (w == 1) {
-        // the policy, one access at a time in (token, rank) order
-        RingState rs{};
-        if (!s_cold) {
-            for (int i = lane; i < n; i += 64) {
-                s_slot[i] = s_pin[i];
-                s_wseq[i] = 0ull;
-            }
-            rs.n_pin = n;
-        } else {
-            ring_load(a.pt, r_owner, r_stamp, r_seq, rs);
-#pragma nounroll
-            for (int i = 0; i < n; ++i) {
-                int slot;
-                uint64_t wseq;
-                ring_access(a.pt, a.layer, s_idx[i], s_pin[i], r_owner, r_stamp, r_seq, rs, slot, wseq);
-                if (lane == 0) {
-                    s_slot[i] = slot;
-                    s_wseq[i] = wseq;
-                }
-            }
-            ring_store(a.pt, r_owner, r_stamp, r_seq, rs);
-        }
-        stats_flush(a.pt, n, rs);
-    }
-    __syncthreads();
-    const int D = s_D;
-    if (t < n) {
-        sel->slot[t] = s_slot[t];
-        sel->dent[s_off[rank] + pos] = t;
-        if (pos == 0) {  // the expert's first access: its slot, and the fill it made (if any)
-            sel->dexp[rank] = e_t;
-            sel->dslot[rank] = s_slot[t];
-            sel->dwait[rank] = s_wseq[t];
-        }
-    }
-    if (t <= D) sel->doff[t] = t < D ? s_off[t] : n;
-    if (t == 0) sel->D = D;
 }
 
 // ---------------------------------------------------------------- gate/up
@@ -377,13 +261,11 @@ constexpr int kGUScaleStride = 66;  // fp16 scales per chunk row in LDS
 // block of u[m][k] (q[n][k] - 8), lane layout A[m = lane%16][p = 8(lane/16)+i],
 // B[p][n = lane%16], D[m = 4(lane/16) + r][n], followed by the block's fp16
 // scale of row n in fp32.  The four waves' sums are added in wave order.
-__device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, const ConstSel* sel, int g, int j,
-                                                 uint32_t* s_code, unsigned short* s_sc, float (*red)[2][16][17]) {
+__device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, int e, int slot, uint64_t wseq, int cn,
+                                                 const int32_t* dent, int g, uint32_t* s_code, unsigned short* s_sc,
+                                                 float (*red)[2][16][17]) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int K = a.K;
-    const int e = sel->dexp[j], slot = sel->dslot[j];
-    const uint64_t wseq = sel->dwait[j];
-    const int c0 = sel->doff[j], cn = sel->doff[j + 1] - c0;
     if (slot < 0 || slot >= a.n_slots || cn < 1 || cn > kMaxB) {  // never expected: refuse rather than fault
         if (t == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
         return;
@@ -418,7 +300,7 @@ __device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, const ConstSel
     const u32x4 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(chunk + 32768) + w * 64 + lane);
     // the tokens' activations of this wave's blocks, A rows = tokens
     const int l16 = lane & 15, kg = lane >> 4;
-    const int tok = l16 < cn ? sel->dent[c0 + l16] / K : -1;
+    const int tok = l16 < cn ? dent[l16] / K : -1;
     f16x8 A[16];
 #pragma unroll
     for (int bb = 0; bb < 16; ++bb)
@@ -470,7 +352,7 @@ __device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, const ConstSel
         if (m < cn) {
             const float gt = ((red[0][0][m][n] + red[1][0][m][n]) + red[2][0][m][n]) + red[3][0][m][n];
             const float ut = ((red[0][1][m][n] + red[1][1][m][n]) + red[2][1][m][n]) + red[3][1][m][n];
-            const int acc_i = sel->dent[c0 + m];
+            const int acc_i = dent[m];
             const int f = g * 16 + n;  // h index, stored in the down launch's operand order
             a.h16[(int64_t)acc_i * kQF + (f & ~31) + mfma_pos(f & 31)] =
                 __builtin_bit_cast(unsigned short, (_Float16)(silu(gt) * ut));
@@ -478,19 +360,170 @@ __device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, const ConstSel
     }
 }
 
-// Grid (f/16, min(B*K, E, 32)): work-group (g, y) takes distinct experts
-// y, y + gridDim.y, ... of the step.
+// Grid (f/16, min(B*K, E, 24)).  Every work-group groups the step's accesses
+// by distinct expert (ascending id; each expert's accesses in (token, rank)
+// order) from the route launch's selections, then takes distinct experts
+// y, y + gridDim.y, ...  Work-group (0,0) also runs the placement policy over
+// the accesses in (token, rank) order — the paragraph "The key components":
+// pinned set, LRU spare ring, fills — writes the grouping and the slots for
+// the down launch, and publishes the slots only when some expert is cold;
+// only cold experts' work-groups wait for that.
 __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
-    __shared__ __align__(16) uint32_t s_code[32 * kGUCodeStride];
+    __shared__ __align__(16) uint32_t s_code[32 * kGUCodeStride];  // work-group (0,0): the ring tables first
     __shared__ unsigned short s_sc[32 * kGUScaleStride];
     __shared__ float red[4][2][16][17];
-    // read-only here (written by the route launch): through the constant
-    // address space, so uniform reads go through the scalar cache
-    const ConstSel* sel = (const ConstSel*)a.sel;
-    const int D = sel->D;
+    __shared__ int32_t s_idx[kMaxBK], s_pin[kMaxBK], s_cnt[kMaxBK], s_off[kMaxBK + 1], s_dexp[kMaxBK],
+        s_dent[kMaxBK], s_slot[kMaxBK];
+    __shared__ unsigned long long s_wseq[kMaxBK];
+    __shared__ uint32_t s_bits[kMaxE / 32];
+    __shared__ int32_t s_pre[kMaxE / 32];
+    __shared__ int s_D, s_cold, s_jslot;
+    __shared__ unsigned long long s_jwait;
+    static_assert(sizeof(s_code) >= kMaxR * (4 + 8 + 8), "the ring tables fit in the code staging area");
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    BatchSel* sel = a.sel;
+    const int nb = *a.nb, K = a.K, E = a.E, n = nb * K;
+    const bool leader = blockIdx.x == 0 && blockIdx.y == 0;
+    const int nw = (E + 31) >> 5;
+
+    // ---- the grouping: rank of an expert among the distinct ones from a
+    // bitmap of the chosen experts; an access's place in its group from the
+    // earlier accesses of the same expert
+    if (t == 0) s_cold = 0;
+    for (int i = t; i < nw; i += kThreads) s_bits[i] = 0u;
+    if (t < kMaxBK) s_cnt[t] = 0;
+    int e_t = -1, pin_t = -1;
+    if (t < n) {
+        e_t = sel->idx[t];
+        pin_t = sel->slot[t];  // pinned slot or -1, from the route launch
+        s_idx[t] = e_t;
+        s_pin[t] = pin_t;
+    }
+    __syncthreads();
+    if (t < n) {
+        atomicOr(&s_bits[e_t >> 5], 1u << (e_t & 31));
+        if (pin_t < 0) s_cold = 1;
+    }
+    __syncthreads();
+    if (w == 0) {  // exclusive prefix of the per-word popcounts
+        const int c = lane < nw ? __popc(s_bits[lane]) : 0;
+        int incl = c;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const int o = __shfl_up(incl, m, 64);
+            if (lane >= m) incl += o;
+        }
+        if (lane < nw) s_pre[lane] = incl - c;
+        if (lane == 63) s_D = incl;
+    }
+    __syncthreads();
+    int rank = 0, pos = 0;
+    if (t < n) {
+        rank = s_pre[e_t >> 5] + __popc(s_bits[e_t >> 5] & ((1u << (e_t & 31)) - 1u));
+        for (int i = 0; i < t; ++i) pos += s_idx[i] == e_t;  // earlier accesses of the same expert
+        atomicAdd(&s_cnt[rank], 1);
+    }
+    __syncthreads();
+    if (w == 0) {  // group offsets: exclusive prefix over the distinct experts, two per lane
+        const int c0 = s_cnt[2 * lane], c1 = s_cnt[2 * lane + 1];
+        int incl = c0 + c1;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const int o = __shfl_up(incl, m, 64);
+            if (lane >= m) incl += o;
+        }
+        const int excl = incl - (c0 + c1);
+        s_off[2 * lane] = excl;
+        s_off[2 * lane + 1] = excl + c0;
+        if (lane == 63) s_off[kMaxBK] = incl;
+    }
+    if (leader && w == 1) {
+        // the policy, one access at a time in (token, rank) order
+        RingState rs{};
+        if (!s_cold) {
+            for (int i = lane; i < n; i += 64) {
+                s_slot[i] = s_pin[i];
+                s_wseq[i] = 0ull;
+            }
+            rs.n_pin = n;
+        } else {
+            int32_t* r_owner = reinterpret_cast<int32_t*>(s_code);
+            uint64_t* r_stamp = reinterpret_cast<uint64_t*>(s_code + kMaxR);
+            uint64_t* r_seq = reinterpret_cast<uint64_t*>(s_code + 3 * kMaxR);
+            ring_load(a.pt, r_owner, r_stamp, r_seq, rs);
+#pragma nounroll
+            for (int i = 0; i < n; ++i) {
+                int slot;
+                uint64_t wseq;
+                ring_access(a.pt, a.layer, s_idx[i], s_pin[i], r_owner, r_stamp, r_seq, rs, slot, wseq);
+                if (lane == 0) {
+                    s_slot[i] = slot;
+                    s_wseq[i] = wseq;
+                }
+            }
+            ring_store(a.pt, r_owner, r_stamp, r_seq, rs);
+        }
+        stats_flush(a.pt, n, rs);
+    }
+    __syncthreads();
+    const int D = s_D;
+    if (t < n) {
+        s_dent[s_off[rank] + pos] = t;
+        if (pos == 0) s_dexp[rank] = e_t;
+    }
+    if (leader) {
+        // the grouping and the slots, for the down launch and the cold
+        // experts' work-groups
+        if (t < n) {
+            sel->slot[t] = s_slot[t];
+            sel->dent[s_off[rank] + pos] = t;
+            if (pos == 0) {  // the expert's first access: its slot, and the fill it made (if any)
+                sel->dexp[rank] = e_t;
+                sel->dslot[rank] = s_slot[t];
+                sel->dwait[rank] = s_wseq[t];
+            }
+        }
+        if (t <= D) sel->doff[t] = t < D ? s_off[t] : n;
+        if (t == 0) sel->D = D;
+        if (s_cold) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            if (t == 0) __hip_atomic_store(a.pub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+
     for (int j = blockIdx.y; j < D; j += gridDim.y) {
         if (j != (int)blockIdx.y) __syncthreads();  // LDS reuse
-        qb_gateup_expert(a, sel, blockIdx.x, j, s_code, s_sc, red);
+        const int c0 = s_off[j], cn = s_cnt[j];
+        const int first = s_dent[c0];
+        int slot = s_pin[first];
+        uint64_t wseq = 0;
+        if (slot < 0) {  // cold: the slot work-group (0,0) chose
+            if (leader) {
+                slot = s_slot[first];
+                wseq = s_wseq[first];
+            } else {
+                if (t == 0) {
+                    const uint64_t t0 = wall_clock64();
+                    while (__hip_atomic_load(a.pub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                        __builtin_amdgcn_s_sleep(1);
+                        if (qb_spin_expired(a, t0)) {
+                            atomicOr(a.pt.error, (int)ERR_FILL_TIMEOUT);
+                            break;
+                        }
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    s_jslot = __hip_atomic_load(&sel->dslot[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_jwait = __hip_atomic_load(&sel->dwait[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __syncthreads();
+                slot = s_jslot;
+                wseq = s_jwait;
+            }
+        }
+        qb_gateup_expert(a, s_dexp[j], slot, wseq, cn, s_dent + c0, blockIdx.x, s_code, s_sc, red);
     }
 }
 
@@ -621,6 +654,7 @@ __global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
             a.ps[(int64_t)t * kNP + p] = s2;
         }
     }
+    if (p == 0 && t == 0) *a.pub = 0u;  // every gate/up work-group of this layer has finished
 }
 
 // ---------------------------------------------------------------- step staging

@@ -105,7 +105,7 @@ struct moe_spark_ctx {
     float* d_bps = nullptr;         // [kMaxB][kNP]
     uint16_t* d_bu16 = nullptr;     // [kMaxB][d] fp16
     BatchSel* d_bsel = nullptr;     // [L]
-    uint32_t* d_bdone = nullptr;    // [1] route launch ticket
+    uint32_t* d_bpub = nullptr;     // [L] cold-slot publish flags
     uint16_t* d_bh16 = nullptr;     // [kMaxBK][f] fp16
 
     // batched prefill (allocated when max_tokens > 0)
@@ -410,7 +410,7 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_ph,
                      ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok,
                      ctx->d_bx,       ctx->d_brows,  ctx->d_bn,     ctx->d_bpl,     ctx->d_bps,
-                     ctx->d_bu16,     ctx->d_bsel,   ctx->d_bdone,  ctx->d_bh16};
+                     ctx->d_bu16,     ctx->d_bsel,   ctx->d_bpub,   ctx->d_bh16};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
@@ -695,7 +695,7 @@ QBArgs qb_args(const moe_spark_ctx* ctx, int layer, int wr_layer, int32_t batch)
     a.n_slots = ctx->n_slots;
     a.ready = ctx->d_ready;
     a.sel = ctx->d_bsel + layer;
-    a.done = ctx->d_bdone;
+    a.pub = ctx->d_bpub + layer;
     a.h16 = ctx->d_bh16;
     a.pt = tables(ctx, ctx->pull_fills);
     a.tr_x = ctx->tr_x;
@@ -876,7 +876,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_bps, (size_t)kMaxB * kNP) == hipSuccess;
         ok &= dalloc(&ctx->d_bu16, (size_t)kMaxB * d) == hipSuccess;
         ok &= dalloc(&ctx->d_bsel, (size_t)L) == hipSuccess;
-        ok &= dalloc(&ctx->d_bdone, 1) == hipSuccess;
+        ok &= dalloc(&ctx->d_bpub, (size_t)L) == hipSuccess;
         ok &= dalloc(&ctx->d_bh16, (size_t)kMaxBK * f) == hipSuccess;
     }
     if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "device table allocation failed");
@@ -942,7 +942,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= hipMemset(ctx->d_brows, 0, sizeof(int32_t) * kMaxB) == hipSuccess;
         ok &= hipMemset(ctx->d_bn, 0, sizeof(int32_t)) == hipSuccess;
         ok &= hipMemset(ctx->d_bsel, 0, sizeof(BatchSel) * L) == hipSuccess;
-        ok &= hipMemset(ctx->d_bdone, 0, sizeof(uint32_t)) == hipSuccess;
+        ok &= hipMemset(ctx->d_bpub, 0, sizeof(uint32_t) * L) == hipSuccess;
         ok &= hipMemset(ctx->d_bh16, 0, sizeof(uint16_t) * kMaxBK * f) == hipSuccess;
         ok &= hipMemset(ctx->d_bu16, 0, sizeof(uint16_t) * kMaxB * d) == hipSuccess;
     }
