@@ -204,3 +204,116 @@ def test_batched_rejects_bad_arguments(model):
         assert ei.value.status == ms.E_INVALID and "Q4_0" in str(ei.value)
     finally:
         ms.moe_spark_destroy(ctx)
+
+
+def _stats_placement(ctx, w, R):
+    return dict(stats=ms.moe_spark_get_stats(ctx), events=events(ctx), placement=placement(ctx, w, R),
+                slot_bytes=ms.moe_spark_slot_bytes(ctx))
+
+
+def _assert_matches_sim(got, sim):
+    st = got["stats"]
+    assert {k: st[k] for k in STAT_KEYS} == sim.stats(), (st, sim.stats())
+    assert got["events"] == sim_events(sim)
+    for g, r in zip(got["placement"], sim.placement()):
+        assert np.array_equal(g, r)
+
+
+def test_batched_short_calls_and_graph_reuse(model):
+    """A call with no tokens (graph only), a call shorter than one step
+    (3 tokens, B = 16), and a second call through the same cached graph
+    (5 tokens): outputs equal one 8-token step's bit for bit, bookkeeping is
+    the simulator's with steps [3] and [5], and the token counter is 8."""
+    w = model.w
+    LE = w.L * w.E
+    P, B = int(round(0.6 * LE)), 16
+    R = B * w.K
+    x = w.tokens(0, WARM + 8)[WARM:]
+    ref = {}
+    for calls in ((8,), (0, 3, 5)):
+        ctx = model.make_ctx(P=P, R=R)
+        try:
+            tr_k = torch.zeros((8, w.L, w.K), dtype=torch.int32, device="cuda")
+            tr_g = torch.zeros((8, w.L, w.K), dtype=torch.float32, device="cuda")
+            ms.moe_spark_set_trace(ctx, None, tr_k.data_ptr(), tr_g.data_ptr(), 8)
+            xd = torch.from_numpy(x.copy()).cuda()
+            done = 0
+            for n in calls:
+                print(f"batched call of {n} tokens (B={B})", flush=True)
+                ms.moe_spark_decode_batched(ctx, xd[done:].data_ptr() if done else xd.data_ptr(), n, B, None)
+                done += n
+            ms.moe_spark_synchronize(ctx)
+            got = _stats_placement(ctx, w, R)
+            got.update(x=xd.cpu().numpy(), trk=tr_k.cpu().numpy())
+        finally:
+            ms.moe_spark_destroy(ctx)
+        assert got["stats"]["tokens"] == 8
+        sim = oracle.Sim(w.L, w.E, P, R, got["slot_bytes"])
+        sim.place_uniform()
+        t0 = 0
+        for n in calls:
+            if n:
+                sim.decode_batch(got["trk"][t0:t0 + n])
+                t0 += n
+        _assert_matches_sim(got, sim)
+        if not ref:
+            ref = got
+        else:
+            assert np.array_equal(got["x"], ref["x"]) and np.array_equal(got["trk"], ref["trk"])
+
+
+def test_batched_with_online_self_tuning(model):
+    """Self-tuning steps fall between batched steps: warm-up and calibration,
+    then 45 tokens in steps of 4 over two calls with a step every 8 tokens.
+    Bookkeeping (counters, fill log, pinned set, ring, counts, steps and
+    swaps) equals the simulator's with a self-tuning step before each batched
+    step that finds 8 or more tokens since the last change; outputs equal the
+    batched runs without self-tuning bit for bit."""
+    w = model.w
+    LE = w.L * w.E
+    P, B, EVERY, HYST, SHIFT = int(round(0.6 * LE)), 4, 8, 25, 1
+    R = B * w.K
+    x = w.tokens(0, WARM + MEAS)
+    ctx = model.make_ctx(P=P, R=R)
+    try:
+        tr_k = torch.zeros((WARM + MEAS, w.L, w.K), dtype=torch.int32, device="cuda")
+        tr_g = torch.zeros((WARM + MEAS, w.L, w.K), dtype=torch.float32, device="cuda")
+        ms.moe_spark_set_trace(ctx, None, tr_k.data_ptr(), tr_g.data_ptr(), WARM + MEAS)
+        xw = torch.from_numpy(x[:WARM].copy()).cuda()
+        xm = torch.from_numpy(x[WARM:].copy()).cuda()
+        ms.moe_spark_decode(ctx, xw.data_ptr(), WARM, None)
+        ms.moe_spark_synchronize(ctx)
+        ms.moe_spark_calibrate(ctx, True)
+        ms.moe_spark_reset_stats(ctx)
+        ms.moe_spark_set_autotune(ctx, EVERY, HYST, SHIFT)
+        print(f"batched decode B={B} with a self-tuning step every {EVERY} tokens", flush=True)
+        ms.moe_spark_decode_batched(ctx, xm.data_ptr(), 20, B, None)
+        ms.moe_spark_decode_batched(ctx, xm[20:].data_ptr(), MEAS - 20, B, None)
+        ms.moe_spark_synchronize(ctx)
+        got = _stats_placement(ctx, w, R)
+        trk = tr_k.cpu().numpy()
+        x_out = np.concatenate([xw.cpu().numpy(), xm.cpu().numpy()])
+    finally:
+        ms.moe_spark_destroy(ctx)
+    sim = oracle.Sim(w.L, w.E, P, R, got["slot_bytes"])
+    sim.place_uniform()
+    for t in range(WARM):
+        sim.decode_token(trk[t])
+    sim.calibrate(True)
+    sim.reset_stats()
+    since = steps = swaps = 0
+    for lo, hi in ((WARM, WARM + 20), (WARM + 20, WARM + MEAS)):
+        for t0 in range(lo, hi, B):
+            if since >= EVERY:
+                swaps += sim.retune(HYST, SHIFT)
+                steps += 1
+                since = 0
+            nb = min(B, hi - t0)
+            sim.decode_batch(trk[t0:t0 + nb])
+            since += nb
+    _assert_matches_sim(got, sim)
+    st = got["stats"]
+    assert st["retunes"] == steps > 0 and st["retune_swaps"] == swaps
+    print(f"self-tuning: {steps} steps, {swaps} swaps", flush=True)
+    if _BATCHED:
+        assert np.array_equal(x_out, _BATCHED["x"])
