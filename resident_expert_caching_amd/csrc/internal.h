@@ -212,8 +212,7 @@ constexpr int kMaxBK = kMaxB * kQ4MaxK;   // accesses per layer-step
 struct BatchSel {
     int32_t idx[kMaxBK];
     float gate[kMaxBK];
-    int32_t slot[kMaxBK];    // slot the access reads
-    float inv_rms[kMaxB];
+    int32_t slot[kMaxBK];    // route: the expert's pinned slot or -1; gate/up (0,0): the slot the access reads
     int32_t D;
     int32_t pad0;
     int32_t dexp[kMaxBK];

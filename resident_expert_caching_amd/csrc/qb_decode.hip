@@ -44,7 +44,7 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 }
 typedef __attribute__((address_space(4))) const BatchSel ConstSel;
 static_assert(kNP == 128, "the route kernel sums the partial squares with two loads per lane");
-static_assert(kMaxBK <= kThreads, "one thread per access in the route kernel's policy pass");
+static_assert(kMaxBK <= kThreads, "one thread per access in the gate/up kernel's grouping");
 
 __device__ __forceinline__ bool qb_spin_expired(const QBArgs& a, uint64_t t0) {
     return wall_clock64() - t0 > a.spin_limit_ticks ||
@@ -206,7 +206,6 @@ __global__ __launch_bounds__(kThreads) void qb_route_kernel(QBArgs a) {
                 a.tr_gates[o] = myg;
             }
         }
-        if (lane == 0) sel->inv_rms[b] = inv;
         // lane q: Q4_0 block q of x; the trace row, then the normalised block
         // rounded to fp16, for the gate/up kernel's matrix-core operand
         f32x4 xx[8];
