@@ -242,7 +242,7 @@ struct QBArgs {
     const uint64_t* ready;
     BatchSel* sel;            // this layer's routing and placement
     uint32_t* pub;            // this layer's flag: slots of cold experts published
-    uint16_t* h16;            // [B*K][f] SwiGLU output per access, fp16 bits
+    uint16_t* h16;            // [B*K][f] SwiGLU output, fp16 bits: row doff[j] + m is distinct expert j's m-th access
     PolicyTables pt;
     float* tr_x;              // traces: token b of the step goes to row *trace_base + b
     int32_t* tr_topk;

@@ -260,7 +260,7 @@ constexpr int kGUScaleStride = 66;  // fp16 scales per chunk row in LDS
 // block of u[m][k] (q[n][k] - 8), lane layout A[m = lane%16][p = 8(lane/16)+i],
 // B[p][n = lane%16], D[m = 4(lane/16) + r][n], followed by the block's fp16
 // scale of row n in fp32.  The four waves' sums are added in wave order.
-__device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, int e, int slot, uint64_t wseq, int cn,
+__device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, int e, int slot, uint64_t wseq, int c0, int cn,
                                                  const int32_t* dent, int g, uint32_t* s_code, unsigned short* s_sc,
                                                  float (*red)[2][16][17]) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -351,9 +351,8 @@ __device__ __forceinline__ void qb_gateup_expert(const QBArgs& a, int e, int slo
         if (m < cn) {
             const float gt = ((red[0][0][m][n] + red[1][0][m][n]) + red[2][0][m][n]) + red[3][0][m][n];
             const float ut = ((red[0][1][m][n] + red[1][1][m][n]) + red[2][1][m][n]) + red[3][1][m][n];
-            const int acc_i = dent[m];
-            const int f = g * 16 + n;  // h index, stored in the down launch's operand order
-            a.h16[(int64_t)acc_i * kQF + (f & ~31) + mfma_pos(f & 31)] =
+            const int f = g * 16 + n;  // h row c0 + m (grouped order), in the down launch's operand order
+            a.h16[(int64_t)(c0 + m) * kQF + (f & ~31) + mfma_pos(f & 31)] =
                 __builtin_bit_cast(unsigned short, (_Float16)(silu(gt) * ut));
         }
     }
@@ -375,6 +374,7 @@ __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
         s_dent[kMaxBK], s_slot[kMaxBK];
     __shared__ unsigned long long s_wseq[kMaxBK];
     __shared__ uint32_t s_bits[kMaxE / 32];
+    __shared__ uint32_t s_tbits[kMaxB][kMaxE / 32];  // experts chosen by each token
     __shared__ int32_t s_pre[kMaxE / 32];
     __shared__ int s_D, s_cold, s_jslot;
     __shared__ unsigned long long s_jwait;
@@ -388,9 +388,11 @@ __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
 
     // ---- the grouping: rank of an expert among the distinct ones from a
     // bitmap of the chosen experts; an access's place in its group from the
-    // earlier accesses of the same expert
+    // earlier tokens that chose the same expert (each token chooses an
+    // expert at most once), read from per-token bitmaps
     if (t == 0) s_cold = 0;
     for (int i = t; i < nw; i += kThreads) s_bits[i] = 0u;
+    for (int i = t; i < nb * nw; i += kThreads) s_tbits[i / nw][i % nw] = 0u;
     if (t < kMaxBK) s_cnt[t] = 0;
     int e_t = -1, pin_t = -1;
     if (t < n) {
@@ -402,6 +404,7 @@ __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
     __syncthreads();
     if (t < n) {
         atomicOr(&s_bits[e_t >> 5], 1u << (e_t & 31));
+        atomicOr(&s_tbits[t / K][e_t >> 5], 1u << (e_t & 31));
         if (pin_t < 0) s_cold = 1;
     }
     __syncthreads();
@@ -420,7 +423,10 @@ __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
     int rank = 0, pos = 0;
     if (t < n) {
         rank = s_pre[e_t >> 5] + __popc(s_bits[e_t >> 5] & ((1u << (e_t & 31)) - 1u));
-        for (int i = 0; i < t; ++i) pos += s_idx[i] == e_t;  // earlier accesses of the same expert
+        const int tb = t / K;
+#pragma unroll
+        for (int b2 = 0; b2 < kMaxB; ++b2)
+            if (b2 < tb) pos += (s_tbits[b2][e_t >> 5] >> (e_t & 31)) & 1u;
         atomicAdd(&s_cnt[rank], 1);
     }
     __syncthreads();
@@ -522,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void qb_gateup_kernel(QBArgs a) {
                 wseq = s_jwait;
             }
         }
-        qb_gateup_expert(a, s_dexp[j], slot, wseq, cn, s_dent + c0, blockIdx.x, s_code, s_sc, red);
+        qb_gateup_expert(a, s_dexp[j], slot, wseq, c0, cn, s_dent + c0, blockIdx.x, s_code, s_sc, red);
     }
 }
 
@@ -574,12 +580,16 @@ __global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) cc[q] = __builtin_nontemporal_load(cr + q * 64);
         const u32x2 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + p * 64 + lane);
-        const int acc_m = l16 < cn ? sel->dent[c0 + l16] : -1;  // the access of A row l16
+        // A row l16: h row c0 + l16 (the expert's tokens are rows c0 .. c0+cn-1);
+        // the accesses of this lane's D rows, for the combine
+        int dm[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dm[q] = 4 * kg + q < cn ? sel->dent[c0 + 4 * kg + q] : 0;
         f16x8 A[16];
 #pragma unroll
         for (int bb = 0; bb < 16; ++bb)
-            A[bb] = acc_m >= 0 ? *reinterpret_cast<const f16x8*>(a.h16 + (int64_t)acc_m * kQF + bb * 32 + 8 * kg)
-                               : f16x8{};
+            A[bb] = l16 < cn ? *reinterpret_cast<const f16x8*>(a.h16 + (int64_t)(c0 + l16) * kQF + bb * 32 + 8 * kg)
+                             : f16x8{};
         __builtin_amdgcn_wave_barrier();  // the wave's LDS region is free again
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -602,7 +612,7 @@ __global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = 4 * kg + q;
-            if (m < cn) zs[sel->dent[c0 + m]][l16] = acc[q];
+            if (m < cn) zs[dm[q]][l16] = acc[q];
         }
     }
     // the next layer's router rows of this work-group's slice, in flight during
