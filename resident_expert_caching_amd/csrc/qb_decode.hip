@@ -545,7 +545,9 @@ constexpr int kDCodeStride = 68;  // words per down row in a wave's LDS (256 B +
 // in rank order, the residual, and the next layer's router partials of every
 // token over the work-group's rows.
 __global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    // the wave index as a uniform value, so the selection reads below are
+    // scalar loads (counted apart from the vector loads)
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int p = blockIdx.x;
     const int nb = *a.nb;
     const int K = a.K, n = nb * K, E = a.E;
@@ -557,17 +559,27 @@ __global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
     __shared__ float xn[kMaxB][kRW];
     __shared__ float s_g[kMaxBK];
 
+    // the combine's inputs are loaded now but stored to LDS after the experts
+    // loop, so the loop's loads do not wait behind them
     const int tb = t >> 4, tr = t & 15;  // combine: token tb, row tr
-    float xr = 0.0f;
+    float xr = 0.0f, gt = 0.0f;
     if (tb < nb) xr = a.xb[(int64_t)tb * kQD + p * kRW + tr];
-    if (t < n) s_g[t] = sel->gate[t];
+    if (t < n) gt = sel->gate[t];
 
     const int l16 = lane & 15, kg = lane >> 4;
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     uint32_t* wcode = s_code[w];
+    // the wave's first expert record is read together with D (w < 16 <= kMaxBK
+    // keeps it in bounds), so its weight loads wait for one round trip, not two
+    static_assert(kDownThreads / 64 <= kMaxBK, "first records in bounds");
+    int nslot = sel->dslot[w], nc0 = sel->doff[w], nc1 = sel->doff[w + 1];
     for (int j = w; j < D; j += kDownThreads / 64) {
-        const int slot = sel->dslot[j];
-        const int c0 = sel->doff[j], cn = sel->doff[j + 1] - c0;
+        const int slot = nslot, c0 = nc0, cn = nc1 - nc0;
+        if (j + kDownThreads / 64 < D) {
+            nslot = sel->dslot[j + kDownThreads / 64];
+            nc0 = sel->doff[j + kDownThreads / 64];
+            nc1 = sel->doff[j + kDownThreads / 64 + 1];
+        }
         if (slot < 0 || slot >= a.n_slots || cn < 1 || cn > kMaxB) {
             if (lane == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
             continue;
@@ -618,6 +630,7 @@ __global__ __launch_bounds__(kDownThreads) void qb_down_kernel(QBArgs a) {
     // the next layer's router rows of this work-group's slice, in flight during
     // the combine: thread t takes expert t % E (every expert when E divides
     // the thread count)
+    if (t < n) s_g[t] = gt;
     const bool wfix = a.wr_part && (kDownThreads % E) == 0;
     f32x4 wpre[4];
     if (wfix) {
