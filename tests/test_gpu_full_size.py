@@ -27,7 +27,7 @@ from spark_harness import (STAT_KEYS, TIE_GAP, Model, events, oracle_topk_and_ga
 
 pytestmark = pytest.mark.gpu
 
-ms = pytest.importorskip("resident_expert_caching_amd")
+import resident_expert_caching_amd as ms  # noqa: E402  (a missing library fails collection: no silent skip)
 
 WARM, MEAS = 256, 128
 _BATCH1 = {}  # outputs and top-k trace of the batch-1 decode test, for the batched test
