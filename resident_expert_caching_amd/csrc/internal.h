@@ -296,10 +296,12 @@ struct PfArgs {
     const int32_t* pf_experts;  // the chunk's experts, ascending, for the policy
     int32_t n_pf_experts;
     int32_t* pslot;           // [E] slot chosen for each expert this layer
-    uint64_t* pwait;          // [E] fill number to wait for (0: resident)
+    uint64_t* pwait;          // [E] fill number to wait for (0: resident, or pulled)
+    const uint8_t* arena;     // pinned host arena (device address) when the fill kernel pulls fills, else null
+    int32_t* pfill;           // [1 + 2 kMaxR]: the last policy run's fill count, then (arena key, slot) pairs
     uint16_t* h;              // [T*K][f] SwiGLU output, bf16 bits
     float* y;                 // [T*K][d] expert outputs
-    const uint8_t* slots;
+    uint8_t* slots;           // slot arena (written by pulled fills)
     int64_t slot_bytes, P, n_slots;
     const uint64_t* ready;
     PolicyTables pt;
@@ -314,7 +316,8 @@ struct PfArgs {
 hipError_t launch_pf_front(const PfArgs& a, hipStream_t s);    // norm, router, top-k + counts + histogram
 hipError_t launch_pf_policy_first(const PfArgs& a, hipStream_t s);
 hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s);  // sort assignments by (expert, token)
-hipError_t launch_pf_chunk(const PfArgs& a, hipStream_t s);    // policy, gate/up GEMM, down GEMM of one chunk
+hipError_t launch_pf_chunk(const PfArgs& a, hipStream_t s);    // policy, pulled fills, gate/up GEMM, down GEMM of one chunk
+hipError_t launch_pf_fill(const PfArgs& a, hipStream_t s);     // pulled fills of the last policy run
 hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s);  // rank-order combine + residual
 hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s);
 

@@ -16,6 +16,10 @@
 //            (same paragraph, item 2); the host runs it in chunks of at most
 //            R cold experts, so every expert of a chunk is resident while the
 //            chunk's GEMMs run.
+//   fill     the policy run's fills pulled from the pinned host arena into
+//            their ring slots by many work-groups at once (the same item's
+//            copy from host memory, done by the GPU; without a pull arena
+//            the host agent copies them and the GEMMs wait for the copies).
 //   gateup   grouped GEMM on the matrix cores: H = silu(U Wg^T) * (U Wu^T)
 //            per expert group; Q4_0 weights are dequantised to bf16 in LDS,
 //            v_mfma_f32_16x16x32_bf16 accumulates in fp32.
@@ -232,6 +236,21 @@ __global__ __launch_bounds__(kPfThreads) void pf_scatter_kernel(PfArgs a) {
 
 // ---------------------------------------------------------------- policy
 
+// Lane 0 keeps an access's slot; a fill that the fill kernel pulls goes on
+// the fill list and needs no wait (the fill kernel runs before the GEMMs on
+// the same stream); a fill copied by the host agent is waited for.
+__device__ __forceinline__ void pf_record(const PfArgs& a, int e, int slot, uint64_t wseq, int& nf) {
+    if (threadIdx.x == 0) {
+        a.pslot[e] = slot;
+        a.pwait[e] = a.arena ? 0ull : wseq;
+        if (a.arena && wseq && nf < a.pt.R) {
+            a.pfill[1 + 2 * nf] = a.layer * a.E + e;
+            a.pfill[2 + 2 * nf] = slot;
+        }
+    }
+    if (a.arena && wseq) ++nf;
+}
+
 // One wave: the chunk's experts (ascending id) through the placement policy.
 __global__ __launch_bounds__(64) void pf_policy_kernel(PfArgs a) {
     __shared__ int32_t r_owner[kMaxR];
@@ -240,17 +259,16 @@ __global__ __launch_bounds__(64) void pf_policy_kernel(PfArgs a) {
     const PolicyTables& pt = a.pt;
     RingState rs{};
     ring_load(pt, r_owner, r_stamp, r_seq, rs);
+    int nf = 0;
     for (int i = 0; i < a.n_pf_experts; ++i) {
         const int e = a.pf_experts[i];
         int slot;
         uint64_t wseq;
         ring_access(pt, a.layer, e, pt.slot_of[(int64_t)a.layer * a.E + e], r_owner, r_stamp, r_seq, rs, slot,
                     wseq);
-        if (threadIdx.x == 0) {
-            a.pslot[e] = slot;
-            a.pwait[e] = wseq;
-        }
+        pf_record(a, e, slot, wseq, nf);
     }
+    if (threadIdx.x == 0) a.pfill[0] = nf;
     ring_store(pt, r_owner, r_stamp, r_seq, rs);
     stats_flush(pt, a.n_pf_experts, rs);
 }
@@ -269,7 +287,7 @@ __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
     const int64_t lbase = (int64_t)a.layer * E;
     RingState rs{};
     ring_load(pt, r_owner, r_stamp, r_seq, rs);
-    int cold = 0, n = 0;
+    int cold = 0, n = 0, nf = 0;
     bool full = false;
     for (int base = 0; base < E && !full; base += 64) {
         const int e = base + lane;
@@ -289,15 +307,43 @@ __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
             int slot;
             uint64_t wseq;
             ring_access(pt, a.layer, ex, pt.slot_of[lbase + ex], r_owner, r_stamp, r_seq, rs, slot, wseq);
-            if (lane == 0) {
-                a.pslot[ex] = slot;
-                a.pwait[ex] = wseq;
-            }
+            pf_record(a, ex, slot, wseq, nf);
             ++n;
         }
     }
+    if (lane == 0) a.pfill[0] = nf;
     ring_store(pt, r_owner, r_stamp, r_seq, rs);
     stats_flush(pt, n, rs);
+}
+
+// ---------------------------------------------------------------- pulled fills
+
+constexpr int kFillPiece = 16384;  // bytes of a slot per work-group
+
+// Grid (ceil(slot_bytes / kFillPiece), R), 256 threads.  Work-group (p, j)
+// copies bytes [p*kFillPiece, (p+1)*kFillPiece) of the j-th fill of the last
+// policy run from the host arena (across PCIe) into the fill's ring slot.
+__global__ __launch_bounds__(kPfThreads) void pf_fill_kernel(PfArgs a) {
+    const int j = blockIdx.y, t = threadIdx.x;
+    const int nf = a.pfill[0];
+    if (j >= nf || j >= a.pt.R) return;
+    const int key = a.pfill[1 + 2 * j], slot = a.pfill[2 + 2 * j];
+    if (key < 0 || key >= a.L * a.E || slot < a.P || slot >= a.n_slots) {
+        if (t == 0 && blockIdx.x == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
+        return;
+    }
+    const int64_t off = (int64_t)blockIdx.x * kFillPiece;
+    const int nw = (int)(min((int64_t)kFillPiece, a.slot_bytes - off) / 16);
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.arena + (int64_t)key * a.slot_bytes + off);
+    u32x4* dst = reinterpret_cast<u32x4*>(a.slots + (int64_t)slot * a.slot_bytes + off);
+    constexpr int kPer = kFillPiece / 16 / kPfThreads;
+    u32x4 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (t + i * kPfThreads < nw) v[i] = __builtin_nontemporal_load(src + t + i * kPfThreads);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (t + i * kPfThreads < nw) __builtin_nontemporal_store(v[i], dst + t + i * kPfThreads);
 }
 
 // ---------------------------------------------------------------- grouped GEMMs
@@ -548,8 +594,20 @@ hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_pf_fill(const PfArgs& a, hipStream_t s) {
+    if (!a.arena || a.pt.R <= 0) return hipSuccess;
+    if (a.slot_bytes % 16 || a.pt.R > kMaxR) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pf_fill_kernel, dim3((unsigned)((a.slot_bytes + kFillPiece - 1) / kFillPiece), a.pt.R),
+                       dim3(kPfThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_pf_chunk(const PfArgs& a, hipStream_t s) {
-    if (a.n_pf_experts > 0) hipLaunchKernelGGL(pf_policy_kernel, dim3(1), dim3(64), 0, s, a);
+    if (a.n_pf_experts > 0) {
+        hipLaunchKernelGGL(pf_policy_kernel, dim3(1), dim3(64), 0, s, a);
+        const hipError_t e = launch_pf_fill(a, s);
+        if (e != hipSuccess) return e;
+    }
     if (a.n_items > 0) {
         hipLaunchKernelGGL(pf_gateup_kernel, dim3(a.n_items, kQF / 64), dim3(kPfThreads), 0, s, a);
         hipLaunchKernelGGL(pf_down_kernel, dim3(a.n_items, kQD / 128), dim3(kPfThreads), 0, s, a);

@@ -120,6 +120,7 @@ struct moe_spark_ctx {
     int32_t* d_papos = nullptr;     // [Tmax][K]
     int32_t* d_pslot = nullptr;     // [E]
     uint64_t* d_pwait = nullptr;    // [E]
+    int32_t* d_pfill = nullptr;     // [1 + 2 kMaxR] the prefill policy's pulled fills
     uint16_t* d_ph = nullptr;       // [Tmax*K][f] bf16
     float* d_py = nullptr;          // [Tmax*K][d]
     int32_t* d_pmeta = nullptr;     // goff [E+1] | experts [E] | items [2*max_items]
@@ -407,7 +408,7 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_sel,    ctx->d_logits,   ctx->d_u,      ctx->d_ut,      ctx->d_h,
                      ctx->d_xscratch, ctx->d_pl,     ctx->d_ps,     ctx->d_pub,     ctx->d_pu,
                      ctx->d_pinv,     ctx->d_plog,   ctx->d_ptopk,  ctx->d_pgate,   ctx->d_phist,
-                     ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_ph,
+                     ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_pfill,  ctx->d_ph,
                      ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok,
                      ctx->d_bx,       ctx->d_brows,  ctx->d_bn,     ctx->d_bpl,     ctx->d_bps,
                      ctx->d_bu16,     ctx->d_bsel,   ctx->d_bpub,   ctx->d_bh16};
@@ -894,6 +895,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_papos, T * K) == hipSuccess;
         ok &= dalloc(&ctx->d_pslot, (size_t)E) == hipSuccess;
         ok &= dalloc(&ctx->d_pwait, (size_t)E) == hipSuccess;
+        ok &= dalloc(&ctx->d_pfill, (size_t)(1 + 2 * kMaxR)) == hipSuccess;
         ok &= dalloc(&ctx->d_ph, T * K * f) == hipSuccess;
         ok &= dalloc(&ctx->d_py, T * K * d) == hipSuccess;
         const size_t meta = (size_t)(2 * E + 1 + 2 * ctx->pf_max_items);
@@ -1394,6 +1396,8 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         a.apos = ctx->d_papos;
         a.pslot = ctx->d_pslot;
         a.pwait = ctx->d_pwait;
+        a.arena = ctx->pull_fills ? ctx->d_arena : nullptr;  // fills pulled by a kernel, else agent copies
+        a.pfill = ctx->d_pfill;
         a.h = ctx->d_ph;
         a.y = ctx->d_py;
         a.slots = ctx->d_slots;
@@ -1401,7 +1405,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         a.P = c.resident_cap;
         a.n_slots = ctx->n_slots;
         a.ready = ctx->d_ready;
-        a.pt = tables(ctx);
+        a.pt = tables(ctx, ctx->pull_fills);
         a.tr_x = ctx->tr_x;
         a.tr_topk = ctx->tr_topk;
         a.tr_gates = ctx->tr_gates;
@@ -1415,6 +1419,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         HIPCHK(hipEventRecord(ctx->pf_hist_ev, ctx->compute));
         // the first chunk's policy (and so its fills) starts while the host plans
         HIPCHK(launch_pf_policy_first(a, ctx->compute));
+        HIPCHK(launch_pf_fill(a, ctx->compute));
         HIPCHK(hipEventSynchronize(ctx->pf_hist_ev));
         // 2. plan: groups in expert order; distinct experts ascending, cut into
         //    chunks of at most R cold (non-pinned) experts, so that every

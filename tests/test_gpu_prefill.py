@@ -120,3 +120,26 @@ def test_prefill_parity_bookkeeping_and_residency_invariance():
               f"{strict:.2e} of max|MoE output|", flush=True)
         assert err <= 2e-3 * scale, (l, err, scale)
     assert ties <= max(1, (T * w.L) // 50)
+
+
+def test_prefill_pulled_and_agent_fills_agree(monkeypatch):
+    """Prefill fills pulled from the host arena by the fill kernel (the
+    default) and fills copied by the host agent (MOE_SPARK_PULL_FILLS=0, read
+    at context creation) give identical outputs, traces, counters, fill log
+    and placement, at 30% residency with an 8-slot ring (several chunks of
+    cold experts per layer, evictions)."""
+    w = _workload()
+    model = Model(w)
+    x = w.tokens(0, T)
+    rows = (np.arange(T) >= T // 2).astype(np.int32)
+    P = int(round(0.3 * w.L * w.E))
+    pulled = _run(model, P, 8, x, rows)
+    monkeypatch.setenv("MOE_SPARK_PULL_FILLS", "0")
+    agent = _run(model, P, 8, x, rows)
+    assert pulled["stats"]["fills"] > 0 and pulled["stats"]["evictions"] > 0
+    assert np.array_equal(pulled["x"], agent["x"])
+    assert np.array_equal(pulled["tr_k"], agent["tr_k"]) and np.array_equal(pulled["tr_g"], agent["tr_g"])
+    assert {k: pulled["stats"][k] for k in STAT_KEYS} == {k: agent["stats"][k] for k in STAT_KEYS}
+    assert pulled["events"] == agent["events"]
+    for a, b in zip(pulled["placement"], agent["placement"]):
+        assert np.array_equal(a, b)
