@@ -17,9 +17,11 @@
 //            R cold experts, so every expert of a chunk is resident while the
 //            chunk's GEMMs run.
 //   fill     the policy run's fills pulled from the pinned host arena into
-//            their ring slots by many work-groups at once (the same item's
-//            copy from host memory, done by the GPU; without a pull arena
-//            the host agent copies them and the GEMMs wait for the copies).
+//            their ring slots (the same item's copy from host memory, done
+//            by the GPU) by extra work-groups of the gate/up launch over the
+//            chunk's pinned experts, so the copies cross PCIe while the
+//            matrix cores work; the cold experts' GEMMs follow.  Without a
+//            pull arena the host agent copies them and the GEMMs wait.
 //   gateup   grouped GEMM on the matrix cores: H = silu(U Wg^T) * (U Wu^T)
 //            per expert group; Q4_0 weights are dequantised to bf16 in LDS,
 //            v_mfma_f32_16x16x32_bf16 accumulates in fp32.
@@ -318,32 +320,35 @@ __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
 
 // ---------------------------------------------------------------- pulled fills
 
-constexpr int kFillPiece = 16384;  // bytes of a slot per work-group
+constexpr int kFillPiece = 16384;  // bytes of a slot per copy step
 
-// Grid (ceil(slot_bytes / kFillPiece), R), 256 threads.  Work-group (p, j)
-// copies bytes [p*kFillPiece, (p+1)*kFillPiece) of the j-th fill of the last
-// policy run from the host arena (across PCIe) into the fill's ring slot.
-__global__ __launch_bounds__(kPfThreads) void pf_fill_kernel(PfArgs a) {
-    const int j = blockIdx.y, t = threadIdx.x;
-    const int nf = a.pfill[0];
-    if (j >= nf || j >= a.pt.R) return;
-    const int key = a.pfill[1 + 2 * j], slot = a.pfill[2 + 2 * j];
-    if (key < 0 || key >= a.L * a.E || slot < a.P || slot >= a.n_slots) {
-        if (t == 0 && blockIdx.x == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
-        return;
-    }
-    const int64_t off = (int64_t)blockIdx.x * kFillPiece;
-    const int nw = (int)(min((int64_t)kFillPiece, a.slot_bytes - off) / 16);
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.arena + (int64_t)key * a.slot_bytes + off);
-    u32x4* dst = reinterpret_cast<u32x4*>(a.slots + (int64_t)slot * a.slot_bytes + off);
+// Work-group wid of nwg: copies pieces wid, wid + nwg, ... of the last policy
+// run's fills (fill j, piece p = bytes [p*kFillPiece, (p+1)*kFillPiece) of
+// the slot) from the host arena, across PCIe, into the fills' ring slots.
+__device__ void pf_fill_pieces(const PfArgs& a, int wid, int nwg) {
+    const int t = threadIdx.x;
+    const int nf = min(a.pfill[0], a.pt.R);
+    const int pieces = (int)((a.slot_bytes + kFillPiece - 1) / kFillPiece);
     constexpr int kPer = kFillPiece / 16 / kPfThreads;
-    u32x4 v[kPer];
+    for (int u = wid; u < nf * pieces; u += nwg) {
+        const int j = u / pieces, p = u - j * pieces;
+        const int key = a.pfill[1 + 2 * j], slot = a.pfill[2 + 2 * j];
+        if (key < 0 || key >= a.L * a.E || slot < a.P || slot >= a.n_slots) {
+            if (t == 0 && p == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
+            continue;
+        }
+        const int64_t off = (int64_t)p * kFillPiece;
+        const int nw = (int)(min((int64_t)kFillPiece, a.slot_bytes - off) / 16);
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.arena + (int64_t)key * a.slot_bytes + off);
+        u32x4* dst = reinterpret_cast<u32x4*>(a.slots + (int64_t)slot * a.slot_bytes + off);
+        u32x4 v[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        if (t + i * kPfThreads < nw) v[i] = __builtin_nontemporal_load(src + t + i * kPfThreads);
+        for (int i = 0; i < kPer; ++i)
+            if (t + i * kPfThreads < nw) v[i] = __builtin_nontemporal_load(src + t + i * kPfThreads);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        if (t + i * kPfThreads < nw) __builtin_nontemporal_store(v[i], dst + t + i * kPfThreads);
+        for (int i = 0; i < kPer; ++i)
+            if (t + i * kPfThreads < nw) __builtin_nontemporal_store(v[i], dst + t + i * kPfThreads);
+    }
 }
 
 // ---------------------------------------------------------------- grouped GEMMs
@@ -413,11 +418,15 @@ __device__ __forceinline__ void mfma_step(const uint16_t* As, const uint16_t* Bs
 // B rows come from the slot's gate/up region (chunk g = row/16: codes at
 // ((ww*8 + i)*64 + b)*16, scales at 32768 + (ww*64 + b)*16 + 2i).
 __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(PfArgs a) {
+    if ((int)blockIdx.x < a.n_fill_x) {  // the leading columns pull the fills
+        pf_fill_pieces(a, (int)(blockIdx.y * a.n_fill_x + blockIdx.x), a.n_fill_x * (int)gridDim.y);
+        return;
+    }
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n0 = blockIdx.y * 64;
     int e, pos0, rows;
     const uint8_t* S;
-    if (!pf_item(a, blockIdx.x, e, pos0, rows, S)) return;
+    if (!pf_item(a, (int)blockIdx.x - a.n_fill_x, e, pos0, rows, S)) return;
     __shared__ __align__(16) uint16_t As[kBM * kLdsRow];
     __shared__ __align__(16) uint16_t Bs[128 * kLdsRow];
     __shared__ int tok[kBM];
@@ -594,24 +603,17 @@ hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_pf_fill(const PfArgs& a, hipStream_t s) {
-    if (!a.arena || a.pt.R <= 0) return hipSuccess;
-    if (a.slot_bytes % 16 || a.pt.R > kMaxR) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pf_fill_kernel, dim3((unsigned)((a.slot_bytes + kFillPiece - 1) / kFillPiece), a.pt.R),
-                       dim3(kPfThreads), 0, s, a);
+hipError_t launch_pf_policy(const PfArgs& a, hipStream_t s) {
+    if (a.n_pf_experts > 0) hipLaunchKernelGGL(pf_policy_kernel, dim3(1), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_pf_chunk(const PfArgs& a, hipStream_t s) {
-    if (a.n_pf_experts > 0) {
-        hipLaunchKernelGGL(pf_policy_kernel, dim3(1), dim3(64), 0, s, a);
-        const hipError_t e = launch_pf_fill(a, s);
-        if (e != hipSuccess) return e;
-    }
-    if (a.n_items > 0) {
-        hipLaunchKernelGGL(pf_gateup_kernel, dim3(a.n_items, kQF / 64), dim3(kPfThreads), 0, s, a);
-        hipLaunchKernelGGL(pf_down_kernel, dim3(a.n_items, kQD / 128), dim3(kPfThreads), 0, s, a);
-    }
+hipError_t launch_pf_gemms(const PfArgs& a, hipStream_t s) {
+    if (a.n_fill_x < 0 || (a.n_fill_x > 0 && (!a.arena || a.slot_bytes % 16 || a.pt.R > kMaxR)))
+        return hipErrorInvalidValue;
+    if (a.n_items + a.n_fill_x > 0)
+        hipLaunchKernelGGL(pf_gateup_kernel, dim3(a.n_items + a.n_fill_x, kQF / 64), dim3(kPfThreads), 0, s, a);
+    if (a.n_items > 0) hipLaunchKernelGGL(pf_down_kernel, dim3(a.n_items, kQD / 128), dim3(kPfThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ using namespace moe;
 namespace {
 
 constexpr int kThrottle = 8;  // decode tokens in flight at most
+constexpr int kPfFillCols = 16;  // prefill: grid columns of fill work-groups in a gate/up launch (x 8 rows)
 
 struct GraphEntry {
     float* x = nullptr;
@@ -1419,7 +1420,6 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         HIPCHK(hipEventRecord(ctx->pf_hist_ev, ctx->compute));
         // the first chunk's policy (and so its fills) starts while the host plans
         HIPCHK(launch_pf_policy_first(a, ctx->compute));
-        HIPCHK(launch_pf_fill(a, ctx->compute));
         HIPCHK(hipEventSynchronize(ctx->pf_hist_ev));
         // 2. plan: groups in expert order; distinct experts ascending, cut into
         //    chunks of at most R cold (non-pinned) experts, so that every
@@ -1427,7 +1427,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         goff[0] = 0;
         for (int e = 0; e < E; ++e) goff[e + 1] = goff[e] + ctx->h_phist[e];
         struct Chunk {
-            int e_begin, e_end, i_begin, i_end;
+            int e_begin, e_end, i_begin, i_cold, i_end;  // items [i_begin, i_cold): pinned experts
         };
         // Within a chunk the GEMM tiles of pinned experts come first and those
         // of cold experts (in fill order) last, so the matrix cores work while
@@ -1435,9 +1435,10 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         std::vector<Chunk> chunks;
         std::vector<int> chunk_experts;
         int ne = 0, ni = 0, cold = 0;
-        Chunk cur{0, 0, 0, 0};
+        Chunk cur{0, 0, 0, 0, 0};
         auto close_chunk = [&]() -> bool {
-            for (int pass = 0; pass < 2; ++pass)
+            for (int pass = 0; pass < 2; ++pass) {
+                if (pass == 1) cur.i_cold = ni;
                 for (int e : chunk_experts) {
                     const bool is_cold = ctx->slot_of[(int64_t)l * E + e] < 0;
                     if (is_cold != (pass == 1)) continue;
@@ -1448,10 +1449,11 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
                         ++ni;
                     }
                 }
+            }
             cur.e_end = ne;
             cur.i_end = ni;
             if (cur.e_end > cur.e_begin) chunks.push_back(cur);
-            cur = Chunk{ne, ne, ni, ni};
+            cur = Chunk{ne, ne, ni, ni, ni};
             chunk_experts.clear();
             cold = 0;
             return true;
@@ -1470,13 +1472,25 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         HIPCHK(hipMemcpyAsync(d_goff, goff, meta * sizeof(int32_t), hipMemcpyHostToDevice, ctx->compute));
         // 3. sort assignments, run each chunk, combine
         HIPCHK(launch_pf_scatter(a, ctx->compute));
+        // Per chunk: its policy (the first chunk's ran already); the GEMMs of
+        // its pinned experts, whose gate/up launch also pulls the chunk's
+        // fills; then the GEMMs of its cold experts.  With agent copies the
+        // cold experts' work-groups wait for each fill's ready flag.
         for (const Chunk& ch : chunks) {
             PfArgs b = a;
-            b.pf_experts = d_experts + ch.e_begin;
-            b.n_pf_experts = &ch == &chunks[0] ? 0 : ch.e_end - ch.e_begin;  // the first ran already
+            if (&ch != &chunks[0]) {
+                b.pf_experts = d_experts + ch.e_begin;
+                b.n_pf_experts = ch.e_end - ch.e_begin;
+                HIPCHK(launch_pf_policy(b, ctx->compute));
+            }
             b.items = d_items + 2 * ch.i_begin;
-            b.n_items = ch.i_end - ch.i_begin;
-            HIPCHK(launch_pf_chunk(b, ctx->compute));
+            b.n_items = ch.i_cold - ch.i_begin;
+            b.n_fill_x = b.arena ? kPfFillCols : 0;
+            HIPCHK(launch_pf_gemms(b, ctx->compute));
+            b.items = d_items + 2 * ch.i_cold;
+            b.n_items = ch.i_end - ch.i_cold;
+            b.n_fill_x = 0;
+            HIPCHK(launch_pf_gemms(b, ctx->compute));
         }
         HIPCHK(launch_pf_combine(a, ctx->compute));
     }
