@@ -35,7 +35,7 @@ using namespace moe;
 namespace {
 
 constexpr int kThrottle = 8;  // decode tokens in flight at most
-constexpr int kPfFillCols = 16;  // prefill: grid columns of fill work-groups in a gate/up launch (x 8 rows)
+constexpr int kPfFillCols = 8;  // prefill: grid columns of fill work-groups in a gate/up launch (x 8 rows)
 
 struct GraphEntry {
     float* x = nullptr;
@@ -157,6 +157,9 @@ struct moe_spark_ctx {
     // MOE_SPARK_COPY_STREAMS=1..kCopyStreams sets the decode figure.
     int n_copy = 1;
     std::atomic<int> burst_fills{0};
+    // prefill with pulled fills: grid columns of fill work-groups in a gate/up
+    // launch (x 8 rows); MOE_SPARK_FILL_COLS=1..128 at creation
+    int pf_fill_cols = kPfFillCols;
 
     // fill agent
     std::thread agent;
@@ -806,6 +809,10 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     if (const char* ev = getenv("MOE_SPARK_COPY_STREAMS")) {
         const int n = atoi(ev);
         if (n >= 1 && n <= kCopyStreams) ctx->n_copy = n;
+    }
+    if (const char* ev = getenv("MOE_SPARK_FILL_COLS")) {
+        const int n = atoi(ev);
+        if (n >= 1 && n <= 128) ctx->pf_fill_cols = n;
     }
     if (compute_stream) {
         ctx->compute = (hipStream_t)compute_stream;
@@ -1485,7 +1492,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
             }
             b.items = d_items + 2 * ch.i_begin;
             b.n_items = ch.i_cold - ch.i_begin;
-            b.n_fill_x = b.arena ? kPfFillCols : 0;
+            b.n_fill_x = b.arena ? ctx->pf_fill_cols : 0;
             HIPCHK(launch_pf_gemms(b, ctx->compute));
             b.items = d_items + 2 * ch.i_cold;
             b.n_items = ch.i_end - ch.i_cold;
