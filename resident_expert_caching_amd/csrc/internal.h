@@ -299,7 +299,7 @@ struct PfArgs {
     uint64_t* pwait;          // [E] fill number to wait for (0: resident, or pulled)
     const uint8_t* arena;     // pinned host arena (device address) when the fill kernel pulls fills, else null
     int32_t* pfill;           // [1 + 2 kMaxR]: the last policy run's fill count, then (arena key, slot) pairs
-    int32_t n_fill_x;         // gate/up launch: leading grid columns that pull those fills (0: none)
+    int32_t n_fill_x;         // gate/up and down launches: leading grid columns that pull those fills (0: none)
     uint16_t* h;              // [T*K][f] SwiGLU output, bf16 bits
     float* y;                 // [T*K][d] expert outputs
     uint8_t* slots;           // slot arena (written by pulled fills)
@@ -318,8 +318,9 @@ hipError_t launch_pf_front(const PfArgs& a, hipStream_t s);    // norm, router, 
 hipError_t launch_pf_policy_first(const PfArgs& a, hipStream_t s);
 hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s);  // sort assignments by (expert, token)
 hipError_t launch_pf_policy(const PfArgs& a, hipStream_t s);   // a chunk's experts through the placement policy
-// gate/up GEMM (plus n_fill_x columns of work-groups pulling the last policy
-// run's fills) and down GEMM over a list of work items
+// gate/up GEMM and down GEMM over a list of work items, each launch with
+// n_fill_x leading grid columns of work-groups pulling a share of the last
+// policy run's fills
 hipError_t launch_pf_gemms(const PfArgs& a, hipStream_t s);
 hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s);  // rank-order combine + residual
 hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s);

@@ -18,8 +18,9 @@
 //            chunk's GEMMs run.
 //   fill     the policy run's fills pulled from the pinned host arena into
 //            their ring slots (the same item's copy from host memory, done
-//            by the GPU) by extra work-groups of the gate/up launch over the
-//            chunk's pinned experts, so the copies cross PCIe while the
+//            by the GPU) by extra work-groups of the gate/up and down
+//            launches over the chunk's pinned experts (three quarters of the
+//            pieces, then the rest), so the copies cross PCIe while the
 //            matrix cores work; the cold experts' GEMMs follow.  Without a
 //            pull arena the host agent copies them and the GEMMs wait.
 //   gateup   grouped GEMM on the matrix cores: H = silu(U Wg^T) * (U Wu^T)
@@ -321,16 +322,20 @@ __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
 // ---------------------------------------------------------------- pulled fills
 
 constexpr int kFillPiece = 16384;  // bytes of a slot per copy step
+constexpr int kFillGUShare = 192;  // of 256: the part of the fill pieces the gate/up launch copies, down the rest
 
-// Work-group wid of nwg: copies pieces wid, wid + nwg, ... of the last policy
-// run's fills (fill j, piece p = bytes [p*kFillPiece, (p+1)*kFillPiece) of
-// the slot) from the host arena, across PCIe, into the fills' ring slots.
-__device__ void pf_fill_pieces(const PfArgs& a, int wid, int nwg) {
+// Work-group wid of nwg: copies pieces lo + wid, lo + wid + nwg, ... below
+// hi of the last policy run's fills, where the pieces are numbered over all
+// fills (fill j, piece p = bytes [p*kFillPiece, (p+1)*kFillPiece) of the
+// slot) and [lo, hi) is the share [s0/256, s1/256) of them; from the host
+// arena, across PCIe, into the fills' ring slots.
+__device__ void pf_fill_pieces(const PfArgs& a, int wid, int nwg, int s0, int s1) {
     const int t = threadIdx.x;
     const int nf = min(a.pfill[0], a.pt.R);
     const int pieces = (int)((a.slot_bytes + kFillPiece - 1) / kFillPiece);
+    const int lo = nf * pieces * s0 / 256, hi = nf * pieces * s1 / 256;
     constexpr int kPer = kFillPiece / 16 / kPfThreads;
-    for (int u = wid; u < nf * pieces; u += nwg) {
+    for (int u = lo + wid; u < hi; u += nwg) {
         const int j = u / pieces, p = u - j * pieces;
         const int key = a.pfill[1 + 2 * j], slot = a.pfill[2 + 2 * j];
         if (key < 0 || key >= a.L * a.E || slot < a.P || slot >= a.n_slots) {
@@ -419,7 +424,7 @@ __device__ __forceinline__ void mfma_step(const uint16_t* As, const uint16_t* Bs
 // ((ww*8 + i)*64 + b)*16, scales at 32768 + (ww*64 + b)*16 + 2i).
 __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(PfArgs a) {
     if ((int)blockIdx.x < a.n_fill_x) {  // the leading columns pull the fills
-        pf_fill_pieces(a, (int)(blockIdx.y * a.n_fill_x + blockIdx.x), a.n_fill_x * (int)gridDim.y);
+        pf_fill_pieces(a, (int)(blockIdx.y * a.n_fill_x + blockIdx.x), a.n_fill_x * (int)gridDim.y, 0, kFillGUShare);
         return;
     }
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -498,11 +503,16 @@ __global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(PfArgs a) {
 // down rows; wave w: rows (w&1)*64.., columns (w>>1)*64...  B rows from the
 // slot's down region: codes [r][b][16 B], scales [r/4][b][4] fp16.
 __global__ __launch_bounds__(kPfThreads) void pf_down_kernel(PfArgs a) {
+    if ((int)blockIdx.x < a.n_fill_x) {  // the leading columns pull the rest of the fills
+        pf_fill_pieces(a, (int)(blockIdx.y * a.n_fill_x + blockIdx.x), a.n_fill_x * (int)gridDim.y, kFillGUShare,
+                       256);
+        return;
+    }
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n0 = blockIdx.y * 128;
     int e, pos0, rows;
     const uint8_t* S;
-    if (!pf_item(a, blockIdx.x, e, pos0, rows, S)) return;
+    if (!pf_item(a, (int)blockIdx.x - a.n_fill_x, e, pos0, rows, S)) return;
     __shared__ __align__(16) uint16_t As[kBM * kLdsRow];
     __shared__ __align__(16) uint16_t Bs[128 * kLdsRow];
     const int ar = tid >> 1, ah = (tid & 1) * 32;
@@ -613,7 +623,8 @@ hipError_t launch_pf_gemms(const PfArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;
     if (a.n_items + a.n_fill_x > 0)
         hipLaunchKernelGGL(pf_gateup_kernel, dim3(a.n_items + a.n_fill_x, kQF / 64), dim3(kPfThreads), 0, s, a);
-    if (a.n_items > 0) hipLaunchKernelGGL(pf_down_kernel, dim3(a.n_items, kQD / 128), dim3(kPfThreads), 0, s, a);
+    if (a.n_items + a.n_fill_x > 0)
+        hipLaunchKernelGGL(pf_down_kernel, dim3(a.n_items + a.n_fill_x, kQD / 128), dim3(kPfThreads), 0, s, a);
     return hipGetLastError();
 }
 
