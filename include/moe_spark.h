@@ -34,6 +34,17 @@
  * describes the last failure.  Calls that launch work are asynchronous on the
  * compute stream; device-side faults of the method (a fill that never
  * arrives) surface at moe_spark_synchronize().
+ *
+ * Environment, read by moe_spark_create (all optional; results never depend
+ * on them):
+ *   MOE_SPARK_PULL_FILLS=0      cold experts are copied by the host fill agent
+ *                               on copy streams, not pulled by the kernels
+ *                               from the pinned arena's device address (Q4_0)
+ *   MOE_SPARK_COPY_STREAMS=1|2  copy streams the agent uses in decode
+ *   MOE_SPARK_FILL_COLS=1..128  prefill: grid columns of fill work-groups in
+ *                               each pinned-expert GEMM launch (default 8)
+ *   MOE_SPARK_DECODE_STREAM=1   decode launches its kernels one by one instead
+ *                               of replaying the token graph
  */
 #ifndef MOE_SPARK_H
 #define MOE_SPARK_H
