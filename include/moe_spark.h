@@ -123,14 +123,16 @@ typedef struct moe_spark_ctx moe_spark_ctx;
 /* Create a context: allocates the HBM slot arena ((P+R) slots), the pinned
  * host arena (L*E slots) and all tables, and starts the fill agent.
  * compute_stream / copy_stream: hipStream_t, or NULL to let the context make
- * its own.  Q4_0 decode fills are pulled by the decode kernels themselves:
- * the cold expert's work-groups read it from the pinned host arena through its
- * device address, compute from it and write it into the ring slot (set
- * MOE_SPARK_PULL_FILLS=0 in the environment to hand them to the fill agent
- * instead).  The fill agent issues the other ring fills on copy_stream; while a prefill
- * runs it also uses one more stream of the context's own whenever
- * copy_stream is busy (fills of one ring slot in flight together share a
- * stream).  moe_spark_synchronize waits for both.  Kernels wait for fills, so
+ * its own.  Q4_0 fills are pulled by the kernels themselves, through the
+ * pinned host arena's device address: in decode the cold expert's
+ * work-groups read it, compute from it and write it into the ring slot; in
+ * prefill extra work-groups of the pinned experts' GEMM launches copy each
+ * chunk's fills into their ring slots before the cold experts' GEMMs run.
+ * Set MOE_SPARK_PULL_FILLS=0 in the environment to hand them to the fill
+ * agent instead.  The fill agent issues the other ring fills on copy_stream;
+ * while a prefill runs it also uses one more stream of the context's own
+ * whenever copy_stream is busy (fills of one ring slot in flight together
+ * share a stream).  moe_spark_synchronize waits for both.  Kernels wait for fills, so
  * neither copy stream may share a hardware queue with the compute stream:
  * keep the process's streams within GPU_MAX_HW_QUEUES (a fill that never
  * starts ends the wait with E_HIP "fill did not arrive in time").
@@ -248,7 +250,8 @@ moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int
  * bf16 activations, fp32 accumulation (gate/up with SwiGLU, then down); the
  * rank-order combine adds the result to x.  The layer's distinct experts are
  * accessed once each in ascending id; non-pinned ones stream through the
- * spare-slot ring in chunks of at most R, filled asynchronously as in decode.
+ * spare-slot ring in chunks of at most R, filled as in moe_spark_create
+ * describes (pulled during the pinned experts' GEMMs, or agent copies).
  * x [T][d] fp32 device, updated in place; bias_row [T] int32 device or NULL.
  * Synchronises the compute stream once per layer (the host plans each layer
  * from its expert histogram).  Errors: E_INVALID (format, n_tokens, x),
