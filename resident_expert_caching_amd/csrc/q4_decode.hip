@@ -432,37 +432,43 @@ __global__ __launch_bounds__(kThreads) void q4_down_kernel(Q4Args a) {
     const int r0 = p * kRW + half * 8;
     const int tok = tok_value(a.tok);
     const int K = a.K;
+    const bool act = kq < K;
+
+    // Loads in dependency order, as straight-line code, so the wait before
+    // the weight loads covers the slot and h loads only, not the router
+    // weights and the residual issued after them (loads retire in order).
+    // Lanes past rank K load rank 0's slot and h rows (in bounds, unused);
+    // an invalid slot is reported and read as slot 0, never used.
+    const int slot = a.sel->slot[act ? kq : 0];
+    f32x4 hh[8];
+    {
+        const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h) + (act ? kq : 0) * 8 * 16 + b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hh[j] = h4[j * 16];
+    }
+    const bool valid = slot >= 0 && slot < a.n_slots;
+    const uint8_t* base = a.slots + (int64_t)(valid ? slot : 0) * a.slot_bytes + kGURegion;
+    u32x4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + i) * 256) + b);
+    const u32x2 s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + b);
+    const u32x2 s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + ((r0 >> 2) + 1) * 16 + b);
 
     f32x4 wpre[4];
     load_wpre(a, p, wpre);
     float xr = 0.0f;
     if (t < kRW && a.residual) xr = a.x_base[(int64_t)tok * kQD + p * kRW + t];
-
-    const bool act = kq < K;
-    float z[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = 0.0f;
-    // loads that do not depend on the slot go out together with the slot
-    const int slot = act ? a.sel->slot[kq] : 0;
-    f32x4 hh[8];
-    if (act) {
-        const f32x4* h4 = reinterpret_cast<const f32x4*>(a.h);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hh[j] = h4[(kq * 8 + j) * 16 + b];
-    }
     float gk[kQ4MaxK];  // the combine's gates, in rank order
 #pragma unroll
     for (int kk = 0; kk < kQ4MaxK; ++kk) gk[kk] = (t < kRW && kk < K) ? a.sel->gate[kk] : 0.0f;
-    if (act && (slot < 0 || slot >= a.n_slots)) {
+
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = 0.0f;
+    if (act && !valid) {
         if (b == 0 && half == 0) atomicOr(a.pt.error, (int)ERR_BAD_SLOT);
     } else if (act) {
-        const uint8_t* base = a.slots + (int64_t)slot * a.slot_bytes + kGURegion;
-        u32x4 c[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + i) * 256) + b);
-        const u32x2 s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + (r0 >> 2) * 16 + b);
-        const u32x2 s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + kDownCodes) + ((r0 >> 2) + 1) * 16 + b);
         f16x2 ha[16];
         const float HO = kQ4Offset * q4_pairs(hh, ha);
         const uint32_t sw[4] = {s0.x, s0.y, s1.x, s1.y};
