@@ -575,13 +575,26 @@ __global__ __launch_bounds__(kPfThreads) void pf_down_kernel(PfArgs a) {
 __global__ __launch_bounds__(kPfThreads) void pf_combine_kernel(PfArgs a) {
     const int t = blockIdx.x, i = blockIdx.y * kPfThreads + threadIdx.x;
     const int K = a.K;
-    float y = 0.0f;
-    for (int k = 0; k < K; ++k) {
-        const int pos = a.apos[(int64_t)t * K + k];
-        y += a.gates[(int64_t)t * K + k] * a.y[(int64_t)pos * kQD + i];
+    // every load first, without branches (ranks past K read rank K-1 again
+    // and are not summed): positions and gates, then the expert outputs and
+    // x; then the sum in rank order
+    int pos[kQ4MaxK];
+    float g[kQ4MaxK], v[kQ4MaxK];
+#pragma unroll
+    for (int k = 0; k < kQ4MaxK; ++k) {
+        const int64_t o = (int64_t)t * K + min(k, K - 1);
+        pos[k] = a.apos[o];
+        g[k] = a.gates[o];
     }
+#pragma unroll
+    for (int k = 0; k < kQ4MaxK; ++k) v[k] = a.y[(int64_t)pos[k] * kQD + i];
     float* xp = a.x + (int64_t)t * kQD + i;
-    *xp = *xp + y;
+    const float x0 = *xp;
+    float y = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kQ4MaxK; ++k)
+        if (k < K) y += g[k] * v[k];
+    *xp = x0 + y;
 }
 
 __global__ void cursor_add_kernel(int32_t* cursor, int32_t n) {
