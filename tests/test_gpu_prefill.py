@@ -143,3 +143,23 @@ def test_prefill_pulled_and_agent_fills_agree(monkeypatch):
     assert pulled["events"] == agent["events"]
     for a, b in zip(pulled["placement"], agent["placement"]):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("cols", [1, 128])
+def test_prefill_fill_columns_do_not_change_results(monkeypatch, cols):
+    """The pulled fills are split over MOE_SPARK_FILL_COLS grid columns of
+    work-groups (each pinned-expert gate/up and down launch); 1 column (every
+    work-group copies many pieces) and 128 columns (most copy none) give the
+    same outputs, traces, counters and fill log as the default."""
+    w = _workload()
+    model = Model(w)
+    x = w.tokens(0, T)
+    rows = (np.arange(T) >= T // 2).astype(np.int32)
+    P = int(round(0.3 * w.L * w.E))
+    base = _run(model, P, 8, x, rows)
+    monkeypatch.setenv("MOE_SPARK_FILL_COLS", str(cols))
+    other = _run(model, P, 8, x, rows)
+    assert base["stats"]["fills"] > 0
+    assert np.array_equal(base["x"], other["x"]) and np.array_equal(base["tr_k"], other["tr_k"])
+    assert {k: base["stats"][k] for k in STAT_KEYS} == {k: other["stats"][k] for k in STAT_KEYS}
+    assert base["events"] == other["events"]
