@@ -264,6 +264,58 @@ def test_stack_zero_experts_keep_x_and_one_layer_is_residual():
     assert np.array_equal(xt[:, 0], x)
 
 
+def _numpy_stack(x, wrs, biases, rows, experts, K, eps=1e-6):
+    """An independent fp64 numpy statement of the residual stack on fp32
+    weights: RMSNorm, router + bias row, top-K by (logit desc, index asc),
+    the softmax over the chosen logits, SwiGLU experts, rank-order combine,
+    x += y, layer after layer."""
+    x = x.astype(np.float64).copy()
+    for l, wr in enumerate(wrs):
+        u = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + eps)
+        lg = u @ wr.astype(np.float64).T + biases[l].astype(np.float64)[rows]
+        y = np.zeros_like(x)
+        for t in range(x.shape[0]):
+            sel = np.lexsort((np.arange(lg.shape[1]), -lg[t]))[:K]
+            g = np.exp(lg[t, sel] - lg[t, sel].max())
+            g /= g.sum()
+            for k, e in enumerate(sel):
+                gw, uw, dw = (m.astype(np.float64) for m in experts[l][e])
+                h = silu(gw @ u[t]) * (uw @ u[t])
+                y[t] += g[k] * (dw @ h)
+        x = x + y
+    return x
+
+
+def test_stack_distinct_layers_equal_chained_layers_and_numpy():
+    """Three layers with distinct routers, bias tables (two rows, chosen per
+    token) and experts: the stack equals the single-layer oracle chained with
+    the residual, bit for bit, and an independent numpy statement to 1e-12.
+    A wrong per-layer offset (layer 0's router, bias or experts reused, or the
+    expert table indexed off by a layer) fails both."""
+    rng = np.random.default_rng(23)
+    E, d, f, K, L, T = 12, 64, 32, 3, 3, 6
+    wrs = [(0.3 * rng.standard_normal((E, d))).astype(np.float32) for _ in range(L)]
+    biases = [(0.5 * rng.standard_normal((2, E))).astype(np.float32) for _ in range(L)]
+    experts = [[tuple((0.2 * rng.standard_normal(s)).astype(np.float32) for s in ((f, d), (f, d), (d, f)))
+                for _ in range(E)] for _ in range(L)]
+    rows = np.array([0, 1, 1, 0, 1, 0], np.int32)
+    x = rng.standard_normal((T, d))
+    xo, idx, xt = oracle.stack(x, wrs, biases, experts, K=K, wfmt=oracle.W_F32, bias_row=rows,
+                               want_trace=True)
+    xc = x.copy()
+    for l in range(L):
+        assert np.array_equal(xt[:, l], xc)
+        y, il, _, _ = oracle.layer(xc, wrs[l], experts[l], K=K, wfmt=oracle.W_F32, norm=True,
+                                   bias=biases[l], bias_row=rows)
+        assert np.array_equal(idx[:, l], il)
+        xc = xc + y
+    assert np.array_equal(xo, xc)
+    ref = _numpy_stack(x, wrs, biases, rows, experts, K)
+    np.testing.assert_allclose(xo, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+    # the layers really differ: each layer's routing is not layer 0's
+    assert any(not np.array_equal(idx[:, l], idx[:, 0]) for l in range(1, L))
+
+
 def test_thread_count_does_not_change_results():
     import subprocess
     import sys
