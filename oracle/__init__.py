@@ -133,6 +133,21 @@ def router(wr, u, bias=None):
     return out
 
 
+def router_logits(x, wr, bias=None, bias_row=None, norm=True, eps=1e-6):
+    """Router logits of many tokens at once, in fp64: RMSNorm of each row of x
+    (when norm), then u @ wr^T plus the token's bias row.  The same definition
+    as ``router`` (a numpy matrix product in place of the per-token loop), for
+    checking every token-layer of a large run."""
+    x = np.atleast_2d(np.asarray(x, np.float64))
+    u = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + eps) if norm else x
+    lg = u @ np.asarray(wr, np.float64).T
+    if bias is not None:
+        b = np.atleast_2d(np.asarray(bias, np.float64))
+        rows = np.zeros(x.shape[0], np.int64) if bias_row is None else np.asarray(bias_row, np.int64)
+        lg = lg + b[rows]
+    return lg
+
+
 def topk(logits, K):
     lg = _f64(logits)
     idx = np.empty(K, dtype=np.int32)

@@ -14,6 +14,9 @@ def build(verbose=False):
     out = LIB_PATH + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # matrix-core results in ordinary VGPRs: the prefill GEMMs scale every
+           # block's MFMA result in fp32, which would otherwise copy it out of AGPRs
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wno-unused-command-line-argument", "-Wno-pass-failed",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
            "-o", out] + SOURCES + ["-lpthread"]

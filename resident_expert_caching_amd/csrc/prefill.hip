@@ -1,8 +1,9 @@
 // gfx950 batched prefill of the Q4_0 MoE stack: T tokens through one layer
 // at a time.
 //
-//   norm     RMSNorm per token; the normalised input in bf16 for the expert
-//            GEMMs, 1/rms kept in fp32 for the router.
+//   norm     RMSNorm per token; the normalised input for the expert GEMMs
+//            as a pair of bf16 operands (hi + lo, 16 significant bits),
+//            1/rms kept in fp32 for the router.
 //   router   logits[t][e] = inv_rms[t] * x[t]·Wr[e] + bias, fp32 MFMA.
 //   topk     exact top-K per token and the softmax renormalised over the
 //            chosen experts ("Luce Spark runs 35B MoE models on 16GB GPU
@@ -24,8 +25,13 @@
 //            matrix cores work; the cold experts' GEMMs follow.  Without a
 //            pull arena the host agent copies them and the GEMMs wait.
 //   gateup   grouped GEMM on the matrix cores: H = silu(U Wg^T) * (U Wu^T)
-//            per expert group; Q4_0 weights are dequantised to bf16 in LDS,
-//            v_mfma_f32_16x16x32_bf16 accumulates in fp32.
+//            per expert group.  Each Q4_0 code enters the matrix cores as an
+//            exact bf16 value; v_mfma_f32_16x16x32_bf16 covers one Q4_0 block
+//            per instruction, twice (activation hi, then lo), with fp32
+//            accumulation, and the block's fp16 scale multiplies the block's
+//            sum in fp32.  So no weight is rounded, and activations carry 16
+//            significant bits: the result is the exact-weight product up to
+//            fp32 rounding.
 //   down     grouped GEMM Y = H Wd^T, same scheme.
 //   combine  x[t] += sum_k g[t][k] Y[pos(t,k)] in rank order.
 //
@@ -46,48 +52,59 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kPfThreads = 256;
 constexpr int kBM = 128;       // tokens per GEMM tile
-constexpr int kBK = 64;        // K per pipeline step (two Q4_0 blocks)
-constexpr int kLdsRow = 72;    // bf16 per LDS tile row (64 + 8 padding)
+constexpr int kNB = 128;       // weight rows per GEMM tile
+constexpr int kOpRow = 72;     // bf16 per LDS operand row: hi 32, lo 32, 8 padding (144 B)
 
-__device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+// Matrix-core operand order of one Q4_0 block.  v_mfma_f32_16x16x32_bf16
+// gives lane (i, g) = (lane % 16, lane / 16) eight consecutive k positions
+// 8g..8g+7 of row i of A and of column i of B.  Position 8g + j holds block
+// element op_elem(8g + j) = 4g + {0, 2, 16, 18, 1, 3, 17, 19}[j]: exactly the
+// eight codes of the block's 32-bit code word g (bytes 4g..4g+3; a byte's low
+// nibble is element 4g + byte, its high nibble element 16 + 4g + byte) in the
+// order q4_operand unpacks them.  Activations are stored in the same order,
+// so a lane's A and B values always meet at the same element.
+__device__ __forceinline__ int op_elem(int p) {
+    const int g = p >> 3, j = p & 7;
+    return 4 * g + ((j >> 1) & 1) * 16 + (j >> 2) + (j & 1) * 2;
+}
+__device__ __forceinline__ int op_pos(int e) {
+    const int lo = e & 15, r = lo & 3;
+    return 8 * (lo >> 2) + (r & 1) * 4 + (e >> 4) * 2 + (r >> 1);
 }
 
-// 32 weights of one Q4_0 block (GGUF nibble order) as bf16 (q - 8) * s into
-// dst[0..31] (LDS, 16-byte aligned).
-__device__ __forceinline__ void dequant_block_bf16(const u32x4 c, float s, uint16_t* dst) {
-    const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
-    uint32_t lo[8], hi[8];
-    const float m8 = -8.0f * s;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint32_t x = wd[m];
-        // bytes 4m..4m+3: low nibbles are weights 4m..4m+3, high nibbles 4m+16..4m+19
-        const float l0 = fmaf((float)(x & 0xfu), s, m8), l1 = fmaf((float)((x >> 8) & 0xfu), s, m8);
-        const float l2 = fmaf((float)((x >> 16) & 0xfu), s, m8), l3 = fmaf((float)((x >> 24) & 0xfu), s, m8);
-        const float h0 = fmaf((float)((x >> 4) & 0xfu), s, m8), h1 = fmaf((float)((x >> 12) & 0xfu), s, m8);
-        const float h2 = fmaf((float)((x >> 20) & 0xfu), s, m8), h3 = fmaf((float)(x >> 28), s, m8);
-        lo[2 * m] = pack_bf16(l0, l1);
-        lo[2 * m + 1] = pack_bf16(l2, l3);
-        hi[2 * m] = pack_bf16(h0, h1);
-        hi[2 * m + 1] = pack_bf16(h2, h3);
-    }
-    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
-    d4[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    d4[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
-    d4[2] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-    d4[3] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+// Code word g of a Q4_0 block -> eight bf16 B operand values 128 + q, exact:
+// 0x4300 is bf16 128.0, whose last 4 mantissa bits count units, so OR-ing a
+// code into it gives 128 + q.  The zero point is handled by the accumulator's
+// start value: sum_k a_k (128 + q_k) - 136 sum_k a_k = sum_k a_k (q_k - 8).
+__device__ __forceinline__ bf16x8 q4_operand(uint32_t w) {
+    constexpr uint32_t kM = 0x000F000Fu, kC = 0x43004300u;
+    const u32x4 v = {(w & kM) | kC, ((w >> 4) & kM) | kC, ((w >> 8) & kM) | kC, ((w >> 12) & kM) | kC};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi): 16 significant bits
+// in two bf16 operands (hi + lo is exact in fp32).
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+    hi = bf16_bits(v);
+    lo = bf16_bits(v - bf16_value(hi));
 }
 
 // ---------------------------------------------------------------- norm
 
-// Grid T, 256 threads: one token per work-group.
+// Grid T, 256 threads: one token per work-group.  Thread (b, g) = (tid / 4,
+// tid % 4) writes operand positions 8g..8g+7 of Q4_0 block b of the normalised
+// input, as bf16 hi and lo, and the four threads of a block add their hi + lo
+// in a fixed tree for the block's accumulator start value.
 __global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const f32x4* x4 = reinterpret_cast<const f32x4*>(a.x + (int64_t)t * kQD);
-    const f32x4 v0 = x4[tid], v1 = x4[tid + kPfThreads];
+    const int b = tid >> 2, g = tid & 3;
+    const float* xt = a.x + (int64_t)t * kQD;
+    // elements 32b + 4g .. +3 and 32b + 16 + 4g .. +3 of x
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(xt + 32 * b + 4 * g);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(xt + 32 * b + 16 + 4 * g);
     float ss = (v0.x * v0.x + v0.y * v0.y) + (v0.z * v0.z + v0.w * v0.w);
     ss += (v1.x * v1.x + v1.y * v1.y) + (v1.z * v1.z + v1.w * v1.w);
     ss = wave_sum(ss);
@@ -97,16 +114,32 @@ __global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
     const float tot = (part[0] + part[1]) + (part[2] + part[3]);
     const float inv = a.norm ? 1.0f / sqrtf(tot / (float)kQD + a.eps) : 1.0f;
     if (tid == 0) a.inv[t] = inv;
-    uint32_t* u2 = reinterpret_cast<uint32_t*>(a.u + (int64_t)t * kQD);
-    u2[2 * tid] = pack_bf16(v0.x * inv, v0.y * inv);
-    u2[2 * tid + 1] = pack_bf16(v0.z * inv, v0.w * inv);
-    u2[2 * (tid + kPfThreads)] = pack_bf16(v1.x * inv, v1.y * inv);
-    u2[2 * (tid + kPfThreads) + 1] = pack_bf16(v1.z * inv, v1.w * inv);
+    // operand order: j = 0..7 -> elements 4g + {0, 2, 16, 18, 1, 3, 17, 19}
+    const float e[8] = {v0.x, v0.z, v1.x, v1.z, v0.y, v0.w, v1.y, v1.w};
+    uint16_t hi[8], lo[8];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        split_bf16(e[j] * inv, hi[j], lo[j]);
+        s += bf16_value(hi[j]) + bf16_value(lo[j]);
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    uint16_t* dst = a.u + ((int64_t)t * (kQD / 32) + b) * 64 + 8 * g;
+    u32x4 vh, vl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        vh[j] = (uint32_t)hi[2 * j] | ((uint32_t)hi[2 * j + 1] << 16);
+        vl[j] = (uint32_t)lo[2 * j] | ((uint32_t)lo[2 * j + 1] << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst) = vh;
+    *reinterpret_cast<u32x4*>(dst + 32) = vl;
+    if (g == 0) a.cu[(int64_t)t * (kQD / 32) + b] = -136.0f * s;
     const int64_t tt = (int64_t)*a.tr_base + t;
     if (a.tr_x && tt < a.tr_cap) {
-        f32x4* tr = reinterpret_cast<f32x4*>(a.tr_x + (tt * a.L + a.layer) * kQD);
-        tr[tid] = v0;
-        tr[tid + kPfThreads] = v1;
+        f32x4* tr = reinterpret_cast<f32x4*>(a.tr_x + (tt * a.L + a.layer) * kQD + 32 * b + 4 * g);
+        tr[0] = v0;
+        tr[4] = v1;
     }
 }
 
@@ -394,178 +427,305 @@ __device__ bool pf_item(const PfArgs& a, int item, int& e, int& pos0, int& rows,
     return true;
 }
 
-// MFMA tile compute of one kBK step: wave (wm, wn) owns rows wm*64..+63 and
-// the 4 16-column groups listed in cols[]; acc[mi][nj] is 16x16.
-__device__ __forceinline__ void mfma_step(const uint16_t* As, const uint16_t* Bs, int wm, const int* cols,
-                                          f32x4 (&acc)[4][4]) {
-    const int lane = threadIdx.x & 63;
-    const int lr = lane & 15, lk = (lane >> 4) * 8;
+// One Q4_0 block of a grouped-GEMM tile (kBM tokens x kNB weight rows),
+// staged in LDS.  The tile is double-buffered over two of these: while the
+// matrix cores work on block b, the next block's global loads are in flight,
+// and their LDS stores go to the other stage, so one barrier per block
+// suffices.
+struct PfStage {
+    uint16_t a[kBM * kOpRow];  // activation rows: hi 32 | lo 32 | pad, operand order
+    uint32_t q[kNB * 4];       // the weight rows' code words (16 B per row)
+    float s[kNB];              // the weight rows' block scales
+    float c[kBM];              // the activation rows' accumulator start values
+};
+
+// Wave (wm, wn) of a 2 x 2 arrangement over the tile: rows wm*64..wm*64+63,
+// the four 16-column groups cols[0..3].  Per 16 x 16 output tile and block:
+// c = start + A_hi B + A_lo B on the matrix cores (B = 128 + q exact, so c is
+// the block's exact-code dot product up to fp32 rounding), then acc += s * c
+// in fp32: the block scale is applied to the block's sum, never rounded into
+// a bf16 weight.
+struct PfAFrag {
+    bf16x8 hi, lo;  // 16 activation rows x 32 k, operand order
+    f32x4 c0;       // their start values
+};
+
+__device__ __forceinline__ PfAFrag pf_afrag(const PfStage& st, int wm, int mi) {
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const uint16_t* row = st.a + (wm * 64 + mi * 16 + li) * kOpRow + 8 * lg;
+    PfAFrag f;
+    f.hi = *reinterpret_cast<const bf16x8*>(row);
+    f.lo = *reinterpret_cast<const bf16x8*>(row + 32);
+    f.c0 = *reinterpret_cast<const f32x4*>(st.c + wm * 64 + mi * 16 + 4 * lg);
+    return f;
+}
+
+// Software-pipelined over the four 16-row groups: group mi's MFMAs are
+// issued together with group mi-1's scale FMAs and group mi+1's LDS operand
+// reads, so the matrix cores need not wait for the VALU or for LDS.
+__device__ __forceinline__ void pf_mfma_block(const PfStage& st, int wm, const int* cols, f32x4 (&acc)[4][4]) {
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    bf16x8 bq[4];
+    float sc[4];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-        bf16x8 af[4], bfr[4];
+    for (int nj = 0; nj < 4; ++nj) {
+        bq[nj] = q4_operand(st.q[(cols[nj] + li) * 4 + lg]);
+        sc[nj] = st.s[cols[nj] + li];
+    }
+    PfAFrag f = pf_afrag(st, wm, 0);
+    f32x4 cp[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-            af[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + mi * 16 + lr) * kLdsRow + kh * 32 + lk);
+    for (int mi = 0; mi < 4; ++mi) {
+        PfAFrag fn;
+        if (mi + 1 < 4) fn = pf_afrag(st, wm, mi + 1);
+        f32x4 c[4];
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj)
-            bfr[nj] = *reinterpret_cast<const bf16x8*>(Bs + (cols[nj] + lr) * kLdsRow + kh * 32 + lk);
+        for (int nj = 0; nj < 4; ++nj) c[nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.hi, bq[nj], f.c0, 0, 0, 0);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int nj = 0; nj < 4; ++nj) c[nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.lo, bq[nj], c[nj], 0, 0, 0);
+        if (mi > 0) {
 #pragma unroll
             for (int nj = 0; nj < 4; ++nj)
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[mi - 1][nj][r] = fmaf(sc[nj], cp[nj][r], acc[mi - 1][nj][r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) cp[nj] = c[nj];
+        if (mi + 1 < 4) f = fn;
+    }
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[3][nj][r] = fmaf(sc[nj], cp[nj][r], acc[3][nj][r]);
+}
+
+// Registers a thread carries from the global loads of a block to its LDS stores.
+struct PfLoad {
+    u32x4 a[4];
+    u32x4 q;
+    uint32_t sc;  // bits of a token row's fp32 start value (threads 0..127) or of a weight row's fp16
+                  // scale (threads 128..255): converted only at the LDS store, so that nothing waits
+                  // for the loads before the block's matrix-core work has been issued
+};
+
+// A thread's global sources for the blocks of a tile, as block-0 pointers
+// and per-block strides.  Thread tid: activation row tid/2, its hi (even tid)
+// or lo (odd tid) half (64 B); threads 0..127 also the start value of token
+// row tid and the code words of weight row tid, threads 128..255 the fp16
+// scale of weight row tid - 128.  Rows past the group read the group's first
+// row instead: a GEMM output row depends only on its own activation row, and
+// those output rows are never stored.
+struct PfSrc {
+    const u32x4* a;      // 8 u32x4 per block
+    const float* c;      // 1 per block
+    const u32x4* q;      // q_stride u32x4 per block
+    const uint16_t* s;   // s_stride halves per block
+    int q_stride, s_stride;
+};
+
+__device__ __forceinline__ void pf_load(PfLoad& ld, int b, const PfSrc& src) {
+    const u32x4* p = src.a + 8 * b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ld.a[j] = p[j];
+    if (threadIdx.x < kNB) {
+        ld.q = __builtin_nontemporal_load(src.q + src.q_stride * b);
+        ld.sc = __float_as_uint(src.c[b]);
+    } else {
+        ld.sc = src.s[src.s_stride * b];
     }
 }
 
-// Grid (n_items, f/64), 256 threads.  Work-group tile: kBM tokens of one
-// expert group x (64 gate rows + the same 64 up rows); wave w: rows
-// (w&1)*64.., gate and up columns (w>>1)*32..; SwiGLU in the epilogue.
-// B rows come from the slot's gate/up region (chunk g = row/16: codes at
-// ((ww*8 + i)*64 + b)*16, scales at 32768 + (ww*64 + b)*16 + 2i).
-__global__ __launch_bounds__(kPfThreads) void pf_gateup_kernel(PfArgs a) {
-    if ((int)blockIdx.x < a.n_fill_x) {  // the leading columns pull the fills
-        pf_fill_pieces(a, (int)(blockIdx.y * a.n_fill_x + blockIdx.x), a.n_fill_x * (int)gridDim.y, 0, kFillGUShare);
+__device__ __forceinline__ void pf_store(PfStage& st, const PfLoad& ld) {
+    const int tid = threadIdx.x;
+    u32x4* ad = reinterpret_cast<u32x4*>(st.a + (tid >> 1) * kOpRow + (tid & 1) * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ad[j] = ld.a[j];
+    if (tid < kNB) {
+        *reinterpret_cast<u32x4*>(st.q + tid * 4) = ld.q;
+        st.c[tid] = __uint_as_float(ld.sc);
+    } else {
+        st.s[tid - kNB] = half_bits_to_float(ld.sc);
+    }
+}
+
+// The k loop of a tile over nb Q4_0 blocks: block b + 1's global loads are
+// in flight while the matrix cores work on block b, then go to the other LDS
+// stage; one barrier per block.
+__device__ __forceinline__ void pf_tile(PfStage (&st)[2], int nb, const PfSrc& src, int wm, const int* cols,
+                                        f32x4 (&acc)[4][4]) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    PfLoad ld;
+    pf_load(ld, 0, src);
+    pf_store(st[0], ld);
+    __syncthreads();
+    for (int b = 0; b < nb; ++b) {
+        if (b + 1 < nb) pf_load(ld, b + 1, src);
+        pf_mfma_block(st[b & 1], wm, cols, acc);
+        if (b + 1 < nb) pf_store(st[(b + 1) & 1], ld);
+        __syncthreads();
+    }
+}
+
+// Work-group -> role in a grouped-GEMM launch (1-D grid).  The first
+// n_fill_x * ncols work-groups pull fills (returns -1, wid = their index).
+// The rest compute tiles, XCD-aware: work-groups are dealt to the 8 XCDs
+// round-robin in launch order, so the (L'/8)-th tile work-group of XCD L'%8
+// gets item X = (L'%8) * per + (L'/8) / ncols, weight-row tile
+// Y = (L'/8) % ncols, with per = ceil(n_items / 8).  Each XCD thus takes a
+// contiguous range of items, all ncols tiles of an item in a row: the tiles
+// that share an item's activation rows, and the items that share an
+// expert's weights (a group's items are adjacent), run under one L2.
+// Returns 1 for a tile, 0 for padding.
+__device__ __forceinline__ int pf_role(const PfArgs& a, int ncols, int& X, int& Y) {
+    const int L = (int)blockIdx.x, nfill = a.n_fill_x * ncols;
+    if (L < nfill) {
+        X = L;
+        return -1;
+    }
+    const int Lp = L - nfill, j = Lp >> 3, per = (a.n_items + 7) >> 3;
+    X = (Lp & 7) * per + j / ncols;
+    Y = j % ncols;
+    return X < a.n_items ? 1 : 0;
+}
+
+// 1-D grid (pf_role), 256 threads.  Work-group tile: kBM tokens of one
+// expert group x (64 gate rows + the same 64 up rows); wave w: token rows
+// (w&1)*64.., gate and up columns (w>>1)*32..; SwiGLU in the epilogue, h
+// written per Q4_0 block of f as bf16 hi and lo in operand order with its
+// start value.  Weight rows come from the slot's gate/up region (chunk
+// g = row/16: codes at ((ww*8 + i)*64 + b)*16, scales at
+// 32768 + (ww*64 + b)*16 + 2i).
+__global__ __launch_bounds__(kPfThreads, 2) void pf_gateup_kernel(PfArgs a) {
+    constexpr int ncols = kQF / 64;
+    int X, Y;
+    const int role = pf_role(a, ncols, X, Y);
+    if (role < 0) {  // the leading work-groups pull the fills
+        pf_fill_pieces(a, X, a.n_fill_x * ncols, 0, kFillGUShare);
         return;
     }
+    if (role == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int n0 = blockIdx.y * 64;
+    const int n0 = Y * 64;
     int e, pos0, rows;
     const uint8_t* S;
-    if (!pf_item(a, (int)blockIdx.x - a.n_fill_x, e, pos0, rows, S)) return;
-    __shared__ __align__(16) uint16_t As[kBM * kLdsRow];
-    __shared__ __align__(16) uint16_t Bs[128 * kLdsRow];
+    if (!pf_item(a, X, e, pos0, rows, S)) return;
+    __shared__ __align__(16) PfStage st[2];
     __shared__ int tok[kBM];
     if (tid < kBM) tok[tid] = tid < rows ? a.perm[pos0 + tid] : -1;
     __syncthreads();
-    // A loads: row tid>>1, 32 bf16 (64 B) at column half (tid&1)*32
-    const int ar = tid >> 1, ah = (tid & 1) * 32;
-    const int atok = tok[ar];
-    const u32x4* arow = atok >= 0 ? reinterpret_cast<const u32x4*>(a.u + (int64_t)atok * kQD + ah) : nullptr;
-    // B loads: row br = tid>>1 (gate rows 0..63, up rows 64..127), block (tid&1) of the step
-    const int br = tid >> 1, bb = tid & 1;
-    const int mrow = n0 + (br & 63);
-    const int ww = (br >= 64 ? 2 : 0) + ((mrow >> 3) & 1);
-    const uint8_t* bchunk = S + (int64_t)(mrow >> 4) * kGUChunk;
-    const int bi = mrow & 7;
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int nbd = kQD / 32;
+    PfSrc src;
+    const int atok = tok[(tid >> 1) < rows ? tid >> 1 : 0];
+    src.a = reinterpret_cast<const u32x4*>(a.u + (int64_t)atok * nbd * 64 + (tid & 1) * 32);
+    src.c = a.cu + (int64_t)tok[(tid & (kBM - 1)) < rows ? tid & (kBM - 1) : 0] * nbd;
+    // weight row r = tid % 128 of the tile: gate rows n0..n0+63, then the
+    // same up rows; chunk mrow/16 holds it as wave-row (ww, bi)
+    {
+        const int r = tid & (kNB - 1);
+        const int mrow = n0 + (r & 63);
+        const int ww = (r >= 64 ? 2 : 0) + ((mrow >> 3) & 1), bi = mrow & 7;
+        const uint8_t* ch = S + (int64_t)(mrow >> 4) * kGUChunk;
+        src.q = reinterpret_cast<const u32x4*>(ch + (ww * 8 + bi) * 64 * 16);
+        src.q_stride = 1;
+        src.s = reinterpret_cast<const uint16_t*>(ch + 32768 + ww * 64 * 16 + bi * 2);
+        src.s_stride = 8;
+    }
     const int wm = w & 1, wn = w >> 1;
     const int cols[4] = {wn * 32, wn * 32 + 16, 64 + wn * 32, 64 + wn * 32 + 16};
+    f32x4 acc[4][4];
+    pf_tile(st, nbd, src, wm, cols, acc);
 
-    u32x4 ra[4], rc;
-    uint32_t rsc;
-    auto load = [&](int k0) {
-        const int b = k0 / 32 + bb;
-        if (arow) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ra[j] = arow[k0 / 8 + j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ra[j] = u32x4{0u, 0u, 0u, 0u};
-        }
-        rc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bchunk + ((ww * 8 + bi) * 64 + b) * 16));
-        rsc = *reinterpret_cast<const uint16_t*>(bchunk + 32768 + (ww * 64 + b) * 16 + bi * 2);
-    };
-    load(0);
-    for (int k0 = 0; k0 < kQD; k0 += kBK) {
-        __syncthreads();
-        {
-            u32x4* ad = reinterpret_cast<u32x4*>(As + ar * kLdsRow + ah);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ad[j] = ra[j];
-            dequant_block_bf16(rc, half_bits_to_float(rsc), Bs + br * kLdsRow + bb * 32);
-        }
-        __syncthreads();
-        if (k0 + kBK < kQD) load(k0 + kBK);
-        mfma_step(As, Bs, wm, cols, acc);
-    }
-    // epilogue: h = silu(gate) * up, bf16
-    const int lr = lane & 15, lq = (lane >> 4) * 4;
+    // Epilogue.  The wave's 32 h columns are one Q4_0 block fb of f: element
+    // nj*16 + li of it for nj = 0, 1.  Rows are staged in LDS (the stages are
+    // free after the loop's last barrier) in operand order, then written out
+    // 16 bytes per lane; the block's start value sums hi + lo over the 32
+    // elements (per lane, then over the 16 lanes of a row, fixed tree).
+    const int li = lane & 15, lg = lane >> 4;
+    const int fb = Y * 2 + wn;
+    static_assert(2 * kBM * 64 * sizeof(uint16_t) <= 2 * sizeof(PfStage), "h staging fits the stages");
+    uint16_t* stage = reinterpret_cast<uint16_t*>(&st[0]) + wn * kBM * 64;  // [wn][128 rows][64]
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 2; ++nj)
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm * 64 + mi * 16 + 4 * lg + r;
+            float sum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = wm * 64 + mi * 16 + lq + r;
-                if (row < rows) {
-                    const float g = acc[mi][nj][r], u = acc[mi][nj + 2][r];
-                    a.h[(int64_t)(pos0 + row) * kQF + n0 + wn * 32 + nj * 16 + lr] = bf16_bits(silu(g) * u);
-                }
+            for (int nj = 0; nj < 2; ++nj) {
+                const float g = acc[mi][nj][r], u = acc[mi][nj + 2][r];
+                uint16_t hi, lo;
+                split_bf16(silu(g) * u, hi, lo);
+                sum += bf16_value(hi) + bf16_value(lo);
+                const int p = op_pos(nj * 16 + li);
+                stage[row * 64 + p] = hi;
+                stage[row * 64 + 32 + p] = lo;
             }
+            sum += __shfl_xor(sum, 1, 64);
+            sum += __shfl_xor(sum, 2, 64);
+            sum += __shfl_xor(sum, 4, 64);
+            sum += __shfl_xor(sum, 8, 64);
+            if (li == 0 && row < rows) a.ch[(int64_t)(pos0 + row) * (kQF / 32) + fb] = -136.0f * sum;
+        }
+    __syncthreads();
+    // 128 rows x 2 blocks x 128 B: thread tid copies 16 B pieces tid, tid + 256, ...
+    for (int i = tid; i < kBM * 2 * 8; i += kPfThreads) {
+        const int row = i >> 4, wb = (i >> 3) & 1, piece = i & 7;
+        if (row < rows) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<uint16_t*>(&st[0]) + wb * kBM * 64 +
+                                                            row * 64 + piece * 8);
+            *reinterpret_cast<u32x4*>(a.h + ((int64_t)(pos0 + row) * (kQF / 32) + Y * 2 + wb) * 64 + piece * 8) = v;
+        }
+    }
 }
 
-// Grid (n_items, d/128), 256 threads.  Work-group tile: kBM tokens x 128
-// down rows; wave w: rows (w&1)*64.., columns (w>>1)*64...  B rows from the
-// slot's down region: codes [r][b][16 B], scales [r/4][b][4] fp16.
-__global__ __launch_bounds__(kPfThreads) void pf_down_kernel(PfArgs a) {
-    if ((int)blockIdx.x < a.n_fill_x) {  // the leading columns pull the rest of the fills
-        pf_fill_pieces(a, (int)(blockIdx.y * a.n_fill_x + blockIdx.x), a.n_fill_x * (int)gridDim.y, kFillGUShare,
-                       256);
+// 1-D grid (pf_role), 256 threads.  Work-group tile: kBM tokens x 128
+// down rows; wave w: token rows (w&1)*64.., columns (w>>1)*64...  Weight
+// rows from the slot's down region: codes [r][b][16 B], scales
+// [r/4][b][4] fp16.
+__global__ __launch_bounds__(kPfThreads, 2) void pf_down_kernel(PfArgs a) {
+    constexpr int ncols = kQD / kNB;
+    int X, Y;
+    const int role = pf_role(a, ncols, X, Y);
+    if (role < 0) {  // the leading work-groups pull the rest of the fills
+        pf_fill_pieces(a, X, a.n_fill_x * ncols, kFillGUShare, 256);
         return;
     }
+    if (role == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int n0 = blockIdx.y * 128;
+    const int n0 = Y * kNB;
     int e, pos0, rows;
     const uint8_t* S;
-    if (!pf_item(a, (int)blockIdx.x - a.n_fill_x, e, pos0, rows, S)) return;
-    __shared__ __align__(16) uint16_t As[kBM * kLdsRow];
-    __shared__ __align__(16) uint16_t Bs[128 * kLdsRow];
-    const int ar = tid >> 1, ah = (tid & 1) * 32;
-    const u32x4* arow = ar < rows ? reinterpret_cast<const u32x4*>(a.h + (int64_t)(pos0 + ar) * kQF + ah) : nullptr;
-    const int br = tid >> 1, bb = tid & 1;
-    const int drow = n0 + br;
-    const uint8_t* dcodes = S + kGURegion + (int64_t)drow * 256;
-    const uint8_t* dscales = S + kGURegion + kDownCodes + (int64_t)(drow >> 2) * 128 + (drow & 3) * 2;
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (!pf_item(a, X, e, pos0, rows, S)) return;
+    __shared__ __align__(16) PfStage st[2];
+    constexpr int nbf = kQF / 32;
+    PfSrc src;
+    const int ar = (tid >> 1) < rows ? tid >> 1 : 0, cr = (tid & (kBM - 1)) < rows ? tid & (kBM - 1) : 0;
+    src.a = reinterpret_cast<const u32x4*>(a.h + (int64_t)(pos0 + ar) * nbf * 64 + (tid & 1) * 32);
+    src.c = a.ch + (int64_t)(pos0 + cr) * nbf;
+    {
+        const int n = n0 + (tid & (kNB - 1));
+        src.q = reinterpret_cast<const u32x4*>(S + kGURegion + (int64_t)n * 256);
+        src.q_stride = 1;
+        src.s = reinterpret_cast<const uint16_t*>(S + kGURegion + kDownCodes + (int64_t)(n >> 2) * 128 + (n & 3) * 2);
+        src.s_stride = 4;
+    }
     const int wm = w & 1, wn = w >> 1;
     const int cols[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
-
-    u32x4 ra[4], rc;
-    uint32_t rsc;
-    auto load = [&](int k0) {
-        const int b = k0 / 32 + bb;
-        if (arow) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ra[j] = arow[k0 / 8 + j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ra[j] = u32x4{0u, 0u, 0u, 0u};
-        }
-        rc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dcodes + b * 16));
-        rsc = *reinterpret_cast<const uint16_t*>(dscales + b * 8);
-    };
-    load(0);
-    for (int k0 = 0; k0 < kQF; k0 += kBK) {
-        __syncthreads();
-        {
-            u32x4* ad = reinterpret_cast<u32x4*>(As + ar * kLdsRow + ah);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ad[j] = ra[j];
-            dequant_block_bf16(rc, half_bits_to_float(rsc), Bs + br * kLdsRow + bb * 32);
-        }
-        __syncthreads();
-        if (k0 + kBK < kQF) load(k0 + kBK);
-        mfma_step(As, Bs, wm, cols, acc);
-    }
-    const int lr = lane & 15, lq = (lane >> 4) * 4;
+    f32x4 acc[4][4];
+    pf_tile(st, nbf, src, wm, cols, acc);
+    const int li = lane & 15, lg = lane >> 4;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int nj = 0; nj < 4; ++nj)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = wm * 64 + mi * 16 + lq + r;
-                if (row < rows) a.y[(int64_t)(pos0 + row) * kQD + n0 + cols[nj] + lr] = acc[mi][nj][r];
+                const int row = wm * 64 + mi * 16 + 4 * lg + r;
+                if (row < rows) a.y[(int64_t)(pos0 + row) * kQD + n0 + cols[nj] + li] = acc[mi][nj][r];
             }
 }
 
@@ -634,10 +794,11 @@ hipError_t launch_pf_policy(const PfArgs& a, hipStream_t s) {
 hipError_t launch_pf_gemms(const PfArgs& a, hipStream_t s) {
     if (a.n_fill_x < 0 || (a.n_fill_x > 0 && (!a.arena || a.slot_bytes % 16 || a.pt.R > kMaxR)))
         return hipErrorInvalidValue;
-    if (a.n_items + a.n_fill_x > 0)
-        hipLaunchKernelGGL(pf_gateup_kernel, dim3(a.n_items + a.n_fill_x, kQF / 64), dim3(kPfThreads), 0, s, a);
-    if (a.n_items + a.n_fill_x > 0)
-        hipLaunchKernelGGL(pf_down_kernel, dim3(a.n_items + a.n_fill_x, kQD / 128), dim3(kPfThreads), 0, s, a);
+    // 1-D grids: the fill work-groups, then the tiles with the item count
+    // padded to a multiple of 8 (the XCD-aware mapping, pf_role)
+    const int nx = a.n_fill_x + ((a.n_items + 7) & ~7);
+    if (nx > 0) hipLaunchKernelGGL(pf_gateup_kernel, dim3(nx * (kQF / 64)), dim3(kPfThreads), 0, s, a);
+    if (nx > 0) hipLaunchKernelGGL(pf_down_kernel, dim3(nx * (kQD / kNB)), dim3(kPfThreads), 0, s, a);
     return hipGetLastError();
 }
 

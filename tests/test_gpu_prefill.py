@@ -10,9 +10,8 @@ Checks, per layer and teacher-forced (the oracle's layer l takes the GPU's
 traced input of layer l):
  * top-k bit-exact except router near-ties (K-th vs (K+1)-th oracle logit
    closer than 1e-5), where the oracle adopts the GPU's selection;
- * layer output x_{l+1} within 2e-3 * max|x_{l+1}| of the fp64 oracle (the
-   stack's layer output is the updated residual stream); the error relative to
-   the MoE term alone is printed;
+ * each layer's MoE term (x_{l+1} - x_l) within 2e-3 * max|MoE term| of the
+   fp64 oracle; the error relative to the residual stream is printed;
  * placement bookkeeping (counts, pinned set, ring owners and stamps, fill log,
    counters) equal to the simulator replaying the GPU's own top-k trace with
    the prefill access order (distinct experts per layer, ascending id);
@@ -112,12 +111,10 @@ def test_prefill_parity_bookkeeping_and_residency_invariance():
                                               bias=bias, bias_row=rows[sample], forced=forced[sample])
         np.testing.assert_allclose(tr_g[sample, l], g_ref, rtol=2e-5, atol=1e-6)
         x_next = (tr_x[sample, l + 1] if l + 1 < w.L else full["x"][sample]).astype(np.float64)
-        ref_next = xs + y_ref
-        err = np.abs(x_next - ref_next).max()
-        scale = np.abs(ref_next).max()
-        strict = err / np.abs(y_ref).max()
-        print(f"layer {l}: max|err| {err:.3e} = {err / scale:.2e} of max|x_next|, "
-              f"{strict:.2e} of max|MoE output|", flush=True)
+        err = np.abs((x_next - xs) - y_ref).max()
+        scale = np.abs(y_ref).max()
+        print(f"layer {l}: max|err| {err:.3e} = {err / scale:.2e} of max|MoE term|, "
+              f"{err / np.abs(xs + y_ref).max():.2e} of max|x_next|", flush=True)
         assert err <= 2e-3 * scale, (l, err, scale)
     assert ties <= max(1, (T * w.L) // 50)
 
