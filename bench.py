@@ -9,27 +9,39 @@ layers at 60% expert residency.
    seeded permutation).
  - Residency: P = 6144 of 10,240 experts pinned, plus a 32-slot LRU spare
    ring.
- - Placement: calibrated from a 256-token warm-up run under uniform placement.
-A step is one decode token through all 40 layers (one graph launch).  The
-same protocol at full residency runs first, giving the ratio and the
+ - Placement: calibrated from a 256-token warm-up trace decoded under uniform
+   placement (always 256 tokens, whatever --warmup says).
+Protocol of a decode setting: the 256 calibration tokens (t = 0..255) under
+uniform placement, calibration, then --warmup untimed decode tokens (drawn
+after the measured stream), a statistics reset, and --steps timed tokens
+(t = 256..): a step is one decode token through all 40 layers (one graph
+launch).  The same protocol at full residency gives the ratio and the
 bit-identity check.
 
-Nested in the same line:
+Nested in the same line, each on the fixed 512-token measured stream
+(t = 256..767), independent of --steps:
  - `sweep`: residency 100/60/30% x {uniform static, calibrated + ring}, with
    tok/s, cold-hit %, fill %, PCIe bytes and bit-identity of the outputs.
+ - `batched`: the same decode in steps of B tokens (moe_spark_decode_batched),
+   the ring widened to B*top_k slots where it is smaller; tok/s, distinct
+   experts per layer-step, algorithmic weight GB/s, the largest difference
+   from batch-1 outputs, counter-measured bytes per launch at B = 16.
+ - `self_tuning`: calibrated under router bias row A, the stream decoded
+   under row B with the placement fixed and with online self-tuning.
+ - `fill_path`: host-to-device rates of cold fills: the pulled fills'
+   effective rate in the fill-bound 60%-uniform arm, and the host agent's
+   copies (MOE_SPARK_PULL_FILLS=0) in the same arm.
+Also:
  - `prefill`: 2048 tokens through the stack in one batch, 60% residency.
    1. Placement is calibrated from the decode warm-up under permutation A.
    2. The Zipf permutation switches to B at token 1024.
    3. Then a 256-token decode probe under B runs before and after
       recalibration.
- - `batched`: the same decode in steps of B tokens (moe_spark_decode_batched),
-   the ring widened to B*top_k slots where it is smaller; tok/s, distinct
-   experts per layer-step, algorithmic weight GB/s, the largest difference
-   from batch-1 outputs, counter-measured bytes per launch at B = 16.
  - `roofline`: the dominant decode kernel, timed by HIP events over isolated
    replays.
  - `h2d_link`: a pinned host-to-device copy probe of the PCIe link.
- - `cpu_baseline`: the fp64 oracle on a bounded sample of the decode stream.
+ - `cpu_baseline`: the fp64 oracle on a bounded sample of the decode stream,
+   on all host threads and on one.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -52,6 +64,8 @@ EXPERT_BYTES = 1_769_472          # one Q4_0 expert: gate | up | down
 GATEUP_BYTES = 8 * 2 * 589_824    # algorithmic bytes of one gate/up launch (8 experts)
 DOWN_BYTES = 8 * 589_824 + 256 * 2048 * 4  # down weights of 8 experts + the next layer's router
 TOKEN_BYTES_PER_LAYER = 8 * EXPERT_BYTES + 256 * 2048 * 4
+CALIB_TOKENS = 256   # the warm-up trace placement is calibrated from
+STREAM_TOKENS = 512  # the measured stream of the sweep, batched and self-tuning legs
 
 
 def log(*a):
@@ -95,21 +109,27 @@ def rates(st):
                 fill_pct=round(100.0 * st["fills"] / acc, 4))
 
 
-def run_decode(ms, torch, model, P, R, warm, meas, row, calibrate, kernel_iters=0):
-    """One residency setting: warm-up under uniform placement, optional
-    calibration, then the timed decode of `meas`."""
+def run_decode(ms, torch, model, P, R, calib, untimed, meas, row, calibrate, kernel_iters=0):
+    """One residency setting: the calibration trace under uniform placement,
+    optional calibration, untimed warm-up tokens, then the timed decode of
+    `meas` (statistics cover exactly the timed tokens)."""
     t0 = time.time()
     ctx = model.make_ctx(P=P, R=R)
     log(f"P={P} R={R} calibrated={calibrate}: context ready in {time.time() - t0:.1f}s")
     try:
-        xw = torch.from_numpy(warm).cuda()
+        xc = torch.from_numpy(calib).cuda()
         xm = torch.from_numpy(meas).cuda()
-        ms.moe_spark_decode(ctx, xw.data_ptr(), xw.shape[0], row.data_ptr())
+        ms.moe_spark_decode(ctx, xc.data_ptr(), xc.shape[0], row.data_ptr())
         ms.moe_spark_synchronize(ctx)
         if calibrate:
             ms.moe_spark_calibrate(ctx, True)
+        if untimed is not None and untimed.shape[0]:
+            xu = torch.from_numpy(untimed).cuda()
+            ms.moe_spark_decode(ctx, xu.data_ptr(), xu.shape[0], row.data_ptr())
+            ms.moe_spark_synchronize(ctx)
         ms.moe_spark_reset_stats(ctx)
         ms.moe_spark_decode(ctx, xm.data_ptr(), 0, row.data_ptr())  # build the graph
+        ms.moe_spark_synchronize(ctx)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms.moe_spark_decode(ctx, xm.data_ptr(), xm.shape[0], row.data_ptr())
@@ -243,7 +263,8 @@ def run_prefill(ms, torch, model, P, R, warm, probe, layers):
                    h2d_bytes=st["h2d_bytes"], cold_hit_pct=rates(st)["cold_hit_pct"],
                    probe_cold_hit_pct_before_recalibration=before,
                    probe_cold_hit_pct_after_recalibration=after,
-                   arithmetic="Q4_0->bf16 dequant in LDS, bf16 activations, MFMA fp32 accumulation")
+                   arithmetic="Q4_0 codes as exact bf16 (128 + q, zero point in the MFMA start value), "
+                              "activations as bf16 hi + lo, fp32 accumulation, fp16 block scales applied in fp32")
         log(f"prefill: {out['tok_s']} tok/s, fills {st['fills']}, cold probe {before}% -> {after}%")
         return out
     finally:
@@ -314,27 +335,85 @@ def h2d_probe(torch, mib=256, reps=5):
     return dict(bytes=mib << 20, gbps=round((mib << 20) / best / 1e9, 2))
 
 
-def cpu_baseline(model, tokens, budget_s):
-    """The fp64 oracle on a bounded sample of the same decode stream."""
+def cpu_baseline(model, tokens, budget_s, single_tokens=1):
+    """The fp64 oracle on a bounded sample of the same decode stream: on all
+    host threads (OpenMP) and on one."""
     import oracle
     w = model.w
     experts = [model.experts(l) for l in range(w.L)]
-    n, t0 = 0, time.perf_counter()
-    while n < tokens.shape[0] and (n < 2 or time.perf_counter() - t0 < budget_s):
-        oracle.stack(tokens[n:n + 1].astype(np.float64), model.routers, model.biases, experts, K=w.K,
-                     wfmt=w.wfmt, bias_row=np.zeros(1, np.int32))
-        n += 1
-    dt = time.perf_counter() - t0
-    return dict(value=round(n / dt, 3), unit="tok/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{n} decode tokens of the 40-layer stack (fp64, all layers), "
-                       f"{dt:.1f} s of CPU work")
+
+    def run(n_max, budget):
+        n, t0 = 0, time.perf_counter()
+        while n < n_max and (n < 1 or time.perf_counter() - t0 < budget):
+            oracle.stack(tokens[n:n + 1].astype(np.float64), model.routers, model.biases, experts, K=w.K,
+                         wfmt=w.wfmt, bias_row=np.zeros(1, np.int32))
+            n += 1
+        return n, time.perf_counter() - t0
+
+    threads = oracle.num_threads()
+    n, dt = run(tokens.shape[0], budget_s)
+    oracle.set_num_threads(1)
+    n1, dt1 = run(single_tokens, 0.0)
+    oracle.set_num_threads(threads)
+    model_name = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model_name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=round(n / dt, 3), unit="tok/s", cores=threads, kind="oracle",
+                sample=f"{n} decode tokens of the 40-layer stack (fp64, all layers) on {threads} threads, "
+                       f"{dt:.1f} s of CPU work; {n1} token(s) on 1 thread, {dt1:.1f} s",
+                single_thread_tok_s=round(n1 / dt1, 4), cpu_model=model_name,
+                host_cpus=os.cpu_count())
+
+
+def fill_path(ms, torch, model, P, R, calib, meas, row, full_tok_s, pulled_row):
+    """Host-to-device rates of cold fills in the fill-bound 60%-uniform arm.
+    Pulled fills (the default) have no copy of their own to time: their
+    effective rate is the arm's fill bytes over the time the arm spends
+    beyond full-residency decode of the same tokens.  Host-agent copies
+    (MOE_SPARK_PULL_FILLS=0, read at context creation) report the agent's
+    request-to-ready latency per fill."""
+    out = {}
+    if pulled_row is not None and full_tok_s:
+        n = pulled_row["x_out"].shape[0]
+        extra = pulled_row["elapsed_s"] - n / full_tok_s
+        st = pulled_row["stats"]
+        out["pulled"] = dict(fills=st["fills"], h2d_bytes=st["h2d_bytes"],
+                             fills_per_token=round(st["fills"] / n, 2),
+                             effective_gbps=round(st["h2d_bytes"] / extra / 1e9, 2) if extra > 0 else None,
+                             us_per_fill=round(extra * 1e6 / max(st["fills"], 1), 2))
+    old = os.environ.get("MOE_SPARK_PULL_FILLS")
+    os.environ["MOE_SPARK_PULL_FILLS"] = "0"
+    try:
+        r = run_decode(ms, torch, model, P, R, calib, None, meas, row, calibrate=False)
+    finally:
+        if old is None:
+            os.environ.pop("MOE_SPARK_PULL_FILLS", None)
+        else:
+            os.environ["MOE_SPARK_PULL_FILLS"] = old
+    st = r["stats"]
+    out["agent"] = dict(tokens=meas.shape[0], tok_s=round(r["tok_s"], 2), fills=st["fills"],
+                        h2d_bytes=st["h2d_bytes"],
+                        gbps_per_fill=round(st["h2d_bytes"] / st["fill_ns_sum"], 2) if st["fill_ns_sum"] else None,
+                        mean_fill_us=round(st["fill_ns_sum"] / max(st["fills"], 1) / 1e3, 2),
+                        max_fill_us=round(st["fill_ns_max"] / 1e3, 2),
+                        note="per fill: slot bytes over the agent's request-seen -> copy-landed time")
+    log(f"fill path: pulled {out.get('pulled')}, agent {out['agent']}")
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=STREAM_TOKENS, help="timed decode tokens of the headline")
+    ap.add_argument("--warmup", type=int, default=16,
+                    help="untimed decode tokens after calibration, before the timed ones")
+    ap.add_argument("--calib-tokens", type=int, default=CALIB_TOKENS,
+                    help="length of the warm-up trace the placement is calibrated from")
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--residency", type=float, default=0.6)
     ap.add_argument("--ring", type=int, default=32)
@@ -342,6 +421,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the residency sweep")
     ap.add_argument("--no-prefill", action="store_true", help="skip the batched prefill")
     ap.add_argument("--no-autotune", action="store_true", help="skip the popularity-shift self-tuning runs")
+    ap.add_argument("--no-fill-path", action="store_true", help="skip the fill-path leg")
     ap.add_argument("--batches", default="4,16",
                     help="batched decode step sizes to run beside batch 1 (empty: none)")
     ap.add_argument("--kernel-iters", type=int, default=10)
@@ -366,17 +446,22 @@ def main():
     log(f"drawing {w.L * w.E} experts ({w.L * w.E * w.expert_bytes / 1e9:.1f} GB Q4_0)")
     model = Model(w)
     log(f"weights ready in {time.time() - t0:.1f}s")
-    toks = w.tokens(0, args.warmup + args.steps)
-    warm, meas = toks[:args.warmup], toks[args.warmup:]
-    row = torch.zeros(max(args.warmup, args.steps, 1), dtype=torch.int32, device="cuda")
+    C = args.calib_tokens
+    n_stream = max(args.steps, STREAM_TOKENS)
+    toks = w.tokens(0, C + n_stream + args.warmup)
+    calib = toks[:C]                               # t = 0..C-1: the calibration trace
+    meas = toks[C:C + args.steps]                  # the headline's timed tokens
+    stream = toks[C:C + STREAM_TOKENS]             # the fixed measured stream of the other legs
+    untimed = toks[C + n_stream:C + n_stream + args.warmup]  # untimed warm-up tokens
+    row = torch.zeros(max(C, n_stream, args.warmup, 1), dtype=torch.int32, device="cuda")
     LE = w.L * w.E
     P = int(round(args.residency * LE))
     R = args.ring if P < LE else 0
 
     full = None
     if not args.no_full and P < LE:
-        full = run_decode(ms, torch, model, LE, 0, warm, meas, row, calibrate=False)
-    part = run_decode(ms, torch, model, P, R, warm, meas, row, calibrate=True,
+        full = run_decode(ms, torch, model, LE, 0, calib, untimed, meas, row, calibrate=False)
+    part = run_decode(ms, torch, model, P, R, calib, untimed, meas, row, calibrate=True,
                       kernel_iters=args.kernel_iters)
 
     st = part["stats"]
@@ -411,9 +496,10 @@ def main():
             "workload": f"{w.L}-layer Q4_0 MoE stack decode, batch 1: d=2048, 256 experts, top-8, "
                         f"SwiGLU f=512, Zipf-routed; {args.residency:.0%} residency "
                         f"(P={P} pinned slots) + {args.ring}-slot LRU ring, placement calibrated "
-                        f"from {args.warmup} warm-up tokens",
+                        f"from a {C}-token warm-up trace; {args.warmup} untimed then {args.steps} timed "
+                        f"decode tokens",
             "layers": w.L, "d_model": w.d, "experts": w.E, "top_k": w.K, "d_ff": w.f,
-            "weights": "Q4_0", "resident_cap": P, "ring_slots": args.ring,
+            "weights": "Q4_0", "resident_cap": P, "ring_slots": args.ring, "calibration_tokens": C,
             "parallelism": "none (one GPU)",
         },
         "roofline": {
@@ -425,8 +511,13 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "traffic_source": ("FETCH_SIZE + WRITE_SIZE counters per launch, scaled by a known-size copy, "
+                               "from profiles/gemv_traffic.json (valid while the kernel sources hash to "
+                               "the measured ones)") if traffic is not None else None,
             "algorithmic_bytes_per_launch": GATEUP_BYTES,
             "avg_launch_us": round(us, 3),
+            "timing": f"HIP events on the compute stream around {args.kernel_iters} x {w.L} isolated "
+                      f"replays of the kernel with each layer's last selection",
             "down_kernel_us": round(part["us_down"], 3),
             "down_kernel_gbps": round(DOWN_BYTES / (part["us_down"] * 1e-6) / 1e9, 1),
             "token_algorithmic_bytes": TOKEN_BYTES_PER_LAYER * w.L,
@@ -435,7 +526,6 @@ def main():
         },
         "fills": st["fills"],
         "h2d_bytes": st["h2d_bytes"],
-        "h2d_gbps_per_fill": round(st["h2d_bytes"] / st["fill_ns_sum"], 3) if st["fill_ns_sum"] else None,
     }
     res.update(rates(st))
     if full is not None:
@@ -443,39 +533,58 @@ def main():
         res["ratio_to_full"] = round(part["tok_s"] / full["tok_s"], 4)
         res["bit_identical_to_full"] = bool(np.array_equal(full["x_out"], part["x_out"]))
         log(f"outputs bit-identical to full residency: {res['bit_identical_to_full']}")
+    same_stream = args.steps == STREAM_TOKENS
+    sweep_rows = {}
     if not args.no_sweep:
         rows = []
-        ref = full["x_out"] if full is not None else part["x_out"]
         for frac in (1.0, 0.6, 0.3):
             Pf = int(round(frac * LE))
             for calibrated in (False, True):
                 if frac == 1.0 and calibrated:
                     continue
-                if frac == 1.0 and full is not None:
+                if frac == 1.0 and full is not None and same_stream:
                     r = full
-                elif frac == args.residency and calibrated:
+                elif frac == args.residency and calibrated and same_stream:
                     r = part
                 else:
-                    r = run_decode(ms, torch, model, Pf, args.ring if Pf < LE else 0, warm, meas, row,
-                                   calibrate=calibrated)
+                    r = run_decode(ms, torch, model, Pf, args.ring if Pf < LE else 0, calib, untimed, stream,
+                                   row, calibrate=calibrated)
+                sweep_rows[(frac, calibrated)] = r
                 s = r["stats"]
                 rows.append(dict(residency=frac, placement="calibrated" if calibrated else "uniform",
-                                 resident_cap=Pf, tok_s=round(r["tok_s"], 2), **rates(s),
+                                 resident_cap=Pf, tokens=STREAM_TOKENS, tok_s=round(r["tok_s"], 2), **rates(s),
                                  fills=s["fills"], h2d_bytes=s["h2d_bytes"],
-                                 h2d_gbps=round(s["h2d_bytes"] / r["elapsed_s"] / 1e9, 3),
-                                 bit_identical=bool(np.array_equal(r["x_out"], ref))))
+                                 h2d_gbps=round(s["h2d_bytes"] / r["elapsed_s"] / 1e9, 3)))
+        ref = sweep_rows[(1.0, False)]["x_out"]
+        for r, key in zip(rows, [k for k in sweep_rows]):
+            r["bit_identical"] = bool(np.array_equal(sweep_rows[key]["x_out"], ref))
+        full_s = sweep_rows[(1.0, False)]["tok_s"]
+        for r in rows:
+            r["ratio_to_full"] = round(r["tok_s"] / full_s, 4)
         res["sweep"] = rows
     batches = [int(b) for b in args.batches.split(",") if b.strip()]
     if batches:
-        ref = full["x_out"] if full is not None else part["x_out"]
-        res["batched"] = [run_batched(ms, torch, model, P, max(R, b * w.K) if P < LE else 0, b, warm, meas, row,
+        ref = sweep_rows[(1.0, False)]["x_out"] if (1.0, False) in sweep_rows else None
+        res["batched"] = [run_batched(ms, torch, model, P, max(R, b * w.K) if P < LE else 0, b, calib, stream, row,
                                       ref, args.traffic_json) for b in batches]
+    if not args.no_fill_path and P < LE:
+        full_s = sweep_rows[(1.0, False)]["tok_s"] if (1.0, False) in sweep_rows else None
+        res["fill_path"] = fill_path(ms, torch, model, P, args.ring, calib, stream[:64], row,
+                                     full_s, sweep_rows.get((args.residency, False)) if full_s else None)
+        if "pulled" in res["fill_path"]:
+            res["fill_path"]["pulled"]["tokens"] = sweep_rows[(args.residency, False)]["x_out"].shape[0]
+        res["h2d_gbps_per_fill"] = {
+            "pulled_effective": res["fill_path"].get("pulled", {}).get("effective_gbps"),
+            "agent_copy": res["fill_path"]["agent"]["gbps_per_fill"],
+        }
     if not args.no_prefill:
-        probe = wl.stack(args.layers).tokens(args.warmup + args.steps, 256)
-        res["prefill"] = run_prefill(ms, torch, model, P, args.ring, warm, probe, args.layers)
+        probe = wl.stack(args.layers).tokens(C + n_stream + args.warmup, 256)
+        res["prefill"] = run_prefill(ms, torch, model, P, args.ring, calib, probe, args.layers)
     if not args.no_autotune and P < LE:
-        res["self_tuning"] = run_autotune(ms, torch, model, P, args.ring, warm, meas, args.layers)
+        res["self_tuning"] = run_autotune(ms, torch, model, P, args.ring, calib, stream, args.layers)
     res["h2d_link"] = h2d_probe(torch)
+    if "h2d_gbps_per_fill" in res:
+        res["h2d_gbps_per_fill"]["link_probe"] = res["h2d_link"]["gbps"]
     if args.copy_probe:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -484,7 +593,7 @@ def main():
         res["copy_probe_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same stream")
-        res["cpu_baseline"] = cpu_baseline(model, meas, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(model, stream, args.cpu_budget)
     print(json.dumps(res), flush=True)
 
 

@@ -48,6 +48,7 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f64.restype = dbl
         L.oracle_q4_0_block.argtypes = [vp, vp]
@@ -103,6 +104,11 @@ def _ptrs(arrs):
 
 def num_threads():
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n):
+    """OpenMP threads of the following calls (timing only; results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def f16_to_f64(h):

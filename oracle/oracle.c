@@ -30,6 +30,11 @@
 /* Threads the OpenMP loops of this library use (for reporting). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads for the OpenMP loops that follow (timing only: results do not depend on it). */
+void oracle_set_num_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+}
+
 /* IEEE binary16 -> fp64, exact (sign, 5-bit exponent, 10-bit fraction). */
 double oracle_f16_to_f64(uint16_t h) {
     int sign = (h >> 15) & 1;

@@ -42,6 +42,8 @@ typedef struct {
 
 /* threads the OpenMP loops use (reporting only) */
 int oracle_num_threads(void);
+/* set the OpenMP thread count (timing only) */
+void oracle_set_num_threads(int n);
 
 /* ---- elementary steps ---- */
 double oracle_f16_to_f64(uint16_t h);
