@@ -24,6 +24,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "policy.h"
 
 namespace moe {
 
@@ -176,8 +177,9 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         gk[k] = gk[k] / z;
     }
 
-    // ---- placement policy, in rank order (single wave)
-    PolicyTables& pt = const_cast<PolicyTables&>(a.pt);
+    // ---- placement policy, in rank order (single wave): the shared policy
+    // of policy.h, as in the Q4_0 decode and the prefill
+    const PolicyTables& pt = a.pt;
     const int32_t kbase = a.layer * E;
     int my_slot = -1;
     uint64_t my_wait = 0;
@@ -194,129 +196,36 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 #pragma unroll
         for (int k = 0; k < kMaxK; ++k)
             if (k == lane) myk = sel_e[k];
-        pt.counts[kbase + myk] += 1;
+        atomicAdd(reinterpret_cast<unsigned long long*>(pt.counts + kbase + myk), 1ull);
     }
-    int64_t n_pin = 0, n_cold = 0, n_ring = 0, n_fill = 0, n_evict = 0;
+    __shared__ int32_t r_owner[kMaxR];
+    __shared__ uint64_t r_stamp[kMaxR];
+    __shared__ uint64_t r_seq[kMaxR];
+    RingState rs{};
     if (!any_cold) {
 #pragma unroll
         for (int k = 0; k < kMaxK; ++k) {
             if (k >= K) continue;
             if (lane == k) my_slot = pin_slot[k];
         }
-        n_pin = K;
+        rs.n_pin = K;
     } else {
-        __shared__ int32_t r_owner[kMaxR];
-        __shared__ uint64_t r_stamp[kMaxR];
-        __shared__ uint64_t r_seq[kMaxR];
-        const int R = pt.R;
-        for (int r = lane; r < R; r += 64) {
-            r_owner[r] = pt.ring_owner[r];
-            r_stamp[r] = pt.ring_stamp[r];
-            r_seq[r] = pt.ring_seq[r];
-        }
-        uint64_t clock = *pt.clock, fseq = *pt.fill_seq, qseq = *pt.req_seq;
-        int64_t nev = *pt.n_events;
+        ring_load(pt, r_owner, r_stamp, r_seq, rs);
 #pragma unroll
         for (int k = 0; k < kMaxK; ++k) {
             if (k >= K) continue;
-            const int32_t key = kbase + sel_e[k];
             int slot;
-            uint64_t wseq = 0;
-            if (pin_slot[k] >= 0) {
-                slot = pin_slot[k];
-                ++n_pin;
-            } else {
-                ++n_cold;
-                int hit = -1;
-                for (int base = 0; base < R && hit < 0; base += 64) {
-                    const int r = base + lane;
-                    const uint64_t m = __ballot(r < R && r_owner[r] == key);
-                    if (m) hit = base + __builtin_ctzll(m);
-                }
-                if (hit >= 0) {
-                    // A ring entry was filled by an earlier route call whose
-                    // expert kernels waited for that copy; it is resident.
-                    ++n_ring;
-                    ++clock;
-                    if (lane == 0) r_stamp[hit] = clock;
-                    slot = (int)(pt.P + hit);
-                } else {
-                    int v = -1;
-                    for (int base = 0; base < R && v < 0; base += 64) {
-                        const int r = base + lane;
-                        const uint64_t m = __ballot(r < R && r_owner[r] < 0);
-                        if (m) v = base + __builtin_ctzll(m);
-                    }
-                    if (v < 0) {  // least recently used: smallest stamp (stamps are unique)
-                        uint64_t bs = ~0ull;
-                        int bi = 0x7fffffff;
-                        for (int r = lane; r < R; r += 64)
-                            if (r_stamp[r] < bs) { bs = r_stamp[r]; bi = r; }
-#pragma unroll
-                        for (int m = 32; m >= 1; m >>= 1) {
-                            const uint64_t os = __shfl_xor(bs, m, 64);
-                            const int oi = __shfl_xor(bi, m, 64);
-                            if (os < bs || (os == bs && oi < bi)) { bs = os; bi = oi; }
-                        }
-                        v = bi;
-                    }
-                    const int32_t victim = r_owner[v];
-                    if (victim >= 0) ++n_evict;
-                    ++clock;
-                    ++fseq;
-                    ++n_fill;
-                    if (lane == 0) {
-                        r_owner[v] = key;
-                        r_stamp[v] = clock;
-                        r_seq[v] = fseq;
-                        if (nev < pt.event_cap) {
-                            moe_spark_event ev;
-                            ev.seq = (int64_t)fseq;
-                            ev.layer = a.layer;
-                            ev.expert = sel_e[k];
-                            ev.slot = (int32_t)(pt.P + v);
-                            ev.kind = MOE_SPARK_EV_FILL;
-                            ev.victim = victim;
-                            ev.pad = 0;
-                            pt.events[nev] = ev;
-                        }
-                        FifoEntry* fe = pt.fifo + (qseq % kFifoCap);
-                        fe->key = key;
-                        fe->ring = v;
-                        fe->fill = fseq;
-                        __threadfence_system();
-                        __hip_atomic_store(&fe->seq, qseq + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-                    }
-                    ++qseq;
-                    ++nev;
-                    wseq = fseq;
-                    slot = (int)(pt.P + v);
-                }
+            uint64_t wseq;
+            ring_access(pt, a.layer, sel_e[k], pin_slot[k], r_owner, r_stamp, r_seq, rs, slot, wseq);
+            if (lane == k) {
+                my_slot = slot;
+                my_wait = wseq;
             }
-            if (lane == k) { my_slot = slot; my_wait = wseq; }
         }
-        for (int r = lane; r < R; r += 64) {
-            pt.ring_owner[r] = r_owner[r];
-            pt.ring_stamp[r] = r_stamp[r];
-            pt.ring_seq[r] = r_seq[r];
-        }
-        if (lane == 0) {
-            *pt.clock = clock;
-            *pt.fill_seq = fseq;
-            *pt.req_seq = qseq;
-            *pt.n_events = nev;
-        }
+        ring_store(pt, r_owner, r_stamp, r_seq, rs);
     }
-    if (lane == 0) {
-        pt.stats[DS_ACC] += K;
-        pt.stats[DS_PIN] += n_pin;
-        pt.stats[DS_COLD] += n_cold;
-        pt.stats[DS_RING] += n_ring;
-        pt.stats[DS_FILL] += n_fill;
-        pt.stats[DS_EVICT] += n_evict;
-        pt.stats[DS_H2D] += n_fill * pt.slot_bytes;
-        a.sel->inv_rms = inv;
-    }
+    stats_flush(pt, K, rs);
+    if (lane == 0) a.sel->inv_rms = inv;
     if (lane < K) {
         int myk = 0;
         float myg = 0.0f;

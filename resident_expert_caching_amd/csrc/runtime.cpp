@@ -983,12 +983,22 @@ const char* moe_spark_last_error(const moe_spark_ctx* ctx) {
 
 int64_t moe_spark_slot_bytes(const moe_spark_ctx* ctx) { return ctx ? ctx->slot_bytes : 0; }
 
+// Before weights or the router change: nothing queued may still read them
+// (kernels, pulled or agent fills in flight, uploads).
+static moe_spark_status quiesce(moe_spark_ctx* ctx) {
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    HIPCHK(sync_copies(ctx));
+    return MOE_SPARK_OK;
+}
+
 moe_spark_status moe_spark_set_router(moe_spark_ctx* ctx, int32_t layer, const float* w, const float* bias) {
     if (!ctx) return MOE_SPARK_E_INVALID;
     const auto& c = ctx->cfg;
     if (layer < 0 || layer >= c.n_layers || !w) return ctx->fail(MOE_SPARK_E_INVALID, "bad layer or NULL weights");
     if ((c.n_bias_rows > 0) != (bias != nullptr))
         return ctx->fail(MOE_SPARK_E_INVALID, "bias must be given iff n_bias_rows > 0");
+    moe_spark_status st = quiesce(ctx);  // kernels still queued may read this layer's router
+    if (st != MOE_SPARK_OK) return st;
     const int64_t ED = (int64_t)c.n_experts * c.d_model;
     if (c.wfmt == MOE_SPARK_W_Q4_0) {
         // [p][e][i] = w[e][16p + i]: one 16-row slice of every router row per partial work-group
@@ -1012,13 +1022,24 @@ moe_spark_status moe_spark_set_router(moe_spark_ctx* ctx, int32_t layer, const f
     return MOE_SPARK_OK;
 }
 
-static moe_spark_status refresh_pinned(moe_spark_ctx* ctx, int64_t first, int64_t n) {
+// After experts first .. first+n-1 were repacked into the host arena: copy
+// every resident copy of them again, in pinned slots and in ring slots, so no
+// slot keeps old weights (outputs stay independent of residency).  The ring
+// tables are unchanged, so the placement state is too.
+static moe_spark_status refresh_resident(moe_spark_ctx* ctx, int64_t first, int64_t n) {
     if (!ctx->placed) return MOE_SPARK_OK;
     std::vector<std::pair<int32_t, int32_t>> moves;
     for (int64_t i = first; i < first + n; ++i)
         if (ctx->slot_of[i] >= 0) moves.push_back({ctx->slot_of[i], (int32_t)i});
+    const int R = ctx->cfg.ring_slots;
+    if (R > 0) {
+        std::vector<int32_t> owner(R);
+        HIPCHK(hipMemcpy(owner.data(), ctx->d_ring_owner, sizeof(int32_t) * R, hipMemcpyDeviceToHost));
+        for (int r = 0; r < R; ++r)
+            if (owner[r] >= first && owner[r] < first + n)
+                moves.push_back({(int32_t)(ctx->cfg.resident_cap + r), owner[r]});
+    }
     if (moves.empty()) return MOE_SPARK_OK;
-    HIPCHK(hipStreamSynchronize(ctx->compute));
     return upload_pinned(ctx, moves);
 }
 
@@ -1029,12 +1050,14 @@ moe_spark_status moe_spark_set_expert(moe_spark_ctx* ctx, int32_t layer, int32_t
     if (layer < 0 || layer >= c.n_layers || expert < 0 || expert >= c.n_experts || !gate || !up || !down)
         return ctx->fail(MOE_SPARK_E_INVALID, "bad layer/expert or NULL weights");
     const int64_t key = (int64_t)layer * c.n_experts + expert;
+    moe_spark_status st = quiesce(ctx);
+    if (st != MOE_SPARK_OK) return st;
     pack_expert(ctx, gate, up, down, ctx->h_arena + key * ctx->slot_bytes);
     if (!ctx->expert_set[key]) {
         ctx->expert_set[key] = 1;
         ++ctx->n_expert_set;
     }
-    return refresh_pinned(ctx, key, 1);
+    return refresh_resident(ctx, key, 1);
 }
 
 moe_spark_status moe_spark_set_experts(moe_spark_ctx* ctx, int64_t first, int64_t n, const void* blob) {
@@ -1046,6 +1069,8 @@ moe_spark_status moe_spark_set_experts(moe_spark_ctx* ctx, int64_t first, int64_
     const int64_t mb = matrix_bytes(f, d, c.wfmt), db = matrix_bytes(d, f, c.wfmt);
     const int64_t per = 2 * mb + db;
     const uint8_t* src = (const uint8_t*)blob;
+    moe_spark_status st = quiesce(ctx);
+    if (st != MOE_SPARK_OK) return st;
     unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
     std::vector<std::thread> th;
     for (unsigned t = 0; t < nt; ++t)
@@ -1061,7 +1086,7 @@ moe_spark_status moe_spark_set_experts(moe_spark_ctx* ctx, int64_t first, int64_
             ctx->expert_set[i] = 1;
             ++ctx->n_expert_set;
         }
-    return refresh_pinned(ctx, first, n);
+    return refresh_resident(ctx, first, n);
 }
 
 moe_spark_status moe_spark_place_uniform(moe_spark_ctx* ctx) {

@@ -10,7 +10,8 @@ oracle and the placement simulator.
    chunks (far more cold experts than ring slots);
  * error paths: prefill beyond max_tokens, prefill without prefill buffers,
    forward before placement;
- * decode fills pulled by the kernels against fills copied by the host agent.
+ * decode fills pulled by the kernels against fills copied by the host agent;
+ * an expert updated after placement while it sits in a ring slot.
 """
 import numpy as np
 import pytest
@@ -207,3 +208,50 @@ def test_pulled_and_agent_fills_agree(monkeypatch):
     assert pulled["events"] == agent["events"]
     for a, b in zip(pulled["placement"], agent["placement"]):
         assert np.array_equal(a, b)
+
+
+def test_expert_update_reaches_ring_copies():
+    """moe_spark_set_expert after placement: an expert that sits in a ring
+    slot is refreshed there too, so decode after the update gives the same
+    bits at 60% residency (the expert ring-resident) as at full residency,
+    and differs from decode without the update."""
+    w = _wl(32, 8, L=2, n_tokens=32)
+    model = Model(w)
+    x = w.tokens()
+    LE = w.L * w.E
+    P60, R = int(round(0.6 * LE)), 8
+    row = torch.zeros(32, dtype=torch.int32, device="cuda")
+
+    def run(P, Rr, key=None, new=None):
+        ctx = model.make_ctx(P=P, R=Rr)
+        try:
+            xa = torch.from_numpy(x[:16].copy()).cuda()
+            xb = torch.from_numpy(x[16:].copy()).cuda()
+            print(f"update test: P={P} R={Rr} key={key}", flush=True)
+            ms.moe_spark_decode(ctx, xa.data_ptr(), 16, row.data_ptr())
+            ms.moe_spark_synchronize(ctx)
+            pl = placement(ctx, w, Rr)
+            if key is not None:
+                l, e = divmod(key, w.E)
+                g, u, d = new
+                ms.moe_spark_set_expert(ctx, l, e, g.ctypes.data, u.ctypes.data, d.ctypes.data)
+            ms.moe_spark_decode(ctx, xb.data_ptr(), 16, row.data_ptr())
+            ms.moe_spark_synchronize(ctx)
+            return xb.cpu().numpy(), pl, ms.moe_spark_get_stats(ctx)
+        finally:
+            ms.moe_spark_destroy(ctx)
+
+    _, (slot_of, owner, _, counts), _ = run(P60, R)
+    ring = [int(k) for k in owner if k >= 0]
+    assert ring, "no expert reached the ring"
+    key = max(ring, key=lambda k: counts.reshape(-1)[k])  # the most-used ring resident
+    assert slot_of.reshape(-1)[key] < 0
+    # new weights: another expert's (a different layer's) bytes
+    src = (key + w.E // 2) % LE
+    new = tuple(np.ascontiguousarray(a) for a in wl.split_expert(model.blob[src], w.d, w.f, w.wfmt))
+    y60, (_, owner2, _, _), st = run(P60, R, key, new)
+    assert key in [int(k) for k in owner2] or st["fills"] > 0
+    y100, _, _ = run(LE, 0, key, new)
+    y_old, _, _ = run(LE, 0)
+    assert np.array_equal(y60, y100)
+    assert not np.array_equal(y100, y_old), "the updated expert was not used after the update"
