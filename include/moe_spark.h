@@ -5,8 +5,9 @@
  * memory (e.g. a torch tensor's data_ptr on ROCm), "host" pointers are
  * ordinary CPU memory.  Streams are hipStream_t passed as void*.
  *
- * What the library implements, and where it is described:
- *  "Luce Spark runs 35B MoE models on 16GB GPU without speed loss"
+ * What the library implements, and where it is described (each entry point
+ * below names its passage, with these short names):
+ *  [Spark] "Luce Spark runs 35B MoE models on 16GB GPU without speed loss"
  *  (theneuralfeed.com):
  *   - opening paragraph: each token is routed to about 8 of 256 experts, so
  *     only a fraction of the experts needs to sit in GPU memory;
@@ -20,10 +21,10 @@
  *     (3) the whole token runs as one graph instead of one graph per layer;
  *     and full residency is bit-identical to all-GPU execution (here: outputs
  *     are bit-identical at every residency).
- *  "Luce Spark: Shattering the VRAM Ceiling for 35B MoEs on 16GB GPUs Without
- *  the Offload Tax" (baguaai.com), "Event Core" and "Actionable Advice": hot
- *  experts live in GPU memory, the long tail in system RAM, and the link
- *  between them becomes the bottleneck.
+ *  [Bagua] "Luce Spark: Shattering the VRAM Ceiling for 35B MoEs on 16GB GPUs
+ *  Without the Offload Tax" (baguaai.com), "Event Core" and "Actionable
+ *  Advice": hot experts live in GPU memory, the long tail in system RAM, and
+ *  the link between them becomes the bottleneck.
  *
  * Ownership: the context owns the HBM slot arena ((P + R) expert slots), the
  * pinned host arena (every expert, copied in by moe_spark_set_expert), all
@@ -136,48 +137,75 @@ typedef struct moe_spark_ctx moe_spark_ctx;
  * neither copy stream may share a hardware queue with the compute stream:
  * keep the process's streams within GPU_MAX_HW_QUEUES (a fill that never
  * starts ends the wait with E_HIP "fill did not arrive in time").
- * Errors: E_INVALID (bad config), E_NOMEM (arena), E_HIP. */
+ * Errors: E_INVALID (bad config), E_NOMEM (arena), E_HIP.
+ * Passage: [Spark] "The key components" (1) and (2): the pinned set and the
+ * fixed ring of spare GPU slots are the slot arena's P and R slots; [Bagua]
+ * "Event Core": the long tail lives in system RAM (the pinned host arena).
+ */
 moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_stream,
                                   void* copy_stream, moe_spark_ctx** out);
 
-/* Stop the fill agent, free everything.  NULL is allowed. */
+/* Stop the fill agent, free everything.  NULL is allowed.
+ * Passage: none of its own (releases what moe_spark_create made).
+ */
 void moe_spark_destroy(moe_spark_ctx* ctx);
 
-/* Text of the last error on this context (never NULL; "" when none). */
+/* Text of the last error on this context (never NULL; "" when none).
+ * Passage: none of its own (error reporting of every entry point).
+ */
 const char* moe_spark_last_error(const moe_spark_ctx* ctx);
 
-/* Bytes of one expert slot (gate + up + down) in the configured format. */
+/* Bytes of one expert slot (gate + up + down) in the configured format.
+ * Passage: [Spark] "The key components" (2): the unit a cold-expert copy moves.
+ */
 int64_t moe_spark_slot_bytes(const moe_spark_ctx* ctx);
 
 /* Router of one layer, host memory: w [E][d] fp32; bias [n_bias_rows][E]
  * fp32 (added to the logits before top-k and softmax), or NULL when
- * n_bias_rows == 0.  Copied; synchronous. */
+ * n_bias_rows == 0.  Copied; synchronous.
+ * Passage: [Spark] opening paragraph: the router picks about 8 of 256 experts
+ * per token.  Synchronises both streams first (queued work may read it).
+ */
 moe_spark_status moe_spark_set_router(moe_spark_ctx* ctx, int32_t layer, const float* w,
                                       const float* bias);
 
 /* One expert, host memory: gate, up [f][d]; down [d][f]; in the configured
  * format (row-major fp32, or GGUF Q4_0 blocks along the input dimension).
  * Repacked into the pinned host arena; the caller may free its buffers.
- * If the expert sits in a pinned slot its slot is refreshed. */
+ * If the expert sits in a pinned slot its slot is refreshed.
+ * Passage: [Bagua] "Event Core" and [Spark] opening paragraph: every expert's
+ * weights live in system RAM (the pinned host arena); the resident ones are
+ * copies.  Synchronises both streams first; every resident copy (pinned slot
+ * or ring slot) is refreshed, so outputs stay independent of residency.
+ */
 moe_spark_status moe_spark_set_expert(moe_spark_ctx* ctx, int32_t layer, int32_t expert,
                                       const void* gate, const void* up, const void* down);
 
 /* n experts with flat ids first .. first+n-1 (id = layer*E + expert) from one
  * host buffer, each expert gate | up | down back to back (same formats as
- * moe_spark_set_expert).  Repacks on host threads. */
+ * moe_spark_set_expert).  Repacks on host threads.
+ * Passage: as moe_spark_set_expert.
+ */
 moe_spark_status moe_spark_set_experts(moe_spark_ctx* ctx, int64_t first, int64_t n,
                                        const void* blob);
 
 /* Initial placement: layer l pins experts 0..q_l-1, q_l = floor(P/L) + [l < P mod L];
  * pinned slots 0..P-1 in (layer, expert) order; the ring is emptied.
- * Uploads the pinned experts; synchronous.  E_STATE before all weights are set. */
+ * Uploads the pinned experts; synchronous.  E_STATE before all weights are set.
+ * Passage: [Spark] "The key components": the "naive uniform offload" the
+ * calibrated placement is measured against (here it keeps the same ring).
+ */
 moe_spark_status moe_spark_place_uniform(moe_spark_ctx* ctx);
 
 /* Calibrated placement: each layer pins its q_l most-counted experts (count
  * descending, expert ascending).  Experts that stay keep their slot; freed
  * slots (ascending) go to newly pinned experts in (layer, expert) order; a
  * newly pinned expert's ring entry is emptied.  reset_counts != 0 zeroes the
- * counts afterwards.  Synchronises both streams (call between tokens). */
+ * counts afterwards.  Synchronises both streams (call between tokens).
+ * Passage: [Spark] "The key components" (1): accumulate per-expert routing
+ * frequencies and pin the most-used set; [Bagua] "Dynamic Expert
+ * Calibration".
+ */
 moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts);
 
 /* Online self-tuning of the placement during decode.  The pages' "The key
@@ -196,7 +224,10 @@ moe_spark_status moe_spark_calibrate(moe_spark_ctx* ctx, int32_t reset_counts);
  * interval_tokens = 0 turns it off (the default).  Only decode tokens count;
  * a step synchronises both streams and uploads the entering experts.
  * Errors: E_INVALID for interval < 0, hysteresis_pct outside [0, 100000] or
- * decay_shift outside [0, 62]. */
+ * decay_shift outside [0, 62].
+ * Passage: [Spark] opening paragraph ("self-tunes over time") and [Bagua]
+ * "Dynamic Expert Calibration" (profiles real-time traffic).
+ */
 moe_spark_status moe_spark_set_autotune(moe_spark_ctx* ctx, int32_t interval_tokens, int32_t hysteresis_pct,
                                         int32_t decay_shift);
 
@@ -206,7 +237,10 @@ moe_spark_status moe_spark_set_autotune(moe_spark_ctx* ctx, int32_t interval_tok
  * bias_row [T] int32 row of the router bias per token (NULL: row 0),
  * topk_out [T][K] int32 and gates_out [T][K] fp32 (either may be NULL).
  * flags: MOE_SPARK_PRE_RMSNORM | MOE_SPARK_RESIDUAL.  Counts, placement and
- * stats are updated exactly as in a decode step of that layer. */
+ * stats are updated exactly as in a decode step of that layer.
+ * Passage: [Spark] opening paragraph (one MoE layer: about 8 of 256 experts
+ * per token) and "The key components" (1)-(2) for the counts and the cache.
+ */
 moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, const float* x,
                                          float* y, int32_t n_tokens, const int32_t* bias_row,
                                          uint32_t flags, int32_t* topk_out, float* gates_out);
@@ -214,7 +248,10 @@ moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, cons
 /* Decode n_tokens independent tokens through all L layers, one graph launch
  * per token: x_{l+1} = x_l + MoE_l(RMSNorm(x_l)).  x [T][d] fp32 device,
  * updated in place; bias_row [T] int32 device or NULL.  The graph for a given
- * (x, bias_row) pair is built once and replayed; n_tokens = 0 only builds it. */
+ * (x, bias_row) pair is built once and replayed; n_tokens = 0 only builds it.
+ * Passage: [Spark] "The key components" (3): the entire token as one graph
+ * instead of one per layer; (2) for cold experts inside it.
+ */
 moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens,
                                   const int32_t* bias_row);
 
@@ -235,11 +272,16 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
  * evicted before the step has read it.  The graph for a given (x, bias_row,
  * batch) is built once and replayed; n_tokens = 0 only builds it.  Online
  * self-tuning (moe_spark_set_autotune) runs between steps.
- * Errors: E_INVALID (format, batch, ring size, n_tokens, x), E_STATE. */
+ * Errors: E_INVALID (format, batch, ring size, n_tokens, x), E_STATE.
+ * Passage: [Spark] "The key components" (3) and the engine's server use
+ * (opening paragraph); the cache is (1)-(2) unchanged.
+ */
 moe_spark_status moe_spark_decode_batched(moe_spark_ctx* ctx, float* x, int32_t n_tokens, int32_t batch,
                                           const int32_t* bias_row);
 
-/* moe_spark_decode with n_tokens = 1. */
+/* moe_spark_decode with n_tokens = 1.
+ * Passage: [Spark] "The key components" (3), one token.
+ */
 moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int32_t* bias_row);
 
 /* Batched prefill of n_tokens (1 <= n_tokens <= max_tokens) through all L
@@ -255,7 +297,11 @@ moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int
  * x [T][d] fp32 device, updated in place; bias_row [T] int32 device or NULL.
  * Synchronises the compute stream once per layer (the host plans each layer
  * from its expert histogram).  Errors: E_INVALID (format, n_tokens, x),
- * E_STATE (max_tokens was 0 at create, weights or placement missing). */
+ * E_STATE (max_tokens was 0 at create, weights or placement missing).
+ * Passage: [Spark] opening paragraph (routing) and "The key components"
+ * (1)-(2): the counts that calibration reads and the ring that streams the
+ * cold experts.
+ */
 moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_tokens,
                                    const int32_t* bias_row);
 
@@ -264,7 +310,13 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
  * topk [cap][L][K] int32, gates [cap][L][K] fp32.  Rows follow a trace cursor
  * that starts at 0 at this call and advances by one per decoded token and by
  * n_tokens per prefill batch; rows at or past cap are not written.
- * layer_forward traces token t of its call at row t, layer `layer`. */
+ * layer_forward traces token t of its call at row t, layer `layer`.
+ * Passage: none of its own (observability for parity checks).
+ * Passage: [Spark] "The key components" (1): the cold-hit rate ("36% to ~7%")
+ * is cold_hits / accesses; [Bagua] "Actionable Advice": fills and their
+ * bytes are the swap traffic between system RAM and the GPU.
+ * Passage: as moe_spark_get_stats.
+ */
 moe_spark_status moe_spark_set_trace(moe_spark_ctx* ctx, float* x_layers, int32_t* topk,
                                      float* gates, int64_t cap_tokens);
 
@@ -273,17 +325,26 @@ moe_spark_status moe_spark_reset_stats(moe_spark_ctx* ctx);
 
 /* Host outputs (each may be NULL): slot_of [L][E] (pinned slot or -1),
  * ring_owner [R] (layer*E+expert or -1), ring_stamp [R] (LRU clock),
- * counts [L][E]. */
+ * counts [L][E].
+ * Passage: [Spark] "The key components" (1)-(2): the pinned set, the ring
+ * and the routing frequencies.
+ */
 moe_spark_status moe_spark_get_placement(moe_spark_ctx* ctx, int32_t* slot_of,
                                          int32_t* ring_owner, int64_t* ring_stamp,
                                          int64_t* counts);
 
 /* Copy up to cap fill events (oldest first) to host memory; *n_total gets
- * the number logged (events past event_cap are counted, not stored). */
+ * the number logged (events past event_cap are counted, not stored).
+ * Passage: [Spark] "The key components" (2): every copy into a spare slot
+ * and the LRU entry it evicted.
+ */
 moe_spark_status moe_spark_get_events(moe_spark_ctx* ctx, moe_spark_event* out, int64_t cap,
                                       int64_t* n_total);
 
-/* Wait for all work of the context; report device-side errors. */
+/* Wait for all work of the context; report device-side errors.
+ * Passage: [Spark] "The key components" (2): a fill costs throughput but
+ * never stalls; one that never lands is reported here, not waited for.
+ */
 moe_spark_status moe_spark_synchronize(moe_spark_ctx* ctx);
 
 /* Time the decode kernels in isolation: replays the gate/up and down kernels
@@ -293,7 +354,10 @@ moe_spark_status moe_spark_synchronize(moe_spark_ctx* ctx);
  * us_gateup (for Q4_0: router-partial reduce + top-k + gate/up GEMV + SwiGLU),
  * us_down (down GEMV + combine + residual + next layer's router partials) and
  * us_route (Q4_0: the first layer's router-partial kernel; fp32: -1).
- * Writes only context scratch buffers.  Call between tokens. */
+ * Writes only context scratch buffers.  Call between tokens.
+ * Passage: none of its own (measures the expert kernels against HBM
+ * bandwidth).
+ */
 moe_spark_status moe_spark_time_expert_kernels(moe_spark_ctx* ctx, int32_t iters,
                                                float* us_gateup, float* us_down,
                                                float* us_route);

@@ -14,11 +14,9 @@
 // every residency (same paragraph: full residency is bit-identical to
 // all-GPU execution).
 //
-// Q4_0 GEMVs stream one 16-byte block of 32 codes per lane per row, keep the
-// activation block in registers and factor the (q - 8) offset out of the
-// inner loop with per-block activation sums:
-//   sum_i s (q_i - 8) u_i = s (sum_i q_i u_i - 8 U_b),  U_b = sum of the block's u.
-// Every reduction has a fixed tree; there are no floating-point atomics.
+// The GEMVs here read fp32 weights only; the Q4_0 expert GEMVs live in
+// q4_decode.hip.  Every reduction has a fixed tree; there are no
+// floating-point atomics.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
