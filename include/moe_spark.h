@@ -245,6 +245,23 @@ moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, cons
                                          float* y, int32_t n_tokens, const int32_t* bias_row,
                                          uint32_t flags, int32_t* topk_out, float* gates_out);
 
+/* moe_spark_layer_forward without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * moe_spark_layer_forward (bit for bit), Q4_0 contexts only.  The per-token
+ * scratch (router partial logits and squares, the layer's selection and
+ * publish flag, the SwiGLU output) lives in a file-scope device array of
+ * 576 KiB per GPU, held until the process ends, instead of the context's
+ * buffers.  Every call on a GPU shares that GPU's array: calls that overlap
+ * on one GPU (two streams, or two contexts) race and must be serialised by
+ * the caller.  The call allocates nothing and calls no allocating routine.
+ * Errors: E_INVALID for a non-Q4_0 context or a shape beyond the scratch
+ * (more than 1024 experts, top_k > 8, d_ff > 512) and for the arguments
+ * moe_spark_layer_forward rejects; E_STATE as moe_spark_layer_forward. */
+moe_spark_status moe_spark_layer_forward_noalloc(moe_spark_ctx* ctx, int32_t layer, const float* x,
+                                                 float* y, int32_t n_tokens, const int32_t* bias_row,
+                                                 uint32_t flags, int32_t* topk_out, float* gates_out);
+
 /* Decode n_tokens independent tokens through all L layers, one graph launch
  * per token: x_{l+1} = x_l + MoE_l(RMSNorm(x_l)).  x [T][d] fp32 device,
  * updated in place; bias_row [T] int32 device or NULL.  The graph for a given

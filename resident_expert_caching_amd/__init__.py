@@ -70,6 +70,7 @@ def _load():
         "moe_spark_calibrate": (st, [vp, i32]),
         "moe_spark_set_autotune": (st, [vp, i32, i32, i32]),
         "moe_spark_layer_forward": (st, [vp, i32, vp, vp, i32, vp, u32, vp, vp]),
+        "moe_spark_layer_forward_noalloc": (st, [vp, i32, vp, vp, i32, vp, u32, vp, vp]),
         "moe_spark_decode": (st, [vp, vp, i32, vp]),
         "moe_spark_decode_batched": (st, [vp, vp, i32, i32, vp]),
         "moe_spark_token_forward": (st, [vp, vp, vp]),
@@ -146,6 +147,12 @@ def moe_spark_layer_forward(ctx, layer, x, y, n_tokens, bias_row=None, flags=0, 
                             gates_out=None):
     _check(ctx, _lib.moe_spark_layer_forward(ctx, layer, x, y, n_tokens, bias_row, flags, topk_out,
                                              gates_out))
+
+
+def moe_spark_layer_forward_noalloc(ctx, layer, x, y, n_tokens, bias_row=None, flags=0, topk_out=None,
+                                    gates_out=None):
+    _check(ctx, _lib.moe_spark_layer_forward_noalloc(ctx, layer, x, y, n_tokens, bias_row, flags, topk_out,
+                                                     gates_out))
 
 
 def moe_spark_decode(ctx, x, n_tokens, bias_row=None):

@@ -23,6 +23,7 @@
 #include <cstring>
 #include <cstdlib>
 #include <deque>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -51,6 +52,56 @@ int64_t now_ns() {
         .count();
 }
 
+}  // namespace
+
+// Device scratch of moe_spark_layer_forward_noalloc: the per-token buffers of
+// the Q4_0 layer kernels (router partial logits and squares, the layer's
+// selection and publish flag, the SwiGLU output), in a file-scope device
+// array so that the call allocates nothing.  Each GPU holds its own copy until
+// the process ends; host code uses the per-device address that
+// hipGetSymbolAddress returns (the array's name is only a host-side stand-in).
+namespace {
+constexpr size_t kNoAllocPL = 0;                                          // float [kNP][kMaxE]
+constexpr size_t kNoAllocPS = kNoAllocPL + sizeof(float) * kNP * kMaxE;     // float [kNP]
+constexpr size_t kNoAllocSel = kNoAllocPS + sizeof(float) * kNP;           // LayerSel
+constexpr size_t kNoAllocPub = kNoAllocSel + 512;                          // uint32_t
+constexpr size_t kNoAllocH = kNoAllocPub + 256;                            // float [kQ4MaxK][kQF]
+constexpr size_t kNoAllocUsed = kNoAllocH + sizeof(float) * kQ4MaxK * kQF;
+constexpr size_t kNoAllocScratchBytes = 576 * 1024;
+static_assert(sizeof(LayerSel) <= 512, "selection fits its scratch slot");
+static_assert(kNoAllocUsed <= kNoAllocScratchBytes, "no-alloc scratch layout fits the array");
+constexpr int kMaxDevices = 64;
+uint8_t* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+// Once per device, with that device current: the device address of this
+// GPU's copy of the scratch array.
+hipError_t scratch_init(int device) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[device]) return hipSuccess;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[device] = static_cast<uint8_t*>(ptr);
+    return hipSuccess;
+}
+
+uint8_t* scratch_of(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch[device];
+}
+
+// Zero a flag with a kernel (a memset node would not replay reliably inside
+// a captured graph).
+__global__ void noalloc_clear_kernel(uint32_t* flag) {
+    if (threadIdx.x == 0) *flag = 0u;
+}
 }  // namespace
 
 struct moe_spark_ctx {
@@ -804,6 +855,9 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     };
     hipError_t e = hipGetDevice(&ctx->device);
     if (e != hipSuccess) return fail_create(MOE_SPARK_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    e = scratch_init(ctx->device);  // this GPU's no-alloc scratch (moe_spark_layer_forward_noalloc)
+    if (e != hipSuccess)
+        return fail_create(MOE_SPARK_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
     int rate_khz = 0;
     if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, ctx->device) != hipSuccess || rate_khz <= 0)
         rate_khz = 100000;
@@ -1301,6 +1355,52 @@ moe_spark_status moe_spark_layer_forward(moe_spark_ctx* ctx, int32_t layer, cons
         const ExpertArgs ea = expert_args(ctx, layer, x, y, tok, res, 0);
         HIPCHK(launch_gateup(ea, c.wfmt, ctx->compute));
         HIPCHK(launch_down(ea, c.wfmt, ctx->compute));
+    }
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_layer_forward_noalloc(moe_spark_ctx* ctx, int32_t layer, const float* x, float* y,
+                                                 int32_t n_tokens, const int32_t* bias_row, uint32_t flags,
+                                                 int32_t* topk_out, float* gates_out) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    const auto& c = ctx->cfg;
+    if (c.wfmt != MOE_SPARK_W_Q4_0)
+        return ctx->fail(MOE_SPARK_E_INVALID, "layer_forward_noalloc runs Q4_0 contexts only");
+    if (c.n_experts > kMaxE || c.top_k > kQ4MaxK || c.d_ff > kQF)
+        return ctx->fail(MOE_SPARK_E_INVALID, "shape exceeds the no-alloc scratch (%zu bytes)",
+                         (size_t)kNoAllocScratchBytes);
+    if (layer < 0 || layer >= c.n_layers || n_tokens < 0 || (n_tokens > 0 && (!x || !y)))
+        return ctx->fail(MOE_SPARK_E_INVALID, "bad layer, token count or NULL buffer");
+    if (flags & ~(MOE_SPARK_PRE_RMSNORM | MOE_SPARK_RESIDUAL)) return ctx->fail(MOE_SPARK_E_INVALID, "unknown flags");
+    if ((topk_out == nullptr) != (gates_out == nullptr))
+        return ctx->fail(MOE_SPARK_E_INVALID, "topk_out and gates_out go together");
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    uint8_t* scr = scratch_of(ctx->device);
+    if (!scr) return ctx->fail(MOE_SPARK_E_STATE, "no-alloc scratch was not set up on device %d", ctx->device);
+    float* pl = reinterpret_cast<float*>(scr + kNoAllocPL);
+    float* ps = reinterpret_cast<float*>(scr + kNoAllocPS);
+    LayerSel* sel = reinterpret_cast<LayerSel*>(scr + kNoAllocSel);
+    uint32_t* pub = reinterpret_cast<uint32_t*>(scr + kNoAllocPub);
+    float* h = reinterpret_cast<float*>(scr + kNoAllocH);
+    // the publish flag starts at zero (every down launch leaves it zero; this
+    // covers the first call on the GPU and a call after an aborted one)
+    hipLaunchKernelGGL(noalloc_clear_kernel, dim3(1), dim3(64), 0, ctx->compute, pub);
+    HIPCHK(hipGetLastError());
+    const int norm = (flags & MOE_SPARK_PRE_RMSNORM) != 0, res = (flags & MOE_SPARK_RESIDUAL) != 0;
+    for (int t = 0; t < n_tokens; ++t) {
+        const TokRef tok{nullptr, t};
+        Q4Args a = q4_args(ctx, layer, x, y, tok, tok, bias_row, norm, res, -1, topk_out, gates_out, 0);
+        a.pl = pl;
+        a.ps = ps;
+        a.sel = sel;
+        a.pub = pub;
+        a.h = h;
+        Q4Args ap = a;
+        ap.wr_part = ctx->d_router + (int64_t)layer * c.n_experts * c.d_model;
+        HIPCHK(launch_q4_router_partial(ap, ctx->compute));
+        HIPCHK(launch_q4_gateup(a, ctx->compute));
+        HIPCHK(launch_q4_down(a, ctx->compute));
     }
     return MOE_SPARK_OK;
 }
