@@ -417,6 +417,8 @@ def main():
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--residency", type=float, default=0.6)
     ap.add_argument("--ring", type=int, default=32)
+    ap.add_argument("--placement", choices=("calibrated", "uniform"), default="calibrated",
+                    help="placement of the headline setting (uniform: the static-placement arm)")
     ap.add_argument("--no-full", action="store_true", help="skip the full-residency run")
     ap.add_argument("--no-sweep", action="store_true", help="skip the residency sweep")
     ap.add_argument("--no-prefill", action="store_true", help="skip the batched prefill")
@@ -461,8 +463,8 @@ def main():
     full = None
     if not args.no_full and P < LE:
         full = run_decode(ms, torch, model, LE, 0, calib, untimed, meas, row, calibrate=False)
-    part = run_decode(ms, torch, model, P, R, calib, untimed, meas, row, calibrate=True,
-                      kernel_iters=args.kernel_iters)
+    part = run_decode(ms, torch, model, P, R, calib, untimed, meas, row,
+                      calibrate=args.placement == "calibrated", kernel_iters=args.kernel_iters)
 
     st = part["stats"]
     us = part["us_gateup"]
@@ -495,11 +497,13 @@ def main():
         "config": {
             "workload": f"{w.L}-layer Q4_0 MoE stack decode, batch 1: d=2048, 256 experts, top-8, "
                         f"SwiGLU f=512, Zipf-routed; {args.residency:.0%} residency "
-                        f"(P={P} pinned slots) + {args.ring}-slot LRU ring, placement calibrated "
-                        f"from a {C}-token warm-up trace; {args.warmup} untimed then {args.steps} timed "
-                        f"decode tokens",
+                        f"(P={P} pinned slots) + {args.ring}-slot LRU ring, "
+                        + (f"placement calibrated from a {C}-token warm-up trace" if args.placement == "calibrated"
+                           else f"uniform static placement ({C}-token warm-up trace, no calibration)")
+                        + f"; {args.warmup} untimed then {args.steps} timed decode tokens",
             "layers": w.L, "d_model": w.d, "experts": w.E, "top_k": w.K, "d_ff": w.f,
             "weights": "Q4_0", "resident_cap": P, "ring_slots": args.ring, "calibration_tokens": C,
+            "placement": args.placement,
             "parallelism": "none (one GPU)",
         },
         "roofline": {
@@ -544,7 +548,7 @@ def main():
                     continue
                 if frac == 1.0 and full is not None and same_stream:
                     r = full
-                elif frac == args.residency and calibrated and same_stream:
+                elif frac == args.residency and calibrated == (args.placement == "calibrated") and same_stream:
                     r = part
                 else:
                     r = run_decode(ms, torch, model, Pf, args.ring if Pf < LE else 0, calib, untimed, stream,
