@@ -16,8 +16,9 @@ _lib = None
 W_F32 = 0
 W_Q4_0 = 1
 EV_FILL = 2
+EV_PREFETCH = 3
 STAT_NAMES = ("accesses", "pinned_hits", "cold_hits", "ring_hits", "fills", "evictions",
-              "h2d_bytes")
+              "h2d_bytes", "prefetches")
 
 
 class Shape(ctypes.Structure):
@@ -75,6 +76,8 @@ def lib():
         L.oracle_sim_decode_layer.argtypes = [vp, i32, i32, vp]
         L.oracle_sim_decode_batch.argtypes = [vp, i32, i32, vp]
         L.oracle_sim_prefill_layer.argtypes = [vp, i32, i32, i32, vp]
+        L.oracle_sim_prefetch.argtypes = [vp, i32, vp]
+        L.oracle_sim_prefetch.restype = ctypes.c_int64
         L.oracle_sim_stats.argtypes = [vp, vp]
         L.oracle_sim_reset_stats.argtypes = [vp]
         L.oracle_sim_placement.argtypes = [vp, vp, vp, vp, vp]
@@ -280,6 +283,12 @@ class Sim:
         idx = np.ascontiguousarray(idx, dtype=np.int32)
         T, K = idx.shape
         lib().oracle_sim_prefill_layer(self._h, layer, T, K, _p(idx))
+
+    def prefetch(self, layer, hist):
+        """After a prefill layer: prefetch layer `layer`'s experts with hist[e] > 0."""
+        hist = np.ascontiguousarray(hist, dtype=np.int32)
+        assert hist.size == self.E
+        return int(lib().oracle_sim_prefetch(self._h, layer, _p(hist)))
 
     def stats(self):
         out = np.zeros(len(STAT_NAMES), dtype=np.int64)

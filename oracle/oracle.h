@@ -89,15 +89,16 @@ typedef struct oracle_sim oracle_sim;
 typedef struct {
     int64_t seq;      /* 1-based fill sequence number */
     int32_t layer, expert, slot;
-    int32_t kind;     /* ORACLE_EV_FILL */
+    int32_t kind;     /* ORACLE_EV_FILL or ORACLE_EV_PREFETCH */
     int32_t victim;   /* evicted l*E+e, or -1 when an empty ring slot was used */
     int32_t pad;
 } oracle_event;
 
 #define ORACLE_EV_FILL 2
+#define ORACLE_EV_PREFETCH 3
 
 /* stats: accesses, pinned_hits, cold_hits, ring_hits, fills, evictions, h2d_bytes */
-#define ORACLE_N_STATS 7
+#define ORACLE_N_STATS 8 /* accesses, pinned, cold, ring, fills, evictions, h2d bytes, prefetches */
 
 oracle_sim* oracle_sim_create(int L, int E, int64_t P, int R, int64_t slot_bytes);
 void oracle_sim_destroy(oracle_sim* s);
@@ -110,6 +111,8 @@ void oracle_sim_decode_layer(oracle_sim* s, int layer, int K, const int32_t* idx
 /* B tokens decoded together: accesses in (layer, token, rank) order */
 void oracle_sim_decode_batch(oracle_sim* s, int B, int K, const int32_t* idx /* [B][L][K] */);
 void oracle_sim_prefill_layer(oracle_sim* s, int layer, int T, int K, const int32_t* idx /* [T][K] */);
+/* after a prefill layer: prefetch the next layer's predicted experts (hist [E]) */
+int64_t oracle_sim_prefetch(oracle_sim* s, int layer, const int32_t* hist);
 void oracle_sim_stats(const oracle_sim* s, int64_t* out);
 void oracle_sim_reset_stats(oracle_sim* s);
 void oracle_sim_placement(const oracle_sim* s, int32_t* slot_of /* [L][E] */,

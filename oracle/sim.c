@@ -45,11 +45,12 @@ struct oracle_sim {
     int64_t clock;
     int64_t fill_seq;
     int64_t st[ORACLE_N_STATS];
+    int pf_last_cold;     /* cold experts in the last chunk of the last prefill layer */
     oracle_event* ev;
     int64_t n_ev, cap_ev;
 };
 
-enum { S_ACC = 0, S_PIN, S_COLD, S_RING, S_FILL, S_EVICT, S_H2D };
+enum { S_ACC = 0, S_PIN, S_COLD, S_RING, S_FILL, S_EVICT, S_H2D, S_PREF };
 
 int64_t oracle_sim_quota(int L, int64_t P, int layer) {
     return P / L + ((int64_t)layer < P % L ? 1 : 0);
@@ -185,14 +186,37 @@ int64_t oracle_sim_retune(oracle_sim* s, int hyst_pct, int decay_shift) {
     return swaps;
 }
 
-static void log_fill(oracle_sim* s, int l, int e, int slot, int victim) {
+static void log_fill(oracle_sim* s, int l, int e, int slot, int victim, int kind) {
     if (s->n_ev == s->cap_ev) {
         s->cap_ev = s->cap_ev ? 2 * s->cap_ev : 1024;
         s->ev = (oracle_event*)realloc(s->ev, sizeof(oracle_event) * (size_t)s->cap_ev);
     }
     oracle_event* v = &s->ev[s->n_ev++];
     v->seq = s->fill_seq; v->layer = l; v->expert = e; v->slot = slot;
-    v->kind = ORACLE_EV_FILL; v->victim = victim; v->pad = 0;
+    v->kind = kind; v->victim = victim; v->pad = 0;
+}
+
+/* Copy (l, e) into a ring slot: the lowest-index empty slot, else the one
+ * with the smallest stamp (least recently used), whose owner is evicted; the
+ * entry takes a fresh stamp.  kind: ORACLE_EV_FILL or ORACLE_EV_PREFETCH. */
+static void sim_fill(oracle_sim* s, int l, int e, int kind) {
+    int32_t key = l * s->E + e;
+    int victim_slot = -1;
+    for (int r = 0; r < s->R; ++r)
+        if (s->ring_owner[r] < 0) { victim_slot = r; break; }
+    if (victim_slot < 0) {
+        victim_slot = 0;
+        for (int r = 1; r < s->R; ++r)
+            if (s->ring_stamp[r] < s->ring_stamp[victim_slot]) victim_slot = r;
+    }
+    int victim = s->ring_owner[victim_slot];
+    if (victim >= 0) s->st[S_EVICT]++;
+    s->ring_owner[victim_slot] = key;
+    s->ring_stamp[victim_slot] = ++s->clock;
+    s->st[kind == ORACLE_EV_PREFETCH ? S_PREF : S_FILL]++;
+    s->st[S_H2D] += s->slot_bytes;
+    s->fill_seq++;
+    log_fill(s, l, e, (int)(s->P + victim_slot), victim, kind);
 }
 
 static void sim_access(oracle_sim* s, int l, int e) {
@@ -208,22 +232,7 @@ static void sim_access(oracle_sim* s, int l, int e) {
         }
     }
     if (s->R == 0) return; /* unreachable for valid shapes: R >= K whenever P < L*E */
-    int victim_slot = -1;
-    for (int r = 0; r < s->R; ++r)
-        if (s->ring_owner[r] < 0) { victim_slot = r; break; }
-    if (victim_slot < 0) {
-        victim_slot = 0;
-        for (int r = 1; r < s->R; ++r)
-            if (s->ring_stamp[r] < s->ring_stamp[victim_slot]) victim_slot = r;
-    }
-    int victim = s->ring_owner[victim_slot];
-    if (victim >= 0) s->st[S_EVICT]++;
-    s->ring_owner[victim_slot] = key;
-    s->ring_stamp[victim_slot] = ++s->clock;
-    s->st[S_FILL]++;
-    s->st[S_H2D] += s->slot_bytes;
-    s->fill_seq++;
-    log_fill(s, l, e, (int)(s->P + victim_slot), victim);
+    sim_fill(s, l, e, ORACLE_EV_FILL);
 }
 
 void oracle_sim_decode_layer(oracle_sim* s, int l, int K, const int32_t* idx) {
@@ -249,9 +258,44 @@ void oracle_sim_prefill_layer(oracle_sim* s, int l, int T, int K, const int32_t*
         s->counts[(int64_t)l * s->E + idx[i]]++;
         hit[idx[i]] = 1;
     }
+    int n_cold = 0;
     for (int e = 0; e < s->E; ++e)
-        if (hit[e]) sim_access(s, l, e);
+        if (hit[e]) {
+            n_cold += s->slot_of[(int64_t)l * s->E + e] < 0;
+            sim_access(s, l, e);
+        }
+    /* the layer's cold experts stream through the ring in chunks of R; the
+     * last chunk holds the remainder (R when it divides evenly) */
+    s->pf_last_cold = (n_cold == 0 || s->R == 0) ? 0 : (n_cold - 1) % s->R + 1;
     free(hit);
+}
+
+/* Speculative prefetch after a prefill layer (a reading of the pages' bounded
+ * async cache, for the next layer's experts before its routing is known):
+ * the candidates are the experts of `layer` whose predicted assignment count
+ * hist[e] is positive, in ascending id.  A candidate that is pinned or
+ * already in the ring is skipped (no access, no stamp change); any other is
+ * filled by the rule of a cold miss, until `budget` prefetches have been
+ * made, budget = R minus the cold experts of the last chunk of the preceding
+ * prefill layer (those ring entries are still being read, and they carry the
+ * newest stamps, so no prefetch evicts them).  Prefetches are not accesses:
+ * they count as prefetches, their evictions as evictions and their bytes as
+ * host-to-device bytes, and the log lists them with kind PREFETCH.  Returns
+ * the number of prefetches. */
+int64_t oracle_sim_prefetch(oracle_sim* s, int layer, const int32_t* hist) {
+    const int budget = s->R - s->pf_last_cold;
+    int64_t n = 0;
+    for (int e = 0; e < s->E && n < budget; ++e) {
+        if (hist[e] <= 0) continue;
+        const int32_t key = layer * s->E + e;
+        if (s->slot_of[key] >= 0) continue;
+        int in_ring = 0;
+        for (int r = 0; r < s->R; ++r) in_ring |= s->ring_owner[r] == key;
+        if (in_ring) continue;
+        sim_fill(s, layer, e, ORACLE_EV_PREFETCH);
+        ++n;
+    }
+    return n;
 }
 
 void oracle_sim_stats(const oracle_sim* s, int64_t* out) {

@@ -28,6 +28,18 @@ def _run_golden(path):
             name = tok[1]
         elif op == "access":
             sim.decode_layer(args[0], np.array([args[1]]))
+        elif op == "prefill":  # one token per listed expert: the layer's distinct experts
+            sim.prefill_layer(args[0], np.array(args[1:], dtype=np.int32).reshape(-1, 1))
+        elif op == "prefetch":
+            hist = np.zeros(sim.E, np.int32)
+            hist[args[1:]] = 1
+            sim.prefetch(args[0], hist)
+        elif op == "expect_prefetches":
+            assert sim.stats()["prefetches"] == args[0], (name, sim.stats())
+            checked += 1
+        elif op == "expect_event_kind":
+            assert int(sim.events()[args[0] - 1]["kind"]) == args[1], name
+            checked += 1
         elif op == "calibrate":
             sim.calibrate(reset_counts=True)
         elif op == "expect_stats":
@@ -35,7 +47,7 @@ def _run_golden(path):
             got = [st[k] for k in ("accesses", "pinned_hits", "cold_hits", "ring_hits", "fills",
                                    "evictions")]
             assert got == args, (name, got, args)
-            assert st["h2d_bytes"] == 100 * st["fills"]
+            assert st["h2d_bytes"] == 100 * (st["fills"] + st["prefetches"])
             checked += 1
         elif op == "expect_event":
             ev = sim.events()
@@ -58,7 +70,7 @@ def _run_golden(path):
 
 
 def test_golden_traces(golden_dir):
-    assert _run_golden(os.path.join(golden_dir, "placement_traces.txt")) == 19
+    assert _run_golden(os.path.join(golden_dir, "placement_traces.txt")) == 30
 
 
 def test_quota_sums_to_budget():
@@ -109,6 +121,36 @@ class ListLRU:
         self.ring[key] = slot
         self.events.append((len(self.events) + 1, l, e, self.P + slot, victim))
 
+    def prefill_layer(self, l, experts):
+        """A prefill batch's distinct experts of layer l, ascending; remembers
+        how many cold experts the layer's last ring chunk (R at a time) holds."""
+        distinct = sorted(set(int(e) for e in experts))
+        cold = sum((l, e) not in self.pinned for e in distinct)
+        for e in distinct:
+            self.access(l, e)
+        self.last_cold = 0 if cold == 0 or self.R == 0 else cold - self.R * ((cold - 1) // self.R)
+
+    def prefetch(self, l, candidates):
+        budget = self.R - getattr(self, "last_cold", 0)
+        n = 0
+        for e in sorted(set(int(c) for c in candidates)):
+            if n >= budget:
+                break
+            key = l * self.E + e
+            if (l, e) in self.pinned or key in self.ring:
+                continue
+            self.stats["prefetches"] = self.stats.get("prefetches", 0) + 1
+            if len(self.ring) < self.R:
+                slot = min(set(range(self.R)) - set(self.ring.values()))
+                victim = -1
+            else:
+                victim, slot = self.ring.popitem(last=False)
+                self.stats["evictions"] += 1
+            self.ring[key] = slot
+            self.events.append((len(self.events) + 1, l, e, self.P + slot, victim))
+            n += 1
+        return n
+
 
 @pytest.mark.parametrize("L,E,P,R,K", [(4, 16, 24, 4, 2), (3, 32, 40, 8, 8), (2, 8, 0, 8, 4),
                                        (40, 256, 6144, 32, 8)])
@@ -137,6 +179,42 @@ def test_simulator_matches_list_lru_on_random_traces(L, E, P, R, K):
     assert st["fills"] > 0 and (P == 0 or st["pinned_hits"] > 0)
     if R < E * L - P:
         assert st["evictions"] > 0 and st["ring_hits"] > 0
+
+
+@pytest.mark.parametrize("L,E,P,R", [(3, 32, 40, 8), (4, 64, 150, 12), (2, 16, 8, 4)])
+def test_prefill_prefetch_matches_list_model_on_random_traces(L, E, P, R):
+    """Random prefill layers (Zipf-skewed distinct sets, often more cold
+    experts than ring slots) each followed by a prefetch of the next layer's
+    random candidates: counters, the fill/prefetch log and the ring contents
+    equal an independent list model."""
+    rng = np.random.default_rng(L * 100 + E + P + R)
+    sim = oracle.Sim(L, E, P, R, slot_bytes=1)
+    sim.place_uniform()
+    ref = ListLRU(L, E, P, R)
+    ref.stats["prefetches"] = 0
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    for step in range(400):
+        l = step % L
+        idx = rng.choice(E, size=(int(rng.integers(1, 40)), 2), p=p).astype(np.int32)
+        sim.prefill_layer(l, idx)
+        ref.prefill_layer(l, idx.ravel())
+        cand = rng.choice(E, size=int(rng.integers(0, 2 * R)), replace=False)
+        hist = np.zeros(E, np.int32)
+        hist[cand] = 1
+        assert sim.prefetch((l + 1) % L, hist) == ref.prefetch((l + 1) % L, cand)
+    st = sim.stats()
+    for k, v in ref.stats.items():
+        assert st[k] == v, (k, st[k], v)
+    assert st["h2d_bytes"] == st["fills"] + st["prefetches"]
+    got = [(int(e["seq"]), int(e["layer"]), int(e["expert"]), int(e["slot"]), int(e["victim"]))
+           for e in sim.events()]
+    assert got == ref.events
+    kinds = [int(e["kind"]) for e in sim.events()]
+    assert kinds.count(oracle.EV_PREFETCH) == st["prefetches"] > 0
+    owner = sim.placement()[1]
+    ring = {slot: key for key, slot in ref.ring.items()}
+    assert [int(o) for o in owner] == [ring.get(r, -1) for r in range(R)]
 
 
 def test_calibration_matches_full_sort_and_keeps_slots():
