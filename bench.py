@@ -37,6 +37,8 @@ Also:
    2. The Zipf permutation switches to B at token 1024.
    3. Then a 256-token decode probe under B runs before and after
       recalibration.
+ - `prefill_prefetch`: the same prefill from the same state with speculative
+   prefetch of each next layer's predicted experts (moe_spark_set_prefetch).
  - `roofline`: the dominant decode kernel, timed by HIP events over isolated
    replays.
  - `h2d_link`: a pinned host-to-device copy probe of the PCIe link.
@@ -222,8 +224,10 @@ def run_batched(ms, torch, model, P, R, B, warm, meas, row, ref_x, traffic_json)
         ms.moe_spark_destroy(ctx)
 
 
-def run_prefill(ms, torch, model, P, R, warm, probe, layers):
-    """Batched prefill with a popularity shift, then recalibration."""
+def run_prefill(ms, torch, model, P, R, warm, probe, layers, prefetch=False):
+    """Batched prefill with a popularity shift, then recalibration; with
+    prefetch, the next layer's predicted experts are copied during each
+    layer's last chunk of cold experts."""
     import workload as wl
     wp = wl.prefill(layers)
     biases = [wp.bias_rows(l) for l in range(model.w.L)]  # rows: permutation A, permutation B
@@ -234,6 +238,7 @@ def run_prefill(ms, torch, model, P, R, warm, probe, layers):
     row_b = torch.ones_like(row_a)
     ctx = model.make_ctx(P=P, R=R, biases=biases, max_tokens=T)
     try:
+        ms.moe_spark_set_prefetch(ctx, prefetch)
         xw = torch.from_numpy(warm).cuda()
         ms.moe_spark_decode(ctx, xw.data_ptr(), xw.shape[0], row_a.data_ptr())
         ms.moe_spark_calibrate(ctx, True)
@@ -260,12 +265,14 @@ def run_prefill(ms, torch, model, P, R, warm, probe, layers):
         out = dict(tokens=T, layers=model.w.L, tok_s=round(T / dt, 1), ms=round(dt * 1e3, 3),
                    expert_gflop=round(gflop, 1), expert_tflops_end_to_end=round(gflop / dt / 1e3, 2),
                    accesses=st["accesses"], fills=st["fills"], evictions=st["evictions"],
+                   prefetches=st["prefetches"], ring_hits=st["ring_hits"],
                    h2d_bytes=st["h2d_bytes"], cold_hit_pct=rates(st)["cold_hit_pct"],
                    probe_cold_hit_pct_before_recalibration=before,
                    probe_cold_hit_pct_after_recalibration=after,
                    arithmetic="Q4_0 codes as exact bf16 (128 + q, zero point in the MFMA start value), "
                               "activations as bf16 hi + lo, fp32 accumulation, fp16 block scales applied in fp32")
-        log(f"prefill: {out['tok_s']} tok/s, fills {st['fills']}, cold probe {before}% -> {after}%")
+        log(f"prefill (prefetch {'on' if prefetch else 'off'}): {out['tok_s']} tok/s, fills {st['fills']}, "
+            f"prefetches {st['prefetches']}, cold probe {before}% -> {after}%")
         return out
     finally:
         ms.moe_spark_destroy(ctx)
@@ -584,6 +591,9 @@ def main():
     if not args.no_prefill:
         probe = wl.stack(args.layers).tokens(C + n_stream + args.warmup, 256)
         res["prefill"] = run_prefill(ms, torch, model, P, args.ring, calib, probe, args.layers)
+        if P < LE:
+            res["prefill_prefetch"] = run_prefill(ms, torch, model, P, args.ring, calib, probe, args.layers,
+                                                  prefetch=True)
     if not args.no_autotune and P < LE:
         res["self_tuning"] = run_autotune(ms, torch, model, P, args.ring, calib, stream, args.layers)
     res["h2d_link"] = h2d_probe(torch)

@@ -106,18 +106,21 @@ typedef struct {
     int64_t tokens;        /* tokens run by the decode graph */
     int64_t retunes;       /* online self-tuning steps taken (moe_spark_set_autotune) */
     int64_t retune_swaps;  /* experts those steps swapped into the pinned set */
+    int64_t prefetches;    /* speculative copies of predicted experts into ring slots (prefill);
+                              counted in h2d_bytes and, when they evict, in evictions */
 } moe_spark_stats;
 
 typedef struct {
     int64_t seq;     /* 1-based fill number */
     int32_t layer, expert;
     int32_t slot;    /* global slot id: pinned 0..P-1, ring P..P+R-1 */
-    int32_t kind;    /* MOE_SPARK_EV_FILL */
+    int32_t kind;    /* MOE_SPARK_EV_FILL or MOE_SPARK_EV_PREFETCH */
     int32_t victim;  /* evicted layer*E+expert, or -1 (slot was empty) */
     int32_t pad;
 } moe_spark_event;
 
 #define MOE_SPARK_EV_FILL 2
+#define MOE_SPARK_EV_PREFETCH 3  /* a speculative copy of a predicted expert (prefill) */
 
 typedef struct moe_spark_ctx moe_spark_ctx;
 
@@ -283,6 +286,8 @@ moe_spark_status moe_spark_decode(moe_spark_ctx* ctx, float* x, int32_t n_tokens
  * before the next layer's, and every counter, the fill log and the ring
  * follow from that order.  Each distinct expert of a layer-step is read once
  * for all the tokens that chose it.
+ * With moe_spark_set_prefetch on, the next layer's predicted experts are
+ * copied into ring entries the layer no longer needs, beside its GEMMs.
  * x [T][d] fp32 device, updated in place; bias_row [T] int32 device or NULL.
  * Q4_0 contexts only.  Below full residency the ring must hold a whole
  * step's accesses (ring_slots >= batch * top_k), so no expert a step uses is
@@ -311,6 +316,8 @@ moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int
  * accessed once each in ascending id; non-pinned ones stream through the
  * spare-slot ring in chunks of at most R, filled as in moe_spark_create
  * describes (pulled during the pinned experts' GEMMs, or agent copies).
+ * With moe_spark_set_prefetch on, the next layer's predicted experts are
+ * copied into ring entries the layer no longer needs, beside its GEMMs.
  * x [T][d] fp32 device, updated in place; bias_row [T] int32 device or NULL.
  * Synchronises the compute stream once per layer (the host plans each layer
  * from its expert histogram).  Errors: E_INVALID (format, n_tokens, x),
@@ -329,15 +336,45 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
  * n_tokens per prefill batch; rows at or past cap are not written.
  * layer_forward traces token t of its call at row t, layer `layer`.
  * Passage: none of its own (observability for parity checks).
- * Passage: [Spark] "The key components" (1): the cold-hit rate ("36% to ~7%")
- * is cold_hits / accesses; [Bagua] "Actionable Advice": fills and their
- * bytes are the swap traffic between system RAM and the GPU.
- * Passage: as moe_spark_get_stats.
  */
 moe_spark_status moe_spark_set_trace(moe_spark_ctx* ctx, float* x_layers, int32_t* topk,
                                      float* gates, int64_t cap_tokens);
 
+/* Speculative prefetch in moe_spark_prefill (off at create; enable != 0
+ * turns it on).  After layer l's routing, layer l+1's router applied to
+ * layer l's input predicts layer l+1's top-K for every token; the predicted
+ * experts that are neither pinned nor in the ring go, in ascending id, into
+ * ring slots: at most R - (the layer's last chunk's non-pinned experts)
+ * copies, chosen after that chunk's policy, so that no slot the chunk reads
+ * or fills is taken.  The host hands these copies to the DMA engine on the
+ * copy stream once layer l is queued; they run beside the rest of layer l
+ * and layer l+1's routing, and layer l+1's first launch that touches slot
+ * data waits for them.  A prefetch is not an access: routing counts and
+ * the access counters do not change; it is counted in stats.prefetches and
+ * logged with kind MOE_SPARK_EV_PREFETCH.  Outputs do not change.
+ * Errors: E_STATE when fills are copied by the host agent
+ * (MOE_SPARK_PULL_FILLS=0) or max_tokens was 0 at create.
+ * Passage: none describes a prefetch; [Bagua] "Actionable Advice" names the
+ * swap latency between system RAM and the GPU as the bottleneck, and this
+ * moves part of it under the matrix-core work.
+ */
+moe_spark_status moe_spark_set_prefetch(moe_spark_ctx* ctx, int32_t enable);
+
+/* The prediction histograms of the last moe_spark_prefill with prefetch on:
+ * out [L][E] int32 host, row l = predicted assignments per expert of layer l
+ * (row 0 and rows of a prefill without prefetch are zero).
+ * Passage: as moe_spark_set_prefetch.
+ */
+moe_spark_status moe_spark_get_prefetch_hist(moe_spark_ctx* ctx, int32_t* out);
+
+/* Copy the counters (see moe_spark_stats) to host memory after waiting for
+ * the compute stream; reset_stats zeroes them.
+ * Passage: [Spark] "The key components" (1): the cold-hit rate ("36% to ~7%")
+ * is cold_hits / accesses; [Bagua] "Actionable Advice": fills and their
+ * bytes are the swap traffic between system RAM and the GPU.
+ */
 moe_spark_status moe_spark_get_stats(moe_spark_ctx* ctx, moe_spark_stats* out);
+/* Passage: as moe_spark_get_stats. */
 moe_spark_status moe_spark_reset_stats(moe_spark_ctx* ctx);
 
 /* Host outputs (each may be NULL): slot_of [L][E] (pinned slot or -1),

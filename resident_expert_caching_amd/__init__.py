@@ -34,7 +34,8 @@ class Config(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "accesses", "pinned_hits", "cold_hits", "ring_hits", "fills", "evictions", "h2d_bytes",
-        "fill_ns_sum", "fill_ns_max", "calib_uploads", "tokens", "retunes", "retune_swaps")]
+        "fill_ns_sum", "fill_ns_max", "calib_uploads", "tokens", "retunes", "retune_swaps",
+        "prefetches")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -76,6 +77,8 @@ def _load():
         "moe_spark_token_forward": (st, [vp, vp, vp]),
         "moe_spark_prefill": (st, [vp, vp, i32, vp]),
         "moe_spark_set_trace": (st, [vp, vp, vp, vp, i64]),
+        "moe_spark_set_prefetch": (st, [vp, i32]),
+        "moe_spark_get_prefetch_hist": (st, [vp, vp]),
         "moe_spark_get_stats": (st, [vp, ctypes.POINTER(Stats)]),
         "moe_spark_reset_stats": (st, [vp]),
         "moe_spark_get_placement": (st, [vp, vp, vp, vp, vp]),
@@ -173,6 +176,15 @@ def moe_spark_prefill(ctx, x, n_tokens, bias_row=None):
 
 def moe_spark_set_trace(ctx, x_layers, topk, gates, cap_tokens):
     _check(ctx, _lib.moe_spark_set_trace(ctx, x_layers, topk, gates, cap_tokens))
+
+
+def moe_spark_set_prefetch(ctx, enable):
+    _check(ctx, _lib.moe_spark_set_prefetch(ctx, 1 if enable else 0))
+
+
+def moe_spark_get_prefetch_hist(ctx, out):
+    """out: host address of an int32 [L][E] buffer (e.g. numpy ``arr.ctypes.data``)."""
+    _check(ctx, _lib.moe_spark_get_prefetch_hist(ctx, out))
 
 
 def moe_spark_get_stats(ctx):

@@ -36,7 +36,7 @@ constexpr int kRW = 16;
 constexpr int kNP = kQD / kRW;   // 128 partial rows
 
 // Device statistics counters (int64 each).
-enum DevStat { DS_ACC = 0, DS_PIN, DS_COLD, DS_RING, DS_FILL, DS_EVICT, DS_H2D, DS_TOKENS, DS_N };
+enum DevStat { DS_ACC = 0, DS_PIN, DS_COLD, DS_RING, DS_FILL, DS_EVICT, DS_H2D, DS_TOKENS, DS_PREF, DS_N };
 
 // Error bits.
 enum DevError { ERR_FILL_TIMEOUT = 1, ERR_FIFO_OVERRUN = 2, ERR_BAD_SLOT = 4 };
@@ -289,6 +289,14 @@ struct PfArgs {
     int32_t* topk;            // [T][K]
     float* gates;             // [T][K]
     int32_t* hist;            // [E] assignments per expert
+    // prediction for the prefetch (all null without it): the next layer's
+    // router applied to this layer's input, its top-K counted per expert
+    const float* wr2;         // the next layer's packed router
+    const float* bias2;       // the next layer's router bias or null
+    float* logits2;           // [T][E]
+    int32_t* hist2;           // [E] predicted assignments per expert of the next layer
+    int32_t* pfill2;          // [1 + 2 kMaxR] the prefetch copies: count, then (arena key, slot) pairs
+    int32_t pf_budget;        // prefetch launch after the last chunk: copies at most this many
     const int32_t* goff;      // [E+1] first sorted position of each expert's group
     int32_t* perm;            // [T*K] token of each sorted position
     int32_t* apos;            // [T][K] sorted position of assignment (t, k)
@@ -316,7 +324,11 @@ struct PfArgs {
     uint64_t spin_limit_ticks;
 };
 
-hipError_t launch_pf_front(const PfArgs& a, hipStream_t s);    // norm, router, top-k + counts + histogram
+// norm, router, top-k + counts + histogram (with a.hist2: also the
+// prediction of the next layer's top-K)
+hipError_t launch_pf_front(const PfArgs& a, hipStream_t s);
+// the first chunk's policy (with a.hist2 and a one-chunk layer: then the
+// prefetch rule)
 hipError_t launch_pf_policy_first(const PfArgs& a, hipStream_t s);
 hipError_t launch_pf_scatter(const PfArgs& a, hipStream_t s);  // sort assignments by (expert, token)
 hipError_t launch_pf_policy(const PfArgs& a, hipStream_t s);   // a chunk's experts through the placement policy
@@ -325,6 +337,10 @@ hipError_t launch_pf_policy(const PfArgs& a, hipStream_t s);   // a chunk's expe
 // policy run's fills
 hipError_t launch_pf_gemms(const PfArgs& a, hipStream_t s);
 hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s);  // rank-order combine + residual
+// after a layer's last chunk: the experts of layer a.layer + 1 with
+// a.hist2 > 0 (ascending) through the prefetch rule, at most a.pf_budget
+// copies, listed in a.pfill2
+hipError_t launch_pf_prefetch(const PfArgs& a, hipStream_t s);
 hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s);
 
 // Launchers (kernels.hip).

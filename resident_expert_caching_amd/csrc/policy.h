@@ -19,7 +19,7 @@ namespace moe {
 struct RingState {
     uint64_t clock, fseq, qseq;
     int64_t nev;
-    int64_t n_pin, n_cold, n_ring, n_fill, n_evict;
+    int64_t n_pin, n_cold, n_ring, n_fill, n_evict, n_pref;
 };
 
 // Copy the ring tables into LDS (whole wave).
@@ -56,36 +56,18 @@ __device__ inline void ring_store(const PolicyTables& pt, const int32_t* r_owner
     }
 }
 
-// One access of (layer, expert) whose pinned slot is `pin` (-1: not pinned).
-// Wave-uniform arguments and results.  wseq: fill number to wait for, 0 when
-// the data is already resident.
-__device__ inline void ring_access(const PolicyTables& pt, int layer, int expert, int pin, int32_t* r_owner,
-                                   uint64_t* r_stamp, uint64_t* r_seq, RingState& s, int& slot, uint64_t& wseq) {
+// Copy (layer, expert) into a ring slot: the lowest-index empty slot, else
+// the entry with the smallest stamp (the least recently used), whose owner is
+// evicted; the entry takes a fresh stamp.  The copy is logged with `kind`
+// (MOE_SPARK_EV_FILL or MOE_SPARK_EV_PREFETCH) and, unless the kernels pull
+// fills themselves, requested from the host fill agent.  Wave-uniform
+// arguments and results: slot (global id) and wseq (the fill number).
+__device__ inline void ring_fill(const PolicyTables& pt, int layer, int expert, int32_t* r_owner,
+                                 uint64_t* r_stamp, uint64_t* r_seq, RingState& s, int kind, int& slot,
+                                 uint64_t& wseq) {
     const int lane = threadIdx.x & 63;
     const int R = pt.R;
     const int32_t key = layer * pt.E + expert;
-    wseq = 0;
-    if (pin >= 0) {
-        slot = pin;
-        ++s.n_pin;
-        return;
-    }
-    ++s.n_cold;
-    int hit = -1;
-    for (int base = 0; base < R && hit < 0; base += 64) {
-        const int r = base + lane;
-        const uint64_t m = __ballot(r < R && r_owner[r] == key);
-        if (m) hit = base + __builtin_ctzll(m);
-    }
-    if (hit >= 0) {
-        // filled by an earlier access whose kernels waited for the copy
-        ++s.n_ring;
-        ++s.clock;
-        if (lane == 0) r_stamp[hit] = s.clock;
-        __builtin_amdgcn_wave_barrier();
-        slot = (int)(pt.P + hit);
-        return;
-    }
     int v = -1;
     for (int base = 0; base < R && v < 0; base += 64) {
         const int r = base + lane;
@@ -115,7 +97,10 @@ __device__ inline void ring_access(const PolicyTables& pt, int layer, int expert
     if (victim >= 0) ++s.n_evict;
     ++s.clock;
     ++s.fseq;
-    ++s.n_fill;
+    if (kind == MOE_SPARK_EV_PREFETCH)
+        ++s.n_pref;
+    else
+        ++s.n_fill;
     if (lane == 0) {
         r_owner[v] = key;
         r_stamp[v] = s.clock;
@@ -126,12 +111,12 @@ __device__ inline void ring_access(const PolicyTables& pt, int layer, int expert
             ev.layer = layer;
             ev.expert = expert;
             ev.slot = (int32_t)(pt.P + v);
-            ev.kind = MOE_SPARK_EV_FILL;
+            ev.kind = kind;
             ev.victim = victim;
             ev.pad = 0;
             pt.events[s.nev] = ev;
         }
-        if (!pt.pull) {  // a copy for the host agent (pulled fills are copied by the decode kernels)
+        if (!pt.pull) {  // a copy for the host agent (pulled fills are copied by the kernels)
             FifoEntry* fe = pt.fifo + (s.qseq % kFifoCap);
             fe->key = key;
             fe->ring = v;
@@ -147,6 +132,56 @@ __device__ inline void ring_access(const PolicyTables& pt, int layer, int expert
     slot = (int)(pt.P + v);
 }
 
+// Index of the ring entry owned by key, or -1 (wave-uniform).
+__device__ inline int ring_find(const PolicyTables& pt, int32_t key, const int32_t* r_owner) {
+    const int lane = threadIdx.x & 63;
+    int hit = -1;
+    for (int base = 0; base < pt.R && hit < 0; base += 64) {
+        const int r = base + lane;
+        const uint64_t m = __ballot(r < pt.R && r_owner[r] == key);
+        if (m) hit = base + __builtin_ctzll(m);
+    }
+    return hit;
+}
+
+// One access of (layer, expert) whose pinned slot is `pin` (-1: not pinned).
+// Wave-uniform arguments and results.  wseq: fill number to wait for, 0 when
+// the data is already resident.
+__device__ inline void ring_access(const PolicyTables& pt, int layer, int expert, int pin, int32_t* r_owner,
+                                   uint64_t* r_stamp, uint64_t* r_seq, RingState& s, int& slot, uint64_t& wseq) {
+    const int lane = threadIdx.x & 63;
+    wseq = 0;
+    if (pin >= 0) {
+        slot = pin;
+        ++s.n_pin;
+        return;
+    }
+    ++s.n_cold;
+    const int hit = ring_find(pt, layer * pt.E + expert, r_owner);
+    if (hit >= 0) {
+        // filled by an earlier access (or prefetch) whose copy has landed
+        ++s.n_ring;
+        ++s.clock;
+        if (lane == 0) r_stamp[hit] = s.clock;
+        __builtin_amdgcn_wave_barrier();
+        slot = (int)(pt.P + hit);
+        return;
+    }
+    ring_fill(pt, layer, expert, r_owner, r_stamp, r_seq, s, MOE_SPARK_EV_FILL, slot, wseq);
+}
+
+// Speculative prefetch of (layer, expert): nothing when it is pinned or
+// already in the ring (no stamp change: a prefetch is not an access);
+// otherwise a copy into a ring slot by the fill rule.  Returns whether a
+// copy was made (slot, wseq as ring_fill).  Wave-uniform.
+__device__ inline bool ring_prefetch(const PolicyTables& pt, int layer, int expert, int pin, int32_t* r_owner,
+                                     uint64_t* r_stamp, uint64_t* r_seq, RingState& s, int& slot,
+                                     uint64_t& wseq) {
+    if (pin >= 0 || ring_find(pt, layer * pt.E + expert, r_owner) >= 0) return false;
+    ring_fill(pt, layer, expert, r_owner, r_stamp, r_seq, s, MOE_SPARK_EV_PREFETCH, slot, wseq);
+    return true;
+}
+
 // Add this policy run's counters to the device statistics (lane 0).
 __device__ inline void stats_flush(const PolicyTables& pt, int64_t accesses, const RingState& s) {
     if ((threadIdx.x & 63) != 0) return;
@@ -155,10 +190,10 @@ __device__ inline void stats_flush(const PolicyTables& pt, int64_t accesses, con
     if (s.n_pin) atomicAdd(st + DS_PIN, (unsigned long long)s.n_pin);
     if (s.n_cold) atomicAdd(st + DS_COLD, (unsigned long long)s.n_cold);
     if (s.n_ring) atomicAdd(st + DS_RING, (unsigned long long)s.n_ring);
-    if (s.n_fill) {
-        atomicAdd(st + DS_FILL, (unsigned long long)s.n_fill);
-        atomicAdd(st + DS_H2D, (unsigned long long)(s.n_fill * pt.slot_bytes));
-    }
+    if (s.n_fill) atomicAdd(st + DS_FILL, (unsigned long long)s.n_fill);
+    if (s.n_pref) atomicAdd(st + DS_PREF, (unsigned long long)s.n_pref);
+    if (s.n_fill + s.n_pref)
+        atomicAdd(st + DS_H2D, (unsigned long long)((s.n_fill + s.n_pref) * pt.slot_bytes));
     if (s.n_evict) atomicAdd(st + DS_EVICT, (unsigned long long)s.n_evict);
 }
 

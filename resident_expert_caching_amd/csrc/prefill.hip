@@ -145,29 +145,38 @@ __global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
 
 // ---------------------------------------------------------------- router
 
-// One work-group of 4 waves per 32 tokens x 32 experts, on the fp32 matrix
+// One work-group of 8 waves per 32 tokens x 32 experts, on the fp32 matrix
 // cores (v_mfma_f32_16x16x4_f32: fp32 products, fp32 accumulation).  Wave w
-// covers d in [512w, 512w + 512).  For a 16-wide slice k0..k0+15 of d, lane
-// (i, g) = (lane % 16, lane / 16) loads the four consecutive values 4g..4g+3
-// of token row i and of expert row i (the router is packed [d/16][E][16], so
-// both are 16-byte loads); MFMA j then takes k = k0 + 4g + j from lane group g
-// on both operands, which covers the slice.  The four waves' partial sums
-// meet in LDS and are added in wave order.
-// Output: logits[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias.
-__global__ __launch_bounds__(256) void pf_router_kernel(PfArgs a) {
+// covers d in [256w, 256w + 256), so that many loads are in flight per tile.
+// For a 16-wide slice k0..k0+15 of d, lane (i, g) = (lane % 16, lane / 16)
+// loads the four consecutive values 4g..4g+3 of token row i and of expert
+// row i (the router is packed [d/16][E][16], so both are 16-byte loads);
+// MFMA j then takes k = k0 + 4g + j from lane group g on both operands,
+// which covers the slice.  The eight waves' partial sums meet in LDS and are
+// added in wave order.
+// Output: logits[t][e] = inv_rms[t] * (x[t] . Wr[e]) + bias.  With a
+// prediction (a.wr2), the grid has twice the rows of expert tiles and the
+// second half applies the next layer's router (a.wr2, a.bias2 -> a.logits2)
+// to the same input.
+constexpr int kRouterWaves = 8;
+__global__ __launch_bounds__(64 * kRouterWaves) void pf_router_kernel(PfArgs a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, i = lane & 15, g = lane >> 4;
-    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-    const int E = a.E;
+    const int E = a.E, ny = (E + 31) / 32;
+    const bool second = (int)blockIdx.y >= ny;
+    const float* __restrict__ wr = second ? a.wr2 : a.wr;
+    const float* __restrict__ bias_tab = second ? a.bias2 : a.bias;
+    float* __restrict__ logits = second ? a.logits2 : a.logits;
+    const int t0 = blockIdx.x * 32, e0 = (blockIdx.y - (second ? ny : 0)) * 32;
     const bool ta = t0 + i < a.T, tb = t0 + 16 + i < a.T;
     const bool ea = e0 + i < E, eb = e0 + 16 + i < E;
     const float* xa = a.x + (int64_t)(ta ? t0 + i : 0) * kQD + 4 * g;
     const float* xb = a.x + (int64_t)(tb ? t0 + 16 + i : 0) * kQD + 4 * g;
-    const float* wa = a.wr + (int64_t)(ea ? e0 + i : 0) * kRW + 4 * g;
-    const float* wb = a.wr + (int64_t)(eb ? e0 + 16 + i : 0) * kRW + 4 * g;
+    const float* wa = wr + (int64_t)(ea ? e0 + i : 0) * kRW + 4 * g;
+    const float* wb = wr + (int64_t)(eb ? e0 + 16 + i : 0) * kRW + 4 * g;
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x4 acc[2][2] = {{zero, zero}, {zero, zero}};
-    constexpr int kSplit = kQD / 4;
-#pragma unroll 4
+    constexpr int kSplit = kQD / kRouterWaves;
+#pragma unroll
     for (int k0 = w * kSplit; k0 < (w + 1) * kSplit; k0 += kRW) {
         const f32x4 A0 = ta ? *reinterpret_cast<const f32x4*>(xa + k0) : zero;
         const f32x4 A1 = tb ? *reinterpret_cast<const f32x4*>(xb + k0) : zero;
@@ -182,13 +191,16 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfArgs a) {
             acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A1[j], B1[j], acc[1][1], 0, 0, 0);
         }
     }
-    __shared__ __align__(16) f32x4 part[4][4][64];  // [wave][tile m*2+n][lane]
+    __shared__ __align__(16) f32x4 part[kRouterWaves][4][64];  // [wave][tile m*2+n][lane]
 #pragma unroll
     for (int q = 0; q < 4; ++q) part[w][q][lane] = acc[q >> 1][q & 1];
     __syncthreads();
-    // wave w finishes tile q = w: lane (i, g) holds rows 4g..4g+3 of column i
+    if (w >= 4) return;
+    // wave w < 4 finishes tile q = w: lane (i, g) holds rows 4g..4g+3 of column i
     const int m = w >> 1, n = w & 1;
-    const f32x4 sum = ((part[0][w][lane] + part[1][w][lane]) + part[2][w][lane]) + part[3][w][lane];
+    f32x4 sum = part[0][w][lane];
+#pragma unroll
+    for (int v = 1; v < kRouterWaves; ++v) sum += part[v][w][lane];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int tok = t0 + 16 * m + 4 * g + r;
@@ -196,12 +208,12 @@ __global__ __launch_bounds__(256) void pf_router_kernel(PfArgs a) {
         if (tok >= a.T || e >= E) continue;
         const float inv = a.inv[tok];
         float bias = 0.0f;
-        if (a.bias) {
+        if (bias_tab) {
             int row = a.bias_row ? a.bias_row[tok] : 0;
             row = row < 0 ? 0 : (row >= a.n_bias_rows ? a.n_bias_rows - 1 : row);
-            bias = a.bias[(int64_t)row * E + e];
+            bias = bias_tab[(int64_t)row * E + e];
         }
-        a.logits[(int64_t)tok * E + e] = sum[r] * inv + bias;
+        logits[(int64_t)tok * E + e] = sum[r] * inv + bias;
     }
 }
 
@@ -236,6 +248,66 @@ __global__ __launch_bounds__(kPfThreads) void pf_topk_kernel(PfArgs a) {
             a.tr_gates[o] = g;
         }
     }
+    if (!a.hist2) return;
+    // the next layer's top-K from its router on this input: a prediction
+    // that only steers the prefetch (hist2 counts it per expert)
+    __syncthreads();
+    for (int e = tid; e < E; e += kPfThreads) lg[e] = a.logits2[(int64_t)t * E + e];
+    __syncthreads();
+    block_topk(lg, E, K, kpad, cand, s_e, s_l);
+    if (tid < K) atomicAdd(a.hist2 + s_e[tid], 1);
+}
+
+// ---------------------------------------------------------------- prefetch
+
+// The prefetch rule, run by one wave after the layer's last policy run, on
+// the ring tables already in LDS: the experts of layer a.layer + 1 that the
+// prediction histogram a.hist2 names (count > 0), in ascending id, each
+// copied into a ring slot unless pinned or already in the ring, at most
+// `budget` copies.  The copies are listed in a.pfill2 (count, then
+// (layer*E + expert, slot) pairs; always written, possibly empty) for the
+// host to hand to the DMA engine.  Not an access: no counts, and the slots
+// of the experts that the layer still computes are never chosen (the
+// caller's budget leaves the least-recently-used victims among older ring
+// entries).
+__device__ void pf_prefetch_run(const PfArgs& a, int budget, int32_t* r_owner, uint64_t* r_stamp, uint64_t* r_seq,
+                                RingState& rs) {
+    const PolicyTables& pt = a.pt;
+    const int lane = threadIdx.x & 63, layer = a.layer + 1;
+    const int64_t lbase = (int64_t)layer * a.E;
+    int nf = 0;
+    for (int base = 0; base < a.E && nf < budget; base += 64) {
+        const int e = base + lane;
+        uint64_t m = __ballot(e < a.E && a.hist2[e] > 0 && pt.slot_of[lbase + e] < 0);  // pinned: nothing to do
+        while (m && nf < budget) {
+            const int ex = base + __builtin_ctzll(m);
+            m &= m - 1;
+            int slot;
+            uint64_t wseq;
+            if (ring_prefetch(pt, layer, ex, pt.slot_of[lbase + ex], r_owner, r_stamp, r_seq, rs, slot, wseq)) {
+                if (lane == 0) {
+                    a.pfill2[1 + 2 * nf] = (int32_t)(lbase + ex);
+                    a.pfill2[2 + 2 * nf] = slot;
+                }
+                ++nf;
+            }
+        }
+    }
+    if (lane == 0) a.pfill2[0] = nf;
+}
+
+// One wave: the prefetch rule after a layer's last chunk when the layer took
+// several chunks (a single-chunk layer runs it in its first policy kernel).
+__global__ __launch_bounds__(64) void pf_prefetch_kernel(PfArgs a) {
+    __shared__ int32_t r_owner[kMaxR];
+    __shared__ uint64_t r_stamp[kMaxR];
+    __shared__ uint64_t r_seq[kMaxR];
+    const PolicyTables& pt = a.pt;
+    RingState rs{};
+    ring_load(pt, r_owner, r_stamp, r_seq, rs);
+    pf_prefetch_run(a, a.pf_budget, r_owner, r_stamp, r_seq, rs);
+    ring_store(pt, r_owner, r_stamp, r_seq, rs);
+    stats_flush(pt, 0, rs);
 }
 
 // ---------------------------------------------------------------- scatter
@@ -313,7 +385,8 @@ __global__ __launch_bounds__(64) void pf_policy_kernel(PfArgs a) {
 // placement policy, so that its fills start before the host has planned the
 // layer.  The chunk is cut by the host's rule: the layer's experts with
 // assignments (hist > 0), ascending, up to and excluding the one that would
-// be the (R+1)-th unpinned expert.
+// be the (R+1)-th unpinned expert.  With prediction (a.hist2), the prefetch
+// rule for the next layer follows when the chunk is the whole layer.
 __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
     __shared__ int32_t r_owner[kMaxR];
     __shared__ uint64_t r_stamp[kMaxR];
@@ -348,6 +421,16 @@ __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
         }
     }
     if (lane == 0) a.pfill[0] = nf;
+    // with prediction: when the whole layer fitted this chunk, the prefetch
+    // rule follows at once, with R minus the chunk's unpinned experts as its
+    // budget; otherwise it runs after the last chunk (empty list here)
+    if (a.hist2) {
+        if (full) {
+            if (lane == 0) a.pfill2[0] = 0;
+        } else {
+            pf_prefetch_run(a, pt.R - cold, r_owner, r_stamp, r_seq, rs);
+        }
+    }
     ring_store(pt, r_owner, r_stamp, r_seq, rs);
     stats_flush(pt, n, rs);
 }
@@ -770,13 +853,24 @@ hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s) {
 
 hipError_t launch_pf_front(const PfArgs& a, hipStream_t s) {
     if (a.T <= 0 || a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE) return hipErrorInvalidValue;
+    const bool predict = a.hist2 != nullptr;
+    if (predict && (!a.wr2 || !a.logits2 || !a.pfill2 || a.layer + 1 >= a.L)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pf_norm_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
-    hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (a.E + 31) / 32), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (predict ? 2 : 1) * ((a.E + 31) / 32)),
+                       dim3(64 * kRouterWaves), 0, s, a);
     hipLaunchKernelGGL(pf_topk_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
     return hipGetLastError();
 }
 
+hipError_t launch_pf_prefetch(const PfArgs& a, hipStream_t s) {
+    if (a.pf_budget < 1 || a.pf_budget > a.pt.R || a.pt.R > kMaxR || !a.hist2 || !a.pfill2 || a.layer + 1 >= a.L)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pf_prefetch_kernel, dim3(1), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_pf_policy_first(const PfArgs& a, hipStream_t s) {
+    if (a.hist2 && (!a.pfill2 || a.layer + 1 >= a.L)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pf_policy_first_kernel, dim3(1), dim3(64), 0, s, a);
     return hipGetLastError();
 }

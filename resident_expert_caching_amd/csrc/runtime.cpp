@@ -166,19 +166,27 @@ struct moe_spark_ctx {
     float* d_pinv = nullptr;        // [Tmax]
     float* d_plog = nullptr;        // [Tmax][E]
     hipEvent_t pf_hist_ev = nullptr;  // prefill: the layer's histogram has reached the host
+    bool pf_prefetch = false;         // prefill: speculative prefetch of the next layer's predicted experts
+    hipEvent_t pf_q_ev = nullptr;     // prefetch list written (compute stream)
+    hipEvent_t pf_done_ev = nullptr;  // prefetch copies landed (side stream)
     int32_t* d_ptopk = nullptr;     // [Tmax][K]
     float* d_pgate = nullptr;       // [Tmax][K]
     int32_t* d_phist = nullptr;     // [E]
+    float* d_plog2 = nullptr;       // [T][E] the next layer's router logits (prefetch prediction)
+    int32_t* d_ppred = nullptr;     // [L][E] predicted assignments of layer l (row 0 stays zero), last prefill
     int32_t* d_pperm = nullptr;     // [Tmax*K]
     int32_t* d_papos = nullptr;     // [Tmax][K]
     int32_t* d_pslot = nullptr;     // [E]
     uint64_t* d_pwait = nullptr;    // [E]
     int32_t* d_pfill = nullptr;     // [1 + 2 kMaxR] the prefill policy's pulled fills
+    int32_t* d_pfill2 = nullptr;    // [1 + 2 kMaxR] the prefetch copies
     uint16_t* d_ph = nullptr;       // [Tmax*K][f/32][64] bf16 hi | lo per Q4_0 block
     float* d_pch = nullptr;         // [Tmax*K][f/32] MFMA start values of those blocks
     float* d_py = nullptr;          // [Tmax*K][d]
     int32_t* d_pmeta = nullptr;     // goff [E+1] | experts [E] | items [2*max_items]
     int32_t* h_pmeta = nullptr;     // pinned staging of the same
+    int32_t* h_pfill2 = nullptr;    // pinned copy of d_pfill2
+    int32_t* h_pfill0 = nullptr;    // pinned copy of d_pfill after the first chunk's policy
     int32_t* h_phist = nullptr;     // pinned [E]
     int64_t pf_max_items = 0;
 
@@ -332,7 +340,9 @@ void agent_loop(moe_spark_ctx* ctx) {
     auto pick = [&](int ring) {
         if (ring_pending[ring] > 0) return ring_stream[ring];
         int best = 0;
-        const int nc = ctx->burst_fills.load(std::memory_order_relaxed) ? kCopyStreams : ctx->n_copy;
+        const int nc = !ctx->copy_x[0] ? 1  // the extra streams exist only without pulled fills
+                       : ctx->burst_fills.load(std::memory_order_relaxed) ? kCopyStreams
+                                                                           : ctx->n_copy;
         for (int i = 1; i < nc && stream_pending[best] > 0; ++i)
             if (stream_pending[i] < stream_pending[best]) best = i;
         return best;
@@ -469,15 +479,19 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok,
                      ctx->d_bx,       ctx->d_brows,  ctx->d_bn,     ctx->d_bpl,     ctx->d_bps,
                      ctx->d_bu16,     ctx->d_bsel,   ctx->d_bpub,   ctx->d_bh16,   ctx->d_pcu,
-                     ctx->d_pch};
+                     ctx->d_pch,      ctx->d_ppred,  ctx->d_pfill2, ctx->d_plog2};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
     if (ctx->h_fifo) hipHostFree(ctx->h_fifo);
     if (ctx->h_ready) hipHostFree(ctx->h_ready);
     if (ctx->h_pmeta) hipHostFree(ctx->h_pmeta);
+    if (ctx->h_pfill2) hipHostFree(ctx->h_pfill2);
+    if (ctx->h_pfill0) hipHostFree(ctx->h_pfill0);
     if (ctx->h_phist) hipHostFree(ctx->h_phist);
     if (ctx->pf_hist_ev) hipEventDestroy(ctx->pf_hist_ev);
+    if (ctx->pf_q_ev) hipEventDestroy(ctx->pf_q_ev);
+    if (ctx->pf_done_ev) hipEventDestroy(ctx->pf_done_ev);
     if (ctx->own_compute && ctx->compute) hipStreamDestroy(ctx->compute);
     if (ctx->own_copy && ctx->copy) hipStreamDestroy(ctx->copy);
     for (hipStream_t st : ctx->copy_x)
@@ -885,9 +899,6 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
             return fail_create(MOE_SPARK_E_HIP, "hipStreamCreate failed");
         ctx->own_copy = true;
     }
-    for (hipStream_t& st : ctx->copy_x)
-        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
-            return fail_create(MOE_SPARK_E_HIP, "hipStreamCreate failed");
     if (hipMalloc((void**)&ctx->d_slots, (size_t)std::max<int64_t>(ctx->n_slots, 1) * ctx->slot_bytes) != hipSuccess) {
         ctx->d_slots = nullptr;
         return fail_create(MOE_SPARK_E_NOMEM, "slot arena allocation failed");
@@ -906,6 +917,13 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
             ctx->pull_fills = true;
         }
     }
+    // The host agent's extra copy streams exist only when it copies fills:
+    // fewer streams leave the copy stream a hardware queue of its own, so
+    // that prefill's prefetch copies on it run beside the compute stream.
+    if (!ctx->pull_fills)
+        for (hipStream_t& st : ctx->copy_x)
+            if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
+                return fail_create(MOE_SPARK_E_HIP, "hipStreamCreate failed");
     const int R = c.ring_slots;
     bool ok = true;
     ok &= dalloc(&ctx->d_router, (size_t)L * E * d) == hipSuccess;
@@ -953,10 +971,15 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_pcu, T * (d / 32)) == hipSuccess;
         ok &= dalloc(&ctx->d_pinv, T) == hipSuccess;
         ok &= dalloc(&ctx->d_plog, T * E) == hipSuccess;
+        ok &= dalloc(&ctx->d_plog2, T * E) == hipSuccess;
         ok &= hipEventCreateWithFlags(&ctx->pf_hist_ev, hipEventDisableTiming) == hipSuccess;
+        ok &= hipEventCreateWithFlags(&ctx->pf_q_ev, hipEventDisableTiming) == hipSuccess;
+        ok &= hipEventCreateWithFlags(&ctx->pf_done_ev, hipEventDisableTiming) == hipSuccess;
+        ok &= dalloc(&ctx->d_pfill2, (size_t)(1 + 2 * kMaxR)) == hipSuccess;
         ok &= dalloc(&ctx->d_ptopk, T * K) == hipSuccess;
         ok &= dalloc(&ctx->d_pgate, T * K) == hipSuccess;
         ok &= dalloc(&ctx->d_phist, (size_t)E) == hipSuccess;
+        ok &= dalloc(&ctx->d_ppred, (size_t)L * E) == hipSuccess;
         ok &= dalloc(&ctx->d_pperm, T * K) == hipSuccess;
         ok &= dalloc(&ctx->d_papos, T * K) == hipSuccess;
         ok &= dalloc(&ctx->d_pslot, (size_t)E) == hipSuccess;
@@ -969,7 +992,11 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_pmeta, meta) == hipSuccess;
         if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "prefill buffer allocation failed");
         if (hipHostMalloc((void**)&ctx->h_pmeta, meta * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
-            hipHostMalloc((void**)&ctx->h_phist, (size_t)E * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
+            hipHostMalloc((void**)&ctx->h_phist, (size_t)E * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+            hipHostMalloc((void**)&ctx->h_pfill0, (size_t)(1 + 2 * kMaxR) * sizeof(int32_t), hipHostMallocDefault) !=
+                hipSuccess ||
+            hipHostMalloc((void**)&ctx->h_pfill2, (size_t)(1 + 2 * kMaxR) * sizeof(int32_t), hipHostMallocDefault) !=
+                hipSuccess)
             return fail_create(MOE_SPARK_E_NOMEM, "prefill staging allocation failed");
     }
     if (hipHostMalloc((void**)&ctx->h_fifo, sizeof(FifoEntry) * kFifoCap, hipHostMallocMapped | hipHostMallocCoherent) !=
@@ -1491,6 +1518,23 @@ struct BurstFills {  // lets the fill agent use every copy stream while a prefil
     ~BurstFills() { ctx->burst_fills.store(0); }
 };
 
+// Copy the slots of a fill list (count, then (layer*E + expert, global slot)
+// pairs, as the prefill policy and prefetch kernels write it) from the host
+// arena by the copy stream's DMA engine.
+static moe_spark_status dma_fill_list(moe_spark_ctx* ctx, const int32_t* list) {
+    const auto& c = ctx->cfg;
+    const int nf = std::min(list[0], c.ring_slots);
+    const int64_t SB = ctx->slot_bytes;
+    for (int j = 0; j < nf; ++j) {
+        const int key = list[1 + 2 * j], slot = list[2 + 2 * j];
+        if (key < 0 || key >= ctx->n_experts_total || slot < c.resident_cap || slot >= ctx->n_slots)
+            return ctx->fail(MOE_SPARK_E_HIP, "a prefill fill list holds an invalid entry");
+        HIPCHK(hipMemcpyAsync(ctx->d_slots + (int64_t)slot * SB, ctx->h_arena + (int64_t)key * SB, SB,
+                              hipMemcpyHostToDevice, ctx->copy));
+    }
+    return MOE_SPARK_OK;
+}
+
 moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_tokens, const int32_t* bias_row) {
     if (!ctx) return MOE_SPARK_E_INVALID;
     const auto& c = ctx->cfg;
@@ -1509,6 +1553,12 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
     int32_t* d_goff = ctx->d_pmeta;
     int32_t* d_experts = d_goff + E + 1;
     int32_t* d_items = d_experts + E;
+    const bool prefetch = ctx->pf_prefetch && ctx->pull_fills && R > 0;
+    HIPCHK(hipMemsetAsync(ctx->d_ppred, 0, sizeof(int32_t) * L * E, ctx->compute));
+    if (prefetch) {  // copies of an earlier call that stopped on an error
+        HIPCHK(hipEventRecord(ctx->pf_done_ev, ctx->copy));
+        HIPCHK(hipStreamWaitEvent(ctx->compute, ctx->pf_done_ev, 0));
+    }
     for (int l = 0; l < L; ++l) {
         PfArgs a{};
         a.x = x;
@@ -1552,13 +1602,33 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         a.tr_cap = ctx->tr_cap;
         a.tr_base = ctx->d_cursors + 1;
         a.spin_limit_ticks = ctx->spin_ticks;
-        // 1. routing of all tokens; the assignment histogram comes back to plan the layer
+        // with prefetch, the routing also predicts the next layer's top-K
+        const bool predict = prefetch && l + 1 < L;
+        if (predict) {
+            a.wr2 = ctx->d_router + (int64_t)(l + 1) * E * c.d_model;
+            a.bias2 = c.n_bias_rows > 0 ? ctx->d_bias + (int64_t)(l + 1) * c.n_bias_rows * E : nullptr;
+            a.logits2 = ctx->d_plog2;
+            a.hist2 = ctx->d_ppred + (int64_t)(l + 1) * E;
+            a.pfill2 = ctx->d_pfill2;
+        }
+        // 1. routing of all tokens; the assignment histogram comes back to
+        //    plan the layer while the first chunk's policy runs (and so its
+        //    fills start).  With prefetch the policy's fill list and the
+        //    prefetch list (when the layer is one chunk) follow, for the
+        //    host to hand to the DMA engine.
         HIPCHK(hipMemsetAsync(ctx->d_phist, 0, sizeof(int32_t) * E, ctx->compute));
         HIPCHK(launch_pf_front(a, ctx->compute));
         HIPCHK(hipMemcpyAsync(ctx->h_phist, ctx->d_phist, sizeof(int32_t) * E, hipMemcpyDeviceToHost, ctx->compute));
         HIPCHK(hipEventRecord(ctx->pf_hist_ev, ctx->compute));
-        // the first chunk's policy (and so its fills) starts while the host plans
         HIPCHK(launch_pf_policy_first(a, ctx->compute));
+        if (prefetch) {
+            HIPCHK(hipMemcpyAsync(ctx->h_pfill0, ctx->d_pfill, sizeof(int32_t) * (1 + 2 * kMaxR),
+                                  hipMemcpyDeviceToHost, ctx->compute));
+            if (predict)
+                HIPCHK(hipMemcpyAsync(ctx->h_pfill2, ctx->d_pfill2, sizeof(int32_t) * (1 + 2 * kMaxR),
+                                      hipMemcpyDeviceToHost, ctx->compute));
+            HIPCHK(hipEventRecord(ctx->pf_q_ev, ctx->compute));
+        }
         HIPCHK(hipEventSynchronize(ctx->pf_hist_ev));
         // 2. plan: groups in expert order; distinct experts ascending, cut into
         //    chunks of at most R cold (non-pinned) experts, so that every
@@ -1567,6 +1637,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         for (int e = 0; e < E; ++e) goff[e + 1] = goff[e] + ctx->h_phist[e];
         struct Chunk {
             int e_begin, e_end, i_begin, i_cold, i_end;  // items [i_begin, i_cold): pinned experts
+            int n_cold;                                  // non-pinned experts
         };
         // Within a chunk the GEMM tiles of pinned experts come first and those
         // of cold experts (in fill order) last, so the matrix cores work while
@@ -1574,7 +1645,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         std::vector<Chunk> chunks;
         std::vector<int> chunk_experts;
         int ne = 0, ni = 0, cold = 0;
-        Chunk cur{0, 0, 0, 0, 0};
+        Chunk cur{0, 0, 0, 0, 0, 0};
         auto close_chunk = [&]() -> bool {
             for (int pass = 0; pass < 2; ++pass) {
                 if (pass == 1) cur.i_cold = ni;
@@ -1591,8 +1662,9 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
             }
             cur.e_end = ne;
             cur.i_end = ni;
+            cur.n_cold = cold;
             if (cur.e_end > cur.e_begin) chunks.push_back(cur);
-            cur = Chunk{ne, ne, ni, ni, ni};
+            cur = Chunk{ne, ne, ni, ni, ni, 0};
             chunk_experts.clear();
             cold = 0;
             return true;
@@ -1611,18 +1683,57 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         HIPCHK(hipMemcpyAsync(d_goff, goff, meta * sizeof(int32_t), hipMemcpyHostToDevice, ctx->compute));
         // 3. sort assignments, run each chunk, combine
         HIPCHK(launch_pf_scatter(a, ctx->compute));
+        // Prefetch: the layer's ring data (this layer's prefetched experts,
+        // copied during the layer before, and the first chunk's fills) come
+        // by DMA on the copy stream; the first launch that touches slot data
+        // waits for them.  After the first layer, the first chunk's fills are
+        // mispredictions (few), so the chunk's pinned and cold experts run in
+        // one launch; the first layer pulls its fills during its pinned
+        // experts' GEMMs.
+        const bool dma_first = prefetch && l > 0;
+        if (prefetch) HIPCHK(hipEventSynchronize(ctx->pf_q_ev));  // the lists are on the host
+        if (dma_first) {
+            st = dma_fill_list(ctx, ctx->h_pfill0);
+            if (st != MOE_SPARK_OK) return st;
+            HIPCHK(hipEventRecord(ctx->pf_done_ev, ctx->copy));
+            HIPCHK(hipStreamWaitEvent(ctx->compute, ctx->pf_done_ev, 0));
+        }
         // Per chunk: its policy (the first chunk's ran already); the GEMMs of
         // its pinned experts, whose gate/up launch also pulls the chunk's
         // fills; then the GEMMs of its cold experts.  With agent copies the
         // cold experts' work-groups wait for each fill's ready flag.
+        // With prefetch, the next layer's predicted experts go through the
+        // prefetch rule after the layer's last policy run (in the first
+        // policy kernel when the layer is one chunk), taking at most the
+        // R - n_cold ring entries that the last chunk does not use (the least
+        // recently used), so no slot that this layer still reads or fills is
+        // overwritten; the host hands their copies to the DMA engine, which
+        // runs them beside the rest of this layer and the next one's routing.
+        bool late_list = false;
         for (const Chunk& ch : chunks) {
             PfArgs b = a;
             if (&ch != &chunks[0]) {
                 b.pf_experts = d_experts + ch.e_begin;
                 b.n_pf_experts = ch.e_end - ch.e_begin;
                 HIPCHK(launch_pf_policy(b, ctx->compute));
+                const int pf_budget = R - ch.n_cold;
+                if (predict && &ch == &chunks.back() && pf_budget > 0) {
+                    PfArgs q = a;
+                    q.pf_budget = pf_budget;
+                    HIPCHK(launch_pf_prefetch(q, ctx->compute));
+                    HIPCHK(hipMemcpyAsync(ctx->h_pfill2, ctx->d_pfill2, sizeof(int32_t) * (1 + 2 * kMaxR),
+                                          hipMemcpyDeviceToHost, ctx->compute));
+                    HIPCHK(hipEventRecord(ctx->pf_q_ev, ctx->compute));
+                    late_list = true;
+                }
             }
             b.items = d_items + 2 * ch.i_begin;
+            if (dma_first && &ch == &chunks[0]) {
+                b.n_items = ch.i_end - ch.i_begin;
+                b.n_fill_x = 0;
+                HIPCHK(launch_pf_gemms(b, ctx->compute));
+                continue;
+            }
             b.n_items = ch.i_cold - ch.i_begin;
             b.n_fill_x = b.arena ? ctx->pf_fill_cols : 0;
             HIPCHK(launch_pf_gemms(b, ctx->compute));
@@ -1632,6 +1743,14 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
             HIPCHK(launch_pf_gemms(b, ctx->compute));
         }
         HIPCHK(launch_pf_combine(a, ctx->compute));
+        if (predict) {
+            // the layer is queued: the prefetch copies go to the DMA engine
+            if (late_list) HIPCHK(hipEventSynchronize(ctx->pf_q_ev));
+            if (late_list || chunks.size() == 1) {
+                st = dma_fill_list(ctx, ctx->h_pfill2);
+                if (st != MOE_SPARK_OK) return st;
+            }
+        }
     }
     HIPCHK(launch_cursor_add(ctx->d_cursors + 1, T, ctx->compute));  // trace rows continue after the batch
     return MOE_SPARK_OK;
@@ -1651,6 +1770,24 @@ moe_spark_status moe_spark_set_trace(moe_spark_ctx* ctx, float* x_layers, int32_
     return MOE_SPARK_OK;
 }
 
+moe_spark_status moe_spark_set_prefetch(moe_spark_ctx* ctx, int32_t enable) {
+    if (!ctx) return MOE_SPARK_E_INVALID;
+    if (enable && !ctx->pull_fills)
+        return ctx->fail(MOE_SPARK_E_STATE, "prefetch needs fills pulled from the host arena by the kernels");
+    if (enable && ctx->cfg.max_tokens <= 0) return ctx->fail(MOE_SPARK_E_STATE, "prefetch needs max_tokens > 0");
+    ctx->pf_prefetch = enable != 0;
+    return MOE_SPARK_OK;
+}
+
+moe_spark_status moe_spark_get_prefetch_hist(moe_spark_ctx* ctx, int32_t* out) {
+    if (!ctx || !out) return MOE_SPARK_E_INVALID;
+    if (!ctx->d_ppred) return ctx->fail(MOE_SPARK_E_STATE, "prefill is not enabled (max_tokens = 0)");
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    HIPCHK(hipMemcpy(out, ctx->d_ppred, sizeof(int32_t) * ctx->cfg.n_layers * ctx->cfg.n_experts,
+                     hipMemcpyDeviceToHost));
+    return MOE_SPARK_OK;
+}
+
 moe_spark_status moe_spark_get_stats(moe_spark_ctx* ctx, moe_spark_stats* out) {
     if (!ctx || !out) return MOE_SPARK_E_INVALID;
     HIPCHK(hipStreamSynchronize(ctx->compute));
@@ -1662,6 +1799,7 @@ moe_spark_status moe_spark_get_stats(moe_spark_ctx* ctx, moe_spark_stats* out) {
     out->ring_hits = s[DS_RING];
     out->fills = s[DS_FILL];
     out->evictions = s[DS_EVICT];
+    out->prefetches = s[DS_PREF];
     out->h2d_bytes = s[DS_H2D];
     out->fill_ns_sum = ctx->fill_ns_sum.load();
     out->fill_ns_max = ctx->fill_ns_max.load();

@@ -73,15 +73,16 @@ def events(ctx):
     n = ms.moe_spark_get_events(ctx, None, 0)
     arr = (ms.Event * max(n, 1))()
     ms.moe_spark_get_events(ctx, arr, n)
-    return [(e.seq, e.layer, e.expert, e.slot, e.victim) for e in arr[:n]]
+    return [(e.seq, e.layer, e.expert, e.slot, e.kind, e.victim) for e in arr[:n]]
 
 
 def sim_events(sim):
-    return [(int(e["seq"]), int(e["layer"]), int(e["expert"]), int(e["slot"]), int(e["victim"]))
-            for e in sim.events()]
+    return [(int(e["seq"]), int(e["layer"]), int(e["expert"]), int(e["slot"]), int(e["kind"]),
+             int(e["victim"])) for e in sim.events()]
 
 
-STAT_KEYS = ("accesses", "pinned_hits", "cold_hits", "ring_hits", "fills", "evictions", "h2d_bytes")
+STAT_KEYS = ("accesses", "pinned_hits", "cold_hits", "ring_hits", "fills", "evictions", "h2d_bytes",
+             "prefetches")
 
 
 def assert_outputs_close(got, ref, what):

@@ -222,8 +222,10 @@ def test_batched_decode_full_stack_16_tokens(stack_model):
     _check_layer_samples(model, trx, trk, x_final, rows, None, samples, 2e-3, "batched decode")
 
 
-def test_prefill_full_stack_popularity_shift(stack_model):
-    model = stack_model
+def _prefill_full(model, prefetch):
+    """The 2048-token prefill through the 40-layer stack at 60% residency with
+    a 32-slot ring, after calibration from the decode warm-up under router
+    bias row A; the batch switches to row B at token 1024."""
     w = model.w
     wp = wl.prefill(40)
     biases = [wp.bias_rows(l) for l in range(w.L)]
@@ -244,6 +246,7 @@ def test_prefill_full_stack_popularity_shift(stack_model):
                                     np.ascontiguousarray(biases[l]).ctypes.data)
         ms.moe_spark_set_experts(ctx, 0, LE, model.blob.ctypes.data)
         ms.moe_spark_place_uniform(ctx)
+        ms.moe_spark_set_prefetch(ctx, prefetch)
         cap = WARM + T
         tr_x = torch.zeros((cap, w.L, w.d), dtype=torch.float32, device="cuda")
         tr_k = torch.zeros((cap, w.L, w.K), dtype=torch.int32, device="cuda")
@@ -258,34 +261,85 @@ def test_prefill_full_stack_popularity_shift(stack_model):
         ms.moe_spark_reset_stats(ctx)
         xd = torch.from_numpy(X.copy()).cuda()
         rd = torch.from_numpy(rows).cuda()
-        print("prefill: 2048 tokens through 40 layers", flush=True)
+        print(f"prefill: 2048 tokens through 40 layers, prefetch={prefetch}", flush=True)
         ms.moe_spark_prefill(ctx, xd.data_ptr(), T, rd.data_ptr())
         ms.moe_spark_synchronize(ctx)
-        st = ms.moe_spark_get_stats(ctx)
-        ev = events(ctx)
-        pl = placement(ctx, w, R)
-        slot_bytes = ms.moe_spark_slot_bytes(ctx)
-        trx, trk = tr_x.cpu().numpy(), tr_k.cpu().numpy()
-        x_out = xd.cpu().numpy()
+        pred = np.zeros((w.L, w.E), np.int32)
+        ms.moe_spark_get_prefetch_hist(ctx, pred.ctypes.data)
+        out = dict(st=ms.moe_spark_get_stats(ctx), ev=events(ctx), pl=placement(ctx, w, R),
+                   slot_bytes=ms.moe_spark_slot_bytes(ctx), trx=tr_x.cpu().numpy(), trk=tr_k.cpu().numpy(),
+                   x_out=xd.cpu().numpy(), pred=pred, P=P, R=R, T=T, rows=rows, biases=biases)
     finally:
         ms.moe_spark_destroy(ctx)
-    print(f"prefill stats {st}", flush=True)
-    assert st["fills"] > 0 and st["evictions"] > 0
-    sim = oracle.Sim(w.L, w.E, P, R, slot_bytes)
+    print(f"prefill stats {out['st']}", flush=True)
+    return out
+
+
+def _prefill_sim(w, r, prefetch):
+    sim = oracle.Sim(w.L, w.E, r["P"], r["R"], r["slot_bytes"])
     sim.place_uniform()
     for t in range(WARM):
-        sim.decode_token(trk[t])
+        sim.decode_token(r["trk"][t])
     sim.calibrate(True)
     sim.reset_stats()
     for l in range(w.L):
-        sim.prefill_layer(l, trk[WARM:, l, :])
+        sim.prefill_layer(l, r["trk"][WARM:, l, :])
+        if prefetch and l + 1 < w.L:
+            sim.prefetch(l + 1, r["pred"][l + 1])
+    return sim
+
+
+def test_prefill_full_stack_popularity_shift(stack_model):
+    model = stack_model
+    w = model.w
+    r = _prefill_full(model, False)
+    st, T, rows, biases = r["st"], r["T"], r["rows"], r["biases"]
+    assert st["fills"] > 0 and st["evictions"] > 0
+    sim = _prefill_sim(w, r, False)
     assert {k: st[k] for k in STAT_KEYS} == sim.stats()
-    assert ev == sim_events(sim)
-    for got, ref in zip(pl, sim.placement()):
+    assert r["ev"] == sim_events(sim)
+    for got, ref in zip(r["pl"], sim.placement()):
         assert np.array_equal(got, ref)
-    trx, trk = trx[WARM:], trk[WARM:]
+    trx, trk = r["trx"][WARM:], r["trk"][WARM:]
     rng = np.random.default_rng(11)
     _check_topk_all(model, trx, trk, rows, biases, np.arange(T))
     samples = [(0, 0), (1023, 10), (1024, 10), (2047, 39)] + \
               [(int(t), int(l)) for t, l in zip(rng.integers(0, T, 12), rng.integers(0, w.L, 12))]
-    _check_layer_samples(model, trx, trk, x_out, rows, biases, samples, 2e-3, "prefill")
+    _check_layer_samples(model, trx, trk, r["x_out"], rows, biases, samples, 2e-3, "prefill")
+
+
+def test_prefill_full_stack_prefetch(stack_model):
+    """The same prefill with speculative prefetch: outputs and traces
+    bit-identical to the run without it; counters, fill/prefetch log and
+    placement equal to the simulator replaying the GPU's top-k trace and
+    prediction histograms; the prediction of sampled layers equal to the
+    oracle's (fp64 router on the traced layer input), up to near-ties."""
+    model = stack_model
+    w = model.w
+    off = _prefill_full(model, False)
+    on = _prefill_full(model, True)
+    assert np.array_equal(on["x_out"], off["x_out"])
+    assert np.array_equal(on["trk"], off["trk"])
+    st = on["st"]
+    assert st["prefetches"] > 0 and st["fills"] < off["st"]["fills"]
+    assert st["accesses"] == off["st"]["accesses"]
+    sim = _prefill_sim(w, on, True)
+    assert {k: st[k] for k in STAT_KEYS} == sim.stats()
+    assert on["ev"] == sim_events(sim)
+    for got, ref in zip(on["pl"], sim.placement()):
+        assert np.array_equal(got, ref)
+    trx = on["trx"][WARM:]
+    pred, rows, biases = on["pred"], on["rows"], on["biases"]
+    assert not pred[0].any()
+    for l in (1, 20, 39):
+        lg = oracle.router_logits(trx[:, l - 1], model.routers[l], biases[l], rows)
+        ref = np.zeros(w.E, np.int64)
+        ties = 0
+        for t in range(on["T"]):
+            idx, gap = oracle_topk_and_gap(lg[t], w.K)
+            ref[idx] += 1
+            ties += gap < TIE_GAP
+        diff = np.abs(pred[l].astype(np.int64) - ref).sum()
+        print(f"layer {l}: prediction differs from the oracle's by {diff} assignments, {ties} near-ties",
+              flush=True)
+        assert pred[l].sum() == on["T"] * w.K and diff <= 2 * w.K * ties

@@ -38,22 +38,26 @@ def _workload():
                        seed=2, n_tokens=T, token_stream=4, bias_seeds=(2, 1002))
 
 
-def _run(model, P, R, x, rows):
+def _run(model, P, R, x, rows, prefetch=False):
     w = model.w
     ctx = model.make_ctx(P=P, R=R, max_tokens=T)
     try:
+        if prefetch:
+            ms.moe_spark_set_prefetch(ctx, True)
         tr_x = torch.zeros((T, w.L, w.d), dtype=torch.float32, device="cuda")
         tr_k = torch.zeros((T, w.L, w.K), dtype=torch.int32, device="cuda")
         tr_g = torch.zeros((T, w.L, w.K), dtype=torch.float32, device="cuda")
         ms.moe_spark_set_trace(ctx, tr_x.data_ptr(), tr_k.data_ptr(), tr_g.data_ptr(), T)
         xd = torch.from_numpy(x.copy()).cuda()
         rd = torch.from_numpy(rows).cuda()
-        print(f"prefill L={w.L} E={w.E} T={T}: P={P} R={R}", flush=True)
+        print(f"prefill L={w.L} E={w.E} T={T}: P={P} R={R} prefetch={prefetch}", flush=True)
         ms.moe_spark_prefill(ctx, xd.data_ptr(), T, rd.data_ptr())
         ms.moe_spark_synchronize(ctx)
+        pred = np.full((w.L, w.E), -1, np.int32)
+        ms.moe_spark_get_prefetch_hist(ctx, pred.ctypes.data)
         return dict(x=xd.cpu().numpy(), tr_x=tr_x.cpu().numpy(), tr_k=tr_k.cpu().numpy(),
                     tr_g=tr_g.cpu().numpy(), stats=ms.moe_spark_get_stats(ctx), events=events(ctx),
-                    placement=placement(ctx, w, R), slot_bytes=ms.moe_spark_slot_bytes(ctx))
+                    placement=placement(ctx, w, R), slot_bytes=ms.moe_spark_slot_bytes(ctx), pred=pred)
     finally:
         ms.moe_spark_destroy(ctx)
 
@@ -160,3 +164,92 @@ def test_prefill_fill_columns_do_not_change_results(monkeypatch, cols):
     assert np.array_equal(base["x"], other["x"]) and np.array_equal(base["tr_k"], other["tr_k"])
     assert {k: base["stats"][k] for k in STAT_KEYS} == {k: other["stats"][k] for k in STAT_KEYS}
     assert base["events"] == other["events"]
+
+
+@pytest.mark.parametrize("frac,R", [(0.3, 8), (0.6, 8), (0.3, 16), (0.6, 16), (0.3, 32)])
+def test_prefill_prefetch(frac, R):
+    """Speculative prefetch (moe_spark_set_prefetch): after layer l's routing,
+    layer l+1's router on layer l's input predicts layer l+1's top-K; the
+    predicted experts that are neither pinned nor in the ring are copied while
+    layer l's last chunk computes, at most R minus that chunk's cold experts.
+
+    * outputs, traces and routing counts bit-identical to the run without
+      prefetch (a prefetch never changes what is computed, nor counts as an
+      access);
+    * the prediction histograms equal the oracle's (fp64 router on the GPU's
+      traced layer input, top-K, counted per expert), up to 2K per token whose
+      oracle K-th/(K+1)-th logits are a near-tie;
+    * counters, fill/prefetch log (with event kinds) and placement equal to
+      the simulator replaying the GPU's top-k trace and its prediction
+      histograms; some prefetches happen and some become ring hits."""
+    w = _workload()
+    model = Model(w)
+    x = w.tokens(0, T)
+    rows = (np.arange(T) >= T // 2).astype(np.int32)
+    P = int(round(frac * w.L * w.E))
+    # several chunks per layer (prefetch after the last chunk's policy) at
+    # R = 8 and (0.3, 16); one chunk (prefetch inside the first policy run,
+    # first-chunk fills by DMA, one launch per layer) at (0.6, 16), (0.3, 32)
+    off = _run(model, P, R, x, rows)
+    on = _run(model, P, R, x, rows, prefetch=True)
+    print(f"P={P} R={R}: off {off['stats']}\n  on {on['stats']}", flush=True)
+    assert np.array_equal(on["x"], off["x"])
+    assert np.array_equal(on["tr_k"], off["tr_k"]) and np.array_equal(on["tr_g"], off["tr_g"])
+    assert np.array_equal(on["placement"][3], off["placement"][3])  # routing counts
+    assert not off["pred"].any()
+
+    # prediction histograms against the oracle
+    pred = on["pred"]
+    assert not pred[0].any()
+    for l in range(1, w.L):
+        lg = oracle.router_logits(on["tr_x"][:, l - 1], model.routers[l], model.biases[l], rows)
+        ref = np.zeros(w.E, np.int64)
+        ties = 0
+        for t in range(T):
+            idx, gap = oracle_topk_and_gap(lg[t], w.K)
+            ref[idx] += 1
+            ties += gap < TIE_GAP
+        diff = np.abs(pred[l].astype(np.int64) - ref).sum()
+        assert pred[l].sum() == T * w.K
+        assert diff <= 2 * w.K * ties, (l, diff, ties)
+
+    # bookkeeping against the simulator
+    sim = oracle.Sim(w.L, w.E, P, R, on["slot_bytes"])
+    sim.place_uniform()
+    for l in range(w.L):
+        sim.prefill_layer(l, on["tr_k"][:, l, :])
+        if l + 1 < w.L:
+            sim.prefetch(l + 1, pred[l + 1])
+    assert {k: on["stats"][k] for k in STAT_KEYS} == sim.stats(), (on["stats"], sim.stats())
+    assert on["events"] == sim_events(sim)
+    for a, b in zip(on["placement"], sim.placement()):
+        assert np.array_equal(a, b)
+    assert on["stats"]["prefetches"] > 0
+    assert on["stats"]["ring_hits"] > off["stats"]["ring_hits"]
+    assert on["stats"]["accesses"] == off["stats"]["accesses"]
+    kinds = [e[4] for e in on["events"]]
+    assert kinds.count(oracle.EV_PREFETCH) == on["stats"]["prefetches"]
+
+
+def test_prefill_prefetch_needs_pulled_fills(monkeypatch):
+    """moe_spark_set_prefetch is refused (E_STATE) when the host agent copies
+    the fills (MOE_SPARK_PULL_FILLS=0 at context creation) and accepted,
+    on and off, otherwise."""
+    w = _workload()
+    model = Model(w)
+    P = int(round(0.3 * w.L * w.E))
+    ctx = model.make_ctx(P=P, R=8, max_tokens=T)
+    try:
+        ms.moe_spark_set_prefetch(ctx, True)
+        ms.moe_spark_set_prefetch(ctx, False)
+    finally:
+        ms.moe_spark_destroy(ctx)
+    monkeypatch.setenv("MOE_SPARK_PULL_FILLS", "0")
+    ctx = model.make_ctx(P=P, R=8, max_tokens=T)
+    try:
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_set_prefetch(ctx, True)
+        assert ei.value.status == ms.E_STATE
+        ms.moe_spark_set_prefetch(ctx, False)
+    finally:
+        ms.moe_spark_destroy(ctx)
