@@ -612,7 +612,7 @@ __device__ __forceinline__ void pf_load(PfLoad& ld, int b, const PfSrc& src) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) ld.a[j] = p[j];
     if (threadIdx.x < kNB) {
-        ld.q = __builtin_nontemporal_load(src.q + src.q_stride * b);
+        ld.q = src.q[src.q_stride * b];  // cached: a 128-byte line serves the row's next blocks too
         ld.sc = __float_as_uint(src.c[b]);
     } else {
         ld.sc = src.s[src.s_stride * b];
