@@ -359,24 +359,47 @@ __device__ __forceinline__ void pf_record(const PfArgs& a, int e, int slot, uint
     if (a.arena && wseq) ++nf;
 }
 
+// A pinned expert's access leaves the ring, its clock and the fill log
+// alone (ring_access only counts it), so the pinned experts of a policy run
+// are recorded lane-parallel; the unpinned ones go through ring_access one
+// by one in ascending id.  Lane `lane` records pinned expert e (is_pinned).
+__device__ __forceinline__ void pf_record_pinned(const PfArgs& a, int e, bool is_pinned, RingState& rs) {
+    if (is_pinned) {
+        a.pslot[e] = a.pt.slot_of[(int64_t)a.layer * a.E + e];
+        a.pwait[e] = 0ull;
+    }
+    rs.n_pin += __popcll(__ballot(is_pinned));
+}
+
 // One wave: the chunk's experts (ascending id) through the placement policy.
 __global__ __launch_bounds__(64) void pf_policy_kernel(PfArgs a) {
     __shared__ int32_t r_owner[kMaxR];
     __shared__ uint64_t r_stamp[kMaxR];
     __shared__ uint64_t r_seq[kMaxR];
     const PolicyTables& pt = a.pt;
+    const int lane = threadIdx.x & 63;
+    const int64_t lbase = (int64_t)a.layer * a.E;
     RingState rs{};
     ring_load(pt, r_owner, r_stamp, r_seq, rs);
     int nf = 0;
-    for (int i = 0; i < a.n_pf_experts; ++i) {
-        const int e = a.pf_experts[i];
-        int slot;
-        uint64_t wseq;
-        ring_access(pt, a.layer, e, pt.slot_of[(int64_t)a.layer * a.E + e], r_owner, r_stamp, r_seq, rs, slot,
-                    wseq);
-        pf_record(a, e, slot, wseq, nf);
+    for (int base = 0; base < a.n_pf_experts; base += 64) {
+        const int i = base + lane;
+        const int e = i < a.n_pf_experts ? a.pf_experts[i] : 0;
+        const bool valid = i < a.n_pf_experts;
+        const bool pinned = valid && pt.slot_of[lbase + e] >= 0;
+        pf_record_pinned(a, e, pinned, rs);
+        uint64_t mc = __ballot(valid && !pinned);
+        while (mc) {
+            const int b = __builtin_ctzll(mc);
+            mc &= mc - 1;
+            const int ex = __shfl(e, b, 64);
+            int slot;
+            uint64_t wseq;
+            ring_access(pt, a.layer, ex, -1, r_owner, r_stamp, r_seq, rs, slot, wseq);
+            pf_record(a, ex, slot, wseq, nf);
+        }
     }
-    if (threadIdx.x == 0) a.pfill[0] = nf;
+    if (lane == 0) a.pfill[0] = nf;
     ring_store(pt, r_owner, r_stamp, r_seq, rs);
     stats_flush(pt, a.n_pf_experts, rs);
 }
@@ -401,23 +424,29 @@ __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
     for (int base = 0; base < E && !full; base += 64) {
         const int e = base + lane;
         const bool used = e < E && a.hist[e] > 0;
-        uint64_t mu = __ballot(used);
-        const uint64_t mc = __ballot(used && pt.slot_of[lbase + e] < 0);
-        while (mu) {
-            const int b = __builtin_ctzll(mu);
-            mu &= mu - 1;
-            const bool is_cold = (mc >> b) & 1ull;
-            if (is_cold && cold == pt.R) {
-                full = true;
-                break;
-            }
-            cold += is_cold;
-            const int ex = base + b;
+        const bool is_cold = used && pt.slot_of[lbase + e] < 0;
+        const uint64_t mc = __ballot(is_cold);
+        // the cut: this group's cold experts up to the one that would be the
+        // (R+1)-th of the chunk; experts from that one on belong to the next chunk
+        int cut = 64;
+        if (cold + __popcll(mc) > pt.R) {
+            uint64_t m = mc;
+            for (int k = 0; k < pt.R - cold; ++k) m &= m - 1;
+            cut = __builtin_ctzll(m);
+            full = true;
+        }
+        const bool in = used && lane < cut;
+        pf_record_pinned(a, e, in && !is_cold, rs);
+        n += __popcll(__ballot(in));
+        uint64_t m = __ballot(in && is_cold);
+        while (m) {
+            const int ex = base + __builtin_ctzll(m);
+            m &= m - 1;
             int slot;
             uint64_t wseq;
-            ring_access(pt, a.layer, ex, pt.slot_of[lbase + ex], r_owner, r_stamp, r_seq, rs, slot, wseq);
+            ring_access(pt, a.layer, ex, -1, r_owner, r_stamp, r_seq, rs, slot, wseq);
             pf_record(a, ex, slot, wseq, nf);
-            ++n;
+            ++cold;
         }
     }
     if (lane == 0) a.pfill[0] = nf;
