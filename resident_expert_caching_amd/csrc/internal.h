@@ -288,12 +288,13 @@ struct PfArgs {
     float* logits;            // [T][E]
     int32_t* topk;            // [T][K]
     float* gates;             // [T][K]
-    int32_t* hist;            // [E] assignments per expert
+    int32_t* hist;            // [E] assignments per expert (zeroed before the routing launches)
     // prediction for the prefetch (all null without it): the next layer's
     // router applied to this layer's input, its top-K counted per expert
     const float* wr2;         // the next layer's packed router
     const float* bias2;       // the next layer's router bias or null
     float* logits2;           // [T][E]
+    int32_t* topk2;           // [T][K] the predicted top-K
     int32_t* hist2;           // [E] predicted assignments per expert of the next layer
     int32_t* pfill2;          // [1 + 2 kMaxR] the prefetch copies: count, then (arena key, slot) pairs
     int32_t pf_budget;        // prefetch launch after the last chunk: copies at most this many

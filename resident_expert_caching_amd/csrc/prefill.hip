@@ -219,8 +219,8 @@ __global__ __launch_bounds__(64 * kRouterWaves) void pf_router_kernel(PfArgs a) 
 
 // ---------------------------------------------------------------- top-k
 
-// Grid T, 256 threads: top-K and gates of one token; routing counts and the
-// assignment histogram (integer atomics: the totals are exact).
+// Grid T, 256 threads: top-K and gates of one token (pf_count_kernel then
+// counts the choices per expert).
 __global__ __launch_bounds__(kPfThreads) void pf_topk_kernel(PfArgs a) {
     const int t = blockIdx.x, tid = threadIdx.x;
     const int E = a.E, K = a.K;
@@ -239,8 +239,6 @@ __global__ __launch_bounds__(kPfThreads) void pf_topk_kernel(PfArgs a) {
         const float g = expf(s_l[tid] - s_l[0]) / z;
         a.topk[(int64_t)t * K + tid] = e;
         a.gates[(int64_t)t * K + tid] = g;
-        atomicAdd(reinterpret_cast<unsigned long long*>(a.pt.counts + (int64_t)a.layer * E + e), 1ull);
-        atomicAdd(a.hist + e, 1);
         const int64_t tt = (int64_t)*a.tr_base + t;
         if (a.tr_topk && tt < a.tr_cap) {
             const int64_t o = (tt * a.L + a.layer) * K + tid;
@@ -250,12 +248,44 @@ __global__ __launch_bounds__(kPfThreads) void pf_topk_kernel(PfArgs a) {
     }
     if (!a.hist2) return;
     // the next layer's top-K from its router on this input: a prediction
-    // that only steers the prefetch (hist2 counts it per expert)
+    // that only steers the prefetch
     __syncthreads();
     for (int e = tid; e < E; e += kPfThreads) lg[e] = a.logits2[(int64_t)t * E + e];
     __syncthreads();
     block_topk(lg, E, K, kpad, cand, s_e, s_l);
-    if (tid < K) atomicAdd(a.hist2 + s_e[tid], 1);
+    if (tid < K) a.topk2[(int64_t)t * K + tid] = s_e[tid];
+}
+
+// Grid ceil(T*K / kCountSlice), 256 threads: each work-group counts its
+// slice of the top-K table per expert in LDS, then adds the non-zero counts
+// to hist (zeroed before the launch) and to the layer's routing counts; with
+// a prediction, the predicted table the same way into hist2.  A popular
+// expert thus gets one global atomic per work-group instead of one per
+// assignment (thousands on one address).
+constexpr int kCountSlice = 2048;
+__global__ __launch_bounds__(kPfThreads) void pf_count_kernel(PfArgs a) {
+    const int tid = threadIdx.x, E = a.E;
+    const int n = a.T * a.K;
+    const int i0 = blockIdx.x * kCountSlice, i1 = min(n, i0 + kCountSlice);
+    __shared__ int h[kMaxE], h2[kMaxE];
+    for (int e = tid; e < E; e += kPfThreads) {
+        h[e] = 0;
+        h2[e] = 0;
+    }
+    __syncthreads();
+    for (int i = i0 + tid; i < i1; i += kPfThreads) {
+        atomicAdd(&h[a.topk[i]], 1);
+        if (a.topk2) atomicAdd(&h2[a.topk2[i]], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kPfThreads) {
+        if (h[e]) {
+            atomicAdd(a.hist + e, h[e]);
+            atomicAdd(reinterpret_cast<unsigned long long*>(a.pt.counts + (int64_t)a.layer * E + e),
+                      (unsigned long long)h[e]);
+        }
+        if (a.topk2 && h2[e]) atomicAdd(a.hist2 + e, h2[e]);
+    }
 }
 
 // ---------------------------------------------------------------- prefetch
@@ -883,11 +913,13 @@ hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s) {
 hipError_t launch_pf_front(const PfArgs& a, hipStream_t s) {
     if (a.T <= 0 || a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE) return hipErrorInvalidValue;
     const bool predict = a.hist2 != nullptr;
-    if (predict && (!a.wr2 || !a.logits2 || !a.pfill2 || a.layer + 1 >= a.L)) return hipErrorInvalidValue;
+    if (predict && (!a.wr2 || !a.logits2 || !a.topk2 || !a.pfill2 || a.layer + 1 >= a.L))
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(pf_norm_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
     hipLaunchKernelGGL(pf_router_kernel, dim3((a.T + 31) / 32, (predict ? 2 : 1) * ((a.E + 31) / 32)),
                        dim3(64 * kRouterWaves), 0, s, a);
     hipLaunchKernelGGL(pf_topk_kernel, dim3(a.T), dim3(kPfThreads), 0, s, a);
+    hipLaunchKernelGGL(pf_count_kernel, dim3((a.T * a.K + kCountSlice - 1) / kCountSlice), dim3(kPfThreads), 0, s, a);
     return hipGetLastError();
 }
 

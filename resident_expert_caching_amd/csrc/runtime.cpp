@@ -173,6 +173,7 @@ struct moe_spark_ctx {
     float* d_pgate = nullptr;       // [Tmax][K]
     int32_t* d_phist = nullptr;     // [E]
     float* d_plog2 = nullptr;       // [T][E] the next layer's router logits (prefetch prediction)
+    int32_t* d_ptopk2 = nullptr;    // [T][K] the next layer's predicted top-K
     int32_t* d_ppred = nullptr;     // [L][E] predicted assignments of layer l (row 0 stays zero), last prefill
     int32_t* d_pperm = nullptr;     // [Tmax*K]
     int32_t* d_papos = nullptr;     // [Tmax][K]
@@ -479,7 +480,7 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok,
                      ctx->d_bx,       ctx->d_brows,  ctx->d_bn,     ctx->d_bpl,     ctx->d_bps,
                      ctx->d_bu16,     ctx->d_bsel,   ctx->d_bpub,   ctx->d_bh16,   ctx->d_pcu,
-                     ctx->d_pch,      ctx->d_ppred,  ctx->d_pfill2, ctx->d_plog2};
+                     ctx->d_pch,      ctx->d_ppred,  ctx->d_pfill2, ctx->d_plog2,  ctx->d_ptopk2};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
@@ -972,6 +973,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_pinv, T) == hipSuccess;
         ok &= dalloc(&ctx->d_plog, T * E) == hipSuccess;
         ok &= dalloc(&ctx->d_plog2, T * E) == hipSuccess;
+        ok &= dalloc(&ctx->d_ptopk2, T * K) == hipSuccess;
         ok &= hipEventCreateWithFlags(&ctx->pf_hist_ev, hipEventDisableTiming) == hipSuccess;
         ok &= hipEventCreateWithFlags(&ctx->pf_q_ev, hipEventDisableTiming) == hipSuccess;
         ok &= hipEventCreateWithFlags(&ctx->pf_done_ev, hipEventDisableTiming) == hipSuccess;
@@ -1608,6 +1610,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
             a.wr2 = ctx->d_router + (int64_t)(l + 1) * E * c.d_model;
             a.bias2 = c.n_bias_rows > 0 ? ctx->d_bias + (int64_t)(l + 1) * c.n_bias_rows * E : nullptr;
             a.logits2 = ctx->d_plog2;
+            a.topk2 = ctx->d_ptopk2;
             a.hist2 = ctx->d_ppred + (int64_t)(l + 1) * E;
             a.pfill2 = ctx->d_pfill2;
         }
