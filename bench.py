@@ -43,7 +43,7 @@ Also:
    replays.
  - `h2d_link`: a pinned host-to-device copy probe of the PCIe link.
  - `cpu_baseline`: the fp64 oracle on a bounded sample of the decode stream,
-   on all host threads and on one.
+   on all host threads and on one, and on 48 tokens of the prefill batch.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -342,9 +342,11 @@ def h2d_probe(torch, mib=256, reps=5):
     return dict(bytes=mib << 20, gbps=round((mib << 20) / best / 1e9, 2))
 
 
-def cpu_baseline(model, tokens, budget_s, single_tokens=1):
+def cpu_baseline(model, tokens, budget_s, single_tokens=1, prefill=None):
     """The fp64 oracle on a bounded sample of the same decode stream: on all
-    host threads (OpenMP) and on one."""
+    host threads (OpenMP) and on one; with prefill = (X, bias rows per layer,
+    token rows, n), also n tokens of the prefill batch through the stack
+    (the oracle's prefill is the same per-token definition)."""
     import oracle
     w = model.w
     experts = [model.experts(l) for l in range(w.L)]
@@ -370,11 +372,24 @@ def cpu_baseline(model, tokens, budget_s, single_tokens=1):
                 break
     except OSError:
         pass
-    return dict(value=round(n / dt, 3), unit="tok/s", cores=threads, kind="oracle",
-                sample=f"{n} decode tokens of the 40-layer stack (fp64, all layers) on {threads} threads, "
-                       f"{dt:.1f} s of CPU work; {n1} token(s) on 1 thread, {dt1:.1f} s",
-                single_thread_tok_s=round(n1 / dt1, 4), cpu_model=model_name,
-                host_cpus=os.cpu_count())
+    out = dict(value=round(n / dt, 3), unit="tok/s", cores=threads, kind="oracle",
+               sample=f"{n} decode tokens of the {w.L}-layer stack (fp64, all layers) on {threads} threads, "
+                      f"{dt:.1f} s of CPU work; {n1} token(s) on 1 thread, {dt1:.1f} s",
+               single_thread_tok_s=round(n1 / dt1, 4), cpu_model=model_name,
+               host_cpus=os.cpu_count())
+    if prefill is not None:
+        X, biases, rows, n_pf = prefill
+        # tokens around the switch of router bias rows, so both rows are used
+        t0 = max(0, X.shape[0] // 2 - n_pf // 2)
+        sl = slice(t0, t0 + n_pf)
+        tp = time.perf_counter()
+        oracle.stack(X[sl].astype(np.float64), model.routers, biases, experts, K=w.K, wfmt=w.wfmt,
+                     bias_row=rows[sl])
+        dtp = time.perf_counter() - tp
+        out["prefill_tok_s"] = round(n_pf / dtp, 3)
+        out["prefill_sample"] = (f"tokens {t0}..{t0 + n_pf - 1} of the {X.shape[0]}-token prefill batch through "
+                                 f"the {w.L}-layer stack on {threads} threads, {dtp:.1f} s")
+    return out
 
 
 def fill_path(ms, torch, model, P, R, calib, meas, row, full_tok_s, pulled_row):
@@ -607,7 +622,12 @@ def main():
         res["copy_probe_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same stream")
-        res["cpu_baseline"] = cpu_baseline(model, stream, args.cpu_budget)
+        wp = wl.prefill(args.layers)
+        Xp = wp.tokens()
+        res["cpu_baseline"] = cpu_baseline(
+            model, stream, args.cpu_budget,
+            prefill=(Xp, [wp.bias_rows(l) for l in range(w.L)],
+                     (np.arange(Xp.shape[0]) >= Xp.shape[0] // 2).astype(np.int32), 48))
     print(json.dumps(res), flush=True)
 
 
