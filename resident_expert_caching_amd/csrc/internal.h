@@ -298,6 +298,12 @@ struct PfArgs {
     int32_t* hist2;           // [E] predicted assignments per expert of the next layer
     int32_t* pfill2;          // [1 + 2 kMaxR] the prefetch copies: count, then (arena key, slot) pairs
     int32_t pf_budget;        // prefetch launch after the last chunk: copies at most this many
+    // mapped host mirror that the first-chunk policy fills for the host
+    // (device address, or null): [0] histogram flag, [1] lists flag, then
+    // hist [E], the fill list [1 + 2 kMaxR], the prefetch list [1 + 2 kMaxR];
+    // a flag takes the value `seq` once what it covers is written
+    int32_t* host_state;
+    int32_t seq;
     const int32_t* goff;      // [E+1] first sorted position of each expert's group
     int32_t* perm;            // [T*K] token of each sorted position
     int32_t* apos;            // [T][K] sorted position of assignment (t, k)

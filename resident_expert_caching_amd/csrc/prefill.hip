@@ -288,6 +288,18 @@ __global__ __launch_bounds__(kPfThreads) void pf_count_kernel(PfArgs a) {
     }
 }
 
+// The host mirror's parts (see PfArgs::host_state).
+__device__ __forceinline__ int32_t* pf_host_hist(const PfArgs& a) { return a.host_state + 2; }
+__device__ __forceinline__ int32_t* pf_host_fills(const PfArgs& a) { return a.host_state + 2 + a.E; }
+__device__ __forceinline__ int32_t* pf_host_prefetch(const PfArgs& a) { return a.host_state + 2 + a.E + 1 + 2 * kMaxR; }
+
+// Publish `seq` in flag f of the host mirror after this wave's earlier
+// stores to it (whole wave calls).
+__device__ __forceinline__ void pf_host_flag(const PfArgs& a, int f) {
+    __threadfence_system();
+    if ((threadIdx.x & 63) == 0) __hip_atomic_store(a.host_state + f, a.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // ---------------------------------------------------------------- prefetch
 
 // The prefetch rule, run by one wave after the layer's last policy run, on
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_count_kernel(PfArgs a) {
 // caller's budget leaves the least-recently-used victims among older ring
 // entries).
 __device__ void pf_prefetch_run(const PfArgs& a, int budget, int32_t* r_owner, uint64_t* r_stamp, uint64_t* r_seq,
-                                RingState& rs) {
+                                RingState& rs, bool host) {
     const PolicyTables& pt = a.pt;
     const int lane = threadIdx.x & 63, layer = a.layer + 1;
     const int64_t lbase = (int64_t)layer * a.E;
@@ -318,12 +330,19 @@ __device__ void pf_prefetch_run(const PfArgs& a, int budget, int32_t* r_owner, u
                 if (lane == 0) {
                     a.pfill2[1 + 2 * nf] = (int32_t)(lbase + ex);
                     a.pfill2[2 + 2 * nf] = slot;
+                    if (a.host_state && host) {
+                        pf_host_prefetch(a)[1 + 2 * nf] = (int32_t)(lbase + ex);
+                        pf_host_prefetch(a)[2 + 2 * nf] = slot;
+                    }
                 }
                 ++nf;
             }
         }
     }
-    if (lane == 0) a.pfill2[0] = nf;
+    if (lane == 0) {
+        a.pfill2[0] = nf;
+        if (a.host_state && host) pf_host_prefetch(a)[0] = nf;
+    }
 }
 
 // One wave: the prefetch rule after a layer's last chunk when the layer took
@@ -335,7 +354,7 @@ __global__ __launch_bounds__(64) void pf_prefetch_kernel(PfArgs a) {
     const PolicyTables& pt = a.pt;
     RingState rs{};
     ring_load(pt, r_owner, r_stamp, r_seq, rs);
-    pf_prefetch_run(a, a.pf_budget, r_owner, r_stamp, r_seq, rs);
+    pf_prefetch_run(a, a.pf_budget, r_owner, r_stamp, r_seq, rs, false);
     ring_store(pt, r_owner, r_stamp, r_seq, rs);
     stats_flush(pt, 0, rs);
 }
@@ -384,6 +403,10 @@ __device__ __forceinline__ void pf_record(const PfArgs& a, int e, int slot, uint
         if (a.arena && wseq && nf < a.pt.R) {
             a.pfill[1 + 2 * nf] = a.layer * a.E + e;
             a.pfill[2 + 2 * nf] = slot;
+            if (a.host_state) {
+                pf_host_fills(a)[1 + 2 * nf] = a.layer * a.E + e;
+                pf_host_fills(a)[2 + 2 * nf] = slot;
+            }
         }
     }
     if (a.arena && wseq) ++nf;
@@ -447,6 +470,10 @@ __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
     const PolicyTables& pt = a.pt;
     const int lane = threadIdx.x, E = a.E;
     const int64_t lbase = (int64_t)a.layer * E;
+    if (a.host_state) {  // the histogram first: the host plans the layer while the policy runs
+        for (int e = lane; e < E; e += 64) pf_host_hist(a)[e] = a.hist[e];
+        pf_host_flag(a, 0);
+    }
     RingState rs{};
     ring_load(pt, r_owner, r_stamp, r_seq, rs);
     int cold = 0, n = 0, nf = 0;
@@ -479,19 +506,26 @@ __global__ __launch_bounds__(64) void pf_policy_first_kernel(PfArgs a) {
             ++cold;
         }
     }
-    if (lane == 0) a.pfill[0] = nf;
+    if (lane == 0) {
+        a.pfill[0] = nf;
+        if (a.host_state) pf_host_fills(a)[0] = nf;
+    }
     // with prediction: when the whole layer fitted this chunk, the prefetch
     // rule follows at once, with R minus the chunk's unpinned experts as its
     // budget; otherwise it runs after the last chunk (empty list here)
     if (a.hist2) {
         if (full) {
-            if (lane == 0) a.pfill2[0] = 0;
+            if (lane == 0) {
+                a.pfill2[0] = 0;
+                if (a.host_state) pf_host_prefetch(a)[0] = 0;
+            }
         } else {
-            pf_prefetch_run(a, pt.R - cold, r_owner, r_stamp, r_seq, rs);
+            pf_prefetch_run(a, pt.R - cold, r_owner, r_stamp, r_seq, rs, true);
         }
     }
     ring_store(pt, r_owner, r_stamp, r_seq, rs);
     stats_flush(pt, n, rs);
+    if (a.host_state) pf_host_flag(a, 1);
 }
 
 // ---------------------------------------------------------------- pulled fills

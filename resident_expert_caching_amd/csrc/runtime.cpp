@@ -14,6 +14,7 @@
 //      layers' kernels once per (x, bias_row) and replays the graph per token;
 //      placement lives in device tables, so the graph never needs recapture.
 #include <hip/hip_runtime.h>
+#include <immintrin.h>
 
 #include <algorithm>
 #include <atomic>
@@ -165,7 +166,6 @@ struct moe_spark_ctx {
     float* d_pcu = nullptr;         // [Tmax][d/32] MFMA start values of those blocks
     float* d_pinv = nullptr;        // [Tmax]
     float* d_plog = nullptr;        // [Tmax][E]
-    hipEvent_t pf_hist_ev = nullptr;  // prefill: the layer's histogram has reached the host
     bool pf_prefetch = false;         // prefill: speculative prefetch of the next layer's predicted experts
     hipEvent_t pf_q_ev = nullptr;     // prefetch list written (compute stream)
     hipEvent_t pf_done_ev = nullptr;  // prefetch copies landed (side stream)
@@ -186,9 +186,12 @@ struct moe_spark_ctx {
     float* d_py = nullptr;          // [Tmax*K][d]
     int32_t* d_pmeta = nullptr;     // goff [E+1] | experts [E] | items [2*max_items]
     int32_t* h_pmeta = nullptr;     // pinned staging of the same
-    int32_t* h_pfill2 = nullptr;    // pinned copy of d_pfill2
-    int32_t* h_pfill0 = nullptr;    // pinned copy of d_pfill after the first chunk's policy
-    int32_t* h_phist = nullptr;     // pinned [E]
+    int32_t* h_pfill2 = nullptr;    // pinned copy of d_pfill2 (prefetch list of a layer of several chunks)
+    // mapped coherent host mirror the first-chunk policy writes (PfArgs::host_state):
+    // [0] histogram flag, [1] lists flag, hist [E], fill list, prefetch list
+    int32_t* h_pstate = nullptr;
+    int32_t* d_pstate = nullptr;    // its device address
+    int32_t pf_seq = 0;             // last flag value
     int64_t pf_max_items = 0;
 
     // host-mapped
@@ -488,9 +491,7 @@ void free_all(moe_spark_ctx* ctx) {
     if (ctx->h_ready) hipHostFree(ctx->h_ready);
     if (ctx->h_pmeta) hipHostFree(ctx->h_pmeta);
     if (ctx->h_pfill2) hipHostFree(ctx->h_pfill2);
-    if (ctx->h_pfill0) hipHostFree(ctx->h_pfill0);
-    if (ctx->h_phist) hipHostFree(ctx->h_phist);
-    if (ctx->pf_hist_ev) hipEventDestroy(ctx->pf_hist_ev);
+    if (ctx->h_pstate) hipHostFree(ctx->h_pstate);
     if (ctx->pf_q_ev) hipEventDestroy(ctx->pf_q_ev);
     if (ctx->pf_done_ev) hipEventDestroy(ctx->pf_done_ev);
     if (ctx->own_compute && ctx->compute) hipStreamDestroy(ctx->compute);
@@ -974,7 +975,6 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_plog, T * E) == hipSuccess;
         ok &= dalloc(&ctx->d_plog2, T * E) == hipSuccess;
         ok &= dalloc(&ctx->d_ptopk2, T * K) == hipSuccess;
-        ok &= hipEventCreateWithFlags(&ctx->pf_hist_ev, hipEventDisableTiming) == hipSuccess;
         ok &= hipEventCreateWithFlags(&ctx->pf_q_ev, hipEventDisableTiming) == hipSuccess;
         ok &= hipEventCreateWithFlags(&ctx->pf_done_ev, hipEventDisableTiming) == hipSuccess;
         ok &= dalloc(&ctx->d_pfill2, (size_t)(1 + 2 * kMaxR)) == hipSuccess;
@@ -993,13 +993,16 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         const size_t meta = (size_t)(2 * E + 1 + 2 * ctx->pf_max_items);
         ok &= dalloc(&ctx->d_pmeta, meta) == hipSuccess;
         if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "prefill buffer allocation failed");
+        const size_t pstate = (size_t)(2 + E + 2 * (1 + 2 * kMaxR));
         if (hipHostMalloc((void**)&ctx->h_pmeta, meta * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
-            hipHostMalloc((void**)&ctx->h_phist, (size_t)E * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
-            hipHostMalloc((void**)&ctx->h_pfill0, (size_t)(1 + 2 * kMaxR) * sizeof(int32_t), hipHostMallocDefault) !=
-                hipSuccess ||
             hipHostMalloc((void**)&ctx->h_pfill2, (size_t)(1 + 2 * kMaxR) * sizeof(int32_t), hipHostMallocDefault) !=
-                hipSuccess)
+                hipSuccess ||
+            hipHostMalloc((void**)&ctx->h_pstate, pstate * sizeof(int32_t),
+                          hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
             return fail_create(MOE_SPARK_E_NOMEM, "prefill staging allocation failed");
+        memset(ctx->h_pstate, 0, pstate * sizeof(int32_t));
+        if (hipHostGetDevicePointer((void**)&ctx->d_pstate, ctx->h_pstate, 0) != hipSuccess || !ctx->d_pstate)
+            return fail_create(MOE_SPARK_E_HIP, "hipHostGetDevicePointer(prefill host state) failed");
     }
     if (hipHostMalloc((void**)&ctx->h_fifo, sizeof(FifoEntry) * kFifoCap, hipHostMallocMapped | hipHostMallocCoherent) !=
             hipSuccess ||
@@ -1520,6 +1523,24 @@ struct BurstFills {  // lets the fill agent use every copy stream while a prefil
     ~BurstFills() { ctx->burst_fills.store(0); }
 };
 
+// Wait until the prefill host mirror's flag f holds seq (written by the
+// first-chunk policy kernel); a device error or 10 s without it fails.
+static moe_spark_status wait_host_flag(moe_spark_ctx* ctx, int f, int32_t seq) {
+    const int64_t t0 = now_ns();
+    for (int polls = 0;; ++polls) {
+        if (__atomic_load_n(ctx->h_pstate + f, __ATOMIC_ACQUIRE) == seq) return MOE_SPARK_OK;
+        if ((polls & 1023) == 1023) {
+            const hipError_t q = hipStreamQuery(ctx->compute);
+            if (q != hipSuccess && q != hipErrorNotReady)
+                return ctx->fail(MOE_SPARK_E_HIP, "prefill: %s", hipGetErrorString(q));
+            if (q == hipSuccess && __atomic_load_n(ctx->h_pstate + f, __ATOMIC_ACQUIRE) != seq)
+                return ctx->fail(MOE_SPARK_E_HIP, "prefill: the policy kernel finished without publishing");
+            if (now_ns() - t0 > 10000000000ll) return ctx->fail(MOE_SPARK_E_HIP, "prefill: policy results timed out");
+        }
+        _mm_pause();
+    }
+}
+
 // Copy the slots of a fill list (count, then (layer*E + expert, global slot)
 // pairs, as the prefill policy and prefetch kernels write it) from the host
 // arena by the copy stream's DMA engine.
@@ -1621,23 +1642,24 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         //    host to hand to the DMA engine.
         HIPCHK(hipMemsetAsync(ctx->d_phist, 0, sizeof(int32_t) * E, ctx->compute));
         HIPCHK(launch_pf_front(a, ctx->compute));
-        HIPCHK(hipMemcpyAsync(ctx->h_phist, ctx->d_phist, sizeof(int32_t) * E, hipMemcpyDeviceToHost, ctx->compute));
-        HIPCHK(hipEventRecord(ctx->pf_hist_ev, ctx->compute));
+        // the first-chunk policy writes the histogram, then its fill list and
+        // the prefetch list, into the mapped host mirror, raising a flag after
+        // each; the host reads them there (no copy on the compute stream)
+        const int32_t seq = ++ctx->pf_seq;
+        a.host_state = ctx->d_pstate;
+        a.seq = seq;
         HIPCHK(launch_pf_policy_first(a, ctx->compute));
-        if (prefetch) {
-            HIPCHK(hipMemcpyAsync(ctx->h_pfill0, ctx->d_pfill, sizeof(int32_t) * (1 + 2 * kMaxR),
-                                  hipMemcpyDeviceToHost, ctx->compute));
-            if (predict)
-                HIPCHK(hipMemcpyAsync(ctx->h_pfill2, ctx->d_pfill2, sizeof(int32_t) * (1 + 2 * kMaxR),
-                                      hipMemcpyDeviceToHost, ctx->compute));
-            HIPCHK(hipEventRecord(ctx->pf_q_ev, ctx->compute));
-        }
-        HIPCHK(hipEventSynchronize(ctx->pf_hist_ev));
+        a.host_state = nullptr;  // no other kernel writes the mirror
+        const int32_t* hist_h = ctx->h_pstate + 2;
+        const int32_t* fills_h = hist_h + E;
+        const int32_t* pref_h = fills_h + 1 + 2 * kMaxR;
+        st = wait_host_flag(ctx, 0, seq);
+        if (st != MOE_SPARK_OK) return st;
         // 2. plan: groups in expert order; distinct experts ascending, cut into
         //    chunks of at most R cold (non-pinned) experts, so that every
         //    expert of a chunk sits in the ring while the chunk computes
         goff[0] = 0;
-        for (int e = 0; e < E; ++e) goff[e + 1] = goff[e] + ctx->h_phist[e];
+        for (int e = 0; e < E; ++e) goff[e + 1] = goff[e] + hist_h[e];
         struct Chunk {
             int e_begin, e_end, i_begin, i_cold, i_end;  // items [i_begin, i_cold): pinned experts
             int n_cold;                                  // non-pinned experts
@@ -1655,7 +1677,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
                 for (int e : chunk_experts) {
                     const bool is_cold = ctx->slot_of[(int64_t)l * E + e] < 0;
                     if (is_cold != (pass == 1)) continue;
-                    for (int m0 = 0; m0 < ctx->h_phist[e]; m0 += 128) {
+                    for (int m0 = 0; m0 < hist_h[e]; m0 += 128) {
                         if (ni >= ctx->pf_max_items) return false;
                         items[2 * ni] = e;
                         items[2 * ni + 1] = m0;
@@ -1673,7 +1695,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
             return true;
         };
         for (int e = 0; e < E; ++e) {
-            if (ctx->h_phist[e] == 0) continue;
+            if (hist_h[e] == 0) continue;
             const bool is_cold = ctx->slot_of[(int64_t)l * E + e] < 0;
             if (is_cold && cold == R && !close_chunk())
                 return ctx->fail(MOE_SPARK_E_STATE, "prefill work list overflow");
@@ -1694,9 +1716,12 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         // one launch; the first layer pulls its fills during its pinned
         // experts' GEMMs.
         const bool dma_first = prefetch && l > 0;
-        if (prefetch) HIPCHK(hipEventSynchronize(ctx->pf_q_ev));  // the lists are on the host
+        if (prefetch) {  // the lists are on the host
+            st = wait_host_flag(ctx, 1, seq);
+            if (st != MOE_SPARK_OK) return st;
+        }
         if (dma_first) {
-            st = dma_fill_list(ctx, ctx->h_pfill0);
+            st = dma_fill_list(ctx, fills_h);
             if (st != MOE_SPARK_OK) return st;
             HIPCHK(hipEventRecord(ctx->pf_done_ev, ctx->copy));
             HIPCHK(hipStreamWaitEvent(ctx->compute, ctx->pf_done_ev, 0));
@@ -1750,7 +1775,7 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
             // the layer is queued: the prefetch copies go to the DMA engine
             if (late_list) HIPCHK(hipEventSynchronize(ctx->pf_q_ev));
             if (late_list || chunks.size() == 1) {
-                st = dma_fill_list(ctx, ctx->h_pfill2);
+                st = dma_fill_list(ctx, late_list ? ctx->h_pfill2 : pref_h);
                 if (st != MOE_SPARK_OK) return st;
             }
         }
