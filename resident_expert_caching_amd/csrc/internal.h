@@ -305,6 +305,11 @@ struct PfArgs {
     int32_t* host_state;
     int32_t seq;
     const int32_t* goff;      // [E+1] first sorted position of each expert's group
+    // the host's plan (goff | experts | items, n_meta ints) in mapped host
+    // memory: the scatter launch reads goff there and copies the whole plan
+    // to the device buffer that goff points into (or null: already there)
+    const int32_t* meta_host;
+    int32_t n_meta;
     int32_t* perm;            // [T*K] token of each sorted position
     int32_t* apos;            // [T][K] sorted position of assignment (t, k)
     const int32_t* items;     // [n_items][2] GEMM work items: (expert, first row of the tile)

@@ -366,9 +366,18 @@ __global__ __launch_bounds__(64) void pf_prefetch_kernel(PfArgs a) {
 __global__ __launch_bounds__(kPfThreads) void pf_scatter_kernel(PfArgs a) {
     const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int K = a.K;
-    if (a.goff[e + 1] == a.goff[e]) return;
+    const int32_t* goff = a.goff;
+    if (a.meta_host) {
+        // the plan comes from mapped host memory: each work-group copies its
+        // share to the device for the GEMM launches, and reads goff there
+        int32_t* dst = const_cast<int32_t*>(a.goff);
+        for (int i = e * kPfThreads + tid; i < a.n_meta; i += gridDim.x * kPfThreads) dst[i] = a.meta_host[i];
+        goff = a.meta_host;
+    }
+    const int g0 = goff[e], g1 = goff[e + 1];
+    if (g1 == g0) return;
     __shared__ int wtot[4];
-    int base = a.goff[e];
+    int base = g0;
     for (int t0 = 0; t0 < a.T; t0 += kPfThreads) {
         const int t = t0 + tid;
         int kk = -1;

@@ -185,7 +185,8 @@ struct moe_spark_ctx {
     float* d_pch = nullptr;         // [Tmax*K][f/32] MFMA start values of those blocks
     float* d_py = nullptr;          // [Tmax*K][d]
     int32_t* d_pmeta = nullptr;     // goff [E+1] | experts [E] | items [2*max_items]
-    int32_t* h_pmeta = nullptr;     // pinned staging of the same
+    int32_t* h_pmeta = nullptr;     // the host's plan, mapped coherent (the scatter launch copies it over)
+    int32_t* dm_pmeta = nullptr;    // its device address
     int32_t* h_pfill2 = nullptr;    // pinned copy of d_pfill2 (prefetch list of a layer of several chunks)
     // mapped coherent host mirror the first-chunk policy writes (PfArgs::host_state):
     // [0] histogram flag, [1] lists flag, hist [E], fill list, prefetch list
@@ -994,15 +995,17 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_pmeta, meta) == hipSuccess;
         if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "prefill buffer allocation failed");
         const size_t pstate = (size_t)(2 + E + 2 * (1 + 2 * kMaxR));
-        if (hipHostMalloc((void**)&ctx->h_pmeta, meta * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+        if (hipHostMalloc((void**)&ctx->h_pmeta, meta * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent) !=
+                hipSuccess ||
             hipHostMalloc((void**)&ctx->h_pfill2, (size_t)(1 + 2 * kMaxR) * sizeof(int32_t), hipHostMallocDefault) !=
                 hipSuccess ||
             hipHostMalloc((void**)&ctx->h_pstate, pstate * sizeof(int32_t),
                           hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess)
             return fail_create(MOE_SPARK_E_NOMEM, "prefill staging allocation failed");
         memset(ctx->h_pstate, 0, pstate * sizeof(int32_t));
-        if (hipHostGetDevicePointer((void**)&ctx->d_pstate, ctx->h_pstate, 0) != hipSuccess || !ctx->d_pstate)
-            return fail_create(MOE_SPARK_E_HIP, "hipHostGetDevicePointer(prefill host state) failed");
+        if (hipHostGetDevicePointer((void**)&ctx->d_pstate, ctx->h_pstate, 0) != hipSuccess || !ctx->d_pstate ||
+            hipHostGetDevicePointer((void**)&ctx->dm_pmeta, ctx->h_pmeta, 0) != hipSuccess || !ctx->dm_pmeta)
+            return fail_create(MOE_SPARK_E_HIP, "hipHostGetDevicePointer(prefill host buffers) failed");
     }
     if (hipHostMalloc((void**)&ctx->h_fifo, sizeof(FifoEntry) * kFifoCap, hipHostMallocMapped | hipHostMallocCoherent) !=
             hipSuccess ||
@@ -1705,9 +1708,14 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         }
         if (!close_chunk()) return ctx->fail(MOE_SPARK_E_STATE, "prefill work list overflow");
         const size_t meta = (size_t)(2 * E + 1) + 2 * (size_t)ni;
-        HIPCHK(hipMemcpyAsync(d_goff, goff, meta * sizeof(int32_t), hipMemcpyHostToDevice, ctx->compute));
-        // 3. sort assignments, run each chunk, combine
-        HIPCHK(launch_pf_scatter(a, ctx->compute));
+        // 3. sort assignments (the launch also copies the plan to the
+        //    device), run each chunk, combine
+        {
+            PfArgs sa = a;
+            sa.meta_host = ctx->dm_pmeta;
+            sa.n_meta = (int32_t)meta;
+            HIPCHK(launch_pf_scatter(sa, ctx->compute));
+        }
         // Prefetch: the layer's ring data (this layer's prefetched experts,
         // copied during the layer before, and the first chunk's fills) come
         // by DMA on the copy stream; the first launch that touches slot data
