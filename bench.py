@@ -144,6 +144,7 @@ def run_decode(ms, torch, model, P, R, calib, untimed, meas, row, calibrate, ker
         if kernel_iters:
             out["us_gateup"], out["us_down"], out["us_route"] = \
                 ms.moe_spark_time_expert_kernels(ctx, kernel_iters)
+            out["us_stream_probe"] = ms.moe_spark_time_stream_probe(ctx, kernel_iters * model.w.L)
         r = rates(st)
         log(f"P={P} calibrated={calibrate}: {out['tok_s']:.1f} tok/s, cold {r['cold_hit_pct']}%, "
             f"fills {st['fills']}")
@@ -544,6 +545,15 @@ def main():
             "avg_launch_us": round(us, 3),
             "timing": f"HIP events on the compute stream around {args.kernel_iters} x {w.L} isolated "
                       f"replays of the kernel with each layer's last selection",
+            "ceiling": {
+                "kernel": "q4_stream_probe_kernel (the gate/up launch's grid and weight loads alone: "
+                          "no routing, no arithmetic)",
+                "bytes_per_launch": GATEUP_BYTES,
+                "avg_launch_us": round(part["us_stream_probe"], 3),
+                "gbps": round(GATEUP_BYTES / (part["us_stream_probe"] * 1e-6) / 1e9, 1),
+                "frac": round(GATEUP_BYTES / (part["us_stream_probe"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                "timing": "HIP events on the compute stream, back-to-back launches",
+            },
             "down_kernel_us": round(part["us_down"], 3),
             "down_kernel_gbps": round(DOWN_BYTES / (part["us_down"] * 1e-6) / 1e9, 1),
             "token_algorithmic_bytes": TOKEN_BYTES_PER_LAYER * w.L,

@@ -416,6 +416,19 @@ moe_spark_status moe_spark_time_expert_kernels(moe_spark_ctx* ctx, int32_t iters
                                                float* us_gateup, float* us_down,
                                                float* us_route);
 
+/* Time a bare streaming read shaped like one batch-1 gate/up launch: the same
+ * grid and the same non-temporal 16-byte loads, over the gate and up rows of
+ * slots 0..top_k-1 (top_k x 1,179,648 B for the target shape), with no
+ * routing and no arithmetic beyond folding the words together; `iters`
+ * back-to-back launches bracketed by HIP events on the compute stream.
+ * Output: microseconds per launch (*us).  This is the ceiling that the
+ * gate/up launch's weight phase runs against on this chip.  Q4_0 only
+ * (E_INVALID otherwise); E_STATE if the context has fewer than top_k slots.
+ * Writes only context scratch.  Call between tokens.
+ * Passage: none of its own (a measurement of the chip, not of the method).
+ */
+moe_spark_status moe_spark_time_stream_probe(moe_spark_ctx* ctx, int32_t iters, float* us);
+
 #ifdef __cplusplus
 }
 #endif

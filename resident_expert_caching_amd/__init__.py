@@ -87,6 +87,7 @@ def _load():
         "moe_spark_time_expert_kernels": (st, [vp, i32, ctypes.POINTER(ctypes.c_float),
                                                ctypes.POINTER(ctypes.c_float),
                                                ctypes.POINTER(ctypes.c_float)]),
+        "moe_spark_time_stream_probe": (st, [vp, i32, ctypes.POINTER(ctypes.c_float)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -217,3 +218,9 @@ def moe_spark_time_expert_kernels(ctx, iters):
     _check(ctx, _lib.moe_spark_time_expert_kernels(ctx, iters, ctypes.byref(a), ctypes.byref(b),
                                                    ctypes.byref(c)))
     return float(a.value), float(b.value), float(c.value)
+
+
+def moe_spark_time_stream_probe(ctx, iters):
+    us = ctypes.c_float()
+    _check(ctx, _lib.moe_spark_time_stream_probe(ctx, iters, ctypes.byref(us)))
+    return float(us.value)

@@ -194,6 +194,8 @@ hipError_t launch_token_end(const TokenIO& io, hipStream_t s);
 hipError_t launch_q4_router_partial(const Q4Args& a, hipStream_t s);
 hipError_t launch_q4_gateup(const Q4Args& a, hipStream_t s);
 hipError_t launch_q4_down(const Q4Args& a, hipStream_t s);
+// slots 0..K-1 read as one gate/up launch reads its experts; out[(f/16) * K]
+hipError_t launch_q4_stream_probe(const uint8_t* slots, int64_t slot_bytes, int32_t K, uint32_t* out, hipStream_t s);
 hipError_t launch_advance(int32_t* cursors, int64_t* stats, hipStream_t s);
 
 // Batched decode (qb_decode.hip): B tokens advance through the stack together,

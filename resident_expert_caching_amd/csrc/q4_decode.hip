@@ -420,6 +420,35 @@ __global__ __launch_bounds__(kThreads) void q4_gateup_kernel(Q4Args a) {
     }
 }
 
+// ---------------------------------------------------------------- streaming probe
+
+// A measurement of the chip, not part of the method: the gate/up launch's
+// grid and weight loads with nothing around them.  Work-group (g, k) reads
+// chunk g of slot k exactly as q4_gateup_kernel's weight phase reads its
+// expert's chunk (eight 1 KiB code lines and one scale line per wave,
+// non-temporal) and folds the words into one per work-group, written to
+// out[k * gridDim.x + g] so that the loads are kept.
+__global__ __launch_bounds__(kThreads) void q4_stream_probe_kernel(const uint8_t* slots, int64_t slot_bytes,
+                                                                   uint32_t* out) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int g = blockIdx.x, k = blockIdx.y;
+    const uint8_t* chunk = slots + (int64_t)k * slot_bytes + (int64_t)g * kGUChunk;
+    const u32x4* cp = reinterpret_cast<const u32x4*>(chunk) + w * 8 * 64 + lane;
+    u32x4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_nontemporal_load(cp + i * 64);
+    const u32x4 sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(chunk + 32768) + w * 64 + lane);
+    uint32_t v = sc.x ^ sc.y ^ sc.z ^ sc.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v ^= c[i].x ^ c[i].y ^ c[i].z ^ c[i].w;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v ^= __shfl_xor(v, o, 64);
+    __shared__ uint32_t red[kThreads / 64];
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    if (t == 0) out[k * gridDim.x + g] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
 // ---------------------------------------------------------------- down + combine + next router partials
 
 // Grid kNP.  Work-group p owns output rows 16p..16p+15.  Thread t: expert rank
@@ -576,6 +605,11 @@ hipError_t launch_q4_router_partial(const Q4Args& a, hipStream_t s) {
 hipError_t launch_q4_gateup(const Q4Args& a, hipStream_t s) {
     if (a.K < 1 || a.K > kQ4MaxK || a.E > kMaxE || a.E < a.K) return hipErrorInvalidValue;
     hipLaunchKernelGGL(q4_gateup_kernel, dim3(kQF / kGURows, a.K), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_stream_probe(const uint8_t* slots, int64_t slot_bytes, int32_t K, uint32_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(q4_stream_probe_kernel, dim3(kQF / kGURows, K), dim3(kThreads), 0, s, slots, slot_bytes, out);
     return hipGetLastError();
 }
 

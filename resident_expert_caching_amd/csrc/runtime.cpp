@@ -1959,4 +1959,30 @@ moe_spark_status moe_spark_time_expert_kernels(moe_spark_ctx* ctx, int32_t iters
     return MOE_SPARK_OK;
 }
 
+moe_spark_status moe_spark_time_stream_probe(moe_spark_ctx* ctx, int32_t iters, float* us) {
+    if (!ctx || iters <= 0 || !us) return MOE_SPARK_E_INVALID;
+    moe_spark_status st = ready_check(ctx);
+    if (st != MOE_SPARK_OK) return st;
+    const auto& c = ctx->cfg;
+    if (c.wfmt != MOE_SPARK_W_Q4_0) return ctx->fail(MOE_SPARK_E_INVALID, "the streaming probe reads Q4_0 slots");
+    if (ctx->n_slots < c.top_k) return ctx->fail(MOE_SPARK_E_STATE, "the streaming probe reads top_k slots");
+    static_assert(kQF / kGURows * kQ4MaxK <= kQD, "probe output fits the scratch row");
+    HIPCHK(hipStreamSynchronize(ctx->compute));
+    hipEvent_t e0, e1;
+    HIPCHK(hipEventCreate(&e0));
+    HIPCHK(hipEventCreate(&e1));
+    uint32_t* out = reinterpret_cast<uint32_t*>(ctx->d_xscratch);
+    HIPCHK(hipEventRecord(e0, ctx->compute));
+    for (int it = 0; it < iters; ++it)
+        HIPCHK(launch_q4_stream_probe(ctx->d_slots, ctx->slot_bytes, c.top_k, out, ctx->compute));
+    HIPCHK(hipEventRecord(e1, ctx->compute));
+    HIPCHK(hipEventSynchronize(e1));
+    float ms = 0;
+    HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    *us = ms * 1000.0f / (float)iters;
+    return MOE_SPARK_OK;
+}
+
 }  // extern "C"

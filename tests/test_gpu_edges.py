@@ -11,7 +11,8 @@ oracle and the placement simulator.
  * error paths: prefill beyond max_tokens, prefill without prefill buffers,
    forward before placement;
  * decode fills pulled by the kernels against fills copied by the host agent;
- * an expert updated after placement while it sits in a ring slot.
+ * an expert updated after placement while it sits in a ring slot;
+ * the measurement calls leave decode's results alone.
 """
 import numpy as np
 import pytest
@@ -255,3 +256,41 @@ def test_expert_update_reaches_ring_copies():
     y_old, _, _ = run(LE, 0)
     assert np.array_equal(y60, y100)
     assert not np.array_equal(y100, y_old), "the updated expert was not used after the update"
+
+
+def test_timing_calls_leave_outputs_alone():
+    """The measurement calls (isolated kernel replays, the streaming probe)
+    return finite positive times and do not change what decode computes; the
+    streaming probe reads Q4_0 slots only."""
+    w = _wl(16, 2, L=2, n_tokens=8)
+    model = Model(w)
+    x = w.tokens(0, 8)
+    row = torch.zeros(8, dtype=torch.int32, device="cuda")
+    outs = []
+    for timed in (False, True):
+        ctx = model.make_ctx(P=16 * 2, R=0)
+        try:
+            xa = torch.from_numpy(x[:4].copy()).cuda()
+            ms.moe_spark_decode(ctx, xa.data_ptr(), 4, row.data_ptr())
+            ms.moe_spark_synchronize(ctx)
+            if timed:
+                times = ms.moe_spark_time_expert_kernels(ctx, 2) + (ms.moe_spark_time_stream_probe(ctx, 4),)
+                assert all(np.isfinite(t) and t > 0 for t in times), times
+                with pytest.raises(ms.MoeSparkError) as ei:
+                    ms.moe_spark_time_stream_probe(ctx, 0)
+                assert ei.value.status == ms.E_INVALID
+            xb = torch.from_numpy(x[4:].copy()).cuda()
+            ms.moe_spark_decode(ctx, xb.data_ptr(), 4, row.data_ptr())
+            ms.moe_spark_synchronize(ctx)
+            outs.append((xa.cpu().numpy(), xb.cpu().numpy()))
+        finally:
+            ms.moe_spark_destroy(ctx)
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    wf = wl.tiny()
+    ctx = Model(wf).make_ctx(P=wf.E, R=0)
+    try:
+        with pytest.raises(ms.MoeSparkError) as ei:
+            ms.moe_spark_time_stream_probe(ctx, 1)
+        assert ei.value.status == ms.E_INVALID
+    finally:
+        ms.moe_spark_destroy(ctx)
