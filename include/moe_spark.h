@@ -41,7 +41,8 @@
  *   MOE_SPARK_PULL_FILLS=0      cold experts are copied by the host fill agent
  *                               on copy streams, not pulled by the kernels
  *                               from the pinned arena's device address (Q4_0)
- *   MOE_SPARK_COPY_STREAMS=1|2  copy streams the agent uses in decode
+ *   MOE_SPARK_COPY_STREAMS=1|2  copy streams the agent spreads decode fills
+ *                               over (default 2)
  *   MOE_SPARK_FILL_COLS=1..128  prefill: grid columns of fill work-groups in
  *                               each pinned-expert GEMM launch (default 8)
  *   MOE_SPARK_DECODE_STREAM=1   decode launches its kernels one by one instead

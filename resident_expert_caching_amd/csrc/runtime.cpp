@@ -217,11 +217,12 @@ struct moe_spark_ctx {
     int64_t tok_launched = 0;
     uint64_t spin_ticks = 0;
     bool stream_decode = false;  // MOE_SPARK_DECODE_STREAM=1: per-kernel launches instead of the token graph
-    // Streams the fill agent may spread a burst of fills over: 1 in decode (a
-    // second queue woken for occasional fills slows the calibrated decode by
-    // about 2%), all kCopyStreams during a prefill, whose fills come in bursts.
-    // MOE_SPARK_COPY_STREAMS=1..kCopyStreams sets the decode figure.
-    int n_copy = 1;
+    // Streams the fill agent may spread a burst of fills over in decode: all
+    // kCopyStreams (a lone fill still takes the first; the calibrated decode
+    // runs the same with one or two, a fill-heavy one 30% faster with two).
+    // Prefill always uses all of them.  MOE_SPARK_COPY_STREAMS=1..kCopyStreams
+    // sets the decode figure.
+    int n_copy = kCopyStreams;
     std::atomic<int> burst_fills{0};
     // prefill with pulled fills: grid columns of fill work-groups in a gate/up
     // launch (x 8 rows); MOE_SPARK_FILL_COLS=1..128 at creation
@@ -334,6 +335,7 @@ void agent_loop(moe_spark_ctx* ctx) {
         hipEvent_t ev;
         int stream;
         int64_t t0;
+        bool flagged;  // the copy stream itself writes the ready flag after the copy
     };
     std::deque<Pending> pend;
     // Stream choice: a ring slot with a copy in flight keeps that copy's
@@ -378,6 +380,10 @@ void agent_loop(moe_spark_ctx* ctx) {
             if (ok)
                 ok = hipMemcpyAsync(ctx->d_slots + (P + ring) * SB, ctx->h_arena + (int64_t)key * SB, SB,
                                     hipMemcpyHostToDevice, st) == hipSuccess;
+            // The ready flag is written by the copy stream right behind the
+            // copy, so the waiting work-groups need not wait for this thread
+            // to see the copy finish; the host writes it only if that fails.
+            const bool flagged = ok && hipStreamWriteValue64(st, ctx->d_ready + ring, fill, 0) == hipSuccess;
             if (ok && ev) ok = hipEventRecord(ev, st) == hipSuccess;
             if (!ok) {
                 ctx->agent_error.store(1);
@@ -386,7 +392,7 @@ void agent_loop(moe_spark_ctx* ctx) {
                 __atomic_store_n(ctx->h_ready + (ring >= 0 && ring < ctx->cfg.ring_slots ? ring : 0), fill,
                                  __ATOMIC_RELEASE);
             } else {
-                pend.push_back({fill, ring, ev, si, t0});
+                pend.push_back({fill, ring, ev, si, t0, flagged});
                 ring_stream[ring] = si;
                 ++ring_pending[ring];
                 ++stream_pending[si];
@@ -403,7 +409,7 @@ void agent_loop(moe_spark_ctx* ctx) {
                 continue;
             }
             if (q != hipSuccess) ctx->agent_error.store(1);
-            __atomic_store_n(ctx->h_ready + it->ring, it->seq, __ATOMIC_RELEASE);
+            if (!it->flagged || q != hipSuccess) __atomic_store_n(ctx->h_ready + it->ring, it->seq, __ATOMIC_RELEASE);
             const int64_t dt = now_ns() - it->t0;
             ctx->fill_ns_sum.fetch_add(dt);
             int64_t m = ctx->fill_ns_max.load();
