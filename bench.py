@@ -30,7 +30,8 @@ Nested in the same line, each on the fixed 512-token measured stream
    under row B with the placement fixed and with online self-tuning.
  - `fill_path`: host-to-device rates of cold fills: the pulled fills'
    effective rate in the fill-bound 60%-uniform arm, and the host agent's
-   copies (MOE_SPARK_PULL_FILLS=0) in the same arm.
+   copies (MOE_SPARK_PULL_FILLS=0) in the same arm; `agent_headline` runs
+   the headline's own protocol and tokens with the agent's copies.
 Also:
  - `prefill`: 2048 tokens through the stack in one batch, 60% residency.
    1. Placement is calibrated from the decode warm-up under permutation A.
@@ -393,6 +394,20 @@ def cpu_baseline(model, tokens, budget_s, single_tokens=1, prefill=None):
     return out
 
 
+def with_agent_fills(fn):
+    """Run fn with contexts created under MOE_SPARK_PULL_FILLS=0: cold fills
+    copied by the host fill agent (hipMemcpyAsync on the copy streams)."""
+    old = os.environ.get("MOE_SPARK_PULL_FILLS")
+    os.environ["MOE_SPARK_PULL_FILLS"] = "0"
+    try:
+        return fn()
+    finally:
+        if old is None:
+            os.environ.pop("MOE_SPARK_PULL_FILLS", None)
+        else:
+            os.environ["MOE_SPARK_PULL_FILLS"] = old
+
+
 def fill_path(ms, torch, model, P, R, calib, meas, row, full_tok_s, pulled_row):
     """Host-to-device rates of cold fills in the fill-bound 60%-uniform arm.
     Pulled fills (the default) have no copy of their own to time: their
@@ -409,15 +424,7 @@ def fill_path(ms, torch, model, P, R, calib, meas, row, full_tok_s, pulled_row):
                              fills_per_token=round(st["fills"] / n, 2),
                              effective_gbps=round(st["h2d_bytes"] / extra / 1e9, 2) if extra > 0 else None,
                              us_per_fill=round(extra * 1e6 / max(st["fills"], 1), 2))
-    old = os.environ.get("MOE_SPARK_PULL_FILLS")
-    os.environ["MOE_SPARK_PULL_FILLS"] = "0"
-    try:
-        r = run_decode(ms, torch, model, P, R, calib, None, meas, row, calibrate=False)
-    finally:
-        if old is None:
-            os.environ.pop("MOE_SPARK_PULL_FILLS", None)
-        else:
-            os.environ["MOE_SPARK_PULL_FILLS"] = old
+    r = with_agent_fills(lambda: run_decode(ms, torch, model, P, R, calib, None, meas, row, calibrate=False))
     st = r["stats"]
     out["agent"] = dict(tokens=meas.shape[0], tok_s=round(r["tok_s"], 2), fills=st["fills"],
                         h2d_bytes=st["h2d_bytes"],
@@ -613,6 +620,15 @@ def main():
             "pulled_effective": res["fill_path"].get("pulled", {}).get("effective_gbps"),
             "agent_copy": res["fill_path"]["agent"]["gbps_per_fill"],
         }
+        # the headline protocol again, with the host agent's copies instead of pulled fills
+        ag = with_agent_fills(lambda: run_decode(ms, torch, model, P, R, calib, untimed, meas, row,
+                                                 calibrate=args.placement == "calibrated"))
+        ra = rates(ag["stats"])
+        res["fill_path"]["agent_headline"] = dict(
+            tok_s=round(ag["tok_s"], 2), ratio_to_pulled=round(ag["tok_s"] / part["tok_s"], 4),
+            fills=ag["stats"]["fills"], cold_hit_pct=ra["cold_hit_pct"],
+            bit_identical_to_pulled=bool(np.array_equal(ag["x_out"], part["x_out"])),
+            note="the headline's protocol and tokens, cold fills copied by the host agent")
     if not args.no_prefill:
         probe = wl.stack(args.layers).tokens(C + n_stream + args.warmup, 256)
         res["prefill"] = run_prefill(ms, torch, model, P, args.ring, calib, probe, args.layers)
