@@ -12,7 +12,8 @@ oracle and the placement simulator.
    forward before placement;
  * decode fills pulled by the kernels against fills copied by the host agent;
  * an expert updated after placement while it sits in a ring slot;
- * the measurement calls leave decode's results alone.
+ * the measurement calls leave decode's results alone;
+ * zero-token calls change nothing.
 """
 import numpy as np
 import pytest
@@ -294,3 +295,38 @@ def test_timing_calls_leave_outputs_alone():
         assert ei.value.status == ms.E_INVALID
     finally:
         ms.moe_spark_destroy(ctx)
+
+
+def test_zero_token_calls_change_nothing():
+    """Empty inputs: decode, layer forward and the no-alloc layer forward
+    with zero tokens leave the buffers, the counters and the placement as
+    they were, and the next real token decodes as in a fresh context."""
+    w = _wl(16, 2, L=2, n_tokens=4)
+    model = Model(w)
+    x = w.tokens(0, 1)
+    outs = []
+    for empty_first in (False, True):
+        ctx = model.make_ctx(P=8, R=4)
+        try:
+            xd = torch.from_numpy(x.copy()).cuda()
+            if empty_first:
+                y = torch.full_like(xd, 7.0)
+                ms.moe_spark_decode(ctx, xd.data_ptr(), 0, None)
+                ms.moe_spark_layer_forward(ctx, 0, xd.data_ptr(), y.data_ptr(), 0, None,
+                                           ms.PRE_RMSNORM | ms.RESIDUAL, None, None)
+                ms.moe_spark_layer_forward_noalloc(ctx, 1, xd.data_ptr(), y.data_ptr(), 0, None,
+                                                   ms.PRE_RMSNORM | ms.RESIDUAL, None, None)
+                ms.moe_spark_synchronize(ctx)
+                assert np.array_equal(xd.cpu().numpy(), x) and bool((y == 7.0).all())
+                st = ms.moe_spark_get_stats(ctx)
+                assert all(st[k] == 0 for k in STAT_KEYS if k in st), st
+            ms.moe_spark_decode(ctx, xd.data_ptr(), 1, None)
+            ms.moe_spark_synchronize(ctx)
+            st = ms.moe_spark_get_stats(ctx)
+            outs.append((xd.cpu().numpy(), {k: st[k] for k in STAT_KEYS}, placement(ctx, w, 4)))
+        finally:
+            ms.moe_spark_destroy(ctx)
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert outs[0][1] == outs[1][1]
+    for a, b in zip(outs[0][2], outs[1][2]):
+        assert np.array_equal(a, b)
