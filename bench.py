@@ -271,8 +271,8 @@ def run_prefill(ms, torch, model, P, R, warm, probe, layers, prefetch=False):
                    h2d_bytes=st["h2d_bytes"], cold_hit_pct=rates(st)["cold_hit_pct"],
                    probe_cold_hit_pct_before_recalibration=before,
                    probe_cold_hit_pct_after_recalibration=after,
-                   arithmetic="Q4_0 codes as exact bf16 (128 + q, zero point in the MFMA start value), "
-                              "activations as bf16 hi + lo, fp32 accumulation, fp16 block scales applied in fp32")
+                   arithmetic="Q4_0 codes as exact fp16 (q - 8), activations rounded once to fp16, "
+                              "fp32 accumulation, fp16 block scales applied in fp32")
         log(f"prefill (prefetch {'on' if prefetch else 'off'}): {out['tok_s']} tok/s, fills {st['fills']}, "
             f"prefetches {st['prefetches']}, cold probe {before}% -> {after}%")
         return out

@@ -311,9 +311,10 @@ moe_spark_status moe_spark_token_forward(moe_spark_ctx* ctx, float* x, const int
  * layers, Q4_0 contexts only.  Per layer: RMSNorm, router GEMM (fp32), exact
  * top-K with the softmax renormalised over the chosen experts, routing counts,
  * a deterministic sort of the (token, rank) assignments by expert, then a
- * grouped expert GEMM on the matrix cores: Q4_0 weights dequantised to bf16,
- * bf16 activations, fp32 accumulation (gate/up with SwiGLU, then down); the
- * rank-order combine adds the result to x.  The layer's distinct experts are
+ * grouped expert GEMM on the matrix cores: the Q4_0 codes as exact fp16
+ * values q - 8, activations rounded once to fp16, fp32 accumulation, each
+ * block's fp16 scale applied to the block's sum in fp32 (gate/up with SwiGLU,
+ * then down); the rank-order combine adds the result to x.  The layer's distinct experts are
  * accessed once each in ascending id; non-pinned ones stream through the
  * spare-slot ring in chunks of at most R, filled as in moe_spark_create
  * describes (pulled during the pinned experts' GEMMs, or agent copies).

@@ -284,8 +284,7 @@ struct PfArgs {
     const float* bias;        // this layer's router bias [n_bias_rows][E] or null
     const int32_t* bias_row;  // [T] or null
     int32_t n_bias_rows;
-    uint16_t* u;              // [T][d/32][64] normalised input per Q4_0 block: bf16 hi, bf16 lo (32 each, operand order)
-    float* cu;                // [T][d/32] per block: -136 * (sum of hi + lo), the MFMA accumulator's start value
+    uint16_t* u;              // [T][d/32][32] normalised input per Q4_0 block, fp16 in operand order
     float* inv;               // [T] 1 / rms
     float* logits;            // [T][E]
     int32_t* topk;            // [T][K]
@@ -323,8 +322,7 @@ struct PfArgs {
     const uint8_t* arena;     // pinned host arena (device address) when the fill kernel pulls fills, else null
     int32_t* pfill;           // [1 + 2 kMaxR]: the last policy run's fill count, then (arena key, slot) pairs
     int32_t n_fill_x;         // gate/up and down launches: leading grid columns that pull those fills (0: none)
-    uint16_t* h;              // [T*K][f/32][64] SwiGLU output per Q4_0 block: bf16 hi, bf16 lo (operand order)
-    float* ch;                // [T*K][f/32] per block: -136 * (sum of hi + lo)
+    uint16_t* h;              // [T*K][f/32][32] SwiGLU output per Q4_0 block, fp16 in operand order
     float* y;                 // [T*K][d] expert outputs
     uint8_t* slots;           // slot arena (written by pulled fills)
     int64_t slot_bytes, P, n_slots;

@@ -2,8 +2,7 @@
 // at a time.
 //
 //   norm     RMSNorm per token; the normalised input for the expert GEMMs
-//            as a pair of bf16 operands (hi + lo, 16 significant bits),
-//            1/rms kept in fp32 for the router.
+//            rounded once to fp16, 1/rms kept in fp32 for the router.
 //   router   logits[t][e] = inv_rms[t] * x[t]·Wr[e] + bias, fp32 MFMA.
 //   topk     exact top-K per token and the softmax renormalised over the
 //            chosen experts ("Luce Spark runs 35B MoE models on 16GB GPU
@@ -25,13 +24,12 @@
 //            matrix cores work; the cold experts' GEMMs follow.  Without a
 //            pull arena the host agent copies them and the GEMMs wait.
 //   gateup   grouped GEMM on the matrix cores: H = silu(U Wg^T) * (U Wu^T)
-//            per expert group.  Each Q4_0 code enters the matrix cores as an
-//            exact bf16 value; v_mfma_f32_16x16x32_bf16 covers one Q4_0 block
-//            per instruction, twice (activation hi, then lo), with fp32
-//            accumulation, and the block's fp16 scale multiplies the block's
-//            sum in fp32.  So no weight is rounded, and activations carry 16
-//            significant bits: the result is the exact-weight product up to
-//            fp32 rounding.
+//            per expert group.  Each Q4_0 code enters the matrix cores as the
+//            exact fp16 value q - 8; v_mfma_f32_16x16x32_f16 covers one Q4_0
+//            block per instruction with fp32 accumulation, and the block's
+//            fp16 scale multiplies the block's sum in fp32.  So no weight is
+//            rounded; each activation is rounded once to fp16, as the batch-1
+//            and batched decode kernels round theirs.
 //   down     grouped GEMM Y = H Wd^T, same scheme.
 //   combine  x[t] += sum_k g[t][k] Y[pos(t,k)] in rank order.
 //
@@ -48,56 +46,51 @@ namespace moe {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kPfThreads = 256;
 constexpr int kBM = 128;       // tokens per GEMM tile
 constexpr int kNB = 128;       // weight rows per GEMM tile
-constexpr int kOpRow = 72;     // bf16 per LDS operand row: hi 32, lo 32, 8 padding (144 B)
 
-// Matrix-core operand order of one Q4_0 block.  v_mfma_f32_16x16x32_bf16
+// Matrix-core operand order of one Q4_0 block.  v_mfma_f32_16x16x32_f16
 // gives lane (i, g) = (lane % 16, lane / 16) eight consecutive k positions
 // 8g..8g+7 of row i of A and of column i of B.  Position 8g + j holds block
-// element op_elem(8g + j) = 4g + {0, 2, 16, 18, 1, 3, 17, 19}[j]: exactly the
+// element op_elem(8g + j) = 4g + {0, 1, 2, 3, 16, 17, 18, 19}[j]: exactly the
 // eight codes of the block's 32-bit code word g (bytes 4g..4g+3; a byte's low
 // nibble is element 4g + byte, its high nibble element 16 + 4g + byte) in the
 // order q4_operand unpacks them.  Activations are stored in the same order,
 // so a lane's A and B values always meet at the same element.
 __device__ __forceinline__ int op_elem(int p) {
     const int g = p >> 3, j = p & 7;
-    return 4 * g + ((j >> 1) & 1) * 16 + (j >> 2) + (j & 1) * 2;
+    return 4 * g + (j & 3) + 16 * (j >> 2);
 }
-__device__ __forceinline__ int op_pos(int e) {
-    const int lo = e & 15, r = lo & 3;
-    return 8 * (lo >> 2) + (r & 1) * 4 + (e >> 4) * 2 + (r >> 1);
+__device__ __forceinline__ int op_pos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e >> 4) + (e & 3); }
+
+// Code word g of a Q4_0 block -> its eight operand values q - 8 as fp16,
+// exact: a byte permute sets each code under the byte 0x64, so each fp16 is
+// 1024 + q (0x6400 is fp16 1024.0, whose last mantissa bits count units), and
+// subtracting 1032 is exact.
+__device__ __forceinline__ u32x4 q4_operand(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    constexpr uint32_t kHi = 0x64646464u, k01 = 0x04010400u, k23 = 0x04030402u;
+    const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t d[4] = {__builtin_amdgcn_perm(kHi, lo, k01), __builtin_amdgcn_perm(kHi, lo, k23),
+                           __builtin_amdgcn_perm(kHi, hi, k01), __builtin_amdgcn_perm(kHi, hi, k23)};
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, d[j]) - off);
+    return v;
 }
 
-// Code word g of a Q4_0 block -> eight bf16 B operand values 128 + q, exact:
-// 0x4300 is bf16 128.0, whose last 4 mantissa bits count units, so OR-ing a
-// code into it gives 128 + q.  The zero point is handled by the accumulator's
-// start value: sum_k a_k (128 + q_k) - 136 sum_k a_k = sum_k a_k (q_k - 8).
-__device__ __forceinline__ bf16x8 q4_operand(uint32_t w) {
-    constexpr uint32_t kM = 0x000F000Fu, kC = 0x43004300u;
-    const u32x4 v = {(w & kM) | kC, ((w >> 4) & kM) | kC, ((w >> 8) & kM) | kC, ((w >> 12) & kM) | kC};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
-__device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi): 16 significant bits
-// in two bf16 operands (hi + lo is exact in fp32).
-__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-    hi = bf16_bits(v);
-    lo = bf16_bits(v - bf16_value(hi));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
 }
 
 // ---------------------------------------------------------------- norm
 
 // Grid T, 256 threads: one token per work-group.  Thread (b, g) = (tid / 4,
 // tid % 4) writes operand positions 8g..8g+7 of Q4_0 block b of the normalised
-// input, as bf16 hi and lo, and the four threads of a block add their hi + lo
-// in a fixed tree for the block's accumulator start value.
+// input, rounded to fp16.
 __global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int b = tid >> 2, g = tid & 3;
@@ -114,27 +107,10 @@ __global__ __launch_bounds__(kPfThreads) void pf_norm_kernel(PfArgs a) {
     const float tot = (part[0] + part[1]) + (part[2] + part[3]);
     const float inv = a.norm ? 1.0f / sqrtf(tot / (float)kQD + a.eps) : 1.0f;
     if (tid == 0) a.inv[t] = inv;
-    // operand order: j = 0..7 -> elements 4g + {0, 2, 16, 18, 1, 3, 17, 19}
-    const float e[8] = {v0.x, v0.z, v1.x, v1.z, v0.y, v0.w, v1.y, v1.w};
-    uint16_t hi[8], lo[8];
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        split_bf16(e[j] * inv, hi[j], lo[j]);
-        s += bf16_value(hi[j]) + bf16_value(lo[j]);
-    }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    uint16_t* dst = a.u + ((int64_t)t * (kQD / 32) + b) * 64 + 8 * g;
-    u32x4 vh, vl;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        vh[j] = (uint32_t)hi[2 * j] | ((uint32_t)hi[2 * j + 1] << 16);
-        vl[j] = (uint32_t)lo[2 * j] | ((uint32_t)lo[2 * j + 1] << 16);
-    }
-    *reinterpret_cast<u32x4*>(dst) = vh;
-    *reinterpret_cast<u32x4*>(dst + 32) = vl;
-    if (g == 0) a.cu[(int64_t)t * (kQD / 32) + b] = -136.0f * s;
+    // operand order: j = 0..7 -> elements 4g + {0, 1, 2, 3, 16, 17, 18, 19}
+    const u32x4 v = {pack_f16x2(v0.x * inv, v0.y * inv), pack_f16x2(v0.z * inv, v0.w * inv),
+                     pack_f16x2(v1.x * inv, v1.y * inv), pack_f16x2(v1.z * inv, v1.w * inv)};
+    *reinterpret_cast<u32x4*>(a.u + ((int64_t)t * (kQD / 32) + b) * 32 + 8 * g) = v;
     const int64_t tt = (int64_t)*a.tr_base + t;
     if (a.tr_x && tt < a.tr_cap) {
         f32x4* tr = reinterpret_cast<f32x4*>(a.tr_x + (tt * a.L + a.layer) * kQD + 32 * b + 4 * g);
@@ -613,61 +589,67 @@ __device__ bool pf_item(const PfArgs& a, int item, int& e, int& pos0, int& rows,
 }
 
 // One Q4_0 block of a grouped-GEMM tile (kBM tokens x kNB weight rows),
-// staged in LDS.  The tile is double-buffered over two of these: while the
-// matrix cores work on block b, the next block's global loads are in flight,
-// and their LDS stores go to the other stage, so one barrier per block
-// suffices.
+// staged in LDS as matrix-core operands.  The tile is double-buffered over
+// two of these: while the matrix cores work on block b, the next block's
+// loads wait in registers, and their LDS stores go to the other stage, so
+// one barrier per block suffices.  The weight codes are converted to fp16
+// once, at the LDS store, so the waves that share them read operands.
+//
+// Operands are kept in fragment order: the 16-byte granule of row r and lane
+// group g (operand positions 8g..8g+7) is granule ((r/16)*4 + g)*16 + slot,
+// slot = (r%16) XOR 12(g/2), so a wave's operand read for 16 rows is one
+// contiguous 1 KiB (in permuted lane order).  Two adjacent threads load the
+// two halves of one row (coalesced global loads); the XOR sends the halves
+// stored by one instruction to other LDS banks than the rows beside them,
+// both when 8 lanes share 32 banks per cycle and when 16 lanes share 64, so
+// no bank is hit twice in a store or a read.
 struct PfStage {
-    uint16_t a[kBM * kOpRow];  // activation rows: hi 32 | lo 32 | pad, operand order
-    uint32_t q[kNB * 4];       // the weight rows' code words (16 B per row)
-    float s[kNB];              // the weight rows' block scales
-    float c[kBM];              // the activation rows' accumulator start values
+    u32x4 a[kBM * 4];  // activation rows, fp16, operand order
+    u32x4 b[kNB * 4];  // weight rows, fp16 q - 8, operand order
+    float s[kNB];      // the weight rows' block scales
 };
+
+__device__ __forceinline__ int pf_granule(int r, int g) {
+    return ((r >> 4) * 4 + g) * 16 + ((r & 15) ^ (12 * (g >> 1)));
+}
+
+// Thread tid's row of the tile and half of that row's operands (positions
+// 16h..16h+15, lane groups 2h and 2h + 1) for the loads and the LDS stores.
+__device__ __forceinline__ int pf_row(int tid) { return tid >> 1; }
+__device__ __forceinline__ int pf_half(int tid) { return tid & 1; }
 
 // Wave (wm, wn) of a 2 x 2 arrangement over the tile: rows wm*64..wm*64+63,
 // the four 16-column groups cols[0..3].  Per 16 x 16 output tile and block:
-// c = start + A_hi B + A_lo B on the matrix cores (B = 128 + q exact, so c is
-// the block's exact-code dot product up to fp32 rounding), then acc += s * c
-// in fp32: the block scale is applied to the block's sum, never rounded into
-// a bf16 weight.
-struct PfAFrag {
-    bf16x8 hi, lo;  // 16 activation rows x 32 k, operand order
-    f32x4 c0;       // their start values
-};
-
-__device__ __forceinline__ PfAFrag pf_afrag(const PfStage& st, int wm, int mi) {
-    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    const uint16_t* row = st.a + (wm * 64 + mi * 16 + li) * kOpRow + 8 * lg;
-    PfAFrag f;
-    f.hi = *reinterpret_cast<const bf16x8*>(row);
-    f.lo = *reinterpret_cast<const bf16x8*>(row + 32);
-    f.c0 = *reinterpret_cast<const f32x4*>(st.c + wm * 64 + mi * 16 + 4 * lg);
-    return f;
+// c = A B on the matrix cores (B = q - 8 exact, so c is the block's
+// exact-code dot product up to fp32 rounding), then acc += s * c in fp32:
+// the block scale is applied to the block's sum, never rounded into a weight.
+__device__ __forceinline__ f16x8 pf_frag(const u32x4* base, int row) {
+    const int lane = threadIdx.x & 63;
+    return __builtin_bit_cast(f16x8, base[pf_granule(row + (lane & 15), lane >> 4)]);
 }
 
 // Software-pipelined over the four 16-row groups: group mi's MFMAs are
 // issued together with group mi-1's scale FMAs and group mi+1's LDS operand
 // reads, so the matrix cores need not wait for the VALU or for LDS.
 __device__ __forceinline__ void pf_mfma_block(const PfStage& st, int wm, const int* cols, f32x4 (&acc)[4][4]) {
-    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    bf16x8 bq[4];
+    const int lane = threadIdx.x & 63, li = lane & 15;
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    f16x8 bq[4];
     float sc[4];
 #pragma unroll
     for (int nj = 0; nj < 4; ++nj) {
-        bq[nj] = q4_operand(st.q[(cols[nj] + li) * 4 + lg]);
+        bq[nj] = pf_frag(st.b, cols[nj]);
         sc[nj] = st.s[cols[nj] + li];
     }
-    PfAFrag f = pf_afrag(st, wm, 0);
+    f16x8 f = pf_frag(st.a, wm * 64);
     f32x4 cp[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-        PfAFrag fn;
-        if (mi + 1 < 4) fn = pf_afrag(st, wm, mi + 1);
+        f16x8 fn;
+        if (mi + 1 < 4) fn = pf_frag(st.a, wm * 64 + (mi + 1) * 16);
         f32x4 c[4];
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) c[nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.hi, bq[nj], f.c0, 0, 0, 0);
-#pragma unroll
-        for (int nj = 0; nj < 4; ++nj) c[nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.lo, bq[nj], c[nj], 0, 0, 0);
+        for (int nj = 0; nj < 4; ++nj) c[nj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f, bq[nj], zero, 0, 0, 0);
         if (mi > 0) {
 #pragma unroll
             for (int nj = 0; nj < 4; ++nj)
@@ -687,70 +669,73 @@ __device__ __forceinline__ void pf_mfma_block(const PfStage& st, int wm, const i
 
 // Registers a thread carries from the global loads of a block to its LDS stores.
 struct PfLoad {
-    u32x4 a[4];
-    u32x4 q;
-    uint32_t sc;  // bits of a token row's fp32 start value (threads 0..127) or of a weight row's fp16
-                  // scale (threads 128..255): converted only at the LDS store, so that nothing waits
-                  // for the loads before the block's matrix-core work has been issued
+    u32x4 a[2];
+    u32x2 q;
+    uint32_t sc;  // bits of a weight row's fp16 scale: converted only at the LDS store, so that
+                  // nothing waits for the loads before the block's matrix-core work has been issued
 };
 
 // A thread's global sources for the blocks of a tile, as block-0 pointers
-// and per-block strides.  Thread tid: activation row tid/2, its hi (even tid)
-// or lo (odd tid) half (64 B); threads 0..127 also the start value of token
-// row tid and the code words of weight row tid, threads 128..255 the fp16
-// scale of weight row tid - 128.  Rows past the group read the group's first
-// row instead: a GEMM output row depends only on its own activation row, and
-// those output rows are never stored.
+// and per-block strides.  Thread tid: activation row pf_row(tid) and weight
+// row pf_row(tid) of the tile, half pf_half(tid) of each (32 B of fp16
+// activations, two code words); threads 0..127 also the fp16 scale of weight
+// row tid (threads 128..255 read row tid - 128's again and store nothing).
+// Rows past the group read the group's first row instead: a GEMM output row
+// depends only on its own activation row, and those output rows are never
+// stored.
 struct PfSrc {
-    const u32x4* a;      // 8 u32x4 per block
-    const float* c;      // 1 per block
-    const u32x4* q;      // q_stride u32x4 per block
+    const u32x4* a;      // 4 u32x4 per block
+    const u32x2* q;      // q_stride u32x2 per block
     const uint16_t* s;   // s_stride halves per block
     int q_stride, s_stride;
 };
 
 __device__ __forceinline__ void pf_load(PfLoad& ld, int b, const PfSrc& src) {
-    const u32x4* p = src.a + 8 * b;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ld.a[j] = p[j];
-    if (threadIdx.x < kNB) {
-        ld.q = src.q[src.q_stride * b];  // cached: a 128-byte line serves the row's next blocks too
-        ld.sc = __float_as_uint(src.c[b]);
-    } else {
-        ld.sc = src.s[src.s_stride * b];
-    }
+    const u32x4* p = src.a + 4 * b;
+    ld.a[0] = p[0];
+    ld.a[1] = p[1];
+    ld.q = src.q[src.q_stride * b];  // cached: a 128-byte line serves the row's next blocks too
+    ld.sc = src.s[src.s_stride * b];  // threads 128..255 load row tid - 128's again: no branch
 }
 
 __device__ __forceinline__ void pf_store(PfStage& st, const PfLoad& ld) {
-    const int tid = threadIdx.x;
-    u32x4* ad = reinterpret_cast<u32x4*>(st.a + (tid >> 1) * kOpRow + (tid & 1) * 32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ad[j] = ld.a[j];
-    if (tid < kNB) {
-        *reinterpret_cast<u32x4*>(st.q + tid * 4) = ld.q;
-        st.c[tid] = __uint_as_float(ld.sc);
-    } else {
-        st.s[tid - kNB] = half_bits_to_float(ld.sc);
-    }
+    const int tid = threadIdx.x, r = pf_row(tid), h = pf_half(tid);
+    const int o0 = pf_granule(r, 2 * h), o1 = pf_granule(r, 2 * h + 1);
+    st.a[o0] = ld.a[0];
+    st.a[o1] = ld.a[1];
+    st.b[o0] = q4_operand(ld.q.x);
+    st.b[o1] = q4_operand(ld.q.y);
+    if (tid < kNB) st.s[tid] = half_bits_to_float(ld.sc);
 }
 
-// The k loop of a tile over nb Q4_0 blocks: block b + 1's global loads are
-// in flight while the matrix cores work on block b, then go to the other LDS
-// stage; one barrier per block.
-__device__ __forceinline__ void pf_tile(PfStage (&st)[2], int nb, const PfSrc& src, int wm, const int* cols,
+// The k loop of a tile over NB Q4_0 blocks, two blocks of loads ahead: while
+// the matrix cores work on block b (in one LDS stage), block b + 1's loads
+// wait in registers for the other stage and block b + 2's are in flight.
+// One barrier per block.  Every load is unconditional (the last blocks'
+// look-ahead re-reads block NB - 1), so the compiler's wait for a block's
+// loads never has to cover the loads issued after them.
+template <int NB>
+__device__ __forceinline__ void pf_tile(PfStage (&st)[2], const PfSrc& src, int wm, const int* cols,
                                         f32x4 (&acc)[4][4]) {
+    static_assert(NB >= 2 && NB % 2 == 0, "the k loop takes the blocks in pairs");
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    PfLoad ld;
-    pf_load(ld, 0, src);
-    pf_store(st[0], ld);
+    PfLoad l0, l1;
+    pf_load(l0, 0, src);
+    pf_load(l1, 1, src);
+    pf_store(st[0], l0);
     __syncthreads();
-    for (int b = 0; b < nb; ++b) {
-        if (b + 1 < nb) pf_load(ld, b + 1, src);
-        pf_mfma_block(st[b & 1], wm, cols, acc);
-        if (b + 1 < nb) pf_store(st[(b + 1) & 1], ld);
+    for (int b = 0; b < NB; b += 2) {
+        // st[0] holds block b; l1 holds block b + 1's loads
+        pf_load(l0, min(b + 2, NB - 1), src);
+        pf_mfma_block(st[0], wm, cols, acc);
+        pf_store(st[1], l1);
+        __syncthreads();
+        pf_load(l1, min(b + 3, NB - 1), src);
+        pf_mfma_block(st[1], wm, cols, acc);
+        pf_store(st[0], l0);
         __syncthreads();
     }
 }
@@ -780,10 +765,9 @@ __device__ __forceinline__ int pf_role(const PfArgs& a, int ncols, int& X, int& 
 // 1-D grid (pf_role), 256 threads.  Work-group tile: kBM tokens of one
 // expert group x (64 gate rows + the same 64 up rows); wave w: token rows
 // (w&1)*64.., gate and up columns (w>>1)*32..; SwiGLU in the epilogue, h
-// written per Q4_0 block of f as bf16 hi and lo in operand order with its
-// start value.  Weight rows come from the slot's gate/up region (chunk
-// g = row/16: codes at ((ww*8 + i)*64 + b)*16, scales at
-// 32768 + (ww*64 + b)*16 + 2i).
+// written per Q4_0 block of f as fp16 in operand order.  Weight rows come
+// from the slot's gate/up region (chunk g = row/16: codes at
+// ((ww*8 + i)*64 + b)*16, scales at 32768 + (ww*64 + b)*16 + 2i).
 __global__ __launch_bounds__(kPfThreads, 2) void pf_gateup_kernel(PfArgs a) {
     constexpr int ncols = kQF / 64;
     int X, Y;
@@ -803,66 +787,59 @@ __global__ __launch_bounds__(kPfThreads, 2) void pf_gateup_kernel(PfArgs a) {
     if (tid < kBM) tok[tid] = tid < rows ? a.perm[pos0 + tid] : -1;
     __syncthreads();
     constexpr int nbd = kQD / 32;
+    const int r2 = pf_row(tid), half = pf_half(tid);
     PfSrc src;
-    const int atok = tok[(tid >> 1) < rows ? tid >> 1 : 0];
-    src.a = reinterpret_cast<const u32x4*>(a.u + (int64_t)atok * nbd * 64 + (tid & 1) * 32);
-    src.c = a.cu + (int64_t)tok[(tid & (kBM - 1)) < rows ? tid & (kBM - 1) : 0] * nbd;
-    // weight row r = tid % 128 of the tile: gate rows n0..n0+63, then the
-    // same up rows; chunk mrow/16 holds it as wave-row (ww, bi)
+    src.a = reinterpret_cast<const u32x4*>(a.u + (int64_t)tok[r2 < rows ? r2 : 0] * nbd * 32) + 2 * half;
+    // weight row r of the tile: gate rows n0..n0+63, then the same up rows;
+    // chunk mrow/16 holds it as wave-row (ww, bi)
     {
-        const int r = tid & (kNB - 1);
+        const int mrow = n0 + (r2 & 63);
+        const int ww = (r2 >= 64 ? 2 : 0) + ((mrow >> 3) & 1), bi = mrow & 7;
+        const uint8_t* ch = S + (int64_t)(mrow >> 4) * kGUChunk;
+        src.q = reinterpret_cast<const u32x2*>(ch + (ww * 8 + bi) * 64 * 16) + half;
+        src.q_stride = 2;
+    }
+    {
+        const int r = tid & (kNB - 1);  // the scale's row (threads 0..127)
         const int mrow = n0 + (r & 63);
         const int ww = (r >= 64 ? 2 : 0) + ((mrow >> 3) & 1), bi = mrow & 7;
         const uint8_t* ch = S + (int64_t)(mrow >> 4) * kGUChunk;
-        src.q = reinterpret_cast<const u32x4*>(ch + (ww * 8 + bi) * 64 * 16);
-        src.q_stride = 1;
         src.s = reinterpret_cast<const uint16_t*>(ch + 32768 + ww * 64 * 16 + bi * 2);
         src.s_stride = 8;
     }
     const int wm = w & 1, wn = w >> 1;
     const int cols[4] = {wn * 32, wn * 32 + 16, 64 + wn * 32, 64 + wn * 32 + 16};
     f32x4 acc[4][4];
-    pf_tile(st, nbd, src, wm, cols, acc);
+    pf_tile<nbd>(st, src, wm, cols, acc);
 
     // Epilogue.  The wave's 32 h columns are one Q4_0 block fb of f: element
     // nj*16 + li of it for nj = 0, 1.  Rows are staged in LDS (the stages are
     // free after the loop's last barrier) in operand order, then written out
-    // 16 bytes per lane; the block's start value sums hi + lo over the 32
-    // elements (per lane, then over the 16 lanes of a row, fixed tree).
+    // 16 bytes per lane.  A staged row takes 40 halves (80 B), so the rows
+    // 4 apart that one store instruction writes fall on distinct LDS banks.
     const int li = lane & 15, lg = lane >> 4;
-    const int fb = Y * 2 + wn;
-    static_assert(2 * kBM * 64 * sizeof(uint16_t) <= 2 * sizeof(PfStage), "h staging fits the stages");
-    uint16_t* stage = reinterpret_cast<uint16_t*>(&st[0]) + wn * kBM * 64;  // [wn][128 rows][64]
+    constexpr int kHRow = 40;
+    static_assert(2 * kBM * kHRow * sizeof(uint16_t) <= 2 * sizeof(PfStage), "h staging fits the stages");
+    uint16_t* stage = reinterpret_cast<uint16_t*>(&st[0]);  // [wn][128 rows][kHRow]
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = wm * 64 + mi * 16 + 4 * lg + r;
-            float sum = 0.0f;
 #pragma unroll
             for (int nj = 0; nj < 2; ++nj) {
                 const float g = acc[mi][nj][r], u = acc[mi][nj + 2][r];
-                uint16_t hi, lo;
-                split_bf16(silu(g) * u, hi, lo);
-                sum += bf16_value(hi) + bf16_value(lo);
-                const int p = op_pos(nj * 16 + li);
-                stage[row * 64 + p] = hi;
-                stage[row * 64 + 32 + p] = lo;
+                stage[(wn * kBM + row) * kHRow + op_pos(nj * 16 + li)] =
+                    __builtin_bit_cast(uint16_t, (_Float16)(silu(g) * u));
             }
-            sum += __shfl_xor(sum, 1, 64);
-            sum += __shfl_xor(sum, 2, 64);
-            sum += __shfl_xor(sum, 4, 64);
-            sum += __shfl_xor(sum, 8, 64);
-            if (li == 0 && row < rows) a.ch[(int64_t)(pos0 + row) * (kQF / 32) + fb] = -136.0f * sum;
         }
     __syncthreads();
-    // 128 rows x 2 blocks x 128 B: thread tid copies 16 B pieces tid, tid + 256, ...
-    for (int i = tid; i < kBM * 2 * 8; i += kPfThreads) {
-        const int row = i >> 4, wb = (i >> 3) & 1, piece = i & 7;
+    // 128 rows x 2 blocks x 64 B: thread tid copies 16 B pieces tid, tid + 256, ...
+    for (int i = tid; i < kBM * 2 * 4; i += kPfThreads) {
+        const int row = i >> 3, wb = (i >> 2) & 1, piece = i & 3;
         if (row < rows) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<uint16_t*>(&st[0]) + wb * kBM * 64 +
-                                                            row * 64 + piece * 8);
-            *reinterpret_cast<u32x4*>(a.h + ((int64_t)(pos0 + row) * (kQF / 32) + Y * 2 + wb) * 64 + piece * 8) = v;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (wb * kBM + row) * kHRow + piece * 8);
+            *reinterpret_cast<u32x4*>(a.h + ((int64_t)(pos0 + row) * (kQF / 32) + Y * 2 + wb) * 32 + piece * 8) = v;
         }
     }
 }
@@ -887,21 +864,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void pf_down_kernel(PfArgs a) {
     if (!pf_item(a, X, e, pos0, rows, S)) return;
     __shared__ __align__(16) PfStage st[2];
     constexpr int nbf = kQF / 32;
+    const int r2 = pf_row(tid), half = pf_half(tid);
     PfSrc src;
-    const int ar = (tid >> 1) < rows ? tid >> 1 : 0, cr = (tid & (kBM - 1)) < rows ? tid & (kBM - 1) : 0;
-    src.a = reinterpret_cast<const u32x4*>(a.h + (int64_t)(pos0 + ar) * nbf * 64 + (tid & 1) * 32);
-    src.c = a.ch + (int64_t)(pos0 + cr) * nbf;
+    src.a = reinterpret_cast<const u32x4*>(a.h + (int64_t)(pos0 + (r2 < rows ? r2 : 0)) * nbf * 32) + 2 * half;
+    src.q = reinterpret_cast<const u32x2*>(S + kGURegion + (int64_t)(n0 + r2) * 256) + half;
+    src.q_stride = 2;
     {
-        const int n = n0 + (tid & (kNB - 1));
-        src.q = reinterpret_cast<const u32x4*>(S + kGURegion + (int64_t)n * 256);
-        src.q_stride = 1;
+        const int n = n0 + (tid & (kNB - 1));  // the scale's row (threads 0..127)
         src.s = reinterpret_cast<const uint16_t*>(S + kGURegion + kDownCodes + (int64_t)(n >> 2) * 128 + (n & 3) * 2);
         src.s_stride = 4;
     }
     const int wm = w & 1, wn = w >> 1;
     const int cols[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
     f32x4 acc[4][4];
-    pf_tile(st, nbf, src, wm, cols, acc);
+    pf_tile<nbf>(st, src, wm, cols, acc);
     const int li = lane & 15, lg = lane >> 4;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)

@@ -162,8 +162,7 @@ struct moe_spark_ctx {
     uint16_t* d_bh16 = nullptr;     // [kMaxBK][f] fp16
 
     // batched prefill (allocated when max_tokens > 0)
-    uint16_t* d_pu = nullptr;       // [Tmax][d/32][64] bf16 hi | lo per Q4_0 block
-    float* d_pcu = nullptr;         // [Tmax][d/32] MFMA start values of those blocks
+    uint16_t* d_pu = nullptr;       // [Tmax][d/32][32] fp16 per Q4_0 block
     float* d_pinv = nullptr;        // [Tmax]
     float* d_plog = nullptr;        // [Tmax][E]
     bool pf_prefetch = false;         // prefill: speculative prefetch of the next layer's predicted experts
@@ -181,8 +180,7 @@ struct moe_spark_ctx {
     uint64_t* d_pwait = nullptr;    // [E]
     int32_t* d_pfill = nullptr;     // [1 + 2 kMaxR] the prefill policy's pulled fills
     int32_t* d_pfill2 = nullptr;    // [1 + 2 kMaxR] the prefetch copies
-    uint16_t* d_ph = nullptr;       // [Tmax*K][f/32][64] bf16 hi | lo per Q4_0 block
-    float* d_pch = nullptr;         // [Tmax*K][f/32] MFMA start values of those blocks
+    uint16_t* d_ph = nullptr;       // [Tmax*K][f/32][32] fp16 per Q4_0 block
     float* d_py = nullptr;          // [Tmax*K][d]
     int32_t* d_pmeta = nullptr;     // goff [E+1] | experts [E] | items [2*max_items]
     int32_t* h_pmeta = nullptr;     // the host's plan, mapped coherent (the scatter launch copies it over)
@@ -489,8 +487,8 @@ void free_all(moe_spark_ctx* ctx) {
                      ctx->d_pperm,    ctx->d_papos,  ctx->d_pslot,  ctx->d_pwait,   ctx->d_pfill,  ctx->d_ph,
                      ctx->d_py,       ctx->d_pmeta,  ctx->d_xbuf,   ctx->d_tokrow,  ctx->d_ntok,
                      ctx->d_bx,       ctx->d_brows,  ctx->d_bn,     ctx->d_bpl,     ctx->d_bps,
-                     ctx->d_bu16,     ctx->d_bsel,   ctx->d_bpub,   ctx->d_bh16,   ctx->d_pcu,
-                     ctx->d_pch,      ctx->d_ppred,  ctx->d_pfill2, ctx->d_plog2,  ctx->d_ptopk2};
+                     ctx->d_bu16,     ctx->d_bsel,   ctx->d_bpub,   ctx->d_bh16,   ctx->d_ppred,
+                     ctx->d_pfill2,   ctx->d_plog2,  ctx->d_ptopk2};
     for (void* p : dptrs)
         if (p) hipFree(p);
     if (ctx->h_arena) hipHostFree(ctx->h_arena);
@@ -976,8 +974,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
     if (c.max_tokens > 0) {
         const size_t T = (size_t)c.max_tokens, K = (size_t)c.top_k;
         ctx->pf_max_items = (int64_t)(T * K / 128 + E + 1);
-        ok &= dalloc(&ctx->d_pu, T * d * 2) == hipSuccess;
-        ok &= dalloc(&ctx->d_pcu, T * (d / 32)) == hipSuccess;
+        ok &= dalloc(&ctx->d_pu, T * d) == hipSuccess;
         ok &= dalloc(&ctx->d_pinv, T) == hipSuccess;
         ok &= dalloc(&ctx->d_plog, T * E) == hipSuccess;
         ok &= dalloc(&ctx->d_plog2, T * E) == hipSuccess;
@@ -994,8 +991,7 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         ok &= dalloc(&ctx->d_pslot, (size_t)E) == hipSuccess;
         ok &= dalloc(&ctx->d_pwait, (size_t)E) == hipSuccess;
         ok &= dalloc(&ctx->d_pfill, (size_t)(1 + 2 * kMaxR)) == hipSuccess;
-        ok &= dalloc(&ctx->d_ph, T * K * f * 2) == hipSuccess;
-        ok &= dalloc(&ctx->d_pch, T * K * (f / 32)) == hipSuccess;
+        ok &= dalloc(&ctx->d_ph, T * K * f) == hipSuccess;
         ok &= dalloc(&ctx->d_py, T * K * d) == hipSuccess;
         const size_t meta = (size_t)(2 * E + 1 + 2 * ctx->pf_max_items);
         ok &= dalloc(&ctx->d_pmeta, meta) == hipSuccess;
@@ -1606,7 +1602,6 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         a.bias_row = bias_row;
         a.n_bias_rows = c.n_bias_rows;
         a.u = ctx->d_pu;
-        a.cu = ctx->d_pcu;
         a.inv = ctx->d_pinv;
         a.logits = ctx->d_plog;
         a.topk = ctx->d_ptopk;
@@ -1620,7 +1615,6 @@ moe_spark_status moe_spark_prefill(moe_spark_ctx* ctx, float* x, int32_t n_token
         a.arena = ctx->pull_fills ? ctx->d_arena : nullptr;  // fills pulled by a kernel, else agent copies
         a.pfill = ctx->d_pfill;
         a.h = ctx->d_ph;
-        a.ch = ctx->d_pch;
         a.y = ctx->d_py;
         a.slots = ctx->d_slots;
         a.slot_bytes = ctx->slot_bytes;
