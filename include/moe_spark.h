@@ -70,7 +70,10 @@ typedef enum {
     MOE_SPARK_W_Q4_0 = 1  /* GGUF Q4_0: per row, blocks of 32 along `in`, 18 bytes each:
                              fp16 scale s (little endian), 16 bytes of codes; weight j in
                              the low nibble of byte j, weight j+16 in the high nibble;
-                             value (q - 8) * s */
+                             value (q - 8) * s.  The Q4_0 paths multiply the codes with
+                             activations rounded to fp16 (the normalised input and the
+                             SwiGLU output), so those must stay inside fp16's range
+                             (|v| <= 65504); fp32 contexts have no such limit. */
 } moe_spark_wfmt;
 
 /* Flags of moe_spark_layer_forward. */
