@@ -144,7 +144,9 @@ typedef struct moe_spark_ctx moe_spark_ctx;
  * neither copy stream may share a hardware queue with the compute stream:
  * keep the process's streams within GPU_MAX_HW_QUEUES (a fill that never
  * starts ends the wait with E_HIP "fill did not arrive in time").
- * Errors: E_INVALID (bad config), E_NOMEM (arena), E_HIP.
+ * Errors: E_INVALID (bad config; for Q4_0 also any shape other than
+ * d_model = 2048, d_ff = 512, top_k <= 8, which the hand-tiled Q4_0 kernels
+ * are built for; fp32 contexts take other shapes), E_NOMEM (arena), E_HIP.
  * Passage: [Spark] "The key components" (1) and (2): the pinned set and the
  * fixed ring of spare GPU slots are the slot arena's P and R slots; [Bagua]
  * "Event Core": the long tail lives in system RAM (the pinned host arena).
