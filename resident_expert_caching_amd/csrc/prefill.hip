@@ -713,9 +713,12 @@ __device__ __forceinline__ void pf_store(PfStage& st, const PfLoad& ld) {
 // wait in registers for the other stage and block b + 2's are in flight.
 // One barrier per block.  Every load is unconditional (the last blocks'
 // look-ahead re-reads block NB - 1), so the compiler's wait for a block's
-// loads never has to cover the loads issued after them.
+// loads never has to cover the loads issued after them.  A wave whose 64
+// token rows all lie past the group's end (`active` false: the tile's last
+// rows are padding) takes part in the loads and barriers but skips the
+// matrix cores and the scale FMAs; its rows are never stored.
 template <int NB>
-__device__ __forceinline__ void pf_tile(PfStage (&st)[2], const PfSrc& src, int wm, const int* cols,
+__device__ __forceinline__ void pf_tile(PfStage (&st)[2], const PfSrc& src, int wm, bool active, const int* cols,
                                         f32x4 (&acc)[4][4]) {
     static_assert(NB >= 2 && NB % 2 == 0, "the k loop takes the blocks in pairs");
 #pragma unroll
@@ -730,11 +733,11 @@ __device__ __forceinline__ void pf_tile(PfStage (&st)[2], const PfSrc& src, int 
     for (int b = 0; b < NB; b += 2) {
         // st[0] holds block b; l1 holds block b + 1's loads
         pf_load(l0, min(b + 2, NB - 1), src);
-        pf_mfma_block(st[0], wm, cols, acc);
+        if (active) pf_mfma_block(st[0], wm, cols, acc);
         pf_store(st[1], l1);
         __syncthreads();
         pf_load(l1, min(b + 3, NB - 1), src);
-        pf_mfma_block(st[1], wm, cols, acc);
+        if (active) pf_mfma_block(st[1], wm, cols, acc);
         pf_store(st[0], l0);
         __syncthreads();
     }
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void pf_gateup_kernel(PfArgs a) {
     const int wm = w & 1, wn = w >> 1;
     const int cols[4] = {wn * 32, wn * 32 + 16, 64 + wn * 32, 64 + wn * 32 + 16};
     f32x4 acc[4][4];
-    pf_tile<nbd>(st, src, wm, cols, acc);
+    pf_tile<nbd>(st, src, wm, wm * 64 < rows, cols, acc);
 
     // Epilogue.  The wave's 32 h columns are one Q4_0 block fb of f: element
     // nj*16 + li of it for nj = 0, 1.  Rows are staged in LDS (the stages are
@@ -886,7 +889,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void pf_down_kernel(PfArgs a) {
     const int wm = w & 1, wn = w >> 1;
     const int cols[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
     f32x4 acc[4][4];
-    pf_tile<nbf>(st, src, wm, cols, acc);
+    pf_tile<nbf>(st, src, wm, wm * 64 < rows, cols, acc);
     const int li = lane & 15, lg = lane >> 4;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
