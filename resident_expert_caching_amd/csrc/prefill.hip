@@ -55,15 +55,12 @@ constexpr int kNB = 128;       // weight rows per GEMM tile
 // Matrix-core operand order of one Q4_0 block.  v_mfma_f32_16x16x32_f16
 // gives lane (i, g) = (lane % 16, lane / 16) eight consecutive k positions
 // 8g..8g+7 of row i of A and of column i of B.  Position 8g + j holds block
-// element op_elem(8g + j) = 4g + {0, 1, 2, 3, 16, 17, 18, 19}[j]: exactly the
+// element 4g + {0, 1, 2, 3, 16, 17, 18, 19}[j]: exactly the
 // eight codes of the block's 32-bit code word g (bytes 4g..4g+3; a byte's low
 // nibble is element 4g + byte, its high nibble element 16 + 4g + byte) in the
 // order q4_operand unpacks them.  Activations are stored in the same order,
-// so a lane's A and B values always meet at the same element.
-__device__ __forceinline__ int op_elem(int p) {
-    const int g = p >> 3, j = p & 7;
-    return 4 * g + (j & 3) + 16 * (j >> 2);
-}
+// so a lane's A and B values always meet at the same element.  op_pos gives
+// the operand position of block element e.
 __device__ __forceinline__ int op_pos(int e) { return 8 * ((e & 15) >> 2) + 4 * (e >> 4) + (e & 3); }
 
 // Code word g of a Q4_0 block -> its eight operand values q - 8 as fp16,
