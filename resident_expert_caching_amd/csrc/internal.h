@@ -354,6 +354,7 @@ hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s);  // rank-order com
 // copies, listed in a.pfill2
 hipError_t launch_pf_prefetch(const PfArgs& a, hipStream_t s);
 hipError_t launch_cursor_add(int32_t* cursor, int32_t n, hipStream_t s);
+hipError_t prepare_pf_kernels();  // resolve the prefill kernels before their first launch
 
 // Launchers (kernels.hip).
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

@@ -990,4 +990,27 @@ hipError_t launch_pf_combine(const PfArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t prepare_pf_kernels() {
+    // Querying each kernel's attributes makes the runtime resolve it now, at
+    // context creation, rather than on its first launch inside a prefill.
+    const void* fns[] = {reinterpret_cast<const void*>(pf_norm_kernel),
+                         reinterpret_cast<const void*>(pf_router_kernel),
+                         reinterpret_cast<const void*>(pf_topk_kernel),
+                         reinterpret_cast<const void*>(pf_count_kernel),
+                         reinterpret_cast<const void*>(pf_prefetch_kernel),
+                         reinterpret_cast<const void*>(pf_scatter_kernel),
+                         reinterpret_cast<const void*>(pf_policy_kernel),
+                         reinterpret_cast<const void*>(pf_policy_first_kernel),
+                         reinterpret_cast<const void*>(pf_gateup_kernel),
+                         reinterpret_cast<const void*>(pf_down_kernel),
+                         reinterpret_cast<const void*>(pf_combine_kernel),
+                         reinterpret_cast<const void*>(cursor_add_kernel)};
+    for (const void* f : fns) {
+        hipFuncAttributes at;
+        const hipError_t e = hipFuncGetAttributes(&at, f);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace moe

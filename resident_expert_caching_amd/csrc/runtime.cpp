@@ -996,6 +996,8 @@ moe_spark_status moe_spark_create(const moe_spark_config* cfg, void* compute_str
         const size_t meta = (size_t)(2 * E + 1 + 2 * ctx->pf_max_items);
         ok &= dalloc(&ctx->d_pmeta, meta) == hipSuccess;
         if (!ok) return fail_create(MOE_SPARK_E_NOMEM, "prefill buffer allocation failed");
+        if (c.wfmt == MOE_SPARK_W_Q4_0 && prepare_pf_kernels() != hipSuccess)
+            return fail_create(MOE_SPARK_E_HIP, "prefill kernels could not be prepared");
         const size_t pstate = (size_t)(2 + E + 2 * (1 + 2 * kMaxR));
         if (hipHostMalloc((void**)&ctx->h_pmeta, meta * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent) !=
                 hipSuccess ||
